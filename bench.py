@@ -1,0 +1,200 @@
+"""Benchmark one routed-MoE step (route -> bucket -> expert FFN) on one MI355X.
+
+A step is one pass of the whole path over one batch: moe_route_topk,
+moe_bucket_routes and moe_expert_ffn, captured together in one HIP graph.
+The default workload is the decode verify step: T=4 tokens, H=2048, I=512,
+E=512 experts, top-10, NVFP4 experts, bf16 activations.
+
+Cache control: NB weight banks (expert e of bank b is expert e-67b of bank 0,
+at distinct addresses) with NB activation/routing sets, one graph per bank,
+replayed round-robin, so no expert's bytes are re-read within ~NB steps of
+traffic (the 256 MB MALL would otherwise hold a step's ~69 MB).
+
+Output: one JSON line.  `value` is the effective HBM bandwidth on unique
+expert bytes (unique experts of the step x 1,769,484 B) divided by the
+measured step time; `us_per_step` is the step time.  `roofline` covers the
+expert FFN call, timed with HIP events around each launch on its stream.
+`cpu_baseline` is the fp64 CPU oracle timed on this host on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+EXPERT_BYTES_EXTRA = 12         # three fp32 global scales per expert
+METRIC = "routed-MoE µs/step + effective HBM TB/s, T=4 E=512 top-10 NVFP4"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--config", default="decode_t4")
+    ap.add_argument("--banks", type=int, default=8)
+    ap.add_argument("--ffn-launches", type=int, default=400,
+                    help="eager moe_expert_ffn launches timed with events for the roofline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle sample budget (0 disables the cpu_baseline leg)")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, budget_s: float, expert_bytes: int):
+    """Time the fp64 oracle (as it stands) on whole steps of the same workload."""
+    import numpy as np
+    import oracle
+    from moe_inputs import make_workload
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    steps, total, nbytes = 0, 0.0, 0
+    seed = 1000
+    while steps == 0 or total < budget_s:
+        wl = make_workload(cfg.name, x_seed=seed + steps)
+        t0 = time.perf_counter()
+        idx, w = oracle.route_topk(wl.logits, wl.bias, wl.k)
+        oracle.bucket_routes(idx, wl.E)
+        oracle.moe_output(wl.x, wl.bank, idx, w)
+        total += time.perf_counter() - t0
+        nbytes += len(np.unique(idx)) * expert_bytes
+        steps += 1
+    s_per_step = total / steps
+    return {
+        "value": round(nbytes / steps / s_per_step / 1e12, 9),
+        "unit": "TB/s",
+        "us_per_step": round(s_per_step * 1e6, 1),
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{steps} whole steps of {cfg.name} (x seeds {seed}..{seed + steps - 1}), "
+                  f"route + buckets + FFN in fp64, {total:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_moe_expert_amd as sme
+    from moe_inputs import get_config, make_workload
+
+    cfg = get_config(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    expert_bytes = cfg.expert_bytes() + EXPERT_BYTES_EXTRA
+    NB = args.banks
+
+    log(f"[bench] generating {cfg.name} inputs and weights")
+    wls = [make_workload(cfg.name, x_seed=b) for b in range(NB)]
+    W0 = sme.expert_weights_from_numpy(wls[0].bank, dev)
+    banks = [W0] + [sme.ExpertWeights(*(torch.roll(t, shifts=67 * b, dims=0).contiguous() for t in W0))
+                    for b in range(1, NB)]
+    xs = [torch.from_numpy(w.x.view(np.int16)).to(dev) for w in wls]
+    ls = [torch.from_numpy(w.logits).to(dev) for w in wls]
+    bias = None if wls[0].bias is None else torch.from_numpy(wls[0].bias).to(dev)
+    step = sme.MoeStep(T, H, I, E, k, dev)
+
+    # unique experts per routing set, and warm-up outside capture
+    n_unique = []
+    for b in range(NB):
+        step.run(xs[b], ls[b], bias, banks[b])
+        torch.cuda.synchronize()
+        n_unique.append(int(step.buckets.n_active.item()))
+    bytes_per_step = float(np.mean(n_unique)) * expert_bytes
+
+    graphs = []
+    for b in range(NB):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step.run(xs[b], ls[b], bias, banks[b])
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    log(f"[bench] warm-up {args.warmup} steps")
+    for i in range(args.warmup):
+        graphs[i % NB].replay()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % NB].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    s_per_step = wall / args.steps
+    eff_tbps = bytes_per_step / s_per_step / 1e12
+    log(f"[bench] {s_per_step * 1e6:.2f} us/step, {eff_tbps:.3f} TB/s effective")
+
+    # Roofline leg: HIP events around each eager moe_expert_ffn call, on the
+    # stream the library launches on (torch's current stream).
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.ffn_launches)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.ffn_launches)]
+    ffn_bytes = []
+    for i in range(args.ffn_launches):
+        b = i % NB
+        step.route(ls[b], bias)
+        step.bucket()
+        starts[i].record(stream)
+        step.ffn(xs[b], banks[b])
+        ends[i].record(stream)
+        ffn_bytes.append(n_unique[b] * expert_bytes + 4 * T * H)
+    torch.cuda.synchronize()
+    durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e-3   # seconds
+    avg = float(durs.mean())
+    achieved = float(np.mean(ffn_bytes)) / avg / 1e9
+    log(f"[bench] moe_expert_ffn avg {avg * 1e6:.2f} us -> {achieved:.1f} GB/s")
+
+    out = {
+        "metric": METRIC,
+        "value": round(eff_tbps, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(s_per_step * 1e3, 6),
+        "us_per_step": round(s_per_step * 1e6, 3),
+        "tokens_per_s": round(T / s_per_step, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "H": H, "I": I, "E": E, "k": k,
+                   "weights": "nvfp4", "banks": NB,
+                   "unique_experts_per_step": round(float(np.mean(n_unique)), 2),
+                   "unique_expert_bytes_per_step": int(bytes_per_step)},
+        "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "avg_launch_us": round(avg * 1e6, 3)},
+    }
+    if args.cpu_seconds > 0:
+        log(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s budget)")
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, expert_bytes)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * Routed NVFP4 mixture-of-experts FFN for one MI355X (gfx950): C ABI.
+ *
+ * One routed-MoE step of a decode/verify/prefill batch is three calls on one
+ * stream:
+ *   moe_route_topk     router logits -> top-k expert ids and gate weights
+ *   moe_bucket_routes  top-k ids -> routes grouped by expert (stable order)
+ *   moe_expert_ffn     bf16 tokens + NVFP4 experts + buckets -> bf16 output
+ * The router projection that produces the logits is a prerequisite outside
+ * these calls (the MonoMoE host wrapper takes precomputed router logits and
+ * the SM70 design note keeps the router GEMV as an explicit prerequisite:
+ * page "Persistent execution for Flash-Next GGUF on SM70", sections "MonoMoE"
+ * and "First implementation boundary").
+ *
+ * Conventions for every call
+ *  - Tensor pointers are DEVICE pointers owned by the caller, row-major and
+ *    contiguous, aligned to 16 bytes (MOE_ERR_MISALIGNED otherwise).  Scalars
+ *    (sizes) are passed by value.
+ *  - A call only enqueues kernels on `stream` (a hipStream_t passed as void*;
+ *    NULL = the null stream).  No call allocates, frees, synchronises, prints
+ *    or keeps per-call host state, so the three calls can be captured into a
+ *    HIP graph and replayed with new input contents.
+ *  - Arguments are checked on the host before any launch; on error nothing is
+ *    launched and a status other than MOE_OK is returned.  Device-side faults
+ *    surface as HIP errors at the caller's next synchronisation.
+ *  - Preconditions the host cannot check (device data): logits and activations
+ *    are finite; topk_idx values lie in [0, E); bucket arrays are the output
+ *    of moe_bucket_routes for the same topk_idx.
+ *  - Results are bitwise reproducible for identical inputs: no floating-point
+ *    atomics; every reduction has a fixed order.
+ *  - Calls are reentrant.  Concurrent calls need distinct outputs and
+ *    workspaces.
+ */
+#ifndef SPARSE_MOE_EXPERT_AMD_MOE_H
+#define SPARSE_MOE_EXPERT_AMD_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+  MOE_ERR_INVALID_SHAPE = 2,       /* T < 0, k < 1, k > E, H or I not a multiple of 32 ... */
+  MOE_ERR_UNSUPPORTED = 3,         /* outside the supported envelope (see each call) */
+  MOE_ERR_MISALIGNED = 4,          /* a tensor pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < moe_expert_ffn_workspace_size() */
+  MOE_ERR_HIP = 6                  /* a HIP runtime call failed (launch or device query) */
+} moe_status;
+
+/*
+ * moe_route_topk — softmax top-k routing with renormalised gate weights.
+ *
+ * Defines: per token the experts are scored z[t,e] = fl32(logits[t,e] +
+ * bias[e]) (one fp32 add; z = logits when bias is NULL).  The k largest z are
+ * chosen by repeated arg-max; equal scores go to the lower expert id, and
+ * -0.0 equals +0.0 (page "How I forked vLLM and made Qwen3.8-Flash-Next
+ * decode 1.6x faster on one GPU", section "5. Hand-written kernels",
+ * paragraph "Fused MoE routing"; page "Persistent execution for Flash-Next
+ * GGUF on SM70", section "Router: selection and expert-task production").
+ * Slot j holds the j-th choice (z descending, id ascending).  Gate weights
+ * are the softmax over all E experts renormalised over the chosen k, i.e.
+ * topk_w[t,j] = exp(z_j - z_0) / sum_i exp(z_i - z_0) over the chosen i,
+ * computed in fp32 (|error| <= 1e-6 against exact arithmetic).
+ *
+ *   logits    [T, E] fp32          in
+ *   bias      [E] fp32 or NULL     in
+ *   topk_idx  [T, k] int32         out
+ *   topk_w    [T, k] fp32          out, each row sums to 1 (to rounding)
+ * Shapes: T >= 0 (T = 0 launches nothing), 1 <= k <= E.  Envelope:
+ * E <= 1024, k <= 32 (else MOE_ERR_UNSUPPORTED).
+ */
+moe_status moe_route_topk(const float* logits, const float* bias,
+                          int T, int E, int k,
+                          int32_t* topk_idx, float* topk_w,
+                          void* stream);
+
+/*
+ * moe_bucket_routes — group the R = T*k routes by expert.
+ *
+ * Defines the counts, scan, expert ids and scatter that follow top-k in the
+ * fused routing kernel (page "How I forked vLLM and made Qwen3.8-Flash-Next
+ * decode 1.6x faster on one GPU", section "5. Hand-written kernels",
+ * paragraph "Fused MoE routing") as the compact expert-presence list and
+ * original route positions asked for by the SM70 design note (page
+ * "Persistent execution for Flash-Next GGUF on SM70", section "First
+ * implementation boundary", step 1).  A route is named by its flat id
+ * r = t*k + j.  Integer-only and exact:
+ *   expert_count   [E]    out  routes per expert
+ *   expert_offset  [E+1]  out  exclusive prefix sum of expert_count
+ *   active_experts [E]    out  ascending ids with count > 0, then -1
+ *   n_active       [1]    out  number of ids with count > 0
+ *   route_src      [R]    out  flat route ids ordered by (expert, r)
+ *   route_pos      [R]    out  inverse: route_pos[route_src[p]] == p
+ * Shapes: T >= 0 (T = 0 launches nothing), 1 <= k <= E.  Envelope:
+ * E <= 1024, R <= 2^24 (else MOE_ERR_UNSUPPORTED).
+ */
+moe_status moe_bucket_routes(const int32_t* topk_idx, int T, int E, int k,
+                             int32_t* expert_count, int32_t* expert_offset,
+                             int32_t* active_experts, int32_t* n_active,
+                             int32_t* route_src, int32_t* route_pos,
+                             void* stream);
+
+/*
+ * Bytes of device workspace moe_expert_ffn needs for these sizes (0 when
+ * T == 0).  The workspace holds per-route intermediates and a small control
+ * region of counters.
+ */
+size_t moe_expert_ffn_workspace_size(int T, int H, int I, int E, int k);
+
+/*
+ * moe_expert_ffn — routed NVFP4 SwiGLU experts with a weighted unroute.
+ *
+ * Defines, per route p = (t, j) with expert e = topk_idx[t,j] (page
+ * "Persistent execution for Flash-Next GGUF on SM70", sections "What the
+ * measurements establish" and "First implementation boundary"):
+ *   h_p = SiLU(Wg_e x_t) * (Wu_e x_t),   o_p = Wd_e h_p,
+ *   y_t = sum_{j=0}^{k-1} topk_w[t,j] * o_(t,j), summed in slot order j
+ *         (a fixed order, never arrival order), rounded once to bf16 (RNE).
+ * Each active expert's weights are streamed from HBM once per call for all
+ * of its routes (unique-expert reuse).  Accumulation is fp32; h is kept as
+ * bf16 between the two projections.
+ *
+ * NVFP4 weights: element = e2m1 * e4m3 * global.  e2m1 codes are packed two
+ * per byte, element 2i in the low nibble of byte i; one e4m3 (OCP E4M3FN)
+ * scale per 16 consecutive elements along the reduction dimension; one fp32
+ * global scale per matrix.
+ *   x           [T, H] bf16 bits        in
+ *   w_gate/w_up [E, I, H/2] uint8       in   (rows = outputs, along H)
+ *   s_gate/s_up [E, I, H/16] uint8      in
+ *   w_down      [E, H, I/2] uint8       in   (rows = outputs, along I)
+ *   s_down      [E, H, I/16] uint8      in
+ *   g_scale     [E, 3] fp32             in   (gate, up, down global scales)
+ *   topk_w      [T, k] fp32             in   (from moe_route_topk)
+ *   expert_count, expert_offset, active_experts, n_active, route_src,
+ *   route_pos                           in   (from moe_bucket_routes)
+ *   workspace   device buffer of workspace_bytes >= moe_expert_ffn_workspace_size(T,H,I,E,k);
+ *               its contents must be zero before the first call that uses
+ *               it (e.g. allocated with hipMemset or torch.zeros); every call
+ *               leaves its control region zero again, so later calls and
+ *               graph replays need no reset.
+ *   y           [T, H] bf16 bits        out
+ * Shapes: T >= 0 (T = 0 launches nothing), 1 <= k <= E, H and I multiples of
+ * 32.  Envelope: E <= 1024, k <= 32, H and I powers of two from 32 to 4096
+ * (the Flash-Next shape H = 2048, I = 512 qualifies); else
+ * MOE_ERR_UNSUPPORTED.
+ */
+moe_status moe_expert_ffn(const uint16_t* x,
+                          const uint8_t* w_gate, const uint8_t* s_gate,
+                          const uint8_t* w_up, const uint8_t* s_up,
+                          const uint8_t* w_down, const uint8_t* s_down,
+                          const float* g_scale,
+                          const float* topk_w,
+                          const int32_t* expert_count, const int32_t* expert_offset,
+                          const int32_t* active_experts, const int32_t* n_active,
+                          const int32_t* route_src, const int32_t* route_pos,
+                          int T, int H, int I, int E, int k,
+                          void* workspace, size_t workspace_bytes,
+                          uint16_t* y,
+                          void* stream);
+
+/* Static English description of a status code (never NULL). */
+const char* moe_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_MOE_EXPERT_AMD_MOE_H */

@@ -1,0 +1,42 @@
+"""Routed NVFP4 mixture-of-experts FFN on MI355X (gfx950).
+
+A C-ABI HIP library (include/moe.h) with three calls per routed-MoE step:
+moe_route_topk -> moe_bucket_routes -> moe_expert_ffn, bound here for torch
+tensors.  PyTorch provides device memory and the stream; the kernels are the
+library's own.
+"""
+
+from ._lib import (
+    Buckets,
+    ExpertWeights,
+    LIB_PATH,
+    MoeError,
+    SIGNATURES,
+    empty_buckets,
+    load_library,
+    make_workspace,
+    moe_bucket_routes,
+    moe_expert_ffn,
+    moe_expert_ffn_workspace_size,
+    moe_route_topk,
+    moe_status_string,
+)
+from .step import MoeStep, expert_weights_from_numpy
+
+__all__ = [
+    "Buckets",
+    "ExpertWeights",
+    "LIB_PATH",
+    "MoeError",
+    "SIGNATURES",
+    "empty_buckets",
+    "load_library",
+    "make_workspace",
+    "moe_bucket_routes",
+    "moe_expert_ffn",
+    "moe_expert_ffn_workspace_size",
+    "moe_route_topk",
+    "moe_status_string",
+    "MoeStep",
+    "expert_weights_from_numpy",
+]

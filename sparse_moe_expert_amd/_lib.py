@@ -1,0 +1,208 @@
+"""ctypes binding to libsparse_moe_expert_amd.so (argument marshalling only).
+
+Every step of the routed-MoE path runs in the HIP library; this module checks
+tensor dtypes, devices and contiguity, passes data pointers and torch's
+current HIP stream, and turns status codes into exceptions.  There is no
+fallback: if the library is missing the import of a call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libsparse_moe_expert_amd.so")
+
+MOE_STATUS = {
+    0: "MOE_OK",
+    1: "MOE_ERR_NULL_POINTER",
+    2: "MOE_ERR_INVALID_SHAPE",
+    3: "MOE_ERR_UNSUPPORTED",
+    4: "MOE_ERR_MISALIGNED",
+    5: "MOE_ERR_WORKSPACE_TOO_SMALL",
+    6: "MOE_ERR_HIP",
+}
+
+# Exported C symbols and their ctypes signatures.
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+SIGNATURES = {
+    "moe_route_topk": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
+    "moe_bucket_routes": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "moe_expert_ffn": (_I, [_P] * 15 + [_I] * 5 + [_P, ctypes.c_size_t, _P, _P]),
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {MOE_STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} not found: build it with `python -m sparse_moe_expert_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        msg = load_library().moe_status_string(status).decode()
+        raise MoeError(fn, status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def moe_route_topk(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int,
+                   topk_idx: Optional[torch.Tensor] = None,
+                   topk_w: Optional[torch.Tensor] = None):
+    """Top-k expert ids (int32 [T,k]) and renormalised weights (fp32 [T,k])."""
+    T, E = logits.shape
+    dev = logits.device
+    _need(logits, "logits", torch.float32)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,), dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    st = load_library().moe_route_topk(_ptr(logits), _ptr(bias), T, E, k, _ptr(topk_idx),
+                                       _ptr(topk_w), _stream(dev))
+    _check("moe_route_topk", st)
+    return topk_idx, topk_w
+
+
+class Buckets(NamedTuple):
+    expert_count: torch.Tensor    # int32 [E]
+    expert_offset: torch.Tensor   # int32 [E+1]
+    active_experts: torch.Tensor  # int32 [E]
+    n_active: torch.Tensor        # int32 [1]
+    route_src: torch.Tensor       # int32 [R]
+    route_pos: torch.Tensor       # int32 [R]
+
+
+def empty_buckets(T: int, E: int, k: int, device) -> Buckets:
+    R = T * k
+    mk = lambda n: torch.empty((n,), dtype=torch.int32, device=device)  # noqa: E731
+    return Buckets(mk(E), mk(E + 1), mk(E), mk(1), mk(R), mk(R))
+
+
+def moe_bucket_routes(topk_idx: torch.Tensor, E: int, out: Optional[Buckets] = None) -> Buckets:
+    """Routes grouped by expert, stable in flat route id t*k+j."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    _need(topk_idx, "topk_idx", torch.int32)
+    b = out if out is not None else empty_buckets(T, E, k, dev)
+    for name, t, n in zip(Buckets._fields, b, (E, E + 1, E, 1, T * k, T * k)):
+        _need(t, name, torch.int32, (n,), dev)
+    st = load_library().moe_bucket_routes(_ptr(topk_idx), T, E, k, *(_ptr(t) for t in b),
+                                          _stream(dev))
+    _check("moe_bucket_routes", st)
+    return b
+
+
+class ExpertWeights(NamedTuple):
+    w_gate: torch.Tensor   # uint8 [E, I, H/2]
+    s_gate: torch.Tensor   # uint8 [E, I, H/16]
+    w_up: torch.Tensor     # uint8 [E, I, H/2]
+    s_up: torch.Tensor     # uint8 [E, I, H/16]
+    w_down: torch.Tensor   # uint8 [E, H, I/2]
+    s_down: torch.Tensor   # uint8 [E, H, I/16]
+    g_scale: torch.Tensor  # fp32  [E, 3]
+
+    @property
+    def shape(self):
+        E, I, H2 = self.w_gate.shape
+        return E, 2 * H2, I
+
+
+def moe_expert_ffn_workspace_size(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(load_library().moe_expert_ffn_workspace_size(T, H, I, E, k))
+
+
+def make_workspace(T: int, H: int, I: int, E: int, k: int, device) -> torch.Tensor:
+    """Zero-filled workspace of the size moe_expert_ffn needs (zero once, then reusable)."""
+    n = max(moe_expert_ffn_workspace_size(T, H, I, E, k), 256)
+    return torch.zeros((n,), dtype=torch.uint8, device=device)
+
+
+def moe_expert_ffn(x: torch.Tensor, weights: ExpertWeights, topk_w: torch.Tensor,
+                   buckets: Buckets, workspace: torch.Tensor,
+                   y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 [T,H] output of the routed experts.  x is bf16 [T,H] (or its uint16 bits)."""
+    T, H = x.shape
+    E, H_w, I = weights.shape
+    k = topk_w.shape[1]
+    dev = x.device
+    if x.dtype == torch.bfloat16:
+        x = x.view(torch.int16)
+    if x.dtype not in (torch.int16, torch.uint16):
+        raise TypeError("x must be bfloat16 (or its 16-bit patterns)")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous device tensor")
+    if H_w != H:
+        raise ValueError(f"weights are for H={H_w}, x has H={H}")
+    shapes = [(E, I, H // 2), (E, I, H // 16), (E, I, H // 2), (E, I, H // 16),
+              (E, H, I // 2), (E, H, I // 16)]
+    for name, t, shp in zip(ExpertWeights._fields, weights, shapes):
+        _need(t, name, torch.uint8, shp, dev)
+    _need(weights.g_scale, "g_scale", torch.float32, (E, 3), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if y.dtype != torch.bfloat16 or tuple(y.shape) != (T, H) or not y.is_contiguous() or y.device != dev:
+        raise ValueError("y must be a contiguous bfloat16 [T, H] tensor on x's device")
+    st = load_library().moe_expert_ffn(
+        _ptr(x), *(_ptr(t) for t in weights), _ptr(topk_w), *(_ptr(t) for t in buckets),
+        T, H, I, E, k, _ptr(workspace), ctypes.c_size_t(workspace.numel()), _ptr(y), _stream(dev))
+    _check("moe_expert_ffn", st)
+    return y
+
+
+def moe_status_string(status: int) -> str:
+    return load_library().moe_status_string(status).decode()

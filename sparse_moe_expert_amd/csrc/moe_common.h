@@ -1,0 +1,78 @@
+// Internal helpers shared by the HIP kernels and their host launchers.
+// Written for gfx950 (CDNA4): 64-lane wavefronts, v_cvt_scalef32_pk_bf16_fp4,
+// v_dot2_f32_bf16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- device
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) {
+  return __builtin_bit_cast(bf16x2, u);
+}
+
+// Two FP4 E2M1 codes (byte B of `word`: low nibble = even element) -> two bf16
+// in one instruction.  Scale 1.0: the conversion is exact (e2m1 values have
+// at most 2 significant bits).
+template <int B>
+__device__ __forceinline__ bf16x2 fp4x2_to_bf16x2(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, B);
+}
+
+// FP8 E4M3FN scale byte -> fp32 value * 2^-8, exactly.  Shifting the 7
+// magnitude bits left by 7 gives the fp16 with the same fields (exponent bias
+// 15 instead of 7, mantissa widened), i.e. value * 2^-8 for normals and
+// subnormals alike; the fp16 -> fp32 conversion is exact.  The 2^8 is folded
+// into the global scale.  Scale bytes are non-negative (sign bit clear) and
+// never NaN (precondition).
+__device__ __forceinline__ float e4m3_to_f32_div256(uint32_t byte) {
+  const uint16_t h = (uint16_t)((byte & 0x7Fu) << 7);
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Fixed-order butterfly sum across the `width` lanes of an aligned lane group
+// (width a power of two <= 64).  Every lane of the group ends with the sum.
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+
+// ---------------------------------------------------------------- host
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute units of the current device (cached per device id).
+int device_cu_count();
+
+inline moe_status launch_status() {
+  hipError_t err = hipGetLastError();
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// Largest power of two <= 64 dividing `chunks` (lanes that share one row).
+inline int lanes_per_row(int chunks) {
+  int l = 64;
+  while (l > 1 && (chunks % l) != 0) l >>= 1;
+  return l;
+}
+
+}  // namespace moe

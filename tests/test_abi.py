@@ -1,0 +1,94 @@
+"""The C-ABI library loads and exports every entry point include/moe.h declares.
+
+Also the host-side argument checks, which return before any HIP call (no
+device needed): shape errors, the T = 0 no-op, NULL pointers, misalignment,
+workspace sizing.  No compute runs here.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_expert_amd as sme
+import sparse_moe_expert_amd.build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sme.LIB_PATH):
+        sme.build.build_library()
+    return sme.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert names == sorted(sme.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert sme.moe_status_string(s)
+    assert sme.moe_status_string(99) == "unknown status"
+
+
+P = ctypes.c_void_p
+A = P(256)           # a fake, 16-byte aligned, never dereferenced address
+
+
+def test_route_topk_host_checks(lib):
+    f = lib.moe_route_topk
+    assert f(A, None, 4, 8, 9, A, A, None) == 2     # k > E
+    assert f(A, None, 4, 8, 0, A, A, None) == 2     # k < 1
+    assert f(A, None, -1, 8, 2, A, A, None) == 2    # T < 0
+    assert f(A, None, 4, 2048, 2, A, A, None) == 3  # E beyond envelope
+    assert f(A, None, 4, 64, 33, A, A, None) == 3   # k beyond envelope
+    assert f(A, None, 0, 8, 2, A, A, None) == 0     # T = 0: nothing launched
+    assert f(None, None, 4, 8, 2, A, A, None) == 1
+    assert f(P(258), None, 4, 8, 2, A, A, None) == 4
+
+
+def test_bucket_routes_host_checks(lib):
+    f = lib.moe_bucket_routes
+    assert f(A, 4, 8, 9, A, A, A, A, A, A, None) == 2
+    assert f(A, 0, 8, 2, A, A, A, A, A, A, None) == 0
+    assert f(A, 4, 8, 2, A, A, None, A, A, A, None) == 1
+    assert f(A, 4, 8, 2, A, A, A, A, P(260), A, None) == 4
+    assert f(A, 1 << 22, 8, 8, A, A, A, A, A, A, None) == 3   # R > 2^24
+
+
+def _ffn(lib, T=4, H=256, I=128, E=8, k=2, ws=1 << 20, null_at=None, bad_at=None):
+    ptrs = [A] * 15
+    if null_at is not None:
+        ptrs[null_at] = None
+    if bad_at is not None:
+        ptrs[bad_at] = P(264)
+    return lib.moe_expert_ffn(*ptrs, T, H, I, E, k, A, ctypes.c_size_t(ws), A, None)
+
+
+def test_expert_ffn_host_checks(lib):
+    assert _ffn(lib, H=48) == 2          # H not a multiple of 32
+    assert _ffn(lib, I=100) == 2
+    assert _ffn(lib, k=9) == 2
+    assert _ffn(lib, H=96) == 3          # not a power of two
+    assert _ffn(lib, H=8192) == 3
+    assert _ffn(lib, T=0) == 0
+    assert _ffn(lib, null_at=3) == 1
+    assert _ffn(lib, bad_at=0) == 4
+    need = lib.moe_expert_ffn_workspace_size(4, 256, 128, 8, 2)
+    assert need > 0 and need % 256 == 0
+    assert _ffn(lib, ws=need - 1) == 5
+    assert lib.moe_expert_ffn_workspace_size(0, 256, 128, 8, 2) == 0
+    # grows with T*k: h (bf16 [R,I]) and o (fp32 [R,H])
+    assert lib.moe_expert_ffn_workspace_size(8, 256, 128, 8, 2) > need

@@ -1,0 +1,206 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Expert ids and route buckets must match bit for bit; gate weights within 1e-6;
+the bf16 output within max|err| <= 2e-2 * rms(ref).  The five workloads run at
+their full sizes in the same launch configuration the benchmark times; the
+oracle computes every token for the small ones and a fixed sample of tokens
+(including ones routed to the hottest experts) for the large ones.  Edge
+cases: ragged token counts, k = E, all tokens on the same experts, all
+routes on distinct experts, zero input, guard regions around the output and
+workspace, bitwise run-to-run determinism, and graph replays with changed
+inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_expert_amd as sme
+from gpu_harness import (
+    DEV,
+    assert_buckets,
+    assert_output,
+    assert_route,
+    collect,
+    device_weights,
+    oracle_all,
+    run_gpu,
+    to_dev,
+    x_bits,
+)
+from moe_inputs import make_workload
+from moe_inputs.configs import CONFIG_ORDER
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_tokens(wl, idx):
+    T = wl.T
+    if T <= 8:
+        return list(range(T))
+    counts = np.bincount(idx.reshape(-1), minlength=wl.E)
+    hot = int(np.argmax(counts))
+    hot_tokens = sorted(set(int(t) for t in np.argwhere(idx == hot)[:, 0]))
+    picks = {0, 1, T // 2, T - 1} | set(hot_tokens[:2]) | set(hot_tokens[-2:])
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name", CONFIG_ORDER)
+def test_workload_parity(name):
+    wl = make_workload(name)
+    print(f"[parity] {name} T={wl.T} E={wl.E} k={wl.k}", flush=True)
+    g = run_gpu(wl.x, wl.logits, wl.bias, wl.bank, wl.k)
+    idx, w = oracle.route_topk(wl.logits, wl.bias, wl.k)
+    assert_route(g, idx, w)
+    assert_buckets(g, oracle.bucket_routes(idx, wl.E))
+    tokens = _sample_tokens(wl, idx)
+    y_ref = oracle.moe_output(wl.x, wl.bank, idx, w, tokens=tokens)
+    err, rms = assert_output(g["y"][tokens], y_ref, name)
+    print(f"[parity] {name}: tokens={len(tokens)} max_err={err:.3e} rms={rms:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("T", [1, 5, 33])
+@pytest.mark.parametrize("shape", ["tiny", "decode_t4"])
+def test_ragged_token_counts(shape, T):
+    wl = make_workload(shape, T=T, x_seed=100 + T)
+    print(f"[ragged] {shape} T={T}", flush=True)
+    g = run_gpu(wl.x, wl.logits, wl.bias, wl.bank, wl.k)
+    idx, w, b, y = oracle_all(wl.x, wl.logits, wl.bias, wl.bank, wl.k,
+                              tokens=range(T) if shape == "tiny" else range(min(T, 5)))
+    assert_route(g, idx, w)
+    assert_buckets(g, b)
+    assert_output(g["y"][: y.shape[0]], y, f"{shape} T={T}")
+
+
+def test_k_equals_E():
+    wl = make_workload("tiny", T=6, x_seed=7)
+    g = run_gpu(wl.x, wl.logits, None, wl.bank, wl.E)
+    idx, w, b, y = oracle_all(wl.x, wl.logits, None, wl.bank, wl.E)
+    assert_route(g, idx, w)
+    assert_buckets(g, b)
+    assert_output(g["y"], y, "k=E")
+
+
+def test_all_tokens_on_same_experts():
+    """Every token routed to the same 10 experts: 33 tokens per expert, so the
+    kernels loop over token groups."""
+    wl = make_workload("decode_t4", T=33, x_seed=3)
+    chosen = [7, 100, 101, 250, 311, 312, 400, 450, 500, 511]
+    bias = np.zeros(wl.E, np.float32)
+    bias[chosen] = 50.0
+    g = run_gpu(wl.x, wl.logits, bias, wl.bank, wl.k)
+    idx, w, b, y = oracle_all(wl.x, wl.logits, bias, wl.bank, wl.k, tokens=[0, 16, 32])
+    assert int(b["n_active"]) == 10 and sorted(np.unique(idx)) == chosen
+    assert_route(g, idx, w)
+    assert_buckets(g, b)
+    assert_output(g["y"][[0, 16, 32]], y, "all-equal experts")
+
+
+def test_all_routes_on_distinct_experts():
+    wl = make_workload("decode_t4", T=40, x_seed=4)
+    T, k, E = 40, 10, 512
+    logits = np.zeros((T, E), np.float32)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(E)[: T * k].reshape(T, k)
+    for t in range(T):
+        logits[t, perm[t]] = 10.0 - np.arange(k, dtype=np.float32) * 0.5
+    g = run_gpu(wl.x, logits, None, wl.bank, k)
+    idx, w, b, y = oracle_all(wl.x, logits, None, wl.bank, k, tokens=[0, 39])
+    assert np.all(b["expert_count"][b["expert_count"] > 0] == 1) and int(b["n_active"]) == 400
+    assert_route(g, idx, w)
+    assert_buckets(g, b)
+    assert_output(g["y"][[0, 39]], y, "all-disjoint experts")
+
+
+def test_zero_input_gives_exact_zero():
+    wl = make_workload("decode_t4")
+    x = np.zeros_like(wl.x)
+    logits = np.zeros_like(wl.logits)
+    g = run_gpu(x, logits, None, wl.bank, wl.k)
+    assert np.array_equal(g["idx"], np.tile(np.arange(wl.k, dtype=np.int32), (wl.T, 1)))
+    assert np.all(g["w"] == np.float32(1.0 / wl.k))
+    assert np.all(g["y_bits"] == 0)
+
+
+def test_guard_regions_untouched():
+    wl = make_workload("decode_t4", T=5, x_seed=9)
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    W = device_weights(wl.bank)
+    step = sme.MoeStep(T, H, I, E, k, DEV)
+    ws_bytes = sme.moe_expert_ffn_workspace_size(T, H, I, E, k)
+    big_ws = torch.zeros(ws_bytes + 512, dtype=torch.uint8, device=DEV)
+    big_ws[:256] = 0xA5
+    big_ws[256 + ws_bytes:] = 0x5A
+    step.workspace = big_ws[256: 256 + ws_bytes]
+    big_y = torch.full((T + 2, H), 3.0, dtype=torch.bfloat16, device=DEV)
+    step.y = big_y[1: T + 1]
+    step.run(x_bits(wl.x), to_dev(wl.logits), None, W)
+    torch.cuda.synchronize()
+    assert torch.all(big_ws[:256] == 0xA5) and torch.all(big_ws[256 + ws_bytes:] == 0x5A)
+    assert torch.all(big_y[0] == 3.0) and torch.all(big_y[T + 1] == 3.0)
+    idx, w, b, y = oracle_all(wl.x, wl.logits, None, wl.bank, k)
+    assert_output(big_y[1: T + 1].float().cpu().numpy().astype(np.float64), y, "guarded")
+
+
+@pytest.mark.parametrize("name", ["decode_t4", "decode_t256_zipf"])
+def test_bitwise_determinism(name):
+    wl = make_workload(name)
+    a = run_gpu(wl.x, wl.logits, wl.bias, wl.bank, wl.k)
+    b = run_gpu(wl.x, wl.logits, wl.bias, wl.bank, wl.k)
+    for key in ("idx", "route_src", "route_pos", "y_bits"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.array_equal(a["w"].view(np.uint32), b["w"].view(np.uint32))
+
+
+def test_graph_replays_with_changed_inputs():
+    """Capture the three calls once; replay with inputs A, B, A, B with eager
+    work and synchronisation between replays; each replay must match the
+    oracle for its inputs (the workspace needs no reset between replays)."""
+    A = make_workload("decode_t4", x_seed=11)
+    B = make_workload("decode_t4", x_seed=12)
+    T, H, I, E, k = A.T, A.H, A.I, A.E, A.k
+    W = device_weights(A.bank)
+    step = sme.MoeStep(T, H, I, E, k, DEV)
+    x_s = x_bits(A.x)
+    l_s = to_dev(A.logits)
+    step.run(x_s, l_s, None, W)          # warm-up outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.run(x_s, l_s, None, W)
+    torch.cuda.synchronize()
+    refs = {}
+    for wl in (A, B):
+        idx, w, b, y = oracle_all(wl.x, wl.logits, None, wl.bank, k)
+        refs[id(wl)] = (idx, w, b, y)
+    for rep, wl in enumerate([A, B, A, B]):
+        x_s.copy_(x_bits(wl.x))
+        l_s.copy_(to_dev(wl.logits))
+        junk = torch.randn(1024, device=DEV).sum()   # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        g = collect(step)
+        idx, w, b, y = refs[id(wl)]
+        assert_route(g, idx, w)
+        assert_buckets(g, b)
+        assert_output(g["y"], y, f"replay {rep}")
+        del junk
+
+
+def test_hand_worked_cases_on_gpu():
+    """The closed-form golden FFN cases (H = I = 32) through the GPU path."""
+    import math
+    import pins
+    from nvfp4_testlib import bank_from_case, x_from_case
+    for case in pins.load_golden("ffn_hand_worked.json")["cases"]:
+        bank = bank_from_case(case)
+        x = x_from_case(case)
+        logits = np.array(case["logits"], dtype=np.float32)
+        g = run_gpu(x, logits, None, bank, case["k"])
+        assert g["idx"].tolist() == case["idx"]
+        ev = lambda s: float(eval(s, {"math": math, "__builtins__": {}}))  # noqa: E731
+        ref = np.empty((case["T"], case["H"]))
+        ref[:, 0::2] = ev(case["y"]["even"])
+        ref[:, 1::2] = ev(case["y"]["odd"])
+        assert_output(g["y"], ref, case["name"])
