@@ -6,9 +6,9 @@ The default workload is the decode verify step: T=4 tokens, H=2048, I=512,
 E=512 experts, top-10, NVFP4 experts, bf16 activations.
 
 Cache control: NB weight banks (expert e of bank b is expert e-67b of bank 0,
-at distinct addresses) with NB activation/routing sets, one graph per bank,
-replayed round-robin, so no expert's bytes are re-read within ~NB steps of
-traffic (the 256 MB MALL would otherwise hold a step's ~69 MB).
+at distinct addresses) with NB activation/routing sets; one HIP graph holds
+the NB steps back to back, so no expert's bytes are re-read within NB steps
+of traffic (the 256 MB MALL would otherwise hold a step's ~69 MB).
 
 Output: one JSON line.  `value` is the effective HBM bandwidth on unique
 expert bytes (unique experts of the step x 1,769,484 B) divided by the
@@ -123,23 +123,32 @@ def main():
         n_unique.append(int(step.buckets.n_active.item()))
     bytes_per_step = float(np.mean(n_unique)) * expert_bytes
 
-    graphs = []
-    for b in range(NB):
+    # One graph holds NB consecutive steps (bank b, routing set b), so the
+    # host-side graph launch cost is paid once per NB steps; a second graph
+    # holds the remainder so that exactly K steps are timed.
+    def capture(nsteps):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step.run(xs[b], ls[b], bias, banks[b])
-        graphs.append(g)
+            for b in range(nsteps):
+                step.run(xs[b], ls[b], bias, banks[b])
+        return g
+
+    full = capture(NB)
+    rem = args.steps % NB
+    tail = capture(rem) if rem else None
     torch.cuda.synchronize()
 
     log(f"[bench] warm-up {args.warmup} steps")
-    for i in range(args.warmup):
-        graphs[i % NB].replay()
+    for _ in range((args.warmup + NB - 1) // NB):
+        full.replay()
     torch.cuda.synchronize()
 
     log(f"[bench] timing {args.steps} steps")
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % NB].replay()
+    for _ in range(args.steps // NB):
+        full.replay()
+    if tail is not None:
+        tail.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     s_per_step = wall / args.steps

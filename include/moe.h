@@ -106,8 +106,8 @@ moe_status moe_bucket_routes(const int32_t* topk_idx, int T, int E, int k,
 
 /*
  * Bytes of device workspace moe_expert_ffn needs for these sizes (0 when
- * T == 0).  The workspace holds per-route intermediates and a small control
- * region of counters.
+ * T == 0): the per-route intermediates, 2*I + 4*H bytes per route, each
+ * region rounded up to 256 bytes.
  */
 size_t moe_expert_ffn_workspace_size(int T, int H, int I, int E, int k);
 
@@ -137,11 +137,10 @@ size_t moe_expert_ffn_workspace_size(int T, int H, int I, int E, int k);
  *   topk_w      [T, k] fp32             in   (from moe_route_topk)
  *   expert_count, expert_offset, active_experts, n_active, route_src,
  *   route_pos                           in   (from moe_bucket_routes)
- *   workspace   device buffer of workspace_bytes >= moe_expert_ffn_workspace_size(T,H,I,E,k);
- *               its contents must be zero before the first call that uses
- *               it (e.g. allocated with hipMemset or torch.zeros); every call
- *               leaves its control region zero again, so later calls and
- *               graph replays need no reset.
+ *   workspace   device buffer of workspace_bytes >= moe_expert_ffn_workspace_size(T,H,I,E,k),
+ *               owned by the caller; holds the per-route intermediates h
+ *               (bf16 [T*k, I]) and o (fp32 [T*k, H]).  Its contents before
+ *               and after a call are unspecified and never need a reset.
  *   y           [T, H] bf16 bits        out
  * Shapes: T >= 0 (T = 0 launches nothing), 1 <= k <= E, H and I multiples of
  * 32.  Envelope: E <= 1024, k <= 32, H and I powers of two from 32 to 4096

@@ -165,9 +165,9 @@ def moe_expert_ffn_workspace_size(T: int, H: int, I: int, E: int, k: int) -> int
 
 
 def make_workspace(T: int, H: int, I: int, E: int, k: int, device) -> torch.Tensor:
-    """Zero-filled workspace of the size moe_expert_ffn needs (zero once, then reusable)."""
+    """Workspace of the size moe_expert_ffn needs (reusable across calls)."""
     n = max(moe_expert_ffn_workspace_size(T, H, I, E, k), 256)
-    return torch.zeros((n,), dtype=torch.uint8, device=device)
+    return torch.empty((n,), dtype=torch.uint8, device=device)
 
 
 def moe_expert_ffn(x: torch.Tensor, weights: ExpertWeights, topk_w: torch.Tensor,

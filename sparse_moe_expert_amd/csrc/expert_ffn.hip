@@ -6,26 +6,32 @@
 // then the weighted unroute with routes summed in a fixed order rather than
 // by arrival-ordered floating-point atomics.  Unique-expert reuse: a task owns
 // (active expert, row tile) and streams those weight rows from HBM once for
-// all of the expert's routes (the page's first boundary, step 2; the b12x
-// kernel's cost is "weight bytes" of the unique experts - page "Qwen3.8 Flash
-// Next on LiL/vLLM", section "11.13 Where the decode step's time actually
-// goes").
+// all of the expert's routes (the note's first boundary, step 2; the b12x
+// kernel's cost is the weight bytes of the unique experts - page "Qwen3.8
+// Flash Next on LiL/vLLM", section "11.13 Where the decode step's time
+// actually goes").
 //
-// Kernels (one stream, no host sync):
-//   gate_up_gemv  task = (active expert a, tile of I rows).  Lane groups of Lr
-//                 lanes share a row; each lane reads 16-byte chunks of codes
-//                 (32 e2m1 values), converts byte pairs to bf16 with
-//                 v_cvt_scalef32_pk_bf16_fp4 (exact), takes v_dot2 products
-//                 with the token's bf16 activations held in registers, applies
-//                 one e4m3 scale per 16 values, then a butterfly sum over the
-//                 Lr lanes.  Epilogue: SiLU(g) * u, rounded to bf16 into h[route].
-//   down_gemv     task = (active expert a, tile of H rows): same structure with
-//                 h as the operand; o[route, row] = fp32 result.
-//   combine       y[t] = bf16( sum_{j=0}^{k-1} w[t,j] * o[route_pos[t*k+j]] )
-//                 in slot order.
-// Tokens of an expert are taken NT at a time (NT <= 4 held in registers);
-// experts with more routes loop over token groups, re-reading their weight
-// rows from L2.
+// Three kernels on one stream; the kernel boundaries order the phases, so no
+// workgroup ever waits for another:
+//   gate_up_kernel  task (active slot a, tile of I rows): h[p, rows] =
+//                   bf16(SiLU(Wg x) * (Wu x)) for every route p of the expert
+//   down_kernel     task (active slot a, tile of H rows): o[p, rows] = Wd h[p]
+//   combine_kernel  y[t] = bf16( sum_{j=0}^{k-1} w[t,j] * o[route_pos[t*k+j]] ),
+//                   j in slot order
+// h and o live in the caller's workspace, indexed by bucket position p.
+//
+// Row tiles (gfx950).  A wavefront reads whole rows: Lr lanes share a row and
+// each lane reads one 16-byte chunk of e2m1 codes (32 values) plus its two
+// e4m3 scales, with buffer loads from a per-expert resource (hardware range
+// check: rows past the matrix read as zero, so ragged tiles need no
+// predication and no index can fault).  Byte pairs become bf16 with
+// v_cvt_scalef32_pk_bf16_fp4 (exact at scale 1), v_dot2 takes bf16 products
+// with the operand (x or h) in fp32, one scale multiplies each 16-value block,
+// and the partial sums of a row are added across its lanes with DPP row
+// operations and v_permlane{16,32}_swap in a fixed order.  A tile's weight
+// rows are loaded once and stay in registers while the expert's routes are
+// processed one at a time, which keeps the kernels at 4 waves per SIMD
+// (<= 128 VGPRs) - the VALU needs that many waves to reach its issue rate.
 #include <algorithm>
 
 #include "moe_common.h"
@@ -46,7 +52,6 @@ struct FfnParams {
   const int32_t* count;
   const int32_t* offset;
   const int32_t* active;
-  const int32_t* n_active;
   const int32_t* route_src;
   const int32_t* route_pos;
   int T, H, I, E, k;
@@ -59,38 +64,53 @@ struct FfnParams {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
-constexpr int kNtMax = 4;
+constexpr int kGuUnits = 4;          // gate rows (and as many up rows) per wave per tile
+constexpr int kDUnits = 8;           // down rows per lane group per tile
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 
-// One 16-byte chunk (32 NVFP4 values, two scale blocks) dotted with NT
-// operand vectors.  xr[t][i] holds operand elements 2i, 2i+1 of the chunk as
-// bf16x2.  acc gets sum * 2^-8 (see e4m3_to_f32_div256).
-template <int NT>
-__device__ __forceinline__ void dot_chunk(const uint4 codes, uint32_t s2,
-                                          const uint32_t (&xr)[NT][16], float (&acc)[NT]) {
-  const float s0 = e4m3_to_f32_div256(s2 & 0xFFu);
-  const float s1 = e4m3_to_f32_div256((s2 >> 8) & 0xFFu);
-  bf16x2 w[16];
-  w[0] = fp4x2_to_bf16x2<0>(codes.x);  w[1] = fp4x2_to_bf16x2<1>(codes.x);
-  w[2] = fp4x2_to_bf16x2<2>(codes.x);  w[3] = fp4x2_to_bf16x2<3>(codes.x);
-  w[4] = fp4x2_to_bf16x2<0>(codes.y);  w[5] = fp4x2_to_bf16x2<1>(codes.y);
-  w[6] = fp4x2_to_bf16x2<2>(codes.y);  w[7] = fp4x2_to_bf16x2<3>(codes.y);
-  w[8] = fp4x2_to_bf16x2<0>(codes.z);  w[9] = fp4x2_to_bf16x2<1>(codes.z);
-  w[10] = fp4x2_to_bf16x2<2>(codes.z); w[11] = fp4x2_to_bf16x2<3>(codes.z);
-  w[12] = fp4x2_to_bf16x2<0>(codes.w); w[13] = fp4x2_to_bf16x2<1>(codes.w);
-  w[14] = fp4x2_to_bf16x2<2>(codes.w); w[15] = fp4x2_to_bf16x2<3>(codes.w);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p0 = __builtin_amdgcn_fdot2_f32_bf16(w[i], as_bf16x2(xr[t][i]), p0, false);
-#pragma unroll
-    for (int i = 8; i < 16; ++i) p1 = __builtin_amdgcn_fdot2_f32_bf16(w[i], as_bf16x2(xr[t][i]), p1, false);
-    acc[t] = fmaf(p0, s0, acc[t]);
-    acc[t] = fmaf(p1, s1, acc[t]);
-  }
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ helpers
+
+// Buffer resource over [base, base + bytes): loads outside it return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
 }
 
-// Load the 64-byte operand chunk `chunk` of a bf16 row into xr (16 dwords).
+__device__ __forceinline__ uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+// Makes a register's value opaque to the optimiser (no instruction).  Used at
+// the top of per-route loops so the weight conversions are not hoisted out of
+// the loop, which would keep every converted value live at once.
+__device__ __forceinline__ void opaque(uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
+
+// One 16-byte chunk (32 NVFP4 values, two scale blocks) dotted with an
+// operand chunk xr (operand elements 2i, 2i+1 as bf16x2 in xr[i]); adds
+// sum_block(scale * sum(code * operand)) to acc.
+__device__ __forceinline__ float dot_chunk(const uint4 codes, uint32_t s2, const uint32_t (&xr)[16], float acc) {
+  const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 0);
+  const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 1);
+  const uint32_t c[4] = {codes.x, codes.y, codes.z, codes.w};
+  float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<0>(c[q]), as_bf16x2(xr[4 * q + 0]), p0, false);
+    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<1>(c[q]), as_bf16x2(xr[4 * q + 1]), p0, false);
+    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<2>(c[q]), as_bf16x2(xr[4 * q + 2]), p0, false);
+    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<3>(c[q]), as_bf16x2(xr[4 * q + 3]), p0, false);
+  }
+#pragma unroll
+  for (int q = 2; q < 4; ++q) {
+    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<0>(c[q]), as_bf16x2(xr[4 * q + 0]), p1, false);
+    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<1>(c[q]), as_bf16x2(xr[4 * q + 1]), p1, false);
+    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<2>(c[q]), as_bf16x2(xr[4 * q + 2]), p1, false);
+    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<3>(c[q]), as_bf16x2(xr[4 * q + 3]), p1, false);
+  }
+  acc = fmaf(p0, s0, acc);
+  return fmaf(p1, s1, acc);
+}
+
+// Load the 64-byte operand chunk `chunk` of a bf16 row into 16 dwords.
 __device__ __forceinline__ void load_operand_chunk(const uint16_t* row, int chunk, uint32_t (&dst)[16]) {
   const uint4* p = reinterpret_cast<const uint4*>(row + (size_t)chunk * 32);
 #pragma unroll
@@ -100,199 +120,228 @@ __device__ __forceinline__ void load_operand_chunk(const uint16_t* row, int chun
   }
 }
 
-// Expert id, route count and first bucket position of active slot a.  The
-// values come from moe_bucket_routes; they are clamped into range so that
-// inputs violating that precondition give wrong results, never out-of-bounds
-// accesses.
-__device__ __forceinline__ void expert_routes(const FfnParams& p, int a, int& e, int& cnt, int& off) {
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each 16-lane row (fixed order); every lane of the row gets it.
+__device__ __forceinline__ float row16_sum(float v) {
+  v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = dpp_add<0x124>(v);   // row_ror:4
+  v = dpp_add<0x128>(v);   // row_ror:8
+  return v;
+}
+
+__device__ __forceinline__ uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float bitsf(uint32_t v) { return __builtin_bit_cast(float, v); }
+
+// a0..a3 hold row sums (uniform within each 16-lane row).  Returns a value
+// whose row r holds a_r summed over all four rows (v_permlane32_swap swaps the
+// upper rows of its first operand with the lower rows of its second;
+// v_permlane16_swap swaps odd rows of the first with even rows of the second).
+__device__ __forceinline__ float rows_scatter4(float a0, float a1, float a2, float a3) {
+  const auto s02 = __builtin_amdgcn_permlane32_swap(fbits(a0), fbits(a2), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(fbits(a1), fbits(a3), false, false);
+  const float b02 = bitsf(s02[0]) + bitsf(s02[1]);
+  const float b13 = bitsf(s13[0]) + bitsf(s13[1]);
+  const auto t = __builtin_amdgcn_permlane16_swap(fbits(b02), fbits(b13), false, false);
+  return bitsf(t[0]) + bitsf(t[1]);
+}
+
+// Lane geometry of one projection.  LR: lanes per row known at compile time
+// (64 for rows of 2048 values, 16 for rows of 512), or 0 for a runtime value.
+template <int LR, int UNITS>
+struct Geo {
+  int lr, rpw, sub, sl, rpt, tiles, wave;
+  __device__ Geo(int lr_rt, int rows_total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    lr = LR ? LR : lr_rt;
+    rpw = kWave / lr;
+    sub = lane / lr;
+    sl = lane & (lr - 1);
+    rpt = kWavesPerBlock * rpw * UNITS;
+    tiles = (rows_total + rpt - 1) / rpt;
+  }
+  // first row of unit u for this wave (wave-uniform); the lane's row adds sub
+  __device__ int row0(int tile, int u) const { return tile * rpt + (u * kWavesPerBlock + wave) * rpw; }
+};
+
+// Expert id, first bucket position and route count of active slot a
+// (wave-uniform).  Values come from moe_bucket_routes and are clamped into
+// range, so inputs that violate that precondition give wrong results but no
+// out-of-bounds access.  Returns false for a slot past the active list.
+__device__ __forceinline__ bool slot_routes(const FfnParams& p, int a, int& e, int& off, int& cnt) {
+  e = __builtin_amdgcn_readfirstlane(p.active[a]);
+  if (e < 0) return false;
+  e = min(e, p.E - 1);
   const int R = p.T * p.k;
-  e = min(max(p.active[a], 0), p.E - 1);
   off = min(max(p.offset[e], 0), R);
   cnt = min(max(p.count[e], 0), R - off);
+  return cnt > 0;
 }
 
 // ------------------------------------------------------------------ gate/up
 
-template <int CPL, int U, int NT>
-__device__ __forceinline__ void gate_up_rows(const FfnParams& p, int e, int first_pos, int tile,
-                                             int rows_per_task, int Lr, int sub, int sl, int wave) {
-  const int rpw = kWave / Lr;
-  const size_t code_row = (size_t)p.H / 2, scale_row = (size_t)p.H / 16;
-  const uint8_t* wg = p.wg + (size_t)e * p.I * code_row;
-  const uint8_t* wu = p.wu + (size_t)e * p.I * code_row;
-  const uint8_t* sg = p.sg + (size_t)e * p.I * scale_row;
-  const uint8_t* su = p.su + (size_t)e * p.I * scale_row;
-
-  uint32_t xr[CPL][NT][16];
+// Gate and up rows of one I tile for all cnt routes of expert e.  Each wave
+// holds kGuUnits gate rows and the same up rows; with 64 lanes per row the
+// four units' sums are scattered so that lane row r ends with unit r.
+template <int LG>
+__device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, kGuUnits>& g, int e, int off,
+                                             int cnt, int tile) {
+  const uint32_t code_row = (uint32_t)p.H / 2, scale_row = (uint32_t)p.H / 16;
+  const uint32_t mat_codes = (uint32_t)p.I * code_row, mat_scales = (uint32_t)p.I * scale_row;
+  const auto rg = make_rsrc(p.wg + (size_t)e * mat_codes, mat_codes);
+  const auto ru = make_rsrc(p.wu + (size_t)e * mat_codes, mat_codes);
+  const auto rgs = make_rsrc(p.sg + (size_t)e * mat_scales, mat_scales);
+  const auto rus = make_rsrc(p.su + (size_t)e * mat_scales, mat_scales);
+  const uint32_t lane_c = (uint32_t)g.sub * code_row + (uint32_t)g.sl * 16;
+  const uint32_t lane_s = (uint32_t)g.sub * scale_row + (uint32_t)g.sl * 2;
+  uint4 cg[kGuUnits], cu[kGuUnits];
+  uint32_t vg[kGuUnits], vu[kGuUnits];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int tok = min(max(p.route_src[first_pos + t] / p.k, 0), p.T - 1);
-    const uint16_t* xrow = p.x + (size_t)tok * p.H;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) load_operand_chunk(xrow, c * Lr + sl, xr[c][t]);
+  for (int u = 0; u < kGuUnits; ++u) {
+    const uint32_t r0 = (uint32_t)g.row0(tile, u);
+    cg[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rg, lane_c, r0 * code_row, 0));
+    cu[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(ru, lane_c, r0 * code_row, 0));
+    vg[u] = __builtin_amdgcn_raw_buffer_load_b16(rgs, lane_s, r0 * scale_row, 0);
+    vu[u] = __builtin_amdgcn_raw_buffer_load_b16(rus, lane_s, r0 * scale_row, 0);
   }
-
-  int rows[U];
-  uint4 cg[U][CPL], cu[U][CPL];
-  uint32_t vg[U][CPL], vu[U][CPL];
+  const float Gg = p.gsc[e * 3 + 0], Gu = p.gsc[e * 3 + 1];
+  for (int t = 0; t < cnt; ++t) {
+    const int pos = off + t;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    rows[u] = tile * rows_per_task + u * (kWavesPerBlock * rpw) + wave * rpw + sub;
-    const bool ok = rows[u] < p.I;
-    const size_t r = ok ? (size_t)rows[u] : 0;
+    for (int u = 0; u < kGuUnits; ++u) {
+      opaque(cg[u]);
+      opaque(cu[u]);
+    }
+    const int tok = min(max(p.route_src[pos] / p.k, 0), p.T - 1);
+    uint32_t xr[16];
+    load_operand_chunk(p.x + (size_t)tok * p.H, g.sl, xr);
+    float ag[kGuUnits], au[kGuUnits];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int chunk = c * Lr + sl;
-      cg[u][c] = ok ? *reinterpret_cast<const uint4*>(wg + r * code_row + (size_t)chunk * 16) : make_uint4(0, 0, 0, 0);
-      cu[u][c] = ok ? *reinterpret_cast<const uint4*>(wu + r * code_row + (size_t)chunk * 16) : make_uint4(0, 0, 0, 0);
-      vg[u][c] = ok ? *reinterpret_cast<const uint16_t*>(sg + r * scale_row + (size_t)chunk * 2) : 0u;
-      vu[u][c] = ok ? *reinterpret_cast<const uint16_t*>(su + r * scale_row + (size_t)chunk * 2) : 0u;
+    for (int u = 0; u < kGuUnits; ++u) {
+      ag[u] = dot_chunk(cg[u], vg[u], xr, 0.0f);
+      au[u] = dot_chunk(cu[u], vu[u], xr, 0.0f);
+    }
+    if constexpr (LG == 64) {
+      static_assert(kGuUnits == 4, "the row scatter maps 4 units to 4 lane rows");
+      const int row = g.row0(tile, (threadIdx.x & (kWave - 1)) >> 4);
+      const float gs = rows_scatter4(row16_sum(ag[0]), row16_sum(ag[1]), row16_sum(ag[2]), row16_sum(ag[3])) * Gg;
+      const float us = rows_scatter4(row16_sum(au[0]), row16_sum(au[1]), row16_sum(au[2]), row16_sum(au[3])) * Gu;
+      if ((threadIdx.x & 15) == 0 && row < p.I)
+        p.h[(size_t)pos * p.I + row] = (uint16_t)f32_to_bf16_rne(silu(gs) * us);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kGuUnits; ++u) {
+        const int row = g.row0(tile, u) + g.sub;
+        const float gs = group_sum(ag[u], g.lr) * Gg;
+        const float us = group_sum(au[u], g.lr) * Gu;
+        if (g.sl == 0 && row < p.I) p.h[(size_t)pos * p.I + row] = (uint16_t)f32_to_bf16_rne(silu(gs) * us);
+      }
     }
   }
-
-  float ag[U][NT], au[U][NT];
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) ag[u][t] = au[u][t] = 0.0f;
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      dot_chunk<NT>(cg[u][c], vg[u][c], xr[c], ag[u]);
-      dot_chunk<NT>(cu[u][c], vu[u][c], xr[c], au[u]);
-    }
-
-  const float Gg = p.gsc[e * 3 + 0] * 256.0f, Gu = p.gsc[e * 3 + 1] * 256.0f;
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float g = group_sum(ag[u][t], Lr) * Gg;
-      const float v = group_sum(au[u][t], Lr) * Gu;
-      if (sl == t % Lr && rows[u] < p.I)   // one lane per (token, row) stores
-        p.h[(size_t)(first_pos + t) * p.I + rows[u]] = (uint16_t)f32_to_bf16_rne(silu(g) * v);
-    }
 }
 
-template <int CPL, int U>
-__global__ __launch_bounds__(kThreads) void gate_up_gemv(FfnParams p) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int Lr = p.lr_gu, rpw = kWave / Lr;
-  const int sub = lane / Lr, sl = lane & (Lr - 1);
-  const int rows_per_task = kWavesPerBlock * rpw * U;
-  const int tiles = (p.I + rows_per_task - 1) / rows_per_task;
-  const int total = min(max(*p.n_active, 0), p.E) * tiles;
-  for (int task = blockIdx.x; task < total; task += gridDim.x) {
-    const int a = task / tiles, tile = task - a * tiles;
-    int e, cnt, off;
-    expert_routes(p, a, e, cnt, off);
-    for (int tg = 0; tg < cnt; tg += kNtMax) {
-      const int nt = min(kNtMax, cnt - tg);
-      if (nt == 1) gate_up_rows<CPL, U, 1>(p, e, off + tg, tile, rows_per_task, Lr, sub, sl, wave);
-      else if (nt == 2) gate_up_rows<CPL, U, 2>(p, e, off + tg, tile, rows_per_task, Lr, sub, sl, wave);
-      else if (nt == 3) gate_up_rows<CPL, U, 3>(p, e, off + tg, tile, rows_per_task, Lr, sub, sl, wave);
-      else gate_up_rows<CPL, U, 4>(p, e, off + tg, tile, rows_per_task, Lr, sub, sl, wave);
-    }
+template <int LG>
+__global__ __launch_bounds__(kThreads, 4) void gate_up_kernel(FfnParams p, int n_tasks) {
+  const Geo<LG, kGuUnits> g(p.lr_gu, p.I);
+  for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
+    const int a = task / g.tiles, tile = task - a * g.tiles;
+    int e, off, cnt;
+    if (!slot_routes(p, a, e, off, cnt)) continue;
+    gate_up_tile<LG>(p, g, e, off, cnt, tile);
   }
 }
 
 // ------------------------------------------------------------------ down
 
-template <int CPL, int U, int NT>
-__device__ __forceinline__ void down_rows(const FfnParams& p, int e, int first_pos, int tile,
-                                          int rows_per_task, int Lr, int sub, int sl, int wave) {
-  const int rpw = kWave / Lr;
-  const size_t code_row = (size_t)p.I / 2, scale_row = (size_t)p.I / 16;
-  const uint8_t* wd = p.wd + (size_t)e * p.H * code_row;
-  const uint8_t* sd = p.sd + (size_t)e * p.H * scale_row;
-
-  uint32_t hr[CPL][NT][16];
+// Down rows of one H tile for all cnt routes of expert e (weights loaded once).
+template <int LD>
+__device__ __forceinline__ void down_tile(const FfnParams& p, const Geo<LD, kDUnits>& g, int e, int off, int cnt,
+                                          int tile) {
+  const uint32_t code_row = (uint32_t)p.I / 2, scale_row = (uint32_t)p.I / 16;
+  const uint32_t mat_codes = (uint32_t)p.H * code_row, mat_scales = (uint32_t)p.H * scale_row;
+  const auto rd = make_rsrc(p.wd + (size_t)e * mat_codes, mat_codes);
+  const auto rds = make_rsrc(p.sd + (size_t)e * mat_scales, mat_scales);
+  const uint32_t lane_c = (uint32_t)g.sub * code_row + (uint32_t)g.sl * 16;
+  const uint32_t lane_s = (uint32_t)g.sub * scale_row + (uint32_t)g.sl * 2;
+  uint4 cd[kDUnits];
+  uint32_t vd[kDUnits];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const uint16_t* hrow = p.h + (size_t)(first_pos + t) * p.I;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) load_operand_chunk(hrow, c * Lr + sl, hr[c][t]);
+  for (int u = 0; u < kDUnits; ++u) {
+    const uint32_t r0 = (uint32_t)g.row0(tile, u);
+    cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, lane_c, r0 * code_row, 0));
+    vd[u] = __builtin_amdgcn_raw_buffer_load_b16(rds, lane_s, r0 * scale_row, 0);
   }
-
-  int rows[U];
-  uint4 cd[U][CPL];
-  uint32_t vd[U][CPL];
+  const float Gd = p.gsc[e * 3 + 2];
+  for (int t = 0; t < cnt; ++t) {
+    const int pos = off + t;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    rows[u] = tile * rows_per_task + u * (kWavesPerBlock * rpw) + wave * rpw + sub;
-    const bool ok = rows[u] < p.H;
-    const size_t r = ok ? (size_t)rows[u] : 0;
+    for (int u = 0; u < kDUnits; ++u) opaque(cd[u]);
+    uint32_t hr[16];
+    load_operand_chunk(p.h + (size_t)pos * p.I, g.sl, hr);
+    float ad[kDUnits];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int chunk = c * Lr + sl;
-      cd[u][c] = ok ? *reinterpret_cast<const uint4*>(wd + r * code_row + (size_t)chunk * 16) : make_uint4(0, 0, 0, 0);
-      vd[u][c] = ok ? *reinterpret_cast<const uint16_t*>(sd + r * scale_row + (size_t)chunk * 2) : 0u;
+    for (int u = 0; u < kDUnits; ++u) ad[u] = dot_chunk(cd[u], vd[u], hr, 0.0f);
+#pragma unroll
+    for (int u = 0; u < kDUnits; ++u) {
+      const int row = g.row0(tile, u) + g.sub;
+      const float v = (LD == 16 ? row16_sum(ad[u]) : group_sum(ad[u], g.lr)) * Gd;
+      // with 16 lanes per row, lane u of the row stores unit u
+      if (g.sl == (LD == 16 ? u : 0) && row < p.H) p.o[(size_t)pos * p.H + row] = v;
     }
   }
-
-  float ad[U][NT];
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) ad[u][t] = 0.0f;
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) dot_chunk<NT>(cd[u][c], vd[u][c], hr[c], ad[u]);
-
-  const float Gd = p.gsc[e * 3 + 2] * 256.0f;
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float v = group_sum(ad[u][t], Lr) * Gd;
-      if (sl == t % Lr && rows[u] < p.H) p.o[(size_t)(first_pos + t) * p.H + rows[u]] = v;
-    }
 }
 
-template <int CPL, int U>
-__global__ __launch_bounds__(kThreads) void down_gemv(FfnParams p) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int Lr = p.lr_d, rpw = kWave / Lr;
-  const int sub = lane / Lr, sl = lane & (Lr - 1);
-  const int rows_per_task = kWavesPerBlock * rpw * U;
-  const int tiles = (p.H + rows_per_task - 1) / rows_per_task;
-  const int total = min(max(*p.n_active, 0), p.E) * tiles;
-  for (int task = blockIdx.x; task < total; task += gridDim.x) {
-    const int a = task / tiles, tile = task - a * tiles;
-    int e, cnt, off;
-    expert_routes(p, a, e, cnt, off);
-    for (int tg = 0; tg < cnt; tg += kNtMax) {
-      const int nt = min(kNtMax, cnt - tg);
-      if (nt == 1) down_rows<CPL, U, 1>(p, e, off + tg, tile, rows_per_task, Lr, sub, sl, wave);
-      else if (nt == 2) down_rows<CPL, U, 2>(p, e, off + tg, tile, rows_per_task, Lr, sub, sl, wave);
-      else if (nt == 3) down_rows<CPL, U, 3>(p, e, off + tg, tile, rows_per_task, Lr, sub, sl, wave);
-      else down_rows<CPL, U, 4>(p, e, off + tg, tile, rows_per_task, Lr, sub, sl, wave);
-    }
+template <int LD>
+__global__ __launch_bounds__(kThreads, 4) void down_kernel(FfnParams p, int n_tasks) {
+  const Geo<LD, kDUnits> g(p.lr_d, p.H);
+  for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
+    const int a = task / g.tiles, tile = task - a * g.tiles;
+    int e, off, cnt;
+    if (!slot_routes(p, a, e, off, cnt)) continue;
+    down_tile<LD>(p, g, e, off, cnt, tile);
   }
 }
 
 // ------------------------------------------------------------------ combine
 
+// y[t, c..c+1] = sum over slots j in order of w[t,j] * o[route_pos[t*k+j], c..c+1].
 __global__ __launch_bounds__(kThreads) void combine_kernel(FfnParams p) {
   const int pairs = p.H / 2;
   const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
   if (gid >= (long long)p.T * pairs) return;
   const int t = (int)(gid / pairs);
   const int c = (int)(gid - (long long)t * pairs) * 2;
+  const int R = p.T * p.k;
+  const float* wrow = p.topk_w + (size_t)t * p.k;
+  const int32_t* prow = p.route_pos + (size_t)t * p.k;
   float y0 = 0.0f, y1 = 0.0f;
-  for (int j = 0; j < p.k; ++j) {                 // slot order: fixed
-    const float w = p.topk_w[(size_t)t * p.k + j];
-    const int pos = min(max(p.route_pos[(size_t)t * p.k + j], 0), p.T * p.k - 1);
-    const float2 ov = *reinterpret_cast<const float2*>(p.o + (size_t)pos * p.H + c);
-    y0 = fmaf(w, ov.x, y0);
-    y1 = fmaf(w, ov.y, y1);
+  for (int j0 = 0; j0 < p.k; j0 += 8) {
+    float w[8];
+    float2 ov[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = j0 + j < p.k;
+      w[j] = ok ? wrow[j0 + j] : 0.0f;
+      const int pos = ok ? min(max(prow[j0 + j], 0), R - 1) : 0;
+      ov[j] = ok ? *reinterpret_cast<const float2*>(p.o + (size_t)pos * p.H + c) : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j0 + j < p.k) {
+        y0 = fmaf(w[j], ov[j].x, y0);
+        y1 = fmaf(w[j], ov[j].y, y1);
+      }
+    }
   }
   reinterpret_cast<uint32_t*>(p.y)[((size_t)t * p.H + c) >> 1] = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
 }
 
-constexpr int kU = 4;
+// ------------------------------------------------------------------ host
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -305,8 +354,22 @@ WorkspaceLayout workspace_layout(int T, int H, int I, int k) {
   const size_t R = (size_t)T * (size_t)k;
   L.h_off = 0;
   L.o_off = align256(R * (size_t)I * 2);
-  L.total = L.o_off + align256(R * (size_t)H * 4) + 256;   // + control region
+  L.total = L.o_off + align256(R * (size_t)H * 4);
   return L;
+}
+
+constexpr long long kMaxGrid = 1 << 20;
+
+template <int LG>
+void launch_gate_up(const FfnParams& p, long long tasks, hipStream_t s) {
+  const unsigned grid = (unsigned)std::max<long long>(1, std::min<long long>(tasks, kMaxGrid));
+  gate_up_kernel<LG><<<grid, kThreads, 0, s>>>(p, (int)tasks);
+}
+
+template <int LD>
+void launch_down(const FfnParams& p, long long tasks, hipStream_t s) {
+  const unsigned grid = (unsigned)std::max<long long>(1, std::min<long long>(tasks, kMaxGrid));
+  down_kernel<LD><<<grid, kThreads, 0, s>>>(p, (int)tasks);
 }
 
 }  // namespace
@@ -332,9 +395,8 @@ extern "C" moe_status moe_expert_ffn(const uint16_t* x, const uint8_t* w_gate, c
   if (E > 1024 || k > 32 || H > 4096 || I > 4096) return MOE_ERR_UNSUPPORTED;
   const int chunks_h = H / 32, chunks_i = I / 32;
   const int lr_gu = lanes_per_row(chunks_h), lr_d = lanes_per_row(chunks_i);
-  const int cpl_gu = chunks_h / lr_gu, cpl_d = chunks_i / lr_d;
-  auto cpl_ok = [](int c) { return c == 1 || c == 2; };
-  if (!cpl_ok(cpl_gu) || !cpl_ok(cpl_d)) return MOE_ERR_UNSUPPORTED;
+  // one 16-byte chunk per lane: H/32 and I/32 must be powers of two <= 64
+  if (chunks_h != lr_gu || chunks_i != lr_d) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   const void* ptrs[] = {x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
                         expert_offset, active_experts, n_active, route_src, route_pos, workspace, y};
@@ -348,31 +410,27 @@ extern "C" moe_status moe_expert_ffn(const uint16_t* x, const uint8_t* w_gate, c
   FfnParams p;
   p.x = x; p.wg = w_gate; p.sg = s_gate; p.wu = w_up; p.su = s_up; p.wd = w_down; p.sd = s_down;
   p.gsc = g_scale; p.topk_w = topk_w; p.count = expert_count; p.offset = expert_offset;
-  p.active = active_experts; p.n_active = n_active; p.route_src = route_src; p.route_pos = route_pos;
+  p.active = active_experts; p.route_src = route_src; p.route_pos = route_pos;
   p.T = T; p.H = H; p.I = I; p.E = E; p.k = k;
-  p.h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.h_off);
-  p.o = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_off);
+  char* ws = static_cast<char*>(workspace);
+  p.h = reinterpret_cast<uint16_t*>(ws + L.h_off);
+  p.o = reinterpret_cast<float*>(ws + L.o_off);
   p.y = y;
   p.lr_gu = lr_gu;
   p.lr_d = lr_d;
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const int cus = device_cu_count();
-  if (cus <= 0) return MOE_ERR_HIP;
-  const long long max_active = std::min<long long>(E, (long long)T * k);
-  const int rpt_gu = kWavesPerBlock * (kWave / lr_gu) * kU;
-  const int rpt_d = kWavesPerBlock * (kWave / lr_d) * kU;
-  const long long tasks_gu = max_active * ((I + rpt_gu - 1) / rpt_gu);
-  const long long tasks_d = max_active * ((H + rpt_d - 1) / rpt_d);
-  const int cap = cus * 4;
-  const dim3 grid_gu((unsigned)std::min<long long>(tasks_gu, cap));
-  const dim3 grid_d((unsigned)std::min<long long>(tasks_d, cap));
+  const long long slots = std::min<long long>(E, (long long)T * k);
+  const int rpt_gu = kWavesPerBlock * (kWave / lr_gu) * kGuUnits;
+  const int rpt_d = kWavesPerBlock * (kWave / lr_d) * kDUnits;
+  const long long tasks_gu = slots * ((I + rpt_gu - 1) / rpt_gu);
+  const long long tasks_d = slots * ((H + rpt_d - 1) / rpt_d);
 
-  if (cpl_gu == 1) gate_up_gemv<1, kU><<<grid_gu, kThreads, 0, s>>>(p);
-  else gate_up_gemv<2, kU><<<grid_gu, kThreads, 0, s>>>(p);
+  if (lr_gu == 64) launch_gate_up<64>(p, tasks_gu, s);
+  else launch_gate_up<0>(p, tasks_gu, s);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
-  if (cpl_d == 1) down_gemv<1, kU><<<grid_d, kThreads, 0, s>>>(p);
-  else down_gemv<2, kU><<<grid_d, kThreads, 0, s>>>(p);
+  if (lr_d == 16) launch_down<16>(p, tasks_d, s);
+  else launch_down<0>(p, tasks_d, s);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   const long long threads = (long long)T * (H / 2);
   combine_kernel<<<(unsigned)((threads + kThreads - 1) / kThreads), kThreads, 0, s>>>(p);
