@@ -26,24 +26,34 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 
+// Inclusive scan across a 64-lane wavefront with DPP: shifts of 1, 2, 4, 8
+// inside each 16-lane row (lanes without a source add 0), then row broadcasts
+// of lanes 15 and 31 into the rows above them.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_shift(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += dpp_shift<0x111, 0xF>(v);   // row_shr:1
+  v += dpp_shift<0x112, 0xF>(v);   // row_shr:2
+  v += dpp_shift<0x114, 0xF>(v);   // row_shr:4
+  v += dpp_shift<0x118, 0xF>(v);   // row_shr:8
+  v += dpp_shift<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_shift<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // Exclusive scan of one value per thread across the workgroup; returns the
 // exclusive prefix and writes the total to *total (all threads).
 __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  int inc = v;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(inc, off, kWave);
-    if (lane >= off) inc += o;
-  }
+  const int inc = wave_inclusive_scan(v);
   if (lane == kWave - 1) s_wave[wave] = inc;
   __syncthreads();
   if (wave == 0) {
-    int w = lane < kWaves ? s_wave[lane] : 0;
-    int winc = w;
-    for (int off = 1; off < kWaves; off <<= 1) {
-      const int o = __shfl_up(winc, off, kWave);
-      if (lane >= off) winc += o;
-    }
+    const int w = lane < kWaves ? s_wave[lane] : 0;
+    const int winc = wave_inclusive_scan(w);
     if (lane < kWaves) s_wave[lane] = winc - w;         // exclusive wave bases
     if (lane == kWaves - 1) s_wave[kWaves] = winc;      // total
   }

@@ -10,12 +10,14 @@
 // selection and expert-task production").
 //
 // Mapping (gfx950): one 64-lane wavefront per token, four tokens per
-// 256-thread workgroup.  Lane l holds experts [l*V, l*V+V) as 64-bit keys
-//   key = ordered(z) << 32 | (0xFFFFFFFF - e)
-// where ordered() maps fp32 to an unsigned integer with the same order
-// (-0.0 first canonicalised to +0.0).  The maximum key is the largest z with
-// the lowest id.  Each of the k rounds takes a per-lane maximum and a
-// butterfly maximum across the wave; the owner lane then retires the winner.
+// 256-thread workgroup.  Lane l holds experts [l*V, l*V+V) as 32-bit keys
+// ordered(z), an unsigned integer with the same order as the fp32 score
+// (-0.0 first canonicalised to +0.0); absent experts hold 0, below every
+// real key.  Each of the k rounds takes the wave maximum of the lanes' best
+// keys (DPP row steps, then the four row maxima as scalars), then the
+// lowest lane holding that key (ballot): lanes own ascending id ranges, so
+// that lane - and its first matching slot - has the lowest id among equal
+// scores.  Only the winning lane recomputes its best key.
 #include "moe_common.h"
 
 namespace moe {
@@ -28,18 +30,39 @@ __device__ __forceinline__ uint32_t ordered_bits(float z) {
 }
 
 __device__ __forceinline__ float from_ordered(uint32_t o) {
-  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  const uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  for (int off = 32; off > 0; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Maximum over the wavefront (wave-uniform result).  DPP steps reduce each
+// 16-lane row; the four row results are then read as scalars.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x124>(v));   // row_ror:4
+  v = max(v, dpp_u32<0x128>(v));   // row_ror:8
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Sum over the wavefront in a fixed order (wave-uniform result).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 template <int V>
@@ -72,38 +95,46 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
       if (e < E) zv[i] = bias ? row[e] + bias[e] : row[e];
     }
   }
-  uint64_t key[V];
+  uint32_t key[V];
+  uint32_t best = 0;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    const int e = e0 + i;
-    key[i] = (e < E) ? (((uint64_t)ordered_bits(zv[i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e))
-                     : 0;                       // 0 sorts below every real key
+    key[i] = (e0 + i < E) ? ordered_bits(zv[i]) : 0u;
+    best = max(best, key[i]);
   }
 
-  // Selected scores live in lane j (slot j) after the loop.
-  float my_z = 0.0f;
+  // slot j's score and id end up in lane j
+  uint32_t my_key = 0;
   int my_e = 0;
-  float z0 = 0.0f;
+  uint32_t key0 = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+    const uint32_t wbest = wave_max_u32(best);
+    const uint64_t holders = __ballot(best == wbest);
+    const int wl = __builtin_ctzll(holders);    // lowest lane: lowest ids
+    int pick = 0;
+    if (lane == wl) {
+      int first = V;
 #pragma unroll
-    for (int i = 1; i < V; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-    const float z = from_ordered((uint32_t)(best >> 32));
-    if (j == 0) z0 = z;
-    if (lane == j) { my_z = z; my_e = e; }
-    // retire the winner in its owner lane
+      for (int i = V - 1; i >= 0; --i)
+        if (key[i] == wbest) first = i;
+      pick = e0 + first;
+      uint32_t nb = 0;
 #pragma unroll
-    for (int i = 0; i < V; ++i)
-      if (e0 + i == e) key[i] = 0;
+      for (int i = 0; i < V; ++i) {
+        if (i == first) key[i] = 0;             // retire the winner
+        nb = max(nb, key[i]);
+      }
+      best = nb;
+    }
+    const int e_sel = __builtin_amdgcn_readlane(pick, wl);
+    if (j == 0) key0 = wbest;
+    if (lane == j) { my_key = wbest; my_e = e_sel; }
   }
 
   // Renormalised softmax over the chosen set: w_j = exp(z_j - z_0) / sum.
-  // The sum runs in slot order j = 0..k-1 on every lane (fixed order).
-  const float p = (lane < k) ? __builtin_expf(my_z - z0) : 0.0f;
-  float s = 0.0f;
-  for (int j = 0; j < k; ++j) s += __shfl(p, j, kWave);
+  const float z0 = from_ordered(key0);
+  const float p = (lane < k) ? __builtin_expf(from_ordered(my_key) - z0) : 0.0f;
+  const float s = wave_sum_f32(p);
   if (lane < k) {
     topk_idx[(size_t)t * k + lane] = my_e;
     topk_w[(size_t)t * k + lane] = p / s;
@@ -111,7 +142,6 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 }
 
 }  // namespace
-
 }  // namespace moe
 
 extern "C" moe_status moe_route_topk(const float* logits, const float* bias, int T, int E, int k,
