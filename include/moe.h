@@ -105,6 +105,24 @@ moe_status moe_bucket_routes(const int32_t* topk_idx, int T, int E, int k,
                              void* stream);
 
 /*
+ * moe_route_bucket — moe_route_topk followed by moe_bucket_routes, fused.
+ *
+ * Same arguments, outputs, envelope and errors as the two calls in sequence
+ * (outputs are identical bit for bit).  For T <= 64 both steps run in one
+ * workgroup of one kernel, the fused routing kernel's design for small
+ * batches (page "How I forked vLLM and made Qwen3.8-Flash-Next decode 1.6x
+ * faster on one GPU", section "5. Hand-written kernels", paragraph "Fused MoE
+ * routing"); larger batches run the two kernels back to back.
+ */
+moe_status moe_route_bucket(const float* logits, const float* bias,
+                            int T, int E, int k,
+                            int32_t* topk_idx, float* topk_w,
+                            int32_t* expert_count, int32_t* expert_offset,
+                            int32_t* active_experts, int32_t* n_active,
+                            int32_t* route_src, int32_t* route_pos,
+                            void* stream);
+
+/*
  * Bytes of device workspace moe_expert_ffn needs for these sizes (0 when
  * T == 0): the per-route intermediates, 2*I + 4*H bytes per route, each
  * region rounded up to 256 bytes.
@@ -160,6 +178,30 @@ moe_status moe_expert_ffn(const uint16_t* x,
                           void* workspace, size_t workspace_bytes,
                           uint16_t* y,
                           void* stream);
+
+/*
+ * moe_expert_ffn_stage — one stage of moe_expert_ffn, same arguments.
+ *   stage 1: gate/up + SiLU * multiply only; leaves h in the workspace.
+ *   stage 2: down + weighted unroute only; reads h from the workspace, which
+ *            must hold stage 1's result for the same routes and inputs.
+ *   stage 3: both (exactly moe_expert_ffn).
+ * Any other stage returns MOE_ERR_INVALID_SHAPE.  Lets a caller time or
+ * interleave the two streaming phases separately.
+ */
+moe_status moe_expert_ffn_stage(int stage,
+                                const uint16_t* x,
+                                const uint8_t* w_gate, const uint8_t* s_gate,
+                                const uint8_t* w_up, const uint8_t* s_up,
+                                const uint8_t* w_down, const uint8_t* s_down,
+                                const float* g_scale,
+                                const float* topk_w,
+                                const int32_t* expert_count, const int32_t* expert_offset,
+                                const int32_t* active_experts, const int32_t* n_active,
+                                const int32_t* route_src, const int32_t* route_pos,
+                                int T, int H, int I, int E, int k,
+                                void* workspace, size_t workspace_bytes,
+                                uint16_t* y,
+                                void* stream);
 
 /* Static English description of a status code (never NULL). */
 const char* moe_status_string(moe_status s);

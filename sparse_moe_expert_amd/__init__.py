@@ -18,6 +18,7 @@ from ._lib import (
     moe_bucket_routes,
     moe_expert_ffn,
     moe_expert_ffn_workspace_size,
+    moe_route_bucket,
     moe_route_topk,
     moe_status_string,
 )
@@ -35,6 +36,7 @@ __all__ = [
     "moe_bucket_routes",
     "moe_expert_ffn",
     "moe_expert_ffn_workspace_size",
+    "moe_route_bucket",
     "moe_route_topk",
     "moe_status_string",
     "MoeStep",

@@ -33,8 +33,10 @@ _I = ctypes.c_int
 SIGNATURES = {
     "moe_route_topk": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
     "moe_bucket_routes": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_route_bucket": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "moe_expert_ffn": (_I, [_P] * 15 + [_I] * 5 + [_P, ctypes.c_size_t, _P, _P]),
+    "moe_expert_ffn_stage": (_I, [_I] + [_P] * 15 + [_I] * 5 + [_P, ctypes.c_size_t, _P, _P]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -145,6 +147,30 @@ def moe_bucket_routes(topk_idx: torch.Tensor, E: int, out: Optional[Buckets] = N
     return b
 
 
+def moe_route_bucket(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int,
+                     topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+                     out: Optional[Buckets] = None):
+    """moe_route_topk and moe_bucket_routes in one call (one kernel for T <= 64)."""
+    T, E = logits.shape
+    dev = logits.device
+    _need(logits, "logits", torch.float32)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,), dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    b = out if out is not None else empty_buckets(T, E, k, dev)
+    for name, t, n in zip(Buckets._fields, b, (E, E + 1, E, 1, T * k, T * k)):
+        _need(t, name, torch.int32, (n,), dev)
+    st = load_library().moe_route_bucket(_ptr(logits), _ptr(bias), T, E, k, _ptr(topk_idx), _ptr(topk_w),
+                                         *(_ptr(t) for t in b), _stream(dev))
+    _check("moe_route_bucket", st)
+    return topk_idx, topk_w, b
+
+
 class ExpertWeights(NamedTuple):
     w_gate: torch.Tensor   # uint8 [E, I, H/2]
     s_gate: torch.Tensor   # uint8 [E, I, H/16]
@@ -172,8 +198,11 @@ def make_workspace(T: int, H: int, I: int, E: int, k: int, device) -> torch.Tens
 
 def moe_expert_ffn(x: torch.Tensor, weights: ExpertWeights, topk_w: torch.Tensor,
                    buckets: Buckets, workspace: torch.Tensor,
-                   y: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """bf16 [T,H] output of the routed experts.  x is bf16 [T,H] (or its uint16 bits)."""
+                   y: Optional[torch.Tensor] = None, stage: int = 3) -> torch.Tensor:
+    """bf16 [T,H] output of the routed experts.  x is bf16 [T,H] (or its uint16 bits).
+
+    stage 3 runs the whole FFN; 1 runs only gate/up (h stays in the workspace);
+    2 runs only down + unroute on the workspace's h."""
     T, H = x.shape
     E, H_w, I = weights.shape
     k = topk_w.shape[1]
@@ -197,10 +226,14 @@ def moe_expert_ffn(x: torch.Tensor, weights: ExpertWeights, topk_w: torch.Tensor
         y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     if y.dtype != torch.bfloat16 or tuple(y.shape) != (T, H) or not y.is_contiguous() or y.device != dev:
         raise ValueError("y must be a contiguous bfloat16 [T, H] tensor on x's device")
-    st = load_library().moe_expert_ffn(
-        _ptr(x), *(_ptr(t) for t in weights), _ptr(topk_w), *(_ptr(t) for t in buckets),
-        T, H, I, E, k, _ptr(workspace), ctypes.c_size_t(workspace.numel()), _ptr(y), _stream(dev))
-    _check("moe_expert_ffn", st)
+    args = (_ptr(x), *(_ptr(t) for t in weights), _ptr(topk_w), *(_ptr(t) for t in buckets),
+            T, H, I, E, k, _ptr(workspace), ctypes.c_size_t(workspace.numel()), _ptr(y), _stream(dev))
+    if stage == 3:
+        st = load_library().moe_expert_ffn(*args)
+        _check("moe_expert_ffn", st)
+    else:
+        st = load_library().moe_expert_ffn_stage(stage, *args)
+        _check("moe_expert_ffn_stage", st)
     return y
 
 

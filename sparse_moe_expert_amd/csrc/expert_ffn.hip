@@ -11,14 +11,16 @@
 // Flash Next on LiL/vLLM", section "11.13 Where the decode step's time
 // actually goes").
 //
-// Three kernels on one stream; the kernel boundaries order the phases, so no
+// Kernels on one stream; the kernel boundaries order the phases, so no
 // workgroup ever waits for another:
 //   gate_up_kernel  task (active slot a, tile of I rows): h[p, rows] =
 //                   bf16(SiLU(Wg x) * (Wu x)) for every route p of the expert
 //   down_kernel     task (active slot a, tile of H rows): o[p, rows] = Wd h[p]
 //   combine_kernel  y[t] = bf16( sum_{j=0}^{k-1} w[t,j] * o[route_pos[t*k+j]] ),
 //                   j in slot order
-// h and o live in the caller's workspace, indexed by bucket position p.
+// h and o live in the caller's workspace, indexed by bucket position p.  For
+// small batches (all routes' h fit in 64 KB of LDS) down_combine_kernel does
+// the down projection and the unroute in one pass split by output rows.
 //
 // Row tiles (gfx950).  A wavefront reads whole rows: Lr lanes share a row and
 // each lane reads one 16-byte chunk of e2m1 codes (32 values) plus its two
@@ -52,6 +54,7 @@ struct FfnParams {
   const int32_t* count;
   const int32_t* offset;
   const int32_t* active;
+  const int32_t* n_active_ptr;
   const int32_t* route_src;
   const int32_t* route_pos;
   int T, H, I, E, k;
@@ -67,6 +70,9 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 constexpr int kGuUnits = 4;          // gate rows (and as many up rows) per wave per tile
 constexpr int kDUnits = 8;           // down rows per lane group per tile
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
+// Scale bytes of one tile: rows_per_tile * cols/16 = 4 waves * (64/Lr) rows *
+// units * 2*Lr bytes = 512 * units bytes when each lane reads one chunk.
+constexpr int kScaleTileBytes = 2048;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -187,29 +193,36 @@ __device__ __forceinline__ bool slot_routes(const FfnParams& p, int a, int& e, i
 
 // Gate and up rows of one I tile for all cnt routes of expert e.  Each wave
 // holds kGuUnits gate rows and the same up rows; with 64 lanes per row the
-// four units' sums are scattered so that lane row r ends with unit r.
+// four units' sums are scattered so that lane row r ends with unit r.  The
+// tile's scale bytes (2 KB of gate, 2 KB of up: rpt rows of H/16 bytes) and
+// the current token's activations (H bf16) are staged in LDS with one
+// 16-byte load per thread instead of one small load per unit and wave.
 template <int LG>
-__device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, kGuUnits>& g, int e, int off,
-                                             int cnt, int tile) {
+__device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, kGuUnits>& g, uint8_t* s_sc,
+                                             uint4* s_x, int e, int off, int cnt, int tile) {
   const uint32_t code_row = (uint32_t)p.H / 2, scale_row = (uint32_t)p.H / 16;
   const uint32_t mat_codes = (uint32_t)p.I * code_row, mat_scales = (uint32_t)p.I * scale_row;
   const auto rg = make_rsrc(p.wg + (size_t)e * mat_codes, mat_codes);
   const auto ru = make_rsrc(p.wu + (size_t)e * mat_codes, mat_codes);
-  const auto rgs = make_rsrc(p.sg + (size_t)e * mat_scales, mat_scales);
-  const auto rus = make_rsrc(p.su + (size_t)e * mat_scales, mat_scales);
   const uint32_t lane_c = (uint32_t)g.sub * code_row + (uint32_t)g.sl * 16;
-  const uint32_t lane_s = (uint32_t)g.sub * scale_row + (uint32_t)g.sl * 2;
   uint4 cg[kGuUnits], cu[kGuUnits];
-  uint32_t vg[kGuUnits], vu[kGuUnits];
 #pragma unroll
   for (int u = 0; u < kGuUnits; ++u) {
     const uint32_t r0 = (uint32_t)g.row0(tile, u);
     cg[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rg, lane_c, r0 * code_row, 0));
     cu[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(ru, lane_c, r0 * code_row, 0));
-    vg[u] = __builtin_amdgcn_raw_buffer_load_b16(rgs, lane_s, r0 * scale_row, 0);
-    vu[u] = __builtin_amdgcn_raw_buffer_load_b16(rus, lane_s, r0 * scale_row, 0);
+  }
+  {
+    // scales of rows [tile*rpt, tile*rpt + rpt): gate in s_sc[0, 2K), up in s_sc[2K, 4K)
+    const uint32_t blk = (uint32_t)g.rpt * scale_row;          // 2048 bytes
+    const int half = (int)(threadIdx.x >= kThreads / 2);
+    const uint32_t byte = (uint32_t)(threadIdx.x & (kThreads / 2 - 1)) * 16;
+    const auto rs = make_rsrc((half ? p.su : p.sg) + (size_t)e * mat_scales, mat_scales);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, byte, (uint32_t)tile * blk, 0);
+    *reinterpret_cast<u32x4*>(s_sc + half * blk + byte) = v;
   }
   const float Gg = p.gsc[e * 3 + 0], Gu = p.gsc[e * 3 + 1];
+  const int chunks = p.H / 8;                                    // 16-byte pieces of one x row
   for (int t = 0; t < cnt; ++t) {
     const int pos = off + t;
 #pragma unroll
@@ -218,13 +231,20 @@ __device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, k
       opaque(cu[u]);
     }
     const int tok = min(max(p.route_src[pos] / p.k, 0), p.T - 1);
+    if (t > 0) __syncthreads();                                  // previous token's x reads done
+    for (int i = threadIdx.x; i < chunks; i += kThreads)
+      s_x[i] = reinterpret_cast<const uint4*>(p.x + (size_t)tok * p.H)[i];
+    __syncthreads();
     uint32_t xr[16];
-    load_operand_chunk(p.x + (size_t)tok * p.H, g.sl, xr);
+    load_operand_chunk(reinterpret_cast<const uint16_t*>(s_x), g.sl, xr);
     float ag[kGuUnits], au[kGuUnits];
 #pragma unroll
     for (int u = 0; u < kGuUnits; ++u) {
-      ag[u] = dot_chunk(cg[u], vg[u], xr, 0.0f);
-      au[u] = dot_chunk(cu[u], vu[u], xr, 0.0f);
+      const int rin = (u * kWavesPerBlock + g.wave) * g.rpw + g.sub;   // row within the tile
+      const uint32_t sg = *reinterpret_cast<const uint16_t*>(s_sc + rin * scale_row + g.sl * 2);
+      const uint32_t su = *reinterpret_cast<const uint16_t*>(s_sc + g.rpt * scale_row + rin * scale_row + g.sl * 2);
+      ag[u] = dot_chunk(cg[u], sg, xr, 0.0f);
+      au[u] = dot_chunk(cu[u], su, xr, 0.0f);
     }
     if constexpr (LG == 64) {
       static_assert(kGuUnits == 4, "the row scatter maps 4 units to 4 lane rows");
@@ -247,34 +267,48 @@ __device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, k
 
 template <int LG>
 __global__ __launch_bounds__(kThreads, 4) void gate_up_kernel(FfnParams p, int n_tasks) {
+  __shared__ __align__(16) uint8_t s_sc[2 * kScaleTileBytes];
+  extern __shared__ uint4 s_x[];                // one activation row (H bf16)
   const Geo<LG, kGuUnits> g(p.lr_gu, p.I);
   for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
     const int a = task / g.tiles, tile = task - a * g.tiles;
     int e, off, cnt;
     if (!slot_routes(p, a, e, off, cnt)) continue;
-    gate_up_tile<LG>(p, g, e, off, cnt, tile);
+    __syncthreads();                            // LDS of the previous task is free
+    gate_up_tile<LG>(p, g, s_sc, s_x, e, off, cnt, tile);
   }
 }
 
 // ------------------------------------------------------------------ down
 
-// Down rows of one H tile for all cnt routes of expert e (weights loaded once).
+// Down rows of one H tile for all cnt routes of expert e (weights loaded
+// once).  The tile's scale bytes (rpt rows of I/16 bytes, 4 KB) are staged in
+// LDS with one 16-byte load per thread.
 template <int LD>
-__device__ __forceinline__ void down_tile(const FfnParams& p, const Geo<LD, kDUnits>& g, int e, int off, int cnt,
-                                          int tile) {
+__device__ __forceinline__ void down_tile(const FfnParams& p, const Geo<LD, kDUnits>& g, uint8_t* s_sc, int e,
+                                          int off, int cnt, int tile) {
   const uint32_t code_row = (uint32_t)p.I / 2, scale_row = (uint32_t)p.I / 16;
   const uint32_t mat_codes = (uint32_t)p.H * code_row, mat_scales = (uint32_t)p.H * scale_row;
   const auto rd = make_rsrc(p.wd + (size_t)e * mat_codes, mat_codes);
-  const auto rds = make_rsrc(p.sd + (size_t)e * mat_scales, mat_scales);
   const uint32_t lane_c = (uint32_t)g.sub * code_row + (uint32_t)g.sl * 16;
-  const uint32_t lane_s = (uint32_t)g.sub * scale_row + (uint32_t)g.sl * 2;
   uint4 cd[kDUnits];
-  uint32_t vd[kDUnits];
 #pragma unroll
   for (int u = 0; u < kDUnits; ++u) {
     const uint32_t r0 = (uint32_t)g.row0(tile, u);
     cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, lane_c, r0 * code_row, 0));
-    vd[u] = __builtin_amdgcn_raw_buffer_load_b16(rds, lane_s, r0 * scale_row, 0);
+  }
+  {
+    const uint32_t blk = (uint32_t)g.rpt * scale_row;          // 4096 bytes
+    const auto rs = make_rsrc(p.sd + (size_t)e * mat_scales, mat_scales);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)threadIdx.x * 16, (uint32_t)tile * blk, 0);
+    *reinterpret_cast<u32x4*>(s_sc + threadIdx.x * 16) = v;
+  }
+  __syncthreads();
+  uint32_t vd[kDUnits];
+#pragma unroll
+  for (int u = 0; u < kDUnits; ++u) {
+    const int rin = (u * kWavesPerBlock + g.wave) * g.rpw + g.sub;
+    vd[u] = *reinterpret_cast<const uint16_t*>(s_sc + rin * scale_row + g.sl * 2);
   }
   const float Gd = p.gsc[e * 3 + 2];
   for (int t = 0; t < cnt; ++t) {
@@ -298,47 +332,143 @@ __device__ __forceinline__ void down_tile(const FfnParams& p, const Geo<LD, kDUn
 
 template <int LD>
 __global__ __launch_bounds__(kThreads, 4) void down_kernel(FfnParams p, int n_tasks) {
+  __shared__ __align__(16) uint8_t s_sc[2 * kScaleTileBytes];
   const Geo<LD, kDUnits> g(p.lr_d, p.H);
   for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
     const int a = task / g.tiles, tile = task - a * g.tiles;
     int e, off, cnt;
     if (!slot_routes(p, a, e, off, cnt)) continue;
-    down_tile<LD>(p, g, e, off, cnt, tile);
+    __syncthreads();                            // LDS of the previous task is free
+    down_tile<LD>(p, g, s_sc, e, off, cnt, tile);
   }
 }
 
 // ------------------------------------------------------------------ combine
 
+constexpr int kCombineCols = 2 * kThreads;   // output columns per workgroup
+constexpr int kMaxK = 32;
+
 // y[t, c..c+1] = sum over slots j in order of w[t,j] * o[route_pos[t*k+j], c..c+1].
+// One workgroup per (token, 512 columns): the token's weights and route
+// positions are staged once, then every o load is issued before the sum.
 __global__ __launch_bounds__(kThreads) void combine_kernel(FfnParams p) {
-  const int pairs = p.H / 2;
-  const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
-  if (gid >= (long long)p.T * pairs) return;
-  const int t = (int)(gid / pairs);
-  const int c = (int)(gid - (long long)t * pairs) * 2;
+  __shared__ float s_w[kMaxK];
+  __shared__ int s_pos[kMaxK];
+  const int col_blocks = (p.H + kCombineCols - 1) / kCombineCols;
+  const int t = blockIdx.x / col_blocks;
+  const int c = (blockIdx.x - t * col_blocks) * kCombineCols + 2 * threadIdx.x;
   const int R = p.T * p.k;
-  const float* wrow = p.topk_w + (size_t)t * p.k;
-  const int32_t* prow = p.route_pos + (size_t)t * p.k;
+  if (threadIdx.x < p.k) {
+    s_w[threadIdx.x] = p.topk_w[(size_t)t * p.k + threadIdx.x];
+    s_pos[threadIdx.x] = min(max(p.route_pos[(size_t)t * p.k + threadIdx.x], 0), R - 1);
+  }
+  __syncthreads();
+  if (c >= p.H) return;
+  float2 ov[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < p.k) ov[j] = *reinterpret_cast<const float2*>(p.o + (size_t)s_pos[j] * p.H + c);
   float y0 = 0.0f, y1 = 0.0f;
-  for (int j0 = 0; j0 < p.k; j0 += 8) {
-    float w[8];
-    float2 ov[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool ok = j0 + j < p.k;
-      w[j] = ok ? wrow[j0 + j] : 0.0f;
-      const int pos = ok ? min(max(prow[j0 + j], 0), R - 1) : 0;
-      ov[j] = ok ? *reinterpret_cast<const float2*>(p.o + (size_t)pos * p.H + c) : make_float2(0.f, 0.f);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j0 + j < p.k) {
-        y0 = fmaf(w[j], ov[j].x, y0);
-        y1 = fmaf(w[j], ov[j].y, y1);
-      }
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < p.k) {
+      y0 = fmaf(s_w[j], ov[j].x, y0);
+      y1 = fmaf(s_w[j], ov[j].y, y1);
     }
   }
   reinterpret_cast<uint32_t*>(p.y)[((size_t)t * p.H + c) >> 1] = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
+}
+
+// ------------------------------------------------------------------ down + combine (small batches)
+
+constexpr int kDcMaxRoutes = 128;          // T*k on the fused down/combine path
+constexpr int kDcMaxHBytes = 65536;        // all routes' h staged in LDS up to this size
+constexpr int kDcChunk = 8;                // expert units in flight per wave
+
+// Down projection and weighted unroute of a small batch in one kernel, with
+// the work split by output rows instead of by expert: workgroup b owns rows
+// [b*rpw, b*rpw + rpw) of y (rpw = 64 / lanes per row) for every token.  It
+// stages all routes' h rows in LDS, its four waves stream those rows of every
+// active expert's W_down (slots a = wave, wave+4, ...; one 16-byte chunk per
+// lane and expert, eight experts in flight), keep o[route, row] in LDS, and
+// finally sum each token's routes in slot order.  No o round trip through
+// memory and no cross-workgroup ordering.
+template <int LD>
+__global__ __launch_bounds__(kThreads, 2) void down_combine_kernel(FfnParams p) {
+  extern __shared__ uint4 s_dyn[];          // [R, I] bf16 h, then [R, rpw] fp32 o
+  __shared__ int s_e[kDcMaxRoutes], s_off[kDcMaxRoutes], s_cnt[kDcMaxRoutes];
+  __shared__ int s_pos[kDcMaxRoutes];
+  __shared__ float s_w[kDcMaxRoutes];
+  __shared__ int s_nact;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ld = LD ? LD : p.lr_d, rpw = kWave / ld, sub = lane / ld, sl = lane & (ld - 1);
+  const int row0 = blockIdx.x * rpw;
+  const int R = p.T * p.k;
+  const int S = min(p.E, R);
+  uint16_t* s_h = reinterpret_cast<uint16_t*>(s_dyn);
+  float* s_o = reinterpret_cast<float*>(s_h + (size_t)R * p.I);
+
+  // prologue: slot metadata, route positions and weights, and every h row
+  if (tid == 0) s_nact = min(max(*p.n_active_ptr, 0), S);
+  for (int i = tid; i < S; i += kThreads) {
+    const int e = min(max(p.active[i], 0), p.E - 1);
+    const int off = min(max(p.offset[e], 0), R);
+    s_e[i] = e;
+    s_off[i] = off;
+    s_cnt[i] = min(max(p.count[e], 0), R - off);
+  }
+  for (int i = tid; i < R; i += kThreads) {
+    s_pos[i] = min(max(p.route_pos[i], 0), R - 1);
+    s_w[i] = p.topk_w[i];
+  }
+  for (int i = tid; i < R * p.I / 8; i += kThreads) s_dyn[i] = reinterpret_cast<const uint4*>(p.h)[i];
+  __syncthreads();
+
+  const int n_act = __builtin_amdgcn_readfirstlane(s_nact);
+  const uint32_t code_row = (uint32_t)p.I / 2, scale_row = (uint32_t)p.I / 16;
+  const auto rd = make_rsrc(p.wd, (uint32_t)p.E * p.H * code_row);
+  const auto rds = make_rsrc(p.sd, (uint32_t)p.E * p.H * scale_row);
+  const uint32_t lane_c = (uint32_t)sub * code_row + (uint32_t)sl * 16;
+  const uint32_t lane_s = (uint32_t)sub * scale_row + (uint32_t)sl * 2;
+  const bool row_ok = row0 + sub < p.H;
+  for (int c0 = wave; c0 < n_act; c0 += kWavesPerBlock * kDcChunk) {
+    uint4 cd[kDcChunk];
+    uint32_t vd[kDcChunk];
+#pragma unroll
+    for (int u = 0; u < kDcChunk; ++u) {
+      const int a = c0 + u * kWavesPerBlock;
+      const uint32_t r = (uint32_t)(a < n_act ? s_e[a] : 0) * (uint32_t)p.H + (uint32_t)row0;
+      cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, lane_c, r * code_row, 0));
+      vd[u] = __builtin_amdgcn_raw_buffer_load_b16(rds, lane_s, r * scale_row, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kDcChunk; ++u) {
+      const int a = c0 + u * kWavesPerBlock;
+      if (a >= n_act) break;
+      const int e = s_e[a], off = s_off[a], cnt = s_cnt[a];
+      const float Gd = p.gsc[e * 3 + 2];
+      for (int t = 0; t < cnt; ++t) {
+        const int pos = off + t;
+        opaque(cd[u]);
+        uint32_t hr[16];
+        load_operand_chunk(s_h + (size_t)pos * p.I, sl, hr);
+        const float acc = dot_chunk(cd[u], vd[u], hr, 0.0f);
+        const float v = (LD == 16 ? row16_sum(acc) : group_sum(acc, ld)) * Gd;
+        if (sl == 0 && row_ok) s_o[pos * rpw + sub] = v;
+      }
+    }
+  }
+  __syncthreads();
+
+  // y[t, row0 + r] = sum over slots j in order of w[t,j] * o[route_pos[t,j], r]
+  for (int i = tid; i < p.T * rpw; i += kThreads) {
+    const int t = i / rpw, r = i - t * rpw;
+    if (row0 + r >= p.H) continue;
+    float acc = 0.0f;
+    for (int j = 0; j < p.k; ++j) acc = fmaf(s_w[t * p.k + j], s_o[s_pos[t * p.k + j] * rpw + r], acc);
+    p.y[(size_t)t * p.H + row0 + r] = (uint16_t)f32_to_bf16_rne(acc);
+  }
 }
 
 // ------------------------------------------------------------------ host
@@ -363,7 +493,7 @@ constexpr long long kMaxGrid = 1 << 20;
 template <int LG>
 void launch_gate_up(const FfnParams& p, long long tasks, hipStream_t s) {
   const unsigned grid = (unsigned)std::max<long long>(1, std::min<long long>(tasks, kMaxGrid));
-  gate_up_kernel<LG><<<grid, kThreads, 0, s>>>(p, (int)tasks);
+  gate_up_kernel<LG><<<grid, kThreads, (size_t)p.H * 2, s>>>(p, (int)tasks);
 }
 
 template <int LD>
@@ -381,7 +511,7 @@ extern "C" size_t moe_expert_ffn_workspace_size(int T, int H, int I, int E, int 
   return moe::workspace_layout(T, H, I, k).total;
 }
 
-extern "C" moe_status moe_expert_ffn(const uint16_t* x, const uint8_t* w_gate, const uint8_t* s_gate,
+extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const uint8_t* w_gate, const uint8_t* s_gate,
                                      const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,
                                      const uint8_t* s_down, const float* g_scale, const float* topk_w,
                                      const int32_t* expert_count, const int32_t* expert_offset,
@@ -390,6 +520,7 @@ extern "C" moe_status moe_expert_ffn(const uint16_t* x, const uint8_t* w_gate, c
                                      int I, int E, int k, void* workspace, size_t workspace_bytes,
                                      uint16_t* y, void* stream) {
   using namespace moe;
+  if (stage < 1 || stage > 3) return MOE_ERR_INVALID_SHAPE;
   if (T < 0 || k < 1 || E < 1 || k > E || H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
     return MOE_ERR_INVALID_SHAPE;
   if (E > 1024 || k > 32 || H > 4096 || I > 4096) return MOE_ERR_UNSUPPORTED;
@@ -410,7 +541,7 @@ extern "C" moe_status moe_expert_ffn(const uint16_t* x, const uint8_t* w_gate, c
   FfnParams p;
   p.x = x; p.wg = w_gate; p.sg = s_gate; p.wu = w_up; p.su = s_up; p.wd = w_down; p.sd = s_down;
   p.gsc = g_scale; p.topk_w = topk_w; p.count = expert_count; p.offset = expert_offset;
-  p.active = active_experts; p.route_src = route_src; p.route_pos = route_pos;
+  p.active = active_experts; p.n_active_ptr = n_active; p.route_src = route_src; p.route_pos = route_pos;
   p.T = T; p.H = H; p.I = I; p.E = E; p.k = k;
   char* ws = static_cast<char*>(workspace);
   p.h = reinterpret_cast<uint16_t*>(ws + L.h_off);
@@ -426,13 +557,41 @@ extern "C" moe_status moe_expert_ffn(const uint16_t* x, const uint8_t* w_gate, c
   const long long tasks_gu = slots * ((I + rpt_gu - 1) / rpt_gu);
   const long long tasks_d = slots * ((H + rpt_d - 1) / rpt_d);
 
-  if (lr_gu == 64) launch_gate_up<64>(p, tasks_gu, s);
-  else launch_gate_up<0>(p, tasks_gu, s);
-  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  if (stage & 1) {
+    if (lr_gu == 64) launch_gate_up<64>(p, tasks_gu, s);
+    else launch_gate_up<0>(p, tasks_gu, s);
+    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  }
+  if (!(stage & 2)) return MOE_OK;
+  const long long R = (long long)T * k;
+  const size_t h_bytes = (size_t)R * I * 2;
+  // one buffer resource spans all of W_down: its byte count must fit 31 bits
+  const bool dc_fits = (size_t)E * H * (I / 2) < (size_t)0x7FFFFFFF;
+  if (R <= kDcMaxRoutes && h_bytes <= (size_t)kDcMaxHBytes && dc_fits) {
+    const int rpw = kWave / lr_d;
+    const size_t dyn = h_bytes + (size_t)R * rpw * 4;
+    const unsigned grid = (unsigned)((H + rpw - 1) / rpw);
+    if (lr_d == 16) down_combine_kernel<16><<<grid, kThreads, dyn, s>>>(p);
+    else down_combine_kernel<0><<<grid, kThreads, dyn, s>>>(p);
+    return launch_status();
+  }
   if (lr_d == 16) launch_down<16>(p, tasks_d, s);
   else launch_down<0>(p, tasks_d, s);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
-  const long long threads = (long long)T * (H / 2);
-  combine_kernel<<<(unsigned)((threads + kThreads - 1) / kThreads), kThreads, 0, s>>>(p);
+  const long long cblocks = (long long)T * ((H + kCombineCols - 1) / kCombineCols);
+  combine_kernel<<<(unsigned)cblocks, kThreads, 0, s>>>(p);
   return launch_status();
+}
+
+extern "C" moe_status moe_expert_ffn(const uint16_t* x, const uint8_t* w_gate, const uint8_t* s_gate,
+                                     const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,
+                                     const uint8_t* s_down, const float* g_scale, const float* topk_w,
+                                     const int32_t* expert_count, const int32_t* expert_offset,
+                                     const int32_t* active_experts, const int32_t* n_active,
+                                     const int32_t* route_src, const int32_t* route_pos, int T, int H,
+                                     int I, int E, int k, void* workspace, size_t workspace_bytes,
+                                     uint16_t* y, void* stream) {
+  return moe_expert_ffn_stage(3, x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
+                              expert_offset, active_experts, n_active, route_src, route_pos, T, H, I, E, k,
+                              workspace, workspace_bytes, y, stream);
 }

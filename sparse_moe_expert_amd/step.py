@@ -19,6 +19,7 @@ from ._lib import (
     make_workspace,
     moe_bucket_routes,
     moe_expert_ffn,
+    moe_route_bucket,
     moe_route_topk,
 )
 
@@ -35,8 +36,12 @@ def expert_weights_from_numpy(bank, device) -> ExpertWeights:
 
 
 class MoeStep:
-    def __init__(self, T: int, H: int, I: int, E: int, k: int, device):
+    """fused_routing: route and bucket with moe_route_bucket (one call) instead
+    of moe_route_topk followed by moe_bucket_routes; the outputs are identical."""
+
+    def __init__(self, T: int, H: int, I: int, E: int, k: int, device, fused_routing: bool = True):
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        self.fused_routing = fused_routing
         self.device = torch.device(device)
         self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=self.device)
         self.topk_w = torch.empty((T, k), dtype=torch.float32, device=self.device)
@@ -50,12 +55,21 @@ class MoeStep:
     def bucket(self):
         moe_bucket_routes(self.topk_idx, self.E, self.buckets)
 
-    def ffn(self, x: torch.Tensor, weights: ExpertWeights):
-        moe_expert_ffn(x, weights, self.topk_w, self.buckets, self.workspace, self.y)
+    def route_bucket(self, logits: torch.Tensor, bias: Optional[torch.Tensor]):
+        moe_route_bucket(logits, bias, self.k, self.topk_idx, self.topk_w, self.buckets)
+
+    def ffn(self, x: torch.Tensor, weights: ExpertWeights, stage: int = 3):
+        moe_expert_ffn(x, weights, self.topk_w, self.buckets, self.workspace, self.y, stage=stage)
+
+    def routing(self, logits: torch.Tensor, bias: Optional[torch.Tensor]):
+        if self.fused_routing:
+            self.route_bucket(logits, bias)
+        else:
+            self.route(logits, bias)
+            self.bucket()
 
     def run(self, x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor],
             weights: ExpertWeights) -> torch.Tensor:
-        self.route(logits, bias)
-        self.bucket()
+        self.routing(logits, bias)
         self.ffn(x, weights)
         return self.y

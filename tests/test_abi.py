@@ -92,3 +92,19 @@ def test_expert_ffn_host_checks(lib):
     assert lib.moe_expert_ffn_workspace_size(0, 256, 128, 8, 2) == 0
     # grows with T*k: h (bf16 [R,I]) and o (fp32 [R,H])
     assert lib.moe_expert_ffn_workspace_size(8, 256, 128, 8, 2) > need
+
+
+def test_route_bucket_host_checks(lib):
+    f = lib.moe_route_bucket
+    assert f(A, None, 4, 8, 9, A, A, A, A, A, A, A, A, None) == 2
+    assert f(A, None, 0, 8, 2, A, A, A, A, A, A, A, A, None) == 0
+    assert f(A, None, 4, 8, 2, A, A, None, A, A, A, A, A, None) == 1
+    assert f(A, None, 4, 2048, 2, A, A, A, A, A, A, A, A, None) == 3
+
+
+def test_ffn_stage_host_checks(lib):
+    ptrs = [A] * 15
+    f = lib.moe_expert_ffn_stage
+    for bad in (0, 4, -1):
+        assert f(bad, *ptrs, 4, 256, 128, 8, 2, A, ctypes.c_size_t(1 << 20), A, None) == 2
+    assert f(1, *ptrs, 0, 256, 128, 8, 2, A, ctypes.c_size_t(1 << 20), A, None) == 0

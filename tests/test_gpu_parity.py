@@ -204,3 +204,38 @@ def test_hand_worked_cases_on_gpu():
         ref[:, 0::2] = ev(case["y"]["even"])
         ref[:, 1::2] = ev(case["y"]["odd"])
         assert_output(g["y"], ref, case["name"])
+
+
+@pytest.mark.parametrize("name", CONFIG_ORDER)
+def test_fused_routing_matches_two_calls(name):
+    """moe_route_bucket gives exactly the outputs of moe_route_topk + moe_bucket_routes."""
+    wl = make_workload(name, with_bank=False)
+    logits = to_dev(wl.logits)
+    bias = None if wl.bias is None else to_dev(wl.bias)
+    a = sme.MoeStep(wl.T, wl.H, wl.I, wl.E, wl.k, DEV, fused_routing=True)
+    b = sme.MoeStep(wl.T, wl.H, wl.I, wl.E, wl.k, DEV, fused_routing=False)
+    a.routing(logits, bias)
+    b.routing(logits, bias)
+    torch.cuda.synchronize()
+    assert torch.equal(a.topk_idx, b.topk_idx)
+    assert torch.equal(a.topk_w.view(torch.int32), b.topk_w.view(torch.int32))
+    for ta, tb in zip(a.buckets, b.buckets):
+        assert torch.equal(ta, tb)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_t4", "verify_t32"])
+def test_stages_compose_to_full_call(name):
+    """moe_expert_ffn_stage 1 then 2 equals moe_expert_ffn bit for bit."""
+    wl = make_workload(name)
+    W = device_weights(wl.bank)
+    st = sme.MoeStep(wl.T, wl.H, wl.I, wl.E, wl.k, DEV)
+    x = x_bits(wl.x)
+    st.routing(to_dev(wl.logits), None if wl.bias is None else to_dev(wl.bias))
+    st.ffn(x, W)
+    torch.cuda.synchronize()
+    full = st.y.clone()
+    st.y.zero_()
+    st.ffn(x, W, stage=1)
+    st.ffn(x, W, stage=2)
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int16), st.y.view(torch.int16))
