@@ -1,7 +1,10 @@
 """Benchmark one routed-MoE step (route -> bucket -> expert FFN) on one MI355X.
 
-A step is one pass of the whole path over one batch: moe_route_topk,
-moe_bucket_routes and moe_expert_ffn, captured together in one HIP graph.
+A step is one pass of the whole path over one batch: routing (top-k and
+bucketing) and the expert FFN with the weighted unroute.  By default it is
+one moe_step call (moe_route_bucket + moe_expert_ffn: three kernels at this
+size); --path calls_unfused runs the three separate calls.  Steps are
+captured in HIP graphs.
 The default workload is the decode verify step: T=4 tokens, H=2048, I=512,
 E=512 experts, top-10, NVFP4 experts, bf16 activations.
 
@@ -13,7 +16,8 @@ of traffic (the 256 MB MALL would otherwise hold a step's ~69 MB).
 Output: one JSON line.  `value` is the effective HBM bandwidth on unique
 expert bytes (unique experts of the step x 1,769,484 B) divided by the
 measured step time; `us_per_step` is the step time.  `roofline` covers the
-expert FFN call, timed with HIP events around each launch on its stream.
+dominant kernel, the gate/up projection: HIP events on its stream around a
+graph of back-to-back launches of that kernel alone.
 `cpu_baseline` is the fp64 CPU oracle timed on this host on a bounded sample.
 """
 
@@ -44,9 +48,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", default="decode_t4")
+    ap.add_argument("--path", default="step", choices=["step", "calls", "calls_unfused"],
+                    help="step: moe_step (one call); calls: moe_route_bucket + moe_expert_ffn; "
+                         "calls_unfused: the three separate calls")
     ap.add_argument("--banks", type=int, default=8)
     ap.add_argument("--ffn-launches", type=int, default=400,
-                    help="eager moe_expert_ffn launches timed with events for the roofline")
+                    help="launches of the dominant kernel timed with events for the roofline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle sample budget (0 disables the cpu_baseline leg)")
     return ap.parse_args()
@@ -116,7 +123,7 @@ def main():
     xs = [torch.from_numpy(w.x.view(np.int16)).to(dev) for w in wls]
     ls = [torch.from_numpy(w.logits).to(dev) for w in wls]
     bias = None if wls[0].bias is None else torch.from_numpy(wls[0].bias).to(dev)
-    step = sme.MoeStep(T, H, I, E, k, dev)
+    step = sme.MoeStep(T, H, I, E, k, dev, path=args.path)
 
     # unique experts per routing set, and warm-up outside capture
     n_unique = []
@@ -159,26 +166,37 @@ def main():
     log(f"[bench] {s_per_step * 1e6:.2f} us/step, {eff_tbps:.3f} TB/s effective")
 
     # Roofline leg: the dominant kernel is the gate/up projection (two thirds
-    # of the weight bytes).  HIP events bracket each eager launch of that stage
-    # alone (moe_expert_ffn_stage 1, one kernel) on the stream the library
-    # launches on (torch's current stream); the down stage runs outside them.
+    # of the weight bytes, the longest kernel of the step).  HIP events on the
+    # stream the library launches on (torch's current stream) bracket the
+    # replay of a graph that holds only launches of that kernel
+    # (moe_expert_ffn_stage 1), back to back over the NB (bank, routing set)
+    # pairs, so the average launch duration includes no host launch gaps.
+    # Each pair keeps its own step object, so the routing stays that pair's.
     stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.ffn_launches)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.ffn_launches)]
-    gu_bytes = []
-    for i in range(args.ffn_launches):
-        b = i % NB
-        step.routing(ls[b], bias)
-        starts[i].record(stream)
-        step.ffn(xs[b], banks[b], stage=1)
-        ends[i].record(stream)
-        step.ffn(xs[b], banks[b], stage=2)
-        gu_bytes.append(n_unique[b] * GATE_UP_BYTES_PER_EXPERT + T * H * 2 + n_routes * I * 2)
+    reps = max(1, args.ffn_launches // NB)
+    kname = "gate_up_kernel"
+    dom_bytes = float(np.mean(n_unique)) * GATE_UP_BYTES_PER_EXPERT + T * H * 2 + n_routes * I * 2
+    gu_steps = []
+    for b in range(NB):
+        sb = sme.MoeStep(T, H, I, E, k, dev, path=args.path)
+        sb.routing(ls[b], bias)
+        gu_steps.append(sb)
+    g_dom = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_dom):
+        for _ in range(reps):
+            for b in range(NB):
+                gu_steps[b].ffn(xs[b], banks[b], stage=1)
+    g_dom.replay()                      # warm-up
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    g_dom.replay()
+    ev1.record(stream)
     torch.cuda.synchronize()
-    durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e-3   # seconds
-    avg = float(durs.mean())
-    achieved = float(np.mean(gu_bytes)) / avg / 1e9
-    log(f"[bench] gate/up kernel avg {avg * 1e6:.2f} us -> {achieved:.1f} GB/s")
+    n_dom = reps * NB
+    avg = ev0.elapsed_time(ev1) * 1e-3 / n_dom          # seconds per launch
+    achieved = dom_bytes / avg / 1e9
+    log(f"[bench] {kname} avg {avg * 1e6:.2f} us over {n_dom} launches -> {achieved:.1f} GB/s")
 
     out = {
         "metric": METRIC,
@@ -196,13 +214,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "H": H, "I": I, "E": E, "k": k,
-                   "weights": "nvfp4", "banks": NB,
+                   "weights": "nvfp4", "banks": NB, "path": args.path,
                    "unique_experts_per_step": round(float(np.mean(n_unique)), 2),
                    "unique_expert_bytes_per_step": int(bytes_per_step)},
-        "roofline": {"bound": "hbm", "kernel": "gate_up_kernel",
+        "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "avg_launch_us": round(avg * 1e6, 3)},
+                     "avg_launch_us": round(avg * 1e6, 3),
+                     "bytes_per_launch": int(dom_bytes), "launches": n_dom},
     }
     if args.cpu_seconds > 0:
         log(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s budget)")

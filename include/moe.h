@@ -6,6 +6,7 @@
  *   moe_route_topk     router logits -> top-k expert ids and gate weights
  *   moe_bucket_routes  top-k ids -> routes grouped by expert (stable order)
  *   moe_expert_ffn     bf16 tokens + NVFP4 experts + buckets -> bf16 output
+ * or the same step in one call, moe_step (one kernel for small batches).
  * The router projection that produces the logits is a prerequisite outside
  * these calls (the MonoMoE host wrapper takes precomputed router logits and
  * the SM70 design note keeps the router GEMV as an explicit prerequisite:
@@ -202,6 +203,41 @@ moe_status moe_expert_ffn_stage(int stage,
                                 void* workspace, size_t workspace_bytes,
                                 uint16_t* y,
                                 void* stream);
+
+/*
+ * Bytes of device workspace moe_step needs for these sizes (0 when T == 0);
+ * equal to moe_expert_ffn_workspace_size.
+ */
+size_t moe_step_workspace_size(int T, int H, int I, int E, int k);
+
+/*
+ * moe_step — one whole routed-MoE step: moe_route_topk, moe_bucket_routes
+ * and moe_expert_ffn in one call, with the same inputs and outputs (all
+ * identical to what those calls produce).  It enqueues moe_route_bucket and
+ * then moe_expert_ffn on `stream`.
+ *   x, w_*, s_*, g_scale  in   as for moe_expert_ffn
+ *   logits, bias          in   as for moe_route_topk
+ *   topk_idx, topk_w      out  as from moe_route_topk
+ *   expert_count ... route_pos  out  as from moe_bucket_routes
+ *   workspace             >= moe_step_workspace_size(T,H,I,E,k) bytes, owned
+ *                         by the caller, as for moe_expert_ffn
+ *   y                     [T, H] bf16 bits out
+ * Shapes, envelope and errors: those of the three calls; arguments are all
+ * checked before anything is launched.
+ */
+moe_status moe_step(const uint16_t* x, const float* logits, const float* bias,
+                    const uint8_t* w_gate, const uint8_t* s_gate,
+                    const uint8_t* w_up, const uint8_t* s_up,
+                    const uint8_t* w_down, const uint8_t* s_down,
+                    const float* g_scale,
+                    int T, int H, int I, int E, int k,
+                    int32_t* topk_idx, float* topk_w,
+                    int32_t* expert_count, int32_t* expert_offset,
+                    int32_t* active_experts, int32_t* n_active,
+                    int32_t* route_src, int32_t* route_pos,
+                    void* workspace, size_t workspace_bytes,
+                    uint16_t* y,
+                    void* stream);
 
 /* Static English description of a status code (never NULL). */
 const char* moe_status_string(moe_status s);

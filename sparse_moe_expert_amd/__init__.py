@@ -1,8 +1,8 @@
 """Routed NVFP4 mixture-of-experts FFN on MI355X (gfx950).
 
 A C-ABI HIP library (include/moe.h) with three calls per routed-MoE step:
-moe_route_topk -> moe_bucket_routes -> moe_expert_ffn, bound here for torch
-tensors.  PyTorch provides device memory and the stream; the kernels are the
+moe_route_topk -> moe_bucket_routes -> moe_expert_ffn (or the whole step in
+one call, moe_step), bound here for torch tensors.  PyTorch provides device memory and the stream; the kernels are the
 library's own.
 """
 
@@ -21,6 +21,8 @@ from ._lib import (
     moe_route_bucket,
     moe_route_topk,
     moe_status_string,
+    moe_step,
+    moe_step_workspace_size,
 )
 from .step import MoeStep, expert_weights_from_numpy
 
@@ -39,6 +41,8 @@ __all__ = [
     "moe_route_bucket",
     "moe_route_topk",
     "moe_status_string",
+    "moe_step",
+    "moe_step_workspace_size",
     "MoeStep",
     "expert_weights_from_numpy",
 ]

@@ -37,6 +37,8 @@ SIGNATURES = {
     "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "moe_expert_ffn": (_I, [_P] * 15 + [_I] * 5 + [_P, ctypes.c_size_t, _P, _P]),
     "moe_expert_ffn_stage": (_I, [_I] + [_P] * 15 + [_I] * 5 + [_P, ctypes.c_size_t, _P, _P]),
+    "moe_step_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "moe_step": (_I, [_P, _P, _P] + [_P] * 7 + [_I] * 5 + [_P] * 8 + [_P, ctypes.c_size_t, _P, _P]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -207,12 +209,7 @@ def moe_expert_ffn(x: torch.Tensor, weights: ExpertWeights, topk_w: torch.Tensor
     E, H_w, I = weights.shape
     k = topk_w.shape[1]
     dev = x.device
-    if x.dtype == torch.bfloat16:
-        x = x.view(torch.int16)
-    if x.dtype not in (torch.int16, torch.uint16):
-        raise TypeError("x must be bfloat16 (or its 16-bit patterns)")
-    if not x.is_cuda or not x.is_contiguous():
-        raise ValueError("x must be a contiguous device tensor")
+    x = _check_x(x)
     if H_w != H:
         raise ValueError(f"weights are for H={H_w}, x has H={H}")
     shapes = [(E, I, H // 2), (E, I, H // 16), (E, I, H // 2), (E, I, H // 16),
@@ -234,6 +231,52 @@ def moe_expert_ffn(x: torch.Tensor, weights: ExpertWeights, topk_w: torch.Tensor
     else:
         st = load_library().moe_expert_ffn_stage(stage, *args)
         _check("moe_expert_ffn_stage", st)
+    return y
+
+
+def _check_x(x: torch.Tensor) -> torch.Tensor:
+    if x.dtype == torch.bfloat16:
+        x = x.view(torch.int16)
+    if x.dtype not in (torch.int16, torch.uint16):
+        raise TypeError("x must be bfloat16 (or its 16-bit patterns)")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous device tensor")
+    return x
+
+
+def moe_step_workspace_size(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(load_library().moe_step_workspace_size(T, H, I, E, k))
+
+
+def moe_step(x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor], weights: ExpertWeights,
+             k: int, topk_idx: torch.Tensor, topk_w: torch.Tensor, buckets: Buckets,
+             workspace: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+    """One whole step (route, bucket, expert FFN) in one call; fills every output."""
+    x = _check_x(x)
+    T, H = x.shape
+    E, H_w, I = weights.shape
+    dev = x.device
+    if H_w != H:
+        raise ValueError(f"weights are for H={H_w}, x has H={H}")
+    _need(logits, "logits", torch.float32, (T, E), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,), dev)
+    shapes = [(E, I, H // 2), (E, I, H // 16), (E, I, H // 2), (E, I, H // 16),
+              (E, H, I // 2), (E, H, I // 16)]
+    for name, t, shp in zip(ExpertWeights._fields, weights, shapes):
+        _need(t, name, torch.uint8, shp, dev)
+    _need(weights.g_scale, "g_scale", torch.float32, (E, 3), dev)
+    _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    for name, t, n in zip(Buckets._fields, buckets, (E, E + 1, E, 1, T * k, T * k)):
+        _need(t, name, torch.int32, (n,), dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    if y.dtype != torch.bfloat16 or tuple(y.shape) != (T, H) or not y.is_contiguous() or y.device != dev:
+        raise ValueError("y must be a contiguous bfloat16 [T, H] tensor on x's device")
+    st = load_library().moe_step(_ptr(x), _ptr(logits), _ptr(bias), *(_ptr(t) for t in weights),
+                                 T, H, I, E, k, _ptr(topk_idx), _ptr(topk_w), *(_ptr(t) for t in buckets),
+                                 _ptr(workspace), ctypes.c_size_t(workspace.numel()), _ptr(y), _stream(dev))
+    _check("moe_step", st)
     return y
 
 

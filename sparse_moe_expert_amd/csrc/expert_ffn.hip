@@ -36,7 +36,7 @@
 // (<= 128 VGPRs) - the VALU needs that many waves to reach its issue rate.
 #include <algorithm>
 
-#include "moe_common.h"
+#include "row_dot.h"
 
 namespace moe {
 namespace {
@@ -65,143 +65,63 @@ struct FfnParams {
   int lr_d;      // lanes per down row
 };
 
-constexpr int kThreads = 256;
-constexpr int kWavesPerBlock = kThreads / kWave;
 constexpr int kGuUnits = 4;          // gate rows (and as many up rows) per wave per tile
 constexpr int kDUnits = 8;           // down rows per lane group per tile
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 // Scale bytes of one tile: rows_per_tile * cols/16 = 4 waves * (64/Lr) rows *
 // units * 2*Lr bytes = 512 * units bytes when each lane reads one chunk.
 constexpr int kScaleTileBytes = 2048;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Routing metadata is read through the scalar memory path (s_load): it is
+// wave-uniform, and scalar loads are counted apart from the vector loads, so
+// a metadata fetch issued while a tile's weight rows are in flight does not
+// have to wait for them (vector loads complete in order).
+typedef const __attribute__((address_space(4))) int32_t* scalar_ptr;
+__device__ __forceinline__ int sload(const int32_t* base, int i) { return ((scalar_ptr)base)[i]; }
 
-// ------------------------------------------------------------------ helpers
-
-// Buffer resource over [base, base + bytes): loads outside it return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+// Expert id of active slot a (-1 past the active list), clamped into range:
+// inputs that violate the bucket precondition give wrong results but no
+// out-of-bounds access.
+__device__ __forceinline__ int slot_expert(const FfnParams& p, int a) {
+  const int e = sload(p.active, a);
+  return e < 0 ? -1 : min(e, p.E - 1);
 }
 
-__device__ __forceinline__ uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
-
-// Makes a register's value opaque to the optimiser (no instruction).  Used at
-// the top of per-route loops so the weight conversions are not hoisted out of
-// the loop, which would keep every converted value live at once.
-__device__ __forceinline__ void opaque(uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
-
-// One 16-byte chunk (32 NVFP4 values, two scale blocks) dotted with an
-// operand chunk xr (operand elements 2i, 2i+1 as bf16x2 in xr[i]); adds
-// sum_block(scale * sum(code * operand)) to acc.
-__device__ __forceinline__ float dot_chunk(const uint4 codes, uint32_t s2, const uint32_t (&xr)[16], float acc) {
-  const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 0);
-  const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 1);
-  const uint32_t c[4] = {codes.x, codes.y, codes.z, codes.w};
-  float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<0>(c[q]), as_bf16x2(xr[4 * q + 0]), p0, false);
-    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<1>(c[q]), as_bf16x2(xr[4 * q + 1]), p0, false);
-    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<2>(c[q]), as_bf16x2(xr[4 * q + 2]), p0, false);
-    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<3>(c[q]), as_bf16x2(xr[4 * q + 3]), p0, false);
-  }
-#pragma unroll
-  for (int q = 2; q < 4; ++q) {
-    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<0>(c[q]), as_bf16x2(xr[4 * q + 0]), p1, false);
-    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<1>(c[q]), as_bf16x2(xr[4 * q + 1]), p1, false);
-    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<2>(c[q]), as_bf16x2(xr[4 * q + 2]), p1, false);
-    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<3>(c[q]), as_bf16x2(xr[4 * q + 3]), p1, false);
-  }
-  acc = fmaf(p0, s0, acc);
-  return fmaf(p1, s1, acc);
-}
-
-// Load the 64-byte operand chunk `chunk` of a bf16 row into 16 dwords.
-__device__ __forceinline__ void load_operand_chunk(const uint16_t* row, int chunk, uint32_t (&dst)[16]) {
-  const uint4* p = reinterpret_cast<const uint4*>(row + (size_t)chunk * 32);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint4 v = p[q];
-    dst[4 * q + 0] = v.x; dst[4 * q + 1] = v.y; dst[4 * q + 2] = v.z; dst[4 * q + 3] = v.w;
-  }
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float v) {
-  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over each 16-lane row (fixed order); every lane of the row gets it.
-__device__ __forceinline__ float row16_sum(float v) {
-  v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
-  v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
-  v = dpp_add<0x124>(v);   // row_ror:4
-  v = dpp_add<0x128>(v);   // row_ror:8
-  return v;
-}
-
-__device__ __forceinline__ uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
-__device__ __forceinline__ float bitsf(uint32_t v) { return __builtin_bit_cast(float, v); }
-
-// a0..a3 hold row sums (uniform within each 16-lane row).  Returns a value
-// whose row r holds a_r summed over all four rows (v_permlane32_swap swaps the
-// upper rows of its first operand with the lower rows of its second;
-// v_permlane16_swap swaps odd rows of the first with even rows of the second).
-__device__ __forceinline__ float rows_scatter4(float a0, float a1, float a2, float a3) {
-  const auto s02 = __builtin_amdgcn_permlane32_swap(fbits(a0), fbits(a2), false, false);
-  const auto s13 = __builtin_amdgcn_permlane32_swap(fbits(a1), fbits(a3), false, false);
-  const float b02 = bitsf(s02[0]) + bitsf(s02[1]);
-  const float b13 = bitsf(s13[0]) + bitsf(s13[1]);
-  const auto t = __builtin_amdgcn_permlane16_swap(fbits(b02), fbits(b13), false, false);
-  return bitsf(t[0]) + bitsf(t[1]);
-}
-
-// Lane geometry of one projection.  LR: lanes per row known at compile time
-// (64 for rows of 2048 values, 16 for rows of 512), or 0 for a runtime value.
-template <int LR, int UNITS>
-struct Geo {
-  int lr, rpw, sub, sl, rpt, tiles, wave;
-  __device__ Geo(int lr_rt, int rows_total) {
-    const int lane = threadIdx.x & (kWave - 1);
-    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    lr = LR ? LR : lr_rt;
-    rpw = kWave / lr;
-    sub = lane / lr;
-    sl = lane & (lr - 1);
-    rpt = kWavesPerBlock * rpw * UNITS;
-    tiles = (rows_total + rpt - 1) / rpt;
-  }
-  // first row of unit u for this wave (wave-uniform); the lane's row adds sub
-  __device__ int row0(int tile, int u) const { return tile * rpt + (u * kWavesPerBlock + wave) * rpw; }
-};
-
-// Expert id, first bucket position and route count of active slot a
-// (wave-uniform).  Values come from moe_bucket_routes and are clamped into
-// range, so inputs that violate that precondition give wrong results but no
-// out-of-bounds access.  Returns false for a slot past the active list.
-__device__ __forceinline__ bool slot_routes(const FfnParams& p, int a, int& e, int& off, int& cnt) {
-  e = __builtin_amdgcn_readfirstlane(p.active[a]);
-  if (e < 0) return false;
-  e = min(e, p.E - 1);
+// First bucket position and route count of expert e, clamped into [0, R].
+__device__ __forceinline__ void expert_routes(const FfnParams& p, int e, int& off, int& cnt) {
   const int R = p.T * p.k;
-  off = min(max(p.offset[e], 0), R);
-  cnt = min(max(p.count[e], 0), R - off);
-  return cnt > 0;
+  off = min(max(sload(p.offset, e), 0), R);
+  cnt = min(max(sload(p.count, e), 0), R - off);
 }
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+__device__ __forceinline__ void wait_vector_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ------------------------------------------------------------------ gate/up
 
-// Gate and up rows of one I tile for all cnt routes of expert e.  Each wave
-// holds kGuUnits gate rows and the same up rows; with 64 lanes per row the
-// four units' sums are scattered so that lane row r ends with unit r.  The
-// tile's scale bytes (2 KB of gate, 2 KB of up: rpt rows of H/16 bytes) and
-// the current token's activations (H bf16) are staged in LDS with one
-// 16-byte load per thread instead of one small load per unit and wave.
+// Activation rows staged per group of routes (16 KB of LDS).
+constexpr int kXStageBytes = 16384;
+
+// Gate and up rows of one I tile for all routes of expert e.  Each wave holds
+// kGuUnits gate rows and the same up rows; with 64 lanes per row the four
+// units' sums are scattered so that lane row r ends with unit r.  Issue
+// order: the tile's scale bytes (2 KB gate + 2 KB up, one 16-byte load per
+// thread), the weight rows, then - through the scalar path - the expert's
+// routes, and the activation rows of its first routes straight into LDS.
+// Only then are the scale bytes written to LDS, so that store waits for the
+// scale loads alone, and nothing issued after the weights is needed before
+// they arrive.
 template <int LG>
 __device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, kGuUnits>& g, uint8_t* s_sc,
-                                             uint4* s_x, int e, int off, int cnt, int tile) {
+                                             uint8_t* s_x, int e, int tile) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const uint32_t code_row = (uint32_t)p.H / 2, scale_row = (uint32_t)p.H / 16;
   const uint32_t mat_codes = (uint32_t)p.I * code_row, mat_scales = (uint32_t)p.I * scale_row;
+  const uint32_t blk = (uint32_t)g.rpt * scale_row;            // 2048 bytes
+  const int half = (int)(tid >= kThreads / 2);
+  const uint32_t sbyte = (uint32_t)(tid & (kThreads / 2 - 1)) * 16;
+  const auto rs = make_rsrc((half ? p.su : p.sg) + (size_t)e * mat_scales, mat_scales);
+  const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rs, sbyte, (uint32_t)tile * blk, 0);
+  compiler_fence();
   const auto rg = make_rsrc(p.wg + (size_t)e * mat_codes, mat_codes);
   const auto ru = make_rsrc(p.wu + (size_t)e * mat_codes, mat_codes);
   const uint32_t lane_c = (uint32_t)g.sub * code_row + (uint32_t)g.sl * 16;
@@ -212,54 +132,66 @@ __device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, k
     cg[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rg, lane_c, r0 * code_row, 0));
     cu[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(ru, lane_c, r0 * code_row, 0));
   }
-  {
-    // scales of rows [tile*rpt, tile*rpt + rpt): gate in s_sc[0, 2K), up in s_sc[2K, 4K)
-    const uint32_t blk = (uint32_t)g.rpt * scale_row;          // 2048 bytes
-    const int half = (int)(threadIdx.x >= kThreads / 2);
-    const uint32_t byte = (uint32_t)(threadIdx.x & (kThreads / 2 - 1)) * 16;
-    const auto rs = make_rsrc((half ? p.su : p.sg) + (size_t)e * mat_scales, mat_scales);
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, byte, (uint32_t)tile * blk, 0);
-    *reinterpret_cast<u32x4*>(s_sc + half * blk + byte) = v;
-  }
+  compiler_fence();
+  int off, cnt;
+  expert_routes(p, e, off, cnt);
   const float Gg = p.gsc[e * 3 + 0], Gu = p.gsc[e * 3 + 1];
-  const int chunks = p.H / 8;                                    // 16-byte pieces of one x row
-  for (int t = 0; t < cnt; ++t) {
-    const int pos = off + t;
-#pragma unroll
-    for (int u = 0; u < kGuUnits; ++u) {
-      opaque(cg[u]);
-      opaque(cu[u]);
+  const int row_bytes = p.H * 2;
+  const int group = max(1, min(kXStageBytes / row_bytes, 64));
+  const int pieces = row_bytes / 16;                             // 16-byte pieces of one x row
+  bool scales_stored = false;
+  for (int g0 = 0; g0 < cnt; g0 += group) {
+    const int ng = min(group, cnt - g0);
+    if (g0 > 0) __syncthreads();                                 // previous group's x reads done
+    // x rows of routes g0 .. g0+ng straight into LDS, one 1 KB wave load per step
+    for (int i = 0; i < ng; ++i) {
+      const int tok = min(max(sload(p.route_src, off + g0 + i) / p.k, 0), p.T - 1);
+      const uint4* src = reinterpret_cast<const uint4*>(p.x + (size_t)tok * p.H);
+      for (int q0 = g.wave * kWave; q0 < pieces; q0 += kThreads) {
+        if (q0 + lane < pieces)
+          __builtin_amdgcn_global_load_lds(src + q0 + lane, s_x + (size_t)i * row_bytes + (size_t)q0 * 16, 16, 0, 0);
+      }
     }
-    const int tok = min(max(p.route_src[pos] / p.k, 0), p.T - 1);
-    if (t > 0) __syncthreads();                                  // previous token's x reads done
-    for (int i = threadIdx.x; i < chunks; i += kThreads)
-      s_x[i] = reinterpret_cast<const uint4*>(p.x + (size_t)tok * p.H)[i];
+    if (!scales_stored) {
+      compiler_fence();
+      *reinterpret_cast<u32x4*>(s_sc + half * blk + sbyte) = sv;
+      scales_stored = true;
+    }
+    wait_vector_loads();
     __syncthreads();
-    uint32_t xr[16];
-    load_operand_chunk(reinterpret_cast<const uint16_t*>(s_x), g.sl, xr);
-    float ag[kGuUnits], au[kGuUnits];
-#pragma unroll
-    for (int u = 0; u < kGuUnits; ++u) {
-      const int rin = (u * kWavesPerBlock + g.wave) * g.rpw + g.sub;   // row within the tile
-      const uint32_t sg = *reinterpret_cast<const uint16_t*>(s_sc + rin * scale_row + g.sl * 2);
-      const uint32_t su = *reinterpret_cast<const uint16_t*>(s_sc + g.rpt * scale_row + rin * scale_row + g.sl * 2);
-      ag[u] = dot_chunk(cg[u], sg, xr, 0.0f);
-      au[u] = dot_chunk(cu[u], su, xr, 0.0f);
-    }
-    if constexpr (LG == 64) {
-      static_assert(kGuUnits == 4, "the row scatter maps 4 units to 4 lane rows");
-      const int row = g.row0(tile, (threadIdx.x & (kWave - 1)) >> 4);
-      const float gs = rows_scatter4(row16_sum(ag[0]), row16_sum(ag[1]), row16_sum(ag[2]), row16_sum(ag[3])) * Gg;
-      const float us = rows_scatter4(row16_sum(au[0]), row16_sum(au[1]), row16_sum(au[2]), row16_sum(au[3])) * Gu;
-      if ((threadIdx.x & 15) == 0 && row < p.I)
-        p.h[(size_t)pos * p.I + row] = (uint16_t)f32_to_bf16_rne(silu(gs) * us);
-    } else {
+    for (int i = 0; i < ng; ++i) {
+      const int pos = off + g0 + i;
 #pragma unroll
       for (int u = 0; u < kGuUnits; ++u) {
-        const int row = g.row0(tile, u) + g.sub;
-        const float gs = group_sum(ag[u], g.lr) * Gg;
-        const float us = group_sum(au[u], g.lr) * Gu;
-        if (g.sl == 0 && row < p.I) p.h[(size_t)pos * p.I + row] = (uint16_t)f32_to_bf16_rne(silu(gs) * us);
+        opaque(cg[u]);
+        opaque(cu[u]);
+      }
+      uint32_t xr[16];
+      load_operand_chunk(reinterpret_cast<const uint16_t*>(s_x + (size_t)i * row_bytes), g.sl, xr);
+      float ag[kGuUnits], au[kGuUnits];
+#pragma unroll
+      for (int u = 0; u < kGuUnits; ++u) {
+        const int rin = (u * kWavesPerBlock + g.wave) * g.rpw + g.sub;   // row within the tile
+        const uint32_t sg = *reinterpret_cast<const uint16_t*>(s_sc + rin * scale_row + g.sl * 2);
+        const uint32_t su = *reinterpret_cast<const uint16_t*>(s_sc + blk + rin * scale_row + g.sl * 2);
+        ag[u] = dot_chunk(cg[u], sg, xr, 0.0f);
+        au[u] = dot_chunk(cu[u], su, xr, 0.0f);
+      }
+      if constexpr (LG == 64) {
+        static_assert(kGuUnits == 4, "the row scatter maps 4 units to 4 lane rows");
+        const int row = g.row0(tile, lane >> 4);
+        const float gs = rows_scatter4(row16_sum(ag[0]), row16_sum(ag[1]), row16_sum(ag[2]), row16_sum(ag[3])) * Gg;
+        const float us = rows_scatter4(row16_sum(au[0]), row16_sum(au[1]), row16_sum(au[2]), row16_sum(au[3])) * Gu;
+        if ((lane & 15) == 0 && row < p.I)
+          p.h[(size_t)pos * p.I + row] = (uint16_t)f32_to_bf16_rne(silu(gs) * us);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kGuUnits; ++u) {
+          const int row = g.row0(tile, u) + g.sub;
+          const float gs = group_sum(ag[u], g.lr) * Gg;
+          const float us = group_sum(au[u], g.lr) * Gu;
+          if (g.sl == 0 && row < p.I) p.h[(size_t)pos * p.I + row] = (uint16_t)f32_to_bf16_rne(silu(gs) * us);
+        }
       }
     }
   }
@@ -268,27 +200,32 @@ __device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, k
 template <int LG>
 __global__ __launch_bounds__(kThreads, 4) void gate_up_kernel(FfnParams p, int n_tasks) {
   __shared__ __align__(16) uint8_t s_sc[2 * kScaleTileBytes];
-  extern __shared__ uint4 s_x[];                // one activation row (H bf16)
+  extern __shared__ __align__(16) uint8_t s_x[];                // activation rows of a group of routes
   const Geo<LG, kGuUnits> g(p.lr_gu, p.I);
   for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
     const int a = task / g.tiles, tile = task - a * g.tiles;
-    int e, off, cnt;
-    if (!slot_routes(p, a, e, off, cnt)) continue;
+    const int e = slot_expert(p, a);
+    if (e < 0) continue;
     __syncthreads();                            // LDS of the previous task is free
-    gate_up_tile<LG>(p, g, s_sc, s_x, e, off, cnt, tile);
+    gate_up_tile<LG>(p, g, s_sc, s_x, e, tile);
   }
 }
 
 // ------------------------------------------------------------------ down
 
-// Down rows of one H tile for all cnt routes of expert e (weights loaded
-// once).  The tile's scale bytes (rpt rows of I/16 bytes, 4 KB) are staged in
-// LDS with one 16-byte load per thread.
+// Down rows of one H tile for all routes of expert e (weights loaded once).
+// The tile's scale bytes (rpt rows of I/16 bytes, 4 KB) go to LDS with one
+// 16-byte load per thread, issued before the weight rows; the expert's route
+// range comes through the scalar path while the rows are in flight.
 template <int LD>
 __device__ __forceinline__ void down_tile(const FfnParams& p, const Geo<LD, kDUnits>& g, uint8_t* s_sc, int e,
-                                          int off, int cnt, int tile) {
+                                          int tile) {
   const uint32_t code_row = (uint32_t)p.I / 2, scale_row = (uint32_t)p.I / 16;
   const uint32_t mat_codes = (uint32_t)p.H * code_row, mat_scales = (uint32_t)p.H * scale_row;
+  const uint32_t blk = (uint32_t)g.rpt * scale_row;            // 4096 bytes
+  const auto rs = make_rsrc(p.sd + (size_t)e * mat_scales, mat_scales);
+  const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)threadIdx.x * 16, (uint32_t)tile * blk, 0);
+  compiler_fence();
   const auto rd = make_rsrc(p.wd + (size_t)e * mat_codes, mat_codes);
   const uint32_t lane_c = (uint32_t)g.sub * code_row + (uint32_t)g.sl * 16;
   uint4 cd[kDUnits];
@@ -297,12 +234,10 @@ __device__ __forceinline__ void down_tile(const FfnParams& p, const Geo<LD, kDUn
     const uint32_t r0 = (uint32_t)g.row0(tile, u);
     cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, lane_c, r0 * code_row, 0));
   }
-  {
-    const uint32_t blk = (uint32_t)g.rpt * scale_row;          // 4096 bytes
-    const auto rs = make_rsrc(p.sd + (size_t)e * mat_scales, mat_scales);
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)threadIdx.x * 16, (uint32_t)tile * blk, 0);
-    *reinterpret_cast<u32x4*>(s_sc + threadIdx.x * 16) = v;
-  }
+  compiler_fence();
+  int off, cnt;
+  expert_routes(p, e, off, cnt);
+  *reinterpret_cast<u32x4*>(s_sc + threadIdx.x * 16) = sv;
   __syncthreads();
   uint32_t vd[kDUnits];
 #pragma unroll
@@ -336,10 +271,10 @@ __global__ __launch_bounds__(kThreads, 4) void down_kernel(FfnParams p, int n_ta
   const Geo<LD, kDUnits> g(p.lr_d, p.H);
   for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
     const int a = task / g.tiles, tile = task - a * g.tiles;
-    int e, off, cnt;
-    if (!slot_routes(p, a, e, off, cnt)) continue;
+    const int e = slot_expert(p, a);
+    if (e < 0) continue;
     __syncthreads();                            // LDS of the previous task is free
-    down_tile<LD>(p, g, s_sc, e, off, cnt, tile);
+    down_tile<LD>(p, g, s_sc, e, tile);
   }
 }
 
@@ -383,73 +318,92 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(FfnParams p) {
 
 constexpr int kDcMaxRoutes = 128;          // T*k on the fused down/combine path
 constexpr int kDcMaxHBytes = 65536;        // all routes' h staged in LDS up to this size
-constexpr int kDcChunk = 8;                // expert units in flight per wave
+constexpr int kDcThreads = 512;            // eight waves share one row block
+constexpr int kDcWaves = kDcThreads / kWave;
+constexpr int kDcSlots = 8;                // expert rows in flight per wave
 
 // Down projection and weighted unroute of a small batch in one kernel, with
 // the work split by output rows instead of by expert: workgroup b owns rows
-// [b*rpw, b*rpw + rpw) of y (rpw = 64 / lanes per row) for every token.  It
-// stages all routes' h rows in LDS, its four waves stream those rows of every
-// active expert's W_down (slots a = wave, wave+4, ...; one 16-byte chunk per
-// lane and expert, eight experts in flight), keep o[route, row] in LDS, and
-// finally sum each token's routes in slot order.  No o round trip through
-// memory and no cross-workgroup ordering.
+// [b*rpw, b*rpw + rpw) of y (rpw = 64 / lanes per row) for every token.  Its
+// eight waves take the active slots a = wave, wave+8, ... and hold one
+// 16-byte chunk per lane of each slot's rows of W_down (up to kDcSlots slots
+// in flight per wave), o[route, row] stays in LDS, and each token's routes
+// are finally summed in slot order.  Issue order: all routes' h rows
+// straight into LDS, the routes' positions and weights, the slots' expert
+// ids (scalar path), then every weight row; route ranges come through the
+// scalar path while the rows are in flight.  No o round trip through memory
+// and no cross-workgroup ordering.
 template <int LD>
-__global__ __launch_bounds__(kThreads, 2) void down_combine_kernel(FfnParams p) {
-  extern __shared__ uint4 s_dyn[];          // [R, I] bf16 h, then [R, rpw] fp32 o
-  __shared__ int s_e[kDcMaxRoutes], s_off[kDcMaxRoutes], s_cnt[kDcMaxRoutes];
+__global__ __launch_bounds__(kDcThreads, 2) void down_combine_kernel(FfnParams p) {
+  extern __shared__ __align__(16) uint8_t s_dyn8[];   // [R, I] bf16 h, then [R, rpw] fp32 o
   __shared__ int s_pos[kDcMaxRoutes];
   __shared__ float s_w[kDcMaxRoutes];
-  __shared__ int s_nact;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ld = LD ? LD : p.lr_d, rpw = kWave / ld, sub = lane / ld, sl = lane & (ld - 1);
   const int row0 = blockIdx.x * rpw;
   const int R = p.T * p.k;
   const int S = min(p.E, R);
-  uint16_t* s_h = reinterpret_cast<uint16_t*>(s_dyn);
-  float* s_o = reinterpret_cast<float*>(s_h + (size_t)R * p.I);
+  uint16_t* s_h = reinterpret_cast<uint16_t*>(s_dyn8);
+  float* s_o = reinterpret_cast<float*>(s_dyn8 + (size_t)R * p.I * 2);
 
-  // prologue: slot metadata, route positions and weights, and every h row
-  if (tid == 0) s_nact = min(max(*p.n_active_ptr, 0), S);
-  for (int i = tid; i < S; i += kThreads) {
-    const int e = min(max(p.active[i], 0), p.E - 1);
-    const int off = min(max(p.offset[e], 0), R);
-    s_e[i] = e;
-    s_off[i] = off;
-    s_cnt[i] = min(max(p.count[e], 0), R - off);
+  // h rows of every route, 1 KB per wave load
+  const int pieces = R * p.I / 8;
+  const uint4* hsrc = reinterpret_cast<const uint4*>(p.h);
+  for (int q0 = wave * kWave; q0 < pieces; q0 += kDcThreads)
+    if (q0 + lane < pieces) __builtin_amdgcn_global_load_lds(hsrc + q0 + lane, s_dyn8 + (size_t)q0 * 16, 16, 0, 0);
+  int pos_r = 0;
+  float w_r = 0.0f;
+  if (tid < R) {
+    pos_r = min(max(p.route_pos[tid], 0), R - 1);
+    w_r = p.topk_w[tid];
   }
-  for (int i = tid; i < R; i += kThreads) {
-    s_pos[i] = min(max(p.route_pos[i], 0), R - 1);
-    s_w[i] = p.topk_w[i];
-  }
-  for (int i = tid; i < R * p.I / 8; i += kThreads) s_dyn[i] = reinterpret_cast<const uint4*>(p.h)[i];
-  __syncthreads();
+  compiler_fence();
 
-  const int n_act = __builtin_amdgcn_readfirstlane(s_nact);
   const uint32_t code_row = (uint32_t)p.I / 2, scale_row = (uint32_t)p.I / 16;
   const auto rd = make_rsrc(p.wd, (uint32_t)p.E * p.H * code_row);
   const auto rds = make_rsrc(p.sd, (uint32_t)p.E * p.H * scale_row);
   const uint32_t lane_c = (uint32_t)sub * code_row + (uint32_t)sl * 16;
   const uint32_t lane_s = (uint32_t)sub * scale_row + (uint32_t)sl * 2;
   const bool row_ok = row0 + sub < p.H;
-  for (int c0 = wave; c0 < n_act; c0 += kWavesPerBlock * kDcChunk) {
-    uint4 cd[kDcChunk];
-    uint32_t vd[kDcChunk];
+  // the trip count is the same for every wave (the loop holds a barrier)
+  for (int c0 = 0; c0 < S; c0 += kDcWaves * kDcSlots) {
+    int e_u[kDcSlots];
+    uint4 cd[kDcSlots];
+    uint32_t vd[kDcSlots];
 #pragma unroll
-    for (int u = 0; u < kDcChunk; ++u) {
-      const int a = c0 + u * kWavesPerBlock;
-      const uint32_t r = (uint32_t)(a < n_act ? s_e[a] : 0) * (uint32_t)p.H + (uint32_t)row0;
-      cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, lane_c, r * code_row, 0));
-      vd[u] = __builtin_amdgcn_raw_buffer_load_b16(rds, lane_s, r * scale_row, 0);
+    for (int u = 0; u < kDcSlots; ++u) {
+      const int a = c0 + wave + u * kDcWaves;
+      e_u[u] = a < S ? slot_expert(p, a) : -1;
     }
 #pragma unroll
-    for (int u = 0; u < kDcChunk; ++u) {
-      const int a = c0 + u * kWavesPerBlock;
-      if (a >= n_act) break;
-      const int e = s_e[a], off = s_off[a], cnt = s_cnt[a];
-      const float Gd = p.gsc[e * 3 + 2];
-      for (int t = 0; t < cnt; ++t) {
-        const int pos = off + t;
+    for (int u = 0; u < kDcSlots; ++u) {
+      if (e_u[u] >= 0) {
+        const uint32_t r = (uint32_t)e_u[u] * (uint32_t)p.H + (uint32_t)row0;
+        cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, lane_c, r * code_row, 0));
+        vd[u] = __builtin_amdgcn_raw_buffer_load_b16(rds, lane_s, r * scale_row, 0);
+      }
+    }
+    compiler_fence();
+    int off_u[kDcSlots], cnt_u[kDcSlots];
+#pragma unroll
+    for (int u = 0; u < kDcSlots; ++u) {
+      off_u[u] = 0;
+      cnt_u[u] = 0;
+      if (e_u[u] >= 0) expert_routes(p, e_u[u], off_u[u], cnt_u[u]);
+    }
+    if (c0 == 0 && tid < R) {
+      s_pos[tid] = pos_r;
+      s_w[tid] = w_r;
+    }
+    wait_vector_loads();
+    __syncthreads();                            // h of every route is in LDS
+#pragma unroll
+    for (int u = 0; u < kDcSlots; ++u) {
+      if (e_u[u] < 0) continue;
+      const float Gd = p.gsc[e_u[u] * 3 + 2];
+      for (int t = 0; t < cnt_u[u]; ++t) {
+        const int pos = off_u[u] + t;
         opaque(cd[u]);
         uint32_t hr[16];
         load_operand_chunk(s_h + (size_t)pos * p.I, sl, hr);
@@ -462,7 +416,7 @@ __global__ __launch_bounds__(kThreads, 2) void down_combine_kernel(FfnParams p) 
   __syncthreads();
 
   // y[t, row0 + r] = sum over slots j in order of w[t,j] * o[route_pos[t,j], r]
-  for (int i = tid; i < p.T * rpw; i += kThreads) {
+  for (int i = tid; i < p.T * rpw; i += kDcThreads) {
     const int t = i / rpw, r = i - t * rpw;
     if (row0 + r >= p.H) continue;
     float acc = 0.0f;
@@ -493,7 +447,9 @@ constexpr long long kMaxGrid = 1 << 20;
 template <int LG>
 void launch_gate_up(const FfnParams& p, long long tasks, hipStream_t s) {
   const unsigned grid = (unsigned)std::max<long long>(1, std::min<long long>(tasks, kMaxGrid));
-  gate_up_kernel<LG><<<grid, kThreads, (size_t)p.H * 2, s>>>(p, (int)tasks);
+  const int row_bytes = p.H * 2;
+  const size_t x_lds = (size_t)std::max(1, std::min(kXStageBytes / row_bytes, 64)) * row_bytes;
+  gate_up_kernel<LG><<<grid, kThreads, x_lds, s>>>(p, (int)tasks);
 }
 
 template <int LD>
@@ -571,8 +527,8 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
     const int rpw = kWave / lr_d;
     const size_t dyn = h_bytes + (size_t)R * rpw * 4;
     const unsigned grid = (unsigned)((H + rpw - 1) / rpw);
-    if (lr_d == 16) down_combine_kernel<16><<<grid, kThreads, dyn, s>>>(p);
-    else down_combine_kernel<0><<<grid, kThreads, dyn, s>>>(p);
+    if (lr_d == 16) down_combine_kernel<16><<<grid, kDcThreads, dyn, s>>>(p);
+    else down_combine_kernel<0><<<grid, kDcThreads, dyn, s>>>(p);
     return launch_status();
   }
   if (lr_d == 16) launch_down<16>(p, tasks_d, s);

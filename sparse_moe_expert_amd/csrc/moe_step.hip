@@ -1,0 +1,54 @@
+// moe_step: one routed-MoE step (routing, bucketing, expert FFN with the
+// weighted unroute) in one call.
+//
+// It enqueues moe_route_bucket and then moe_expert_ffn on the caller's
+// stream: three kernels at decode sizes (route + bucket in one workgroup,
+// gate/up, down + unroute).  A one-kernel form of the step - every workgroup
+// routing the batch itself, gate/up publishing each expert's intermediate
+// through device-coherent stores and per-expert counters, down waiting on
+// them, the last route of a token combining it - was built and measured on
+// gfx950 and lost: the replicated routing is VALU-bound (all 1280
+// workgroups select at once), and every cross-workgroup hand-off made while
+// the weight stream is in flight waits behind that stream in the memory
+// queues, so the hand-offs cost more than the kernel boundaries they remove
+// (page "Persistent execution for Flash-Next GGUF on SM70", section
+// "Persistent cross-expert pipeline", proposes that pipeline for another
+// machine).
+#include "moe_common.h"
+
+extern "C" size_t moe_step_workspace_size(int T, int H, int I, int E, int k) {
+  return moe_expert_ffn_workspace_size(T, H, I, E, k);
+}
+
+extern "C" moe_status moe_step(const uint16_t* x, const float* logits, const float* bias,
+                               const uint8_t* w_gate, const uint8_t* s_gate, const uint8_t* w_up,
+                               const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                               const float* g_scale, int T, int H, int I, int E, int k,
+                               int32_t* topk_idx, float* topk_w, int32_t* expert_count,
+                               int32_t* expert_offset, int32_t* active_experts, int32_t* n_active,
+                               int32_t* route_src, int32_t* route_pos, void* workspace,
+                               size_t workspace_bytes, uint16_t* y, void* stream) {
+  // argument checks of the FFN call first, so that an invalid call launches nothing
+  if (T < 0 || k < 1 || E < 1 || k > E || H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
+    return MOE_ERR_INVALID_SHAPE;
+  if (E > 1024 || k > 32 || H > 4096 || I > 4096) return MOE_ERR_UNSUPPORTED;
+  const int chunks_h = H / 32, chunks_i = I / 32;
+  if (chunks_h != moe::lanes_per_row(chunks_h) || chunks_i != moe::lanes_per_row(chunks_i))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  const void* ptrs[] = {x, logits, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_idx, topk_w,
+                        expert_count, expert_offset, active_experts, n_active, route_src, route_pos,
+                        workspace, y};
+  for (const void* q : ptrs)
+    if (!q) return MOE_ERR_NULL_POINTER;
+  for (const void* q : ptrs)
+    if (!moe::aligned16(q)) return MOE_ERR_MISALIGNED;
+  if (bias && !moe::aligned16(bias)) return MOE_ERR_MISALIGNED;
+  if (workspace_bytes < moe_step_workspace_size(T, H, I, E, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const moe_status st = moe_route_bucket(logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset,
+                                         active_experts, n_active, route_src, route_pos, stream);
+  if (st != MOE_OK) return st;
+  return moe_expert_ffn(x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
+                        expert_offset, active_experts, n_active, route_src, route_pos, T, H, I, E, k, workspace,
+                        workspace_bytes, y, stream);
+}

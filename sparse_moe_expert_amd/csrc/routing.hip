@@ -15,14 +15,8 @@
 // same page paragraph describes one workgroup doing all of it for batches of
 // up to 64 tokens; moe_route_bucket does that here.
 //
-// Selection (gfx950): one 64-lane wavefront per token.  Lane l holds experts
-// [l*V, l*V+V) as 32-bit keys ordered(z), an unsigned integer with the same
-// order as the fp32 score (-0.0 first canonicalised to +0.0); absent experts
-// hold 0, below every real key.  Each of the k rounds takes the wave maximum
-// of the lanes' best keys (DPP row steps, then the four row maxima as
-// scalars), then the lowest lane holding that key (ballot): lanes own
-// ascending id ranges, so that lane - and its first matching slot - has the
-// lowest id among equal scores.  Only the winning lane recomputes its best.
+// Selection (gfx950, select.h): one 64-lane wavefront per token, k rounds of
+// a wave-wide arg-max over order-preserving integer keys.
 //
 // Bucketing (one 1024-thread workgroup): LDS histogram of expert ids
 // (integer atomics: counts do not depend on their order), block-wide
@@ -31,7 +25,7 @@
 // are found with one ballot per id bit; rank among them + counts of earlier
 // wavefronts in the chunk + the expert's running base gives the position.
 // Positions never depend on timing, so the result is exact and reproducible.
-#include "moe_common.h"
+#include "select.h"
 
 namespace moe {
 namespace {
@@ -40,111 +34,6 @@ constexpr int kBucketThreads = 1024;
 constexpr int kBucketWaves = kBucketThreads / kWave;
 constexpr int kFusedMaxTokens = 64;        // one workgroup routes and buckets up to this many tokens
 constexpr int kFusedMaxRoutes = 2048;
-
-__device__ __forceinline__ uint32_t ordered_bits(float z) {
-  uint32_t u = __float_as_uint(z);
-  if (u == 0x80000000u) u = 0;                 // -0.0 == +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float from_ordered(uint32_t o) {
-  const uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
-  return __uint_as_float(u);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-
-// Maximum over the wavefront (wave-uniform result).  DPP steps reduce each
-// 16-lane row; the four row results are then read as scalars.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<0xB1>(v));    // quad_perm [1,0,3,2]
-  v = max(v, dpp_u32<0x4E>(v));    // quad_perm [2,3,0,1]
-  v = max(v, dpp_u32<0x124>(v));   // row_ror:4
-  v = max(v, dpp_u32<0x128>(v));   // row_ror:8
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-  return max(max(r0, r1), max(r2, r3));
-}
-
-// Sum over the wavefront in a fixed order (wave-uniform result).
-__device__ __forceinline__ float wave_sum_f32(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
-  const int b = __builtin_bit_cast(int, v);
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-  return (r0 + r1) + (r2 + r3);
-}
-
-// Top-k of one token's row: idx/weights of slot j end up in lane j.
-template <int V>
-__device__ __forceinline__ void select_token(const float* __restrict__ row, const float* __restrict__ bias, int E,
-                                             int k, int lane, int& my_e, float& my_w) {
-  const int e0 = lane * V;
-  float zv[V];
-  const bool full = (V % 4 == 0) && (E % 4 == 0) && (e0 + V <= E);
-  if (full) {                                   // 16-byte vector loads
-#pragma unroll
-    for (int i = 0; i < V; i += 4) {
-      const float4 l4 = *reinterpret_cast<const float4*>(row + e0 + i);
-      zv[i] = l4.x; zv[i + 1] = l4.y; zv[i + 2] = l4.z; zv[i + 3] = l4.w;
-      if (bias) {
-        const float4 b4 = *reinterpret_cast<const float4*>(bias + e0 + i);
-        zv[i] += b4.x; zv[i + 1] += b4.y; zv[i + 2] += b4.z; zv[i + 3] += b4.w;  // fp32 adds, RNE
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const int e = e0 + i;
-      zv[i] = 0.0f;
-      if (e < E) zv[i] = bias ? row[e] + bias[e] : row[e];
-    }
-  }
-  uint32_t key[V];
-  uint32_t best = 0;
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    key[i] = (e0 + i < E) ? ordered_bits(zv[i]) : 0u;
-    best = max(best, key[i]);
-  }
-  uint32_t my_key = 0, key0 = 0;
-  my_e = 0;
-  for (int j = 0; j < k; ++j) {
-    const uint32_t wbest = wave_max_u32(best);
-    const uint64_t holders = __ballot(best == wbest);
-    const int wl = __builtin_ctzll(holders);    // lowest lane: lowest ids
-    int pick = 0;
-    if (lane == wl) {
-      int first = V;
-#pragma unroll
-      for (int i = V - 1; i >= 0; --i)
-        if (key[i] == wbest) first = i;
-      pick = e0 + first;
-      uint32_t nb = 0;
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        if (i == first) key[i] = 0;             // retire the winner
-        nb = max(nb, key[i]);
-      }
-      best = nb;
-    }
-    const int e_sel = __builtin_amdgcn_readlane(pick, wl);
-    if (j == 0) key0 = wbest;
-    if (lane == j) { my_key = wbest; my_e = e_sel; }
-  }
-  // Renormalised softmax over the chosen set: w_j = exp(z_j - z_0) / sum.
-  const float z0 = from_ordered(key0);
-  const float pj = (lane < k) ? __builtin_expf(from_ordered(my_key) - z0) : 0.0f;
-  my_w = pj / wave_sum_f32(pj);
-}
 
 template <int V>
 __global__ __launch_bounds__(256) void route_topk_kernel(
@@ -160,24 +49,6 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     topk_idx[(size_t)t * k + lane] = e;
     topk_w[(size_t)t * k + lane] = w;
   }
-}
-
-// Inclusive scan across a 64-lane wavefront with DPP: shifts of 1, 2, 4, 8
-// inside each 16-lane row (lanes without a source add 0), then row broadcasts
-// of lanes 15 and 31 into the rows above them.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ int dpp_shift(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
-}
-
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  v += dpp_shift<0x111, 0xF>(v);   // row_shr:1
-  v += dpp_shift<0x112, 0xF>(v);   // row_shr:2
-  v += dpp_shift<0x114, 0xF>(v);   // row_shr:4
-  v += dpp_shift<0x118, 0xF>(v);   // row_shr:8
-  v += dpp_shift<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
-  v += dpp_shift<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
-  return v;
 }
 
 // Exclusive scan of one value per thread across the workgroup; returns the
@@ -305,6 +176,84 @@ __global__ __launch_bounds__(kBucketThreads) void route_bucket_kernel(
                route_pos);
 }
 
+// Route and bucket a batch of up to 16 tokens in one 1024-thread workgroup:
+// wavefront w selects token w; bucketing is an LDS histogram, one packed
+// scan over one expert per thread (route offsets in the low half,
+// active-expert positions in the high half), and a stable scatter whose rank
+// is the number of earlier routes to the same expert (ballots per id bit
+// inside a 64-route group, per-expert counts of earlier groups).
+constexpr int kSmallMaxTokens = 16;
+constexpr int kSmallMaxRoutes = 256;
+
+template <int V>
+__global__ __launch_bounds__(kBucketThreads) void route_bucket_small_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k, int id_bits,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
+    int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos) {
+  __shared__ int s_cnt[1024];
+  __shared__ int s_ids[kSmallMaxRoutes];
+  __shared__ int s_wt[kBucketWaves];
+  __shared__ uint8_t s_wcnt[kSmallMaxRoutes / kWave][1024];   // routes per expert in each 64-route group
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int R = T * k;
+  s_cnt[tid] = 0;
+  reinterpret_cast<int*>(&s_wcnt[0][0])[tid] = 0;
+  if (wave < T) {
+    int e;
+    float w;
+    select_token<V>(logits + (size_t)wave * E, bias, E, k, lane, e, w);
+    if (lane < k) {
+      topk_idx[(size_t)wave * k + lane] = e;
+      topk_w[(size_t)wave * k + lane] = w;
+      s_ids[wave * k + lane] = e;
+    }
+  }
+  __syncthreads();
+  if (tid < R) atomicAdd(&s_cnt[s_ids[tid]], 1);   // integer counts: order-free
+  __syncthreads();
+  const int c = s_cnt[tid];                          // expert tid
+  int total;
+  const int scan = block_scan<kBucketWaves>(c + ((c > 0) << 16), s_wt, total);
+  const int off = scan & 0xFFFF, apos = scan >> 16;
+  const int total_active = total >> 16;
+  if (tid < E) {
+    expert_count[tid] = c;
+    expert_offset[tid] = off;
+    if (c > 0) active_experts[apos] = tid;
+    if (tid >= total_active) active_experts[tid] = -1;
+    s_cnt[tid] = off;                              // base for the scatter
+  }
+  if (tid == 0) {
+    expert_offset[E] = total & 0xFFFF;
+    *n_active = total_active;
+  }
+  // stable rank among routes of the same expert: lanes of a 64-route group
+  // with the same id are found with one ballot per id bit; earlier groups
+  // contribute their per-expert counts
+  int rank = 0, e = 0;
+  if (wave * kWave < R) {
+    const bool valid = tid < R;
+    e = valid ? s_ids[tid] : 0;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < id_bits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
+    }
+    rank = __popcll(same & ((1ull << lane) - 1ull));
+    if (valid && rank == 0) s_wcnt[wave][e] = (uint8_t)__popcll(same);
+  }
+  __syncthreads();
+  if (tid < R) {
+    for (int w = 0; w < wave; ++w) rank += s_wcnt[w][e];
+    const int pos = s_cnt[e] + rank;
+    route_src[pos] = tid;
+    route_pos[tid] = pos;
+  }
+}
+
 int id_bits_for(int E) {
   int b = 0;
   while ((1 << b) < E) ++b;
@@ -385,8 +334,21 @@ extern "C" moe_status moe_route_bucket(const float* logits, const float* bias, i
   if (st != MOE_OK || T == 0) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int bits = id_bits_for(E);
+  const int V = (E + kWave - 1) / kWave;
+  if (T <= kSmallMaxTokens && T * k <= kSmallMaxRoutes) {
+#define MOE_RBS(VV)                                                                                          \
+  route_bucket_small_kernel<VV><<<1, kBucketThreads, 0, s>>>(logits, bias, T, E, k, bits, topk_idx, topk_w, \
+                                                             expert_count, expert_offset, active_experts,     \
+                                                             n_active, route_src, route_pos)
+    if (V <= 1) MOE_RBS(1);
+    else if (V <= 2) MOE_RBS(2);
+    else if (V <= 4) MOE_RBS(4);
+    else if (V <= 8) MOE_RBS(8);
+    else MOE_RBS(16);
+#undef MOE_RBS
+    return launch_status();
+  }
   if (T <= kFusedMaxTokens && T * k <= kFusedMaxRoutes) {
-    const int V = (E + kWave - 1) / kWave;
 #define MOE_RB(VV)                                                                                          \
   route_bucket_kernel<VV><<<1, kBucketThreads, 0, s>>>(logits, bias, T, E, k, bits, topk_idx, topk_w,       \
                                                         expert_count, expert_offset, active_experts, n_active, \

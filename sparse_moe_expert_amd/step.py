@@ -1,7 +1,7 @@
 """One routed-MoE step with preallocated outputs, for graph capture and reuse.
 
 MoeStep owns every output and the workspace for fixed sizes (T, H, I, E, k)
-and enqueues the three library calls on torch's current stream.  Because no
+and enqueues the library calls on torch's current stream.  Because no
 call allocates or synchronises, `run` can be captured in a torch.cuda.CUDAGraph
 (a HIP graph under ROCm) and replayed after the input tensors' contents change.
 """
@@ -21,6 +21,7 @@ from ._lib import (
     moe_expert_ffn,
     moe_route_bucket,
     moe_route_topk,
+    moe_step,
 )
 
 
@@ -36,12 +37,19 @@ def expert_weights_from_numpy(bank, device) -> ExpertWeights:
 
 
 class MoeStep:
-    """fused_routing: route and bucket with moe_route_bucket (one call) instead
-    of moe_route_topk followed by moe_bucket_routes; the outputs are identical."""
+    """Outputs and workspace for one step of fixed sizes, and the ways to run it.
 
-    def __init__(self, T: int, H: int, I: int, E: int, k: int, device, fused_routing: bool = True):
+    path "step": moe_step (the whole step in one call).  "calls":
+    moe_route_bucket then moe_expert_ffn.  "calls_unfused": moe_route_topk,
+    moe_bucket_routes, moe_expert_ffn.  All three produce the same outputs."""
+
+    PATHS = ("step", "calls", "calls_unfused")
+
+    def __init__(self, T: int, H: int, I: int, E: int, k: int, device, path: str = "step"):
+        if path not in self.PATHS:
+            raise ValueError(f"path must be one of {self.PATHS}")
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
-        self.fused_routing = fused_routing
+        self.path = path
         self.device = torch.device(device)
         self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=self.device)
         self.topk_w = torch.empty((T, k), dtype=torch.float32, device=self.device)
@@ -58,18 +66,22 @@ class MoeStep:
     def route_bucket(self, logits: torch.Tensor, bias: Optional[torch.Tensor]):
         moe_route_bucket(logits, bias, self.k, self.topk_idx, self.topk_w, self.buckets)
 
+    def routing(self, logits: torch.Tensor, bias: Optional[torch.Tensor]):
+        if self.path == "calls_unfused":
+            self.route(logits, bias)
+            self.bucket()
+        else:
+            self.route_bucket(logits, bias)
+
     def ffn(self, x: torch.Tensor, weights: ExpertWeights, stage: int = 3):
         moe_expert_ffn(x, weights, self.topk_w, self.buckets, self.workspace, self.y, stage=stage)
 
-    def routing(self, logits: torch.Tensor, bias: Optional[torch.Tensor]):
-        if self.fused_routing:
-            self.route_bucket(logits, bias)
-        else:
-            self.route(logits, bias)
-            self.bucket()
-
     def run(self, x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor],
             weights: ExpertWeights) -> torch.Tensor:
-        self.routing(logits, bias)
-        self.ffn(x, weights)
+        if self.path == "step":
+            moe_step(x, logits, bias, weights, self.k, self.topk_idx, self.topk_w, self.buckets,
+                     self.workspace, self.y)
+        else:
+            self.routing(logits, bias)
+            self.ffn(x, weights)
         return self.y

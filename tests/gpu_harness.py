@@ -36,12 +36,13 @@ def x_bits(x_u16: np.ndarray) -> torch.Tensor:
     return to_dev(np.ascontiguousarray(x_u16).view(np.int16))
 
 
-def run_gpu(x_u16, logits, bias, bank, k, step: sme.MoeStep = None):
+def run_gpu(x_u16, logits, bias, bank, k, step: sme.MoeStep = None, path: str = "step"):
+    """One step through the C ABI (moe_step, or the separate calls)."""
     T, H = x_u16.shape
     E = logits.shape[1]
     W = device_weights(bank)
     I = W.shape[2]
-    st = step or sme.MoeStep(T, H, I, E, k, DEV)
+    st = step or sme.MoeStep(T, H, I, E, k, DEV, path=path)
     st.run(x_bits(x_u16), to_dev(logits.astype(np.float32)),
            None if bias is None else to_dev(bias.astype(np.float32)), W)
     torch.cuda.synchronize()
@@ -49,6 +50,7 @@ def run_gpu(x_u16, logits, bias, bank, k, step: sme.MoeStep = None):
 
 
 def collect(st: sme.MoeStep) -> dict:
+    """Copy every output to the host."""
     b = st.buckets
     return {
         "idx": st.topk_idx.cpu().numpy(),

@@ -108,3 +108,34 @@ def test_ffn_stage_host_checks(lib):
     for bad in (0, 4, -1):
         assert f(bad, *ptrs, 4, 256, 128, 8, 2, A, ctypes.c_size_t(1 << 20), A, None) == 2
     assert f(1, *ptrs, 0, 256, 128, 8, 2, A, ctypes.c_size_t(1 << 20), A, None) == 0
+
+
+def _step(lib, T=4, H=256, I=128, E=8, k=2, ws=1 << 24, null_at=None, bad_at=None, bias=None):
+    ins = [A] * 10          # x, logits, bias, 6 weight arrays, g_scale
+    ins[2] = bias
+    outs = [A] * 8          # topk_idx, topk_w, 6 bucket arrays
+    if null_at is not None:
+        (ins if null_at < 10 else outs)[null_at if null_at < 10 else null_at - 10] = None
+    if bad_at is not None:
+        (ins if bad_at < 10 else outs)[bad_at if bad_at < 10 else bad_at - 10] = P(264)
+    return lib.moe_step(*ins, T, H, I, E, k, *outs, A, ctypes.c_size_t(ws), A, None)
+
+
+def test_step_host_checks(lib):
+    assert _step(lib, k=9) == 2
+    assert _step(lib, H=48) == 2
+    assert _step(lib, H=96) == 3
+    assert _step(lib, E=2048) == 3
+    assert _step(lib, T=0) == 0
+    assert _step(lib, null_at=1) == 1           # logits
+    assert _step(lib, null_at=14) == 1          # an output
+    assert _step(lib, bad_at=0) == 4
+    assert _step(lib, bias=P(8)) == 4           # a misaligned bias
+    need = lib.moe_step_workspace_size(4, 256, 128, 8, 2)
+    assert _step(lib, ws=need - 1) == 5
+
+
+def test_step_workspace_size(lib):
+    for shape in [(4, 2048, 512, 512, 10), (4, 256, 128, 8, 2), (33, 2048, 512, 512, 10), (1, 32, 32, 2, 1)]:
+        assert lib.moe_step_workspace_size(*shape) == lib.moe_expert_ffn_workspace_size(*shape)
+    assert lib.moe_step_workspace_size(0, 2048, 512, 512, 10) == 0

@@ -46,11 +46,15 @@ def _sample_tokens(wl, idx):
     return sorted(picks)
 
 
+PATHS = ["step", "calls"]
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("name", CONFIG_ORDER)
-def test_workload_parity(name):
+def test_workload_parity(name, path):
     wl = make_workload(name)
-    print(f"[parity] {name} T={wl.T} E={wl.E} k={wl.k}", flush=True)
-    g = run_gpu(wl.x, wl.logits, wl.bias, wl.bank, wl.k)
+    print(f"[parity] {name} T={wl.T} E={wl.E} k={wl.k} path={path}", flush=True)
+    g = run_gpu(wl.x, wl.logits, wl.bias, wl.bank, wl.k, path=path)
     idx, w = oracle.route_topk(wl.logits, wl.bias, wl.k)
     assert_route(g, idx, w)
     assert_buckets(g, oracle.bucket_routes(idx, wl.E))
@@ -60,12 +64,13 @@ def test_workload_parity(name):
     print(f"[parity] {name}: tokens={len(tokens)} max_err={err:.3e} rms={rms:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("T", [1, 5, 33])
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("T", [1, 5, 12, 33])
 @pytest.mark.parametrize("shape", ["tiny", "decode_t4"])
-def test_ragged_token_counts(shape, T):
+def test_ragged_token_counts(shape, T, path):
     wl = make_workload(shape, T=T, x_seed=100 + T)
-    print(f"[ragged] {shape} T={T}", flush=True)
-    g = run_gpu(wl.x, wl.logits, wl.bias, wl.bank, wl.k)
+    print(f"[ragged] {shape} T={T} path={path}", flush=True)
+    g = run_gpu(wl.x, wl.logits, wl.bias, wl.bank, wl.k, path=path)
     idx, w, b, y = oracle_all(wl.x, wl.logits, wl.bias, wl.bank, wl.k,
                               tokens=range(T) if shape == "tiny" else range(min(T, 5)))
     assert_route(g, idx, w)
@@ -73,44 +78,50 @@ def test_ragged_token_counts(shape, T):
     assert_output(g["y"][: y.shape[0]], y, f"{shape} T={T}")
 
 
-def test_k_equals_E():
+@pytest.mark.parametrize("path", PATHS)
+def test_k_equals_E(path):
     wl = make_workload("tiny", T=6, x_seed=7)
-    g = run_gpu(wl.x, wl.logits, None, wl.bank, wl.E)
+    g = run_gpu(wl.x, wl.logits, None, wl.bank, wl.E, path=path)
     idx, w, b, y = oracle_all(wl.x, wl.logits, None, wl.bank, wl.E)
     assert_route(g, idx, w)
     assert_buckets(g, b)
     assert_output(g["y"], y, "k=E")
 
 
-def test_all_tokens_on_same_experts():
-    """Every token routed to the same 10 experts: 33 tokens per expert, so the
-    kernels loop over token groups."""
-    wl = make_workload("decode_t4", T=33, x_seed=3)
+@pytest.mark.parametrize("T", [12, 33])
+def test_all_tokens_on_same_experts(T):
+    """Every token routed to the same 10 experts: T routes per expert, so the
+    kernels loop over the expert's tokens (T = 12: the small-batch routing
+    kernel and the fused down/unroute kernel; T = 33: the larger-batch
+    kernels)."""
+    wl = make_workload("decode_t4", T=T, x_seed=3)
     chosen = [7, 100, 101, 250, 311, 312, 400, 450, 500, 511]
     bias = np.zeros(wl.E, np.float32)
     bias[chosen] = 50.0
     g = run_gpu(wl.x, wl.logits, bias, wl.bank, wl.k)
-    idx, w, b, y = oracle_all(wl.x, wl.logits, bias, wl.bank, wl.k, tokens=[0, 16, 32])
+    toks = [0, T // 2, T - 1]
+    idx, w, b, y = oracle_all(wl.x, wl.logits, bias, wl.bank, wl.k, tokens=toks)
     assert int(b["n_active"]) == 10 and sorted(np.unique(idx)) == chosen
     assert_route(g, idx, w)
     assert_buckets(g, b)
-    assert_output(g["y"][[0, 16, 32]], y, "all-equal experts")
+    assert_output(g["y"][toks], y, "all-equal experts")
 
 
-def test_all_routes_on_distinct_experts():
-    wl = make_workload("decode_t4", T=40, x_seed=4)
-    T, k, E = 40, 10, 512
+@pytest.mark.parametrize("T", [12, 40])
+def test_all_routes_on_distinct_experts(T):
+    wl = make_workload("decode_t4", T=T, x_seed=4)
+    k, E = 10, 512
     logits = np.zeros((T, E), np.float32)
     rng = np.random.default_rng(0)
     perm = rng.permutation(E)[: T * k].reshape(T, k)
     for t in range(T):
         logits[t, perm[t]] = 10.0 - np.arange(k, dtype=np.float32) * 0.5
     g = run_gpu(wl.x, logits, None, wl.bank, k)
-    idx, w, b, y = oracle_all(wl.x, logits, None, wl.bank, k, tokens=[0, 39])
-    assert np.all(b["expert_count"][b["expert_count"] > 0] == 1) and int(b["n_active"]) == 400
+    idx, w, b, y = oracle_all(wl.x, logits, None, wl.bank, k, tokens=[0, T - 1])
+    assert np.all(b["expert_count"][b["expert_count"] > 0] == 1) and int(b["n_active"]) == T * k
     assert_route(g, idx, w)
     assert_buckets(g, b)
-    assert_output(g["y"][[0, 39]], y, "all-disjoint experts")
+    assert_output(g["y"][[0, T - 1]], y, "all-disjoint experts")
 
 
 def test_zero_input_gives_exact_zero():
@@ -123,12 +134,13 @@ def test_zero_input_gives_exact_zero():
     assert np.all(g["y_bits"] == 0)
 
 
-def test_guard_regions_untouched():
+@pytest.mark.parametrize("path", PATHS)
+def test_guard_regions_untouched(path):
     wl = make_workload("decode_t4", T=5, x_seed=9)
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
     W = device_weights(wl.bank)
-    step = sme.MoeStep(T, H, I, E, k, DEV)
-    ws_bytes = sme.moe_expert_ffn_workspace_size(T, H, I, E, k)
+    step = sme.MoeStep(T, H, I, E, k, DEV, path=path)
+    ws_bytes = sme.moe_step_workspace_size(T, H, I, E, k)
     big_ws = torch.zeros(ws_bytes + 512, dtype=torch.uint8, device=DEV)
     big_ws[:256] = 0xA5
     big_ws[256 + ws_bytes:] = 0x5A
@@ -153,15 +165,16 @@ def test_bitwise_determinism(name):
     assert np.array_equal(a["w"].view(np.uint32), b["w"].view(np.uint32))
 
 
-def test_graph_replays_with_changed_inputs():
-    """Capture the three calls once; replay with inputs A, B, A, B with eager
-    work and synchronisation between replays; each replay must match the
-    oracle for its inputs (the workspace needs no reset between replays)."""
+@pytest.mark.parametrize("path", PATHS)
+def test_graph_replays_with_changed_inputs(path):
+    """Capture the step once; replay with inputs A, B, A, B with eager work
+    and synchronisation between replays; each replay must match the oracle
+    for its inputs (the workspace needs no reset between replays)."""
     A = make_workload("decode_t4", x_seed=11)
     B = make_workload("decode_t4", x_seed=12)
     T, H, I, E, k = A.T, A.H, A.I, A.E, A.k
     W = device_weights(A.bank)
-    step = sme.MoeStep(T, H, I, E, k, DEV)
+    step = sme.MoeStep(T, H, I, E, k, DEV, path=path)
     x_s = x_bits(A.x)
     l_s = to_dev(A.logits)
     step.run(x_s, l_s, None, W)          # warm-up outside capture
@@ -208,19 +221,23 @@ def test_hand_worked_cases_on_gpu():
 
 @pytest.mark.parametrize("name", CONFIG_ORDER)
 def test_fused_routing_matches_two_calls(name):
-    """moe_route_bucket gives exactly the outputs of moe_route_topk + moe_bucket_routes."""
-    wl = make_workload(name, with_bank=False)
+    """moe_route_bucket and moe_step give exactly the routing outputs of
+    moe_route_topk + moe_bucket_routes."""
+    wl = make_workload(name)
     logits = to_dev(wl.logits)
     bias = None if wl.bias is None else to_dev(wl.bias)
-    a = sme.MoeStep(wl.T, wl.H, wl.I, wl.E, wl.k, DEV, fused_routing=True)
-    b = sme.MoeStep(wl.T, wl.H, wl.I, wl.E, wl.k, DEV, fused_routing=False)
+    a = sme.MoeStep(wl.T, wl.H, wl.I, wl.E, wl.k, DEV, path="calls")
+    b = sme.MoeStep(wl.T, wl.H, wl.I, wl.E, wl.k, DEV, path="calls_unfused")
+    c = sme.MoeStep(wl.T, wl.H, wl.I, wl.E, wl.k, DEV, path="step")
     a.routing(logits, bias)
     b.routing(logits, bias)
+    c.run(x_bits(wl.x), logits, bias, device_weights(wl.bank))
     torch.cuda.synchronize()
-    assert torch.equal(a.topk_idx, b.topk_idx)
-    assert torch.equal(a.topk_w.view(torch.int32), b.topk_w.view(torch.int32))
-    for ta, tb in zip(a.buckets, b.buckets):
-        assert torch.equal(ta, tb)
+    for s in (a, c):
+        assert torch.equal(s.topk_idx, b.topk_idx)
+        assert torch.equal(s.topk_w.view(torch.int32), b.topk_w.view(torch.int32))
+        for ta, tb in zip(s.buckets, b.buckets):
+            assert torch.equal(ta, tb)
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode_t4", "verify_t32"])
