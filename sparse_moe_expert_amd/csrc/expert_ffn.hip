@@ -8,11 +8,13 @@
 // (active expert, row tile) and streams those weight rows from HBM once for
 // all of the expert's routes (the note's first boundary, step 2; the b12x
 // kernel's cost is the weight bytes of the unique experts - page "Qwen3.8
-// Flash Next on LiL/vLLM", section "11.13 Where the decode step's time
-// actually goes").
+// Flash Next on LiL/vLLM: why the MTP decode step is host-bound, and what
+// LMCache does and does not do to it", section "11.13 Where the decode
+// step's time actually goes").
 //
 // Kernels on one stream; the kernel boundaries order the phases, so no
-// workgroup ever waits for another:
+// workgroup ever waits for another (small batches replace the last two with
+// down_combine_kernel):
 //   gate_up_kernel  task (active slot a, tile of I rows): h[p, rows] =
 //                   bf16(SiLU(Wg x) * (Wu x)) for every route p of the expert
 //   down_kernel     task (active slot a, tile of H rows): o[p, rows] = Wd h[p]
@@ -27,13 +29,21 @@
 // e4m3 scales, with buffer loads from a per-expert resource (hardware range
 // check: rows past the matrix read as zero, so ragged tiles need no
 // predication and no index can fault).  Byte pairs become bf16 with
-// v_cvt_scalef32_pk_bf16_fp4 (exact at scale 1), v_dot2 takes bf16 products
-// with the operand (x or h) in fp32, one scale multiplies each 16-value block,
-// and the partial sums of a row are added across its lanes with DPP row
-// operations and v_permlane{16,32}_swap in a fixed order.  A tile's weight
-// rows are loaded once and stay in registers while the expert's routes are
-// processed one at a time, which keeps the kernels at 4 waves per SIMD
-// (<= 128 VGPRs) - the VALU needs that many waves to reach its issue rate.
+// v_cvt_scalef32_pk_bf16_fp4 (exact at scale 1), v_dot2 multiplies them
+// pairwise with the bf16 operand (x or h) and accumulates in fp32, one scale
+// multiplies each 16-value block, and the partial sums of a row are added
+// across its lanes with DPP row operations and v_permlane{16,32}_swap in a
+// fixed order.  A tile's weight rows are loaded once and stay in registers
+// while the expert's routes are processed one at a time, which keeps the
+// kernels at 4+ waves per SIMD - the VALU needs that many waves to reach its
+// issue rate.
+//
+// Issue order.  Vector loads complete in order (one counter per wave), so a
+// load issued after a tile's weight rows cannot be used before all of them
+// have arrived.  Each kernel therefore issues everything its first use needs
+// before the weight stream (scale tiles, operand rows) or fetches it through
+// the scalar path (routing metadata: s_load, its own counter), and a WG's
+// dependent round trips all happen while its weights are in flight.
 #include <algorithm>
 
 #include "row_dot.h"

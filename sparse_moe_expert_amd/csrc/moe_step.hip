@@ -10,10 +10,13 @@
 // gfx950 and lost: the replicated routing is VALU-bound (all 1280
 // workgroups select at once), and every cross-workgroup hand-off made while
 // the weight stream is in flight waits behind that stream in the memory
-// queues, so the hand-offs cost more than the kernel boundaries they remove
-// (page "Persistent execution for Flash-Next GGUF on SM70", section
-// "Persistent cross-expert pipeline", proposes that pipeline for another
-// machine).
+// queues, so the hand-offs cost more than the kernel boundaries they remove.
+// That pipeline is the one proposed for another machine on page "Persistent
+// execution for Flash-Next GGUF on SM70" (section "First implementation
+// boundary", steps 2-4; section "Primary sources and transferable
+// mechanisms", paragraphs "MonoMoE" and "Hazy Research Megakernels", the
+// latter noting that publication and readiness checks are a cost of their
+// own).
 #include "moe_common.h"
 
 extern "C" size_t moe_step_workspace_size(int T, int H, int I, int E, int k) {
