@@ -56,7 +56,38 @@ def parse():
                     help="launches of the dominant kernel timed with events for the roofline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle sample budget (0 disables the cpu_baseline leg)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="after the bench, run a plain device-to-device copy of this many MiB three times "
+                         "(the known-size kernel that calibrates FETCH_SIZE / WRITE_SIZE counter runs)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_kernel_decode_t4_traffic.json")
+KERNEL_SOURCES = ["sparse_moe_expert_amd/csrc/expert_ffn.hip", "sparse_moe_expert_amd/csrc/row_dot.h",
+                  "sparse_moe_expert_amd/csrc/moe_common.h"]
+
+
+def kernel_sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per gate/up launch from the committed counter runs (FETCH_SIZE
+    + WRITE_SIZE, calibrated against a copy of known size), or None when
+    there are none for this workload or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("sources_sha256") != kernel_sources_digest():
+        return None
+    return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
 
 def cpu_baseline(cfg, budget_s: float, expert_bytes: int):
@@ -219,10 +250,19 @@ def main():
                    "unique_expert_bytes_per_step": int(bytes_per_step)},
         "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg.name),
                      "avg_launch_us": round(avg * 1e6, 3),
                      "bytes_per_launch": int(dom_bytes), "launches": n_dom},
     }
+    if args.copy_mb > 0:
+        nbytes = args.copy_mb << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copies: 3 x {nbytes} bytes device to device")
+        del src, dst
     if args.cpu_seconds > 0:
         log(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s budget)")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, expert_bytes)
