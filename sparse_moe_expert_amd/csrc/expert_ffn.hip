@@ -73,6 +73,7 @@ struct FfnParams {
   uint16_t* y;
   int lr_gu;     // lanes per gate/up row (power of two, <= 64)
   int lr_d;      // lanes per down row
+  int mfma_min;  // experts with at least this many routes take the MFMA kernels (0: none do)
 };
 
 constexpr int kGuUnits = 4;          // gate rows (and as many up rows) per wave per tile
@@ -101,6 +102,15 @@ __device__ __forceinline__ void expert_routes(const FfnParams& p, int e, int& of
   const int R = p.T * p.k;
   off = min(max(sload(p.offset, e), 0), R);
   cnt = min(max(sload(p.count, e), 0), R - off);
+}
+
+// True when expert e's routes go to the MFMA kernels instead (decided before
+// any weight load is issued, so the two paths never both stream an expert).
+__device__ __forceinline__ bool takes_mfma(const FfnParams& p, int e) {
+  if (p.mfma_min <= 0) return false;
+  int off, cnt;
+  expert_routes(p, e, off, cnt);
+  return cnt >= p.mfma_min;
 }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 4) void gate_up_kernel(FfnParams p, int n
   for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
     const int a = task / g.tiles, tile = task - a * g.tiles;
     const int e = slot_expert(p, a);
-    if (e < 0) continue;
+    if (e < 0 || takes_mfma(p, e)) continue;
     __syncthreads();                            // LDS of the previous task is free
     gate_up_tile<LG>(p, g, s_sc, s_x, e, tile);
   }
@@ -282,9 +292,213 @@ __global__ __launch_bounds__(kThreads, 4) void down_kernel(FfnParams p, int n_ta
   for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
     const int a = task / g.tiles, tile = task - a * g.tiles;
     const int e = slot_expert(p, a);
-    if (e < 0) continue;
+    if (e < 0 || takes_mfma(p, e)) continue;
     __syncthreads();                            // LDS of the previous task is free
     down_tile<LD>(p, g, s_sc, e, tile);
+  }
+}
+
+// ------------------------------------------------------------------ MFMA tiles (experts with many routes)
+
+// For an expert with many routes the projections are dense contractions:
+// gate/up is [routes x H] x [H x I] twice, down is [routes x I] x [I x H].
+// A workgroup owns 128 weight rows of one expert (both gate and up rows for
+// gate/up) and all of the expert's routes in chunks of 128.  Per 64-wide
+// step of the reduction it dequantises its weight rows once into LDS -
+// e2m1 * e4m3 is exact in bf16, the fp32 global scale is applied to the
+// accumulator - stages the routes' operand rows (gathered x for gate/up,
+// the contiguous h rows for down) next to them, and runs
+// v_mfma_f32_32x32x16_bf16 with the weights as the A operand (32 rows x 16)
+// and the operand rows as B (16 x 32 routes).  Each wave holds a 64 x 64
+// block per matrix (four 32 x 32 accumulators); the next step's codes,
+// scales and operand rows are loaded into registers while the current step
+// runs on the matrix cores.  Epilogue: gate/up writes
+// h = bf16(SiLU(g Gg) * (u Gu)); down writes o = Gd * acc (fp32) for the
+// combine kernel.  Lane layout of the instruction (checked on the device):
+// A lane l holds row l%32, k = 8*(l/32)..+8; B lane l holds column l%32,
+// same k; D register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+constexpr int kMmThreads = 256;
+constexpr int kMmRows = 128;                 // weight rows per workgroup
+constexpr int kMmRoutes = 128;               // routes per chunk
+constexpr int kMmK = 64;                     // reduction per step
+constexpr int kMmLd = kMmK + 8;              // LDS row stride in bf16 (144 B): spreads rows over banks
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2v v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 32 NVFP4 values (16 code bytes, scale bytes of its two 16-value blocks) ->
+// 32 bf16 = code value * block scale (exact) at dst (16-byte aligned LDS).
+__device__ __forceinline__ void dequant32_to_lds(const uint4 codes, uint32_t s2, uint16_t* dst) {
+  const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 0);
+  const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 1);
+  const uint32_t c[4] = {codes.x, codes.y, codes.z, codes.w};
+  uint32_t out[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float sc = q < 2 ? s0 : s1;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      f32x2 v;
+      switch (b) {
+        case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[q], 1.0f, 0); break;
+        case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[q], 1.0f, 1); break;
+        case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[q], 1.0f, 2); break;
+        default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[q], 1.0f, 3); break;
+      }
+      out[4 * q + b] = pack_bf16x2(v.x * sc, v.y * sc);
+    }
+  }
+  uint4* d = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d[q] = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+}
+
+template <bool GU>
+__global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
+  constexpr int NMAT = GU ? 2 : 1;
+  extern __shared__ __align__(16) uint16_t s_mm[];          // [NMAT][128][kMmLd] weights, [128][kMmLd] operand
+  __shared__ int s_row[kMmRoutes];                           // operand row per route of the chunk (-1: none)
+  uint16_t* s_w = s_mm;
+  uint16_t* s_b = s_mm + NMAT * kMmRows * kMmLd;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nw = wave & 1, mw = wave >> 1;
+  const int N = GU ? p.I : p.H;                              // weight rows
+  const int K = GU ? p.H : p.I;                              // reduction length
+  const int tiles_n = (N + kMmRows - 1) / kMmRows;
+  const int a = blockIdx.x / tiles_n, n0 = (blockIdx.x - a * tiles_n) * kMmRows;
+  const int e = slot_expert(p, a);
+  if (e < 0) return;
+  int off, cnt;
+  expert_routes(p, e, off, cnt);
+  if (p.mfma_min <= 0 || cnt < p.mfma_min) return;
+
+  const uint32_t code_row = (uint32_t)K / 2, scale_row = (uint32_t)K / 16;
+  const uint32_t mat_codes = (uint32_t)N * code_row, mat_scales = (uint32_t)N * scale_row;
+  const uint8_t* wbase[2] = {GU ? p.wg : p.wd, p.wu};
+  const uint8_t* sbase[2] = {GU ? p.sg : p.sd, p.su};
+  __amdgpu_buffer_rsrc_t rc[NMAT], rs[NMAT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) {
+    rc[m] = make_rsrc(wbase[m] + (size_t)e * mat_codes, mat_codes);
+    rs[m] = make_rsrc(sbase[m] + (size_t)e * mat_scales, mat_scales);
+  }
+  const int R = p.T * p.k;
+  const auto rb = GU ? make_rsrc(p.x, (uint32_t)p.T * (uint32_t)p.H * 2u)
+                     : make_rsrc(p.h, (uint32_t)R * (uint32_t)p.I * 2u);
+  // this thread's dequant slice: weight row r, 32 values at 32*hf of each step;
+  // and operand slice: route row r, the same 32 columns
+  const int r = tid >> 1, hf = tid & 1;
+  const uint32_t w_voff = (uint32_t)(n0 + r) * code_row + (uint32_t)hf * 16;
+  const uint32_t s_voff = (uint32_t)(n0 + r) * scale_row + (uint32_t)hf * 2;
+  const int n_steps = K / kMmK;
+
+  for (int m0 = 0; m0 < cnt; m0 += kMmRoutes) {
+    const int mc = min(kMmRoutes, cnt - m0);
+    __syncthreads();                                         // previous chunk done with LDS
+    if (tid < kMmRoutes) {
+      int row = -1;
+      if (tid < mc) {
+        const int pos = off + m0 + tid;
+        row = GU ? min(max(p.route_src[pos] / p.k, 0), p.T - 1) : pos;
+      }
+      s_row[tid] = row;
+    }
+    __syncthreads();
+    const int brow = s_row[r];
+    const uint32_t b_voff = (uint32_t)max(brow, 0) * (uint32_t)K * 2u + (uint32_t)hf * 64;
+
+    f32x16 acc[NMAT][2][2];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[m][i][j] = f32x16{};
+
+    uint4 wc[NMAT];
+    uint32_t wsv[NMAT];
+    u32x4 bv[4];
+    auto load_step = [&](int ks) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        wc[m] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rc[m], w_voff, (uint32_t)ks * (kMmK / 2), 0));
+        wsv[m] = __builtin_amdgcn_raw_buffer_load_b16(rs[m], s_voff, (uint32_t)ks * (kMmK / 16), 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        bv[q] = brow >= 0 ? __builtin_amdgcn_raw_buffer_load_b128(rb, b_voff + q * 16, (uint32_t)ks * (kMmK * 2), 0)
+                          : u32x4{0u, 0u, 0u, 0u};
+    };
+    load_step(0);
+    for (int ks = 0; ks < n_steps; ++ks) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) dequant32_to_lds(wc[m], wsv[m], s_w + (m * kMmRows + r) * kMmLd + hf * 32);
+      u32x4* bd = reinterpret_cast<u32x4*>(s_b + r * kMmLd + hf * 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bd[q] = bv[q];
+      if (ks + 1 < n_steps) load_step(ks + 1);
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < kMmK / 16; ++kk) {
+        const int kcol = kk * 16 + (lane >> 5) * 8;
+        bf16x8 bfr[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8*>(s_b + (mw * 64 + j * 32 + (lane & 31)) * kMmLd + kcol);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const bf16x8 afr =
+                *reinterpret_cast<const bf16x8*>(s_w + (m * kMmRows + nw * 64 + i * 32 + (lane & 31)) * kMmLd + kcol);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[j], acc[m][i][j], 0, 0, 0);
+          }
+        }
+      }
+      __syncthreads();
+    }
+
+    // epilogue: lane holds, per 32 x 32 block, rows 8*(q) + 4*(lane/32) + 0..3 of one route column
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int m_loc = mw * 64 + j * 32 + (lane & 31);
+        if (m_loc >= mc) continue;
+        const int pos = off + m0 + m_loc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + nw * 64 + i * 32 + q * 8 + (lane >> 5) * 4;
+          if (n >= N) continue;
+          if constexpr (GU) {
+            const float Gg = p.gsc[e * 3 + 0], Gu = p.gsc[e * 3 + 1];
+            uint32_t hv[2];
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+              const float g0 = acc[0][i][j][4 * q + 2 * t2] * Gg, g1 = acc[0][i][j][4 * q + 2 * t2 + 1] * Gg;
+              const float u0 = acc[1][i][j][4 * q + 2 * t2] * Gu, u1 = acc[1][i][j][4 * q + 2 * t2 + 1] * Gu;
+              hv[t2] = f32_to_bf16_rne(silu(g0) * u0) | (f32_to_bf16_rne(silu(g1) * u1) << 16);
+            }
+            *reinterpret_cast<uint2*>(p.h + (size_t)pos * p.I + n) = make_uint2(hv[0], hv[1]);
+          } else {
+            const float Gd = p.gsc[e * 3 + 2];
+            *reinterpret_cast<float4*>(p.o + (size_t)pos * p.H + n) =
+                make_float4(acc[0][i][j][4 * q] * Gd, acc[0][i][j][4 * q + 1] * Gd, acc[0][i][j][4 * q + 2] * Gd,
+                            acc[0][i][j][4 * q + 3] * Gd);
+          }
+        }
+      }
+    }
   }
 }
 
@@ -453,6 +667,8 @@ WorkspaceLayout workspace_layout(int T, int H, int I, int k) {
 }
 
 constexpr long long kMaxGrid = 1 << 20;
+constexpr int kMfmaMinTokens = 64;      // batches from this size launch the MFMA kernels
+constexpr int kMfmaMinRoutes = 16;      // experts with this many routes use them
 
 template <int LG>
 void launch_gate_up(const FfnParams& p, long long tasks, hipStream_t s) {
@@ -515,6 +731,17 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
   p.y = y;
   p.lr_gu = lr_gu;
   p.lr_d = lr_d;
+  const long long R = (long long)T * k;
+  const size_t h_bytes = (size_t)R * I * 2;
+  // one buffer resource spans all of W_down: its byte count must fit 31 bits
+  const bool dc_fits = (size_t)E * H * (I / 2) < (size_t)0x7FFFFFFF;
+  const bool down_combine = R <= kDcMaxRoutes && h_bytes <= (size_t)kDcMaxHBytes && dc_fits;
+  // Experts with many routes go to the MFMA kernels; only batches large
+  // enough to have such experts (and not small enough for the fused
+  // down/unroute kernel) launch them.  K (H for gate/up, I for down) must be a
+  // multiple of the 64-wide step.
+  const bool mfma = !down_combine && T >= kMfmaMinTokens && H % kMmK == 0 && I % kMmK == 0;
+  p.mfma_min = mfma ? kMfmaMinRoutes : 0;
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const long long slots = std::min<long long>(E, (long long)T * k);
@@ -523,17 +750,20 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
   const long long tasks_gu = slots * ((I + rpt_gu - 1) / rpt_gu);
   const long long tasks_d = slots * ((H + rpt_d - 1) / rpt_d);
 
+  const size_t mm_lds_gu = (size_t)(2 * kMmRows + kMmRoutes) * kMmLd * 2;
+  const size_t mm_lds_d = (size_t)(kMmRows + kMmRoutes) * kMmLd * 2;
   if (stage & 1) {
     if (lr_gu == 64) launch_gate_up<64>(p, tasks_gu, s);
     else launch_gate_up<0>(p, tasks_gu, s);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+    if (mfma) {
+      const unsigned grid = (unsigned)(slots * ((I + kMmRows - 1) / kMmRows));
+      ffn_mfma_kernel<true><<<grid, kMmThreads, mm_lds_gu, s>>>(p);
+      if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+    }
   }
   if (!(stage & 2)) return MOE_OK;
-  const long long R = (long long)T * k;
-  const size_t h_bytes = (size_t)R * I * 2;
-  // one buffer resource spans all of W_down: its byte count must fit 31 bits
-  const bool dc_fits = (size_t)E * H * (I / 2) < (size_t)0x7FFFFFFF;
-  if (R <= kDcMaxRoutes && h_bytes <= (size_t)kDcMaxHBytes && dc_fits) {
+  if (down_combine) {
     const int rpw = kWave / lr_d;
     const size_t dyn = h_bytes + (size_t)R * rpw * 4;
     const unsigned grid = (unsigned)((H + rpw - 1) / rpw);
@@ -544,6 +774,11 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
   if (lr_d == 16) launch_down<16>(p, tasks_d, s);
   else launch_down<0>(p, tasks_d, s);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  if (mfma) {
+    const unsigned grid = (unsigned)(slots * ((H + kMmRows - 1) / kMmRows));
+    ffn_mfma_kernel<false><<<grid, kMmThreads, mm_lds_d, s>>>(p);
+    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  }
   const long long cblocks = (long long)T * ((H + kCombineCols - 1) / kCombineCols);
   combine_kernel<<<(unsigned)cblocks, kThreads, 0, s>>>(p);
   return launch_status();
