@@ -45,6 +45,7 @@
 // the scalar path (routing metadata: s_load, its own counter), and a WG's
 // dependent round trips all happen while its weights are in flight.
 #include <algorithm>
+#include <type_traits>
 
 #include "row_dot.h"
 
@@ -301,27 +302,42 @@ __global__ __launch_bounds__(kThreads, 4) void down_kernel(FfnParams p, int n_ta
 // ------------------------------------------------------------------ MFMA tiles (experts with many routes)
 
 // For an expert with many routes the projections are dense contractions:
-// gate/up is [routes x H] x [H x I] twice, down is [routes x I] x [I x H].
-// A workgroup owns 128 weight rows of one expert (both gate and up rows for
-// gate/up) and all of the expert's routes in chunks of 128.  Per 64-wide
-// step of the reduction it dequantises its weight rows once into LDS -
-// e2m1 * e4m3 is exact in bf16, the fp32 global scale is applied to the
-// accumulator - stages the routes' operand rows (gathered x for gate/up,
-// the contiguous h rows for down) next to them, and runs
-// v_mfma_f32_32x32x16_bf16 with the weights as the A operand (32 rows x 16)
-// and the operand rows as B (16 x 32 routes).  Each wave holds a 64 x 64
-// block per matrix (four 32 x 32 accumulators); the next step's codes,
-// scales and operand rows are loaded into registers while the current step
-// runs on the matrix cores.  Epilogue: gate/up writes
-// h = bf16(SiLU(g Gg) * (u Gu)); down writes o = Gd * acc (fp32) for the
-// combine kernel.  Lane layout of the instruction (checked on the device):
-// A lane l holds row l%32, k = 8*(l/32)..+8; B lane l holds column l%32,
-// same k; D register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+// gate/up is [I x H] x [H x routes] twice, down is [H x I] x [I x routes].
+// A workgroup owns 128 weight rows of one expert (the same rows of W_gate
+// and W_up for gate/up) and the expert's routes in chunks of 128; each of
+// its four waves owns 32 of the rows and all of the chunk's routes.
+//
+// v_mfma_f32_32x32x16_bf16 with the weights as A (32 rows x 16) and the
+// routes' operand rows as B (16 x 32 routes).  Lane layout (checked on the
+// device): A lane l holds row l%32, reduction indices 8*(l/32)..+8; B lane l
+// holds column l%32, the same indices; D register r of lane l is row
+// 8*(r/4) + 4*(l/32) + r%4, column l%32.  The reduction index is permuted
+// consistently in A and B: within a 64-wide step, instruction kk of lane
+// half h covers k = 32h + 8kk .. +8, so a lane's four A fragments of a step
+// are 32 consecutive weights of its row - one 16-byte load of e2m1 codes and
+// the two e4m3 scales of those blocks, dequantised in registers to exact
+// bf16 (e2m1 * e4m3 is exact in bf16; the fp32 global scale is applied to
+// the accumulator).  Each weight is loaded and dequantised once.
+//
+// The operand rows (x gathered by token for gate/up, the expert's contiguous
+// h rows for down) go straight into a three-stage LDS ring with
+// global_load_lds, 16-byte chunks placed at chunk ^ ((row >> 1) & 7) so that
+// the B-fragment reads of 16 lanes hit 16 different bank groups.  Weight
+// codes and scales run three steps ahead in a four-entry register ring (the
+// loop is latency-bound on these loads otherwise).
+// Workgroups are numbered so that the n-tiles of one expert share an XCD
+// (workgroups are dealt round robin to the 8 XCDs): its gathered rows are
+// then read from that XCD's L2 after the first tile.
+//
+// Epilogue: gate/up writes h = bf16(SiLU(g Gg) * (u Gu)); down writes
+// o = Gd * acc (fp32) for the combine kernel.
 constexpr int kMmThreads = 256;
-constexpr int kMmRows = 128;                 // weight rows per workgroup
+constexpr int kMmRows = 128;                 // weight rows per workgroup (32 per wave)
 constexpr int kMmRoutes = 128;               // routes per chunk
 constexpr int kMmK = 64;                     // reduction per step
-constexpr int kMmLd = kMmK + 8;              // LDS row stride in bf16 (144 B): spreads rows over banks
+constexpr int kMmStages = 4;                 // operand-ring stages: three steps in flight
+constexpr int kMmStageBytes = kMmRoutes * kMmK * 2;   // 16 KB of operand rows per step
+constexpr int kXcds = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -333,169 +349,217 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// 32 NVFP4 values (16 code bytes, scale bytes of its two 16-value blocks) ->
-// 32 bf16 = code value * block scale (exact) at dst (16-byte aligned LDS).
-__device__ __forceinline__ void dequant32_to_lds(const uint4 codes, uint32_t s2, uint16_t* dst) {
+// e2m1 code pair `B` of `word` times `scale`, as two bf16 (exact).
+template <int B>
+__device__ __forceinline__ uint32_t fp4x2_scaled(uint32_t word, float scale) {
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, B);
+  return pack_bf16x2(v.x * scale, v.y * scale);
+}
+
+// 32 weights (16 code bytes, two block-scale bytes) -> four A fragments of 8 bf16.
+__device__ __forceinline__ void dequant_frags(const uint4 codes, uint32_t s2, bf16x8 (&fr)[4]) {
   const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 0);
   const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 1);
   const uint32_t c[4] = {codes.x, codes.y, codes.z, codes.w};
-  uint32_t out[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const float sc = q < 2 ? s0 : s1;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      f32x2 v;
-      switch (b) {
-        case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[q], 1.0f, 0); break;
-        case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[q], 1.0f, 1); break;
-        case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[q], 1.0f, 2); break;
-        default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[q], 1.0f, 3); break;
-      }
-      out[4 * q + b] = pack_bf16x2(v.x * sc, v.y * sc);
-    }
+    const uint4 v = make_uint4(fp4x2_scaled<0>(c[q], sc), fp4x2_scaled<1>(c[q], sc), fp4x2_scaled<2>(c[q], sc),
+                               fp4x2_scaled<3>(c[q], sc));
+    fr[q] = __builtin_bit_cast(bf16x8, v);
   }
-  uint4* d = reinterpret_cast<uint4*>(dst);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) d[q] = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without a memory fence.  __syncthreads() adds a
+// workgroup-scope fence, which waits for every outstanding vector load -
+// including the prefetched steps.  Inside the step loop the only data other
+// waves read is operand rows written to LDS by buffer_load ... lds, whose
+// completion each wave establishes with wait_vm before the barrier, and LDS
+// reads that the MFMAs have already consumed.
+__device__ __forceinline__ void step_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
 }
 
 template <bool GU>
+struct MmTile {
+  static constexpr int NMAT = GU ? 2 : 1;
+  static constexpr int kLoadsPerStep = 4 + 2 * NMAT;   // per thread: 4 operand chunks, codes + scales per matrix
+  uint8_t* s_x[kMmStages];                             // one LDS array per stage
+  __amdgpu_buffer_rsrc_t rc[NMAT], rs[NMAT], rb;
+  uint32_t w_voff, s_voff;                             // this lane's weight row slice
+  uint32_t x_goff[4];                                  // operand chunk sources, per step add ks*128
+  int wave, lane;
+  uint4 wc[kMmStages][NMAT];
+  uint32_t wsv[kMmStages][NMAT];
+
+  template <int T>
+  __device__ __forceinline__ void issue(int ks) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      wc[T][m] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rc[m], w_voff, (uint32_t)ks * (kMmK / 2), 0));
+      wsv[T][m] = __builtin_amdgcn_raw_buffer_load_b16(rs[m], s_voff, (uint32_t)ks * (kMmK / 16), 0);
+    }
+    uint8_t* stage = s_x[T];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, stage + (i * 4 + wave) * 1024, 16, x_goff[i], (uint32_t)ks * (kMmK * 2),
+                                               0, 0);
+  }
+};
+
+template <bool GU>
 __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
-  constexpr int NMAT = GU ? 2 : 1;
-  extern __shared__ __align__(16) uint16_t s_mm[];          // [NMAT][128][kMmLd] weights, [128][kMmLd] operand
-  __shared__ int s_row[kMmRoutes];                           // operand row per route of the chunk (-1: none)
-  uint16_t* s_w = s_mm;
-  uint16_t* s_b = s_mm + NMAT * kMmRows * kMmLd;
+  using Tile = MmTile<GU>;
+  constexpr int NMAT = Tile::NMAT;
+  constexpr int LPS = Tile::kLoadsPerStep;
+  // separate arrays per stage, so that reads of one stage are seen not to
+  // alias the buffer_load ... lds writes in flight to the others
+  __shared__ __align__(16) uint8_t s_x0[kMmStageBytes];
+  __shared__ __align__(16) uint8_t s_x1[kMmStageBytes];
+  __shared__ __align__(16) uint8_t s_x2[kMmStageBytes];
+  __shared__ __align__(16) uint8_t s_x3[kMmStageBytes];
+  __shared__ int s_row[kMmRoutes];                           // operand row per route of the chunk
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nw = wave & 1, mw = wave >> 1;
+  const int l32 = lane & 31, half = lane >> 5;
   const int N = GU ? p.I : p.H;                              // weight rows
   const int K = GU ? p.H : p.I;                              // reduction length
   const int tiles_n = (N + kMmRows - 1) / kMmRows;
-  const int a = blockIdx.x / tiles_n, n0 = (blockIdx.x - a * tiles_n) * kMmRows;
+  // workgroup b: XCD b % 8, j = b / 8; the tiles_n tiles of slot a share an XCD
+  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  const int a = (j / tiles_n) * kXcds + xcd, n0 = (j % tiles_n) * kMmRows;
+  if (a >= min(p.E, p.T * p.k)) return;
   const int e = slot_expert(p, a);
   if (e < 0) return;
   int off, cnt;
   expert_routes(p, e, off, cnt);
   if (p.mfma_min <= 0 || cnt < p.mfma_min) return;
 
+  Tile t;
+  t.s_x[0] = s_x0;
+  t.s_x[1] = s_x1;
+  t.s_x[2] = s_x2;
+  t.s_x[3] = s_x3;
+  t.wave = wave;
+  t.lane = lane;
   const uint32_t code_row = (uint32_t)K / 2, scale_row = (uint32_t)K / 16;
   const uint32_t mat_codes = (uint32_t)N * code_row, mat_scales = (uint32_t)N * scale_row;
   const uint8_t* wbase[2] = {GU ? p.wg : p.wd, p.wu};
   const uint8_t* sbase[2] = {GU ? p.sg : p.sd, p.su};
-  __amdgpu_buffer_rsrc_t rc[NMAT], rs[NMAT];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m) {
-    rc[m] = make_rsrc(wbase[m] + (size_t)e * mat_codes, mat_codes);
-    rs[m] = make_rsrc(sbase[m] + (size_t)e * mat_scales, mat_scales);
+    t.rc[m] = make_rsrc(wbase[m] + (size_t)e * mat_codes, mat_codes);
+    t.rs[m] = make_rsrc(sbase[m] + (size_t)e * mat_scales, mat_scales);
   }
   const int R = p.T * p.k;
-  const auto rb = GU ? make_rsrc(p.x, (uint32_t)p.T * (uint32_t)p.H * 2u)
-                     : make_rsrc(p.h, (uint32_t)R * (uint32_t)p.I * 2u);
-  // this thread's dequant slice: weight row r, 32 values at 32*hf of each step;
-  // and operand slice: route row r, the same 32 columns
-  const int r = tid >> 1, hf = tid & 1;
-  const uint32_t w_voff = (uint32_t)(n0 + r) * code_row + (uint32_t)hf * 16;
-  const uint32_t s_voff = (uint32_t)(n0 + r) * scale_row + (uint32_t)hf * 2;
-  const int n_steps = K / kMmK;
+  t.rb = GU ? make_rsrc(p.x, (uint32_t)p.T * (uint32_t)p.H * 2u) : make_rsrc(p.h, (uint32_t)R * (uint32_t)p.I * 2u);
+  const int wrow = n0 + wave * 32 + l32;                     // this lane's weight row
+  t.w_voff = (uint32_t)wrow * code_row + (uint32_t)half * 16;
+  t.s_voff = (uint32_t)wrow * scale_row + (uint32_t)half * 2;
+  const int steps = K / kMmK;
 
   for (int m0 = 0; m0 < cnt; m0 += kMmRoutes) {
     const int mc = min(kMmRoutes, cnt - m0);
+    const int mtiles = (mc + 31) >> 5;
     __syncthreads();                                         // previous chunk done with LDS
     if (tid < kMmRoutes) {
-      int row = -1;
-      if (tid < mc) {
-        const int pos = off + m0 + tid;
-        row = GU ? min(max(p.route_src[pos] / p.k, 0), p.T - 1) : pos;
-      }
-      s_row[tid] = row;
+      const int pos = off + m0 + min(tid, mc - 1);           // rows past the chunk repeat its last route
+      s_row[tid] = GU ? min(max(p.route_src[pos] / p.k, 0), p.T - 1) : pos;
     }
     __syncthreads();
-    const int brow = s_row[r];
-    const uint32_t b_voff = (uint32_t)max(brow, 0) * (uint32_t)K * 2u + (uint32_t)hf * 64;
-
-    f32x16 acc[NMAT][2][2];
+    // operand chunk q = (4i + wave)*64 + lane sits at row q/8, position q%8,
+    // and holds source chunk (q%8) ^ ((row >> 1) & 7) of that row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = (i * 4 + wave) * 64 + lane;
+      const int row = q >> 3, c = (q & 7) ^ ((row >> 1) & 7);
+      t.x_goff[i] = (uint32_t)s_row[row] * (uint32_t)K * 2u + (uint32_t)c * 16;
+    }
+    f32x16 acc[NMAT][4];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[m][i][j] = f32x16{};
+      for (int jt = 0; jt < 4; ++jt) acc[m][jt] = f32x16{};
 
-    uint4 wc[NMAT];
-    uint32_t wsv[NMAT];
-    u32x4 bv[4];
-    auto load_step = [&](int ks) {
+    t.template issue<0>(0);
+    t.template issue<1>(min(1, steps - 1));
+    t.template issue<2>(min(2, steps - 1));
+
+    auto body = [&](auto stage_c, int ks) {
+      constexpr int S = decltype(stage_c)::value;
+      step_barrier();                                        // every wave is done with step ks-1's stage
+      // Always three steps ahead, so that every path has the same loads in
+      // flight (the last three re-read the final step into a free stage).
+      t.template issue<(S + 3) % kMmStages>(min(ks + 3, steps - 1));
+      wait_vm<3 * LPS>();
+      step_barrier();                                        // step ks's operand rows are in LDS
+      const uint8_t* stage = S == 0 ? s_x0 : (S == 1 ? s_x1 : (S == 2 ? s_x2 : s_x3));
+      bf16x8 af[NMAT][4];
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-        wc[m] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rc[m], w_voff, (uint32_t)ks * (kMmK / 2), 0));
-        wsv[m] = __builtin_amdgcn_raw_buffer_load_b16(rs[m], s_voff, (uint32_t)ks * (kMmK / 16), 0);
-      }
+      for (int m = 0; m < NMAT; ++m) dequant_frags(t.wc[S][m], t.wsv[S][m], af[m]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        bv[q] = brow >= 0 ? __builtin_amdgcn_raw_buffer_load_b128(rb, b_voff + q * 16, (uint32_t)ks * (kMmK * 2), 0)
-                          : u32x4{0u, 0u, 0u, 0u};
-    };
-    load_step(0);
-    for (int ks = 0; ks < n_steps; ++ks) {
+      for (int jt = 0; jt < 4; ++jt) {
+        if (jt < mtiles) {
+          const int row = jt * 32 + l32;
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) dequant32_to_lds(wc[m], wsv[m], s_w + (m * kMmRows + r) * kMmLd + hf * 32);
-      u32x4* bd = reinterpret_cast<u32x4*>(s_b + r * kMmLd + hf * 32);
+          for (int kk = 0; kk < 4; ++kk) {
+            const int c = (half * 4 + kk) ^ ((row >> 1) & 7);
+            const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(stage + row * (kMmK * 2) + c * 16);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) bd[q] = bv[q];
-      if (ks + 1 < n_steps) load_step(ks + 1);
-      __syncthreads();
-#pragma unroll
-      for (int kk = 0; kk < kMmK / 16; ++kk) {
-        const int kcol = kk * 16 + (lane >> 5) * 8;
-        bf16x8 bfr[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8*>(s_b + (mw * 64 + j * 32 + (lane & 31)) * kMmLd + kcol);
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const bf16x8 afr =
-                *reinterpret_cast<const bf16x8*>(s_w + (m * kMmRows + nw * 64 + i * 32 + (lane & 31)) * kMmLd + kcol);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[j], acc[m][i][j], 0, 0, 0);
+            for (int m = 0; m < NMAT; ++m)
+              acc[m][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[m][kk], bfr, acc[m][jt], 0, 0, 0);
           }
         }
       }
-      __syncthreads();
+    };
+    // whole groups of four steps in the loop (one pattern of loads in flight
+    // at the back edge, so the compiler's own waits stay as loose as ours),
+    // then the remainder
+    int s0 = 0;
+    for (; s0 + kMmStages <= steps; s0 += kMmStages) {
+      body(std::integral_constant<int, 0>{}, s0);
+      body(std::integral_constant<int, 1>{}, s0 + 1);
+      body(std::integral_constant<int, 2>{}, s0 + 2);
+      body(std::integral_constant<int, 3>{}, s0 + 3);
     }
+    if (s0 < steps) body(std::integral_constant<int, 0>{}, s0);
+    if (s0 + 1 < steps) body(std::integral_constant<int, 1>{}, s0 + 1);
+    if (s0 + 2 < steps) body(std::integral_constant<int, 2>{}, s0 + 2);
+    wait_vm<0>();                                            // the surplus loads have landed
 
-    // epilogue: lane holds, per 32 x 32 block, rows 8*(q) + 4*(lane/32) + 0..3 of one route column
+    // epilogue: per 32 x 32 block, a lane holds 4 runs of 4 consecutive weight
+    // rows 8*q + 4*(lane/32) + 0..3 for one route column
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int jt = 0; jt < 4; ++jt) {
+      const int m_loc = jt * 32 + l32;
+      if (m_loc >= mc) continue;
+      const int pos = off + m0 + m_loc;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int m_loc = mw * 64 + j * 32 + (lane & 31);
-        if (m_loc >= mc) continue;
-        const int pos = off + m0 + m_loc;
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wave * 32 + q * 8 + half * 4;
+        if (n >= N) continue;
+        if constexpr (GU) {
+          const float Gg = p.gsc[e * 3 + 0], Gu = p.gsc[e * 3 + 1];
+          uint32_t hv[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + nw * 64 + i * 32 + q * 8 + (lane >> 5) * 4;
-          if (n >= N) continue;
-          if constexpr (GU) {
-            const float Gg = p.gsc[e * 3 + 0], Gu = p.gsc[e * 3 + 1];
-            uint32_t hv[2];
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-              const float g0 = acc[0][i][j][4 * q + 2 * t2] * Gg, g1 = acc[0][i][j][4 * q + 2 * t2 + 1] * Gg;
-              const float u0 = acc[1][i][j][4 * q + 2 * t2] * Gu, u1 = acc[1][i][j][4 * q + 2 * t2 + 1] * Gu;
-              hv[t2] = f32_to_bf16_rne(silu(g0) * u0) | (f32_to_bf16_rne(silu(g1) * u1) << 16);
-            }
-            *reinterpret_cast<uint2*>(p.h + (size_t)pos * p.I + n) = make_uint2(hv[0], hv[1]);
-          } else {
-            const float Gd = p.gsc[e * 3 + 2];
-            *reinterpret_cast<float4*>(p.o + (size_t)pos * p.H + n) =
-                make_float4(acc[0][i][j][4 * q] * Gd, acc[0][i][j][4 * q + 1] * Gd, acc[0][i][j][4 * q + 2] * Gd,
-                            acc[0][i][j][4 * q + 3] * Gd);
+          for (int t2 = 0; t2 < 2; ++t2) {
+            const float g0 = acc[0][jt][4 * q + 2 * t2] * Gg, g1 = acc[0][jt][4 * q + 2 * t2 + 1] * Gg;
+            const float u0 = acc[1][jt][4 * q + 2 * t2] * Gu, u1 = acc[1][jt][4 * q + 2 * t2 + 1] * Gu;
+            hv[t2] = f32_to_bf16_rne(silu(g0) * u0) | (f32_to_bf16_rne(silu(g1) * u1) << 16);
           }
+          *reinterpret_cast<uint2*>(p.h + (size_t)pos * p.I + n) = make_uint2(hv[0], hv[1]);
+        } else {
+          const float Gd = p.gsc[e * 3 + 2];
+          *reinterpret_cast<float4*>(p.o + (size_t)pos * p.H + n) =
+              make_float4(acc[0][jt][4 * q] * Gd, acc[0][jt][4 * q + 1] * Gd, acc[0][jt][4 * q + 2] * Gd,
+                          acc[0][jt][4 * q + 3] * Gd);
         }
       }
     }
@@ -750,15 +814,14 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
   const long long tasks_gu = slots * ((I + rpt_gu - 1) / rpt_gu);
   const long long tasks_d = slots * ((H + rpt_d - 1) / rpt_d);
 
-  const size_t mm_lds_gu = (size_t)(2 * kMmRows + kMmRoutes) * kMmLd * 2;
-  const size_t mm_lds_d = (size_t)(kMmRows + kMmRoutes) * kMmLd * 2;
+  const long long slots8 = (slots + kXcds - 1) / kXcds * kXcds;   // slot count padded for the XCD numbering
   if (stage & 1) {
     if (lr_gu == 64) launch_gate_up<64>(p, tasks_gu, s);
     else launch_gate_up<0>(p, tasks_gu, s);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
     if (mfma) {
-      const unsigned grid = (unsigned)(slots * ((I + kMmRows - 1) / kMmRows));
-      ffn_mfma_kernel<true><<<grid, kMmThreads, mm_lds_gu, s>>>(p);
+      const unsigned grid = (unsigned)(slots8 * ((I + kMmRows - 1) / kMmRows));
+      ffn_mfma_kernel<true><<<grid, kMmThreads, 0, s>>>(p);
       if (launch_status() != MOE_OK) return MOE_ERR_HIP;
     }
   }
@@ -775,8 +838,8 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
   else launch_down<0>(p, tasks_d, s);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   if (mfma) {
-    const unsigned grid = (unsigned)(slots * ((H + kMmRows - 1) / kMmRows));
-    ffn_mfma_kernel<false><<<grid, kMmThreads, mm_lds_d, s>>>(p);
+    const unsigned grid = (unsigned)(slots8 * ((H + kMmRows - 1) / kMmRows));
+    ffn_mfma_kernel<false><<<grid, kMmThreads, 0, s>>>(p);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
   const long long cblocks = (long long)T * ((H + kCombineCols - 1) / kCombineCols);
