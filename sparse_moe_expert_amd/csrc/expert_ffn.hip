@@ -141,7 +141,7 @@ __device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, k
   const int half = (int)(tid >= kThreads / 2);
   const uint32_t sbyte = (uint32_t)(tid & (kThreads / 2 - 1)) * 16;
   const auto rs = make_rsrc((half ? p.su : p.sg) + (size_t)e * mat_scales, mat_scales);
-  const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rs, sbyte, (uint32_t)tile * blk, 0);
+  const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rs, sbyte, (uint32_t)tile * blk, kStreamAux);
   compiler_fence();
   const auto rg = make_rsrc(p.wg + (size_t)e * mat_codes, mat_codes);
   const auto ru = make_rsrc(p.wu + (size_t)e * mat_codes, mat_codes);
@@ -150,8 +150,8 @@ __device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, k
 #pragma unroll
   for (int u = 0; u < kGuUnits; ++u) {
     const uint32_t r0 = (uint32_t)g.row0(tile, u);
-    cg[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rg, lane_c, r0 * code_row, 0));
-    cu[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(ru, lane_c, r0 * code_row, 0));
+    cg[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rg, lane_c, r0 * code_row, kStreamAux));
+    cu[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(ru, lane_c, r0 * code_row, kStreamAux));
   }
   compiler_fence();
   int off, cnt;
@@ -245,7 +245,8 @@ __device__ __forceinline__ void down_tile(const FfnParams& p, const Geo<LD, kDUn
   const uint32_t mat_codes = (uint32_t)p.H * code_row, mat_scales = (uint32_t)p.H * scale_row;
   const uint32_t blk = (uint32_t)g.rpt * scale_row;            // 4096 bytes
   const auto rs = make_rsrc(p.sd + (size_t)e * mat_scales, mat_scales);
-  const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)threadIdx.x * 16, (uint32_t)tile * blk, 0);
+  const u32x4 sv =
+      __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)threadIdx.x * 16, (uint32_t)tile * blk, kStreamAux);
   compiler_fence();
   const auto rd = make_rsrc(p.wd + (size_t)e * mat_codes, mat_codes);
   const uint32_t lane_c = (uint32_t)g.sub * code_row + (uint32_t)g.sl * 16;
@@ -253,7 +254,7 @@ __device__ __forceinline__ void down_tile(const FfnParams& p, const Geo<LD, kDUn
 #pragma unroll
   for (int u = 0; u < kDUnits; ++u) {
     const uint32_t r0 = (uint32_t)g.row0(tile, u);
-    cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, lane_c, r0 * code_row, 0));
+    cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, lane_c, r0 * code_row, kStreamAux));
   }
   compiler_fence();
   int off, cnt;
@@ -403,6 +404,8 @@ struct MmTile {
   __device__ __forceinline__ void issue(int ks) {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
+      // default cache policy: each load uses 32 of a row's 128 cached bytes,
+      // the next three K steps use the rest
       wc[T][m] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rc[m], w_voff, (uint32_t)ks * (kMmK / 2), 0));
       wsv[T][m] = __builtin_amdgcn_raw_buffer_load_b16(rs[m], s_voff, (uint32_t)ks * (kMmK / 16), 0);
     }
@@ -668,8 +671,8 @@ __global__ __launch_bounds__(kDcThreads, 2) void down_combine_kernel(FfnParams p
     for (int u = 0; u < kDcSlots; ++u) {
       if (e_u[u] >= 0) {
         const uint32_t r = (uint32_t)e_u[u] * (uint32_t)p.H + (uint32_t)row0;
-        cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, lane_c, r * code_row, 0));
-        vd[u] = __builtin_amdgcn_raw_buffer_load_b16(rds, lane_s, r * scale_row, 0);
+        cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, lane_c, r * code_row, kStreamAux));
+        vd[u] = __builtin_amdgcn_raw_buffer_load_b16(rds, lane_s, r * scale_row, kStreamAux);
       }
     }
     compiler_fence();

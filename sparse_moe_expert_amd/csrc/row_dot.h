@@ -17,6 +17,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
+// Cache policy of the row-dot weight streams: non-temporal.  Each of these
+// loads consumes whole cache lines and every weight and scale byte of a step
+// is read once, so they are marked as streaming and do not displace the small
+// reused data (routing metadata, activations, h) from the caches; measured on
+// gfx950 this shortens the decode step by ~10%.
+constexpr int kStreamAux = 2;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
