@@ -26,9 +26,11 @@
 //
 // Row tiles (gfx950).  A wavefront reads whole rows: Lr lanes share a row and
 // each lane reads one 16-byte chunk of e2m1 codes (32 values) plus its two
-// e4m3 scales, with buffer loads from a per-expert resource (hardware range
-// check: rows past the matrix read as zero, so ragged tiles need no
-// predication and no index can fault).  Byte pairs become bf16 with
+// e4m3 scales, with buffer loads from a per-expert resource.  The whole byte
+// offset goes in the instruction's vector offset, which the hardware range
+// check covers (the scalar offset is added after the check): rows past the
+// matrix read as zero, so ragged tiles need no predication and no index can
+// fault.  Byte pairs become bf16 with
 // v_cvt_scalef32_pk_bf16_fp4 (exact at scale 1), v_dot2 multiplies them
 // pairwise with the bf16 operand (x or h) and accumulates in fp32, one scale
 // multiplies each 16-value block, and the partial sums of a row are added
@@ -88,7 +90,9 @@ constexpr int kScaleTileBytes = 2048;
 // a metadata fetch issued while a tile's weight rows are in flight does not
 // have to wait for them (vector loads complete in order).
 typedef const __attribute__((address_space(4))) int32_t* scalar_ptr;
+typedef const __attribute__((address_space(4))) float* scalar_fptr;
 __device__ __forceinline__ int sload(const int32_t* base, int i) { return ((scalar_ptr)base)[i]; }
+__device__ __forceinline__ float sload(const float* base, int i) { return ((scalar_fptr)base)[i]; }
 
 // Expert id of active slot a (-1 past the active list), clamped into range:
 // inputs that violate the bucket precondition give wrong results but no
@@ -141,7 +145,7 @@ __device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, k
   const int half = (int)(tid >= kThreads / 2);
   const uint32_t sbyte = (uint32_t)(tid & (kThreads / 2 - 1)) * 16;
   const auto rs = make_rsrc((half ? p.su : p.sg) + (size_t)e * mat_scales, mat_scales);
-  const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rs, sbyte, (uint32_t)tile * blk, kStreamAux);
+  const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rs, sbyte + (uint32_t)tile * blk, 0, kStreamAux);
   compiler_fence();
   const auto rg = make_rsrc(p.wg + (size_t)e * mat_codes, mat_codes);
   const auto ru = make_rsrc(p.wu + (size_t)e * mat_codes, mat_codes);
@@ -150,13 +154,13 @@ __device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, k
 #pragma unroll
   for (int u = 0; u < kGuUnits; ++u) {
     const uint32_t r0 = (uint32_t)g.row0(tile, u);
-    cg[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rg, lane_c, r0 * code_row, kStreamAux));
-    cu[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(ru, lane_c, r0 * code_row, kStreamAux));
+    cg[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rg, lane_c + r0 * code_row, 0, kStreamAux));
+    cu[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(ru, lane_c + r0 * code_row, 0, kStreamAux));
   }
   compiler_fence();
   int off, cnt;
   expert_routes(p, e, off, cnt);
-  const float Gg = p.gsc[e * 3 + 0], Gu = p.gsc[e * 3 + 1];
+  const float Gg = sload(p.gsc, e * 3 + 0), Gu = sload(p.gsc, e * 3 + 1);
   const int row_bytes = p.H * 2;
   const int group = max(1, min(kXStageBytes / row_bytes, 64));
   const int pieces = row_bytes / 16;                             // 16-byte pieces of one x row
@@ -246,7 +250,7 @@ __device__ __forceinline__ void down_tile(const FfnParams& p, const Geo<LD, kDUn
   const uint32_t blk = (uint32_t)g.rpt * scale_row;            // 4096 bytes
   const auto rs = make_rsrc(p.sd + (size_t)e * mat_scales, mat_scales);
   const u32x4 sv =
-      __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)threadIdx.x * 16, (uint32_t)tile * blk, kStreamAux);
+      __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)threadIdx.x * 16 + (uint32_t)tile * blk, 0, kStreamAux);
   compiler_fence();
   const auto rd = make_rsrc(p.wd + (size_t)e * mat_codes, mat_codes);
   const uint32_t lane_c = (uint32_t)g.sub * code_row + (uint32_t)g.sl * 16;
@@ -254,7 +258,7 @@ __device__ __forceinline__ void down_tile(const FfnParams& p, const Geo<LD, kDUn
 #pragma unroll
   for (int u = 0; u < kDUnits; ++u) {
     const uint32_t r0 = (uint32_t)g.row0(tile, u);
-    cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, lane_c, r0 * code_row, kStreamAux));
+    cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, lane_c + r0 * code_row, 0, kStreamAux));
   }
   compiler_fence();
   int off, cnt;
@@ -267,7 +271,7 @@ __device__ __forceinline__ void down_tile(const FfnParams& p, const Geo<LD, kDUn
     const int rin = (u * kWavesPerBlock + g.wave) * g.rpw + g.sub;
     vd[u] = *reinterpret_cast<const uint16_t*>(s_sc + rin * scale_row + g.sl * 2);
   }
-  const float Gd = p.gsc[e * 3 + 2];
+  const float Gd = sload(p.gsc, e * 3 + 2);
   for (int t = 0; t < cnt; ++t) {
     const int pos = off + t;
 #pragma unroll
@@ -549,7 +553,7 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
         const int n = n0 + wave * 32 + q * 8 + half * 4;
         if (n >= N) continue;
         if constexpr (GU) {
-          const float Gg = p.gsc[e * 3 + 0], Gu = p.gsc[e * 3 + 1];
+          const float Gg = sload(p.gsc, e * 3 + 0), Gu = sload(p.gsc, e * 3 + 1);
           uint32_t hv[2];
 #pragma unroll
           for (int t2 = 0; t2 < 2; ++t2) {
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
           }
           *reinterpret_cast<uint2*>(p.h + (size_t)pos * p.I + n) = make_uint2(hv[0], hv[1]);
         } else {
-          const float Gd = p.gsc[e * 3 + 2];
+          const float Gd = sload(p.gsc, e * 3 + 2);
           *reinterpret_cast<float4*>(p.o + (size_t)pos * p.H + n) =
               make_float4(acc[0][jt][4 * q] * Gd, acc[0][jt][4 * q + 1] * Gd, acc[0][jt][4 * q + 2] * Gd,
                           acc[0][jt][4 * q + 3] * Gd);
@@ -608,24 +612,36 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(FfnParams p) {
 // ------------------------------------------------------------------ down + combine (small batches)
 
 constexpr int kDcMaxRoutes = 128;          // T*k on the fused down/combine path
-constexpr int kDcMaxHBytes = 65536;        // all routes' h staged in LDS up to this size
-constexpr int kDcThreads = 512;            // eight waves share one row block
+constexpr int kDcMaxLds = 65536;           // all routes' h and o staged in LDS up to this size
+constexpr int kDcThreads = 1024;           // sixteen waves share one row block
 constexpr int kDcWaves = kDcThreads / kWave;
-constexpr int kDcSlots = 8;                // expert rows in flight per wave
+constexpr int kDcLoadsPerSlot = 2;         // one b128 code load and one b16 scale load
+constexpr int kDcHLoads = kDcMaxLds / 16 / kDcThreads;   // 16-byte h pieces per thread
 
 // Down projection and weighted unroute of a small batch in one kernel, with
 // the work split by output rows instead of by expert: workgroup b owns rows
 // [b*rpw, b*rpw + rpw) of y (rpw = 64 / lanes per row) for every token.  Its
-// eight waves take the active slots a = wave, wave+8, ... and hold one
-// 16-byte chunk per lane of each slot's rows of W_down (up to kDcSlots slots
-// in flight per wave), o[route, row] stays in LDS, and each token's routes
-// are finally summed in slot order.  Issue order: all routes' h rows
-// straight into LDS, the routes' positions and weights, the slots' expert
-// ids (scalar path), then every weight row; route ranges come through the
-// scalar path while the rows are in flight.  No o round trip through memory
-// and no cross-workgroup ordering.
-template <int LD>
-__global__ __launch_bounds__(kDcThreads, 2) void down_combine_kernel(FfnParams p) {
+// sixteen waves take the active slots a = wave + 16*u, u < SLOTS (SLOTS =
+// ceil(slots / 16), so one pass covers them all), and hold one 16-byte chunk
+// per lane of each slot's rows of W_down: many waves with few loads each keep
+// more row pieces in flight than few waves with many.  o[route, row] stays in
+// LDS, and each token's routes are finally summed in slot order.  No o round
+// trip through memory and no cross-workgroup ordering.
+//
+// Issue order: all routes' h rows (kDcHLoads 16-byte pieces per thread into
+// registers), the routes' positions and weights, the slots' expert ids
+// (scalar path), then every slot's weight row, and then route ranges and
+// global scales through the scalar path.  Every vector load is issued
+// unconditionally - a piece or slot past the end reads out of range, which
+// returns zeros without memory traffic - so the loads land in a fixed order.
+// h goes to LDS as soon as it has landed, the waves meet at a barrier that
+// does not drain the weight loads, and each wave computes slot by slot as
+// their rows arrive (vector loads complete in order).  All of them are
+// ordinary buffer loads and none sits in a loop, which keeps the compiler's
+// wait counts exact (with LDS-direct loads in flight as well it waits for
+// everything).
+template <int LD, int SLOTS>
+__global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_kernel(FfnParams p) {
   extern __shared__ __align__(16) uint8_t s_dyn8[];   // [R, I] bf16 h, then [R, rpw] fp32 o
   __shared__ int s_pos[kDcMaxRoutes];
   __shared__ float s_w[kDcMaxRoutes];
@@ -638,70 +654,82 @@ __global__ __launch_bounds__(kDcThreads, 2) void down_combine_kernel(FfnParams p
   uint16_t* s_h = reinterpret_cast<uint16_t*>(s_dyn8);
   float* s_o = reinterpret_cast<float*>(s_dyn8 + (size_t)R * p.I * 2);
 
-  // h rows of every route, 1 KB per wave load
-  const int pieces = R * p.I / 8;
-  const uint4* hsrc = reinterpret_cast<const uint4*>(p.h);
-  for (int q0 = wave * kWave; q0 < pieces; q0 += kDcThreads)
-    if (q0 + lane < pieces) __builtin_amdgcn_global_load_lds(hsrc + q0 + lane, s_dyn8 + (size_t)q0 * 16, 16, 0, 0);
-  int pos_r = 0;
-  float w_r = 0.0f;
-  if (tid < R) {
-    pos_r = min(max(p.route_pos[tid], 0), R - 1);
-    w_r = p.topk_w[tid];
-  }
+  // h rows of every route: piece q = tid + i*kDcThreads of the [R, I] block
+  const uint32_t h_bytes = (uint32_t)R * p.I * 2;
+  const auto rh = make_rsrc(p.h, h_bytes);
+  u32x4 hv[kDcHLoads];
+#pragma unroll
+  for (int i = 0; i < kDcHLoads; ++i)
+    hv[i] = __builtin_amdgcn_raw_buffer_load_b128(rh, (uint32_t)(tid + i * kDcThreads) * 16, 0, 0);
+  // route positions and gate weights (an index past R re-reads the last)
+  const int rt = min(tid, R - 1);
+  const int pos_r = p.route_pos[rt];
+  const float w_r = p.topk_w[rt];
   compiler_fence();
 
+  int e_u[SLOTS];
+#pragma unroll
+  for (int u = 0; u < SLOTS; ++u) {
+    const int a = wave + u * kDcWaves;
+    e_u[u] = a < S ? slot_expert(p, a) : -1;
+  }
   const uint32_t code_row = (uint32_t)p.I / 2, scale_row = (uint32_t)p.I / 16;
+  // one resource spans all of W_down (and one its scales); the host checks
+  // that their byte counts fit 31 bits
   const auto rd = make_rsrc(p.wd, (uint32_t)p.E * p.H * code_row);
   const auto rds = make_rsrc(p.sd, (uint32_t)p.E * p.H * scale_row);
   const uint32_t lane_c = (uint32_t)sub * code_row + (uint32_t)sl * 16;
   const uint32_t lane_s = (uint32_t)sub * scale_row + (uint32_t)sl * 2;
+  constexpr uint32_t kOutOfRange = 0x80000000u;       // past both resources: reads zero
+  uint4 cd[SLOTS];
+  uint32_t vd[SLOTS];
+#pragma unroll
+  for (int u = 0; u < SLOTS; ++u) {
+    const uint32_t r = (uint32_t)max(e_u[u], 0) * (uint32_t)p.H + (uint32_t)row0;
+    const uint32_t oc = e_u[u] >= 0 ? lane_c + r * code_row : kOutOfRange;
+    const uint32_t os = e_u[u] >= 0 ? lane_s + r * scale_row : kOutOfRange;
+    cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, oc, 0, kStreamAux));
+    vd[u] = __builtin_amdgcn_raw_buffer_load_b16(rds, os, 0, kStreamAux);
+  }
+  compiler_fence();
+  int off_u[SLOTS], cnt_u[SLOTS];
+  float gd_u[SLOTS];
+#pragma unroll
+  for (int u = 0; u < SLOTS; ++u) {
+    off_u[u] = 0;
+    cnt_u[u] = 0;
+    gd_u[u] = 0.0f;
+    if (e_u[u] >= 0) {
+      expert_routes(p, e_u[u], off_u[u], cnt_u[u]);
+      gd_u[u] = sload(p.gsc, e_u[u] * 3 + 2);
+    }
+  }
+  // h and the route data were issued before the weight loads
+#pragma unroll
+  for (int i = 0; i < kDcHLoads; ++i) {
+    const uint32_t q = (uint32_t)(tid + i * kDcThreads) * 16;
+    if (q < h_bytes) *reinterpret_cast<u32x4*>(s_dyn8 + q) = hv[i];
+  }
+  if (tid < R) {
+    s_pos[tid] = min(max(pos_r, 0), R - 1);
+    s_w[tid] = w_r;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();                // h of every route is in LDS; weights still in flight
+  compiler_fence();
+
   const bool row_ok = row0 + sub < p.H;
-  // the trip count is the same for every wave (the loop holds a barrier)
-  for (int c0 = 0; c0 < S; c0 += kDcWaves * kDcSlots) {
-    int e_u[kDcSlots];
-    uint4 cd[kDcSlots];
-    uint32_t vd[kDcSlots];
 #pragma unroll
-    for (int u = 0; u < kDcSlots; ++u) {
-      const int a = c0 + wave + u * kDcWaves;
-      e_u[u] = a < S ? slot_expert(p, a) : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kDcSlots; ++u) {
-      if (e_u[u] >= 0) {
-        const uint32_t r = (uint32_t)e_u[u] * (uint32_t)p.H + (uint32_t)row0;
-        cd[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, lane_c, r * code_row, kStreamAux));
-        vd[u] = __builtin_amdgcn_raw_buffer_load_b16(rds, lane_s, r * scale_row, kStreamAux);
-      }
-    }
-    compiler_fence();
-    int off_u[kDcSlots], cnt_u[kDcSlots];
-#pragma unroll
-    for (int u = 0; u < kDcSlots; ++u) {
-      off_u[u] = 0;
-      cnt_u[u] = 0;
-      if (e_u[u] >= 0) expert_routes(p, e_u[u], off_u[u], cnt_u[u]);
-    }
-    if (c0 == 0 && tid < R) {
-      s_pos[tid] = pos_r;
-      s_w[tid] = w_r;
-    }
-    wait_vector_loads();
-    __syncthreads();                            // h of every route is in LDS
-#pragma unroll
-    for (int u = 0; u < kDcSlots; ++u) {
-      if (e_u[u] < 0) continue;
-      const float Gd = p.gsc[e_u[u] * 3 + 2];
-      for (int t = 0; t < cnt_u[u]; ++t) {
-        const int pos = off_u[u] + t;
-        opaque(cd[u]);
-        uint32_t hr[16];
-        load_operand_chunk(s_h + (size_t)pos * p.I, sl, hr);
-        const float acc = dot_chunk(cd[u], vd[u], hr, 0.0f);
-        const float v = (LD == 16 ? row16_sum(acc) : group_sum(acc, ld)) * Gd;
-        if (sl == 0 && row_ok) s_o[pos * rpw + sub] = v;
-      }
+  for (int u = 0; u < SLOTS; ++u) {
+    if (e_u[u] < 0) continue;
+    for (int t = 0; t < cnt_u[u]; ++t) {
+      const int pos = off_u[u] + t;
+      opaque(cd[u]);
+      uint32_t hr[16];
+      load_operand_chunk(s_h + (size_t)pos * p.I, sl, hr);
+      const float acc = dot_chunk(cd[u], vd[u], hr, 0.0f);
+      const float v = (LD == 16 ? row16_sum(acc) : group_sum(acc, ld)) * gd_u[u];
+      if (sl == 0 && row_ok) s_o[pos * rpw + sub] = v;
     }
   }
   __syncthreads();
@@ -714,6 +742,16 @@ __global__ __launch_bounds__(kDcThreads, 2) void down_combine_kernel(FfnParams p
     for (int j = 0; j < p.k; ++j) acc = fmaf(s_w[t * p.k + j], s_o[s_pos[t * p.k + j] * rpw + r], acc);
     p.y[(size_t)t * p.H + row0 + r] = (uint16_t)f32_to_bf16_rne(acc);
   }
+}
+
+template <int LD>
+void launch_down_combine(const FfnParams& p, unsigned grid, size_t dyn, int slots, hipStream_t s) {
+  const int per_wave = (slots + kDcWaves - 1) / kDcWaves;
+  if (per_wave <= 1) down_combine_kernel<LD, 1><<<grid, kDcThreads, dyn, s>>>(p);
+  else if (per_wave == 2) down_combine_kernel<LD, 2><<<grid, kDcThreads, dyn, s>>>(p);
+  else if (per_wave == 3) down_combine_kernel<LD, 3><<<grid, kDcThreads, dyn, s>>>(p);
+  else if (per_wave == 4) down_combine_kernel<LD, 4><<<grid, kDcThreads, dyn, s>>>(p);
+  else down_combine_kernel<LD, kDcMaxRoutes / kDcWaves><<<grid, kDcThreads, dyn, s>>>(p);
 }
 
 // ------------------------------------------------------------------ host
@@ -802,7 +840,8 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
   const size_t h_bytes = (size_t)R * I * 2;
   // one buffer resource spans all of W_down: its byte count must fit 31 bits
   const bool dc_fits = (size_t)E * H * (I / 2) < (size_t)0x7FFFFFFF;
-  const bool down_combine = R <= kDcMaxRoutes && h_bytes <= (size_t)kDcMaxHBytes && dc_fits;
+  const size_t dc_lds = h_bytes + (size_t)R * (kWave / lr_d) * 4;   // h and o of the fused down/unroute kernel
+  const bool down_combine = R <= kDcMaxRoutes && dc_lds <= (size_t)kDcMaxLds && dc_fits;
   // Experts with many routes go to the MFMA kernels; only batches large
   // enough to have such experts (and not small enough for the fused
   // down/unroute kernel) launch them.  K (H for gate/up, I for down) must be a
@@ -833,8 +872,8 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
     const int rpw = kWave / lr_d;
     const size_t dyn = h_bytes + (size_t)R * rpw * 4;
     const unsigned grid = (unsigned)((H + rpw - 1) / rpw);
-    if (lr_d == 16) down_combine_kernel<16><<<grid, kDcThreads, dyn, s>>>(p);
-    else down_combine_kernel<0><<<grid, kDcThreads, dyn, s>>>(p);
+    if (lr_d == 16) launch_down_combine<16>(p, grid, dyn, (int)slots, s);
+    else launch_down_combine<0>(p, grid, dyn, (int)slots, s);
     return launch_status();
   }
   if (lr_d == 16) launch_down<16>(p, tasks_d, s);

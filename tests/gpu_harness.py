@@ -3,7 +3,11 @@
 Acceptance (fixed before any kernel ran): expert ids and every bucket array
 bit-exact; gate weights within 1e-6 absolute; the bf16 output within
 max|y - y_ref| <= 2e-2 * rms(y_ref), rms over the compared outputs (exactly 0
-when the reference is exactly 0).
+when the reference is exactly 0).  That bound is the one for the five
+workloads.  Small edge-case shapes outside them (a few dozen outputs per token)
+can have max|y_ref| well above 5 * rms, where the bf16 rounding of the output
+itself (relative 2^-8) already reaches the bound; their tests use
+assert_output_rounded, which adds half a bf16 ulp of each reference value.
 """
 
 from __future__ import annotations
@@ -86,6 +90,28 @@ def assert_output(y_gpu: np.ndarray, y_ref: np.ndarray, tag: str = ""):
     else:
         assert err <= Y_REL_TOL * rms, f"{tag}: max err {err:.3e} > {Y_REL_TOL} * rms {rms:.3e}"
     return err, rms
+
+
+def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
+    """Half the bf16 spacing at |v| (8 significant bits): the largest error of
+    rounding an exact value to bf16."""
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.maximum(a, np.finfo(np.float32).tiny)))
+    return np.ldexp(1.0, (e - 8).astype(np.int64))
+
+
+def assert_output_rounded(y_gpu: np.ndarray, y_ref: np.ndarray, tag: str = ""):
+    """|y - y_ref| <= 2e-2 * rms(y_ref) + half a bf16 ulp of y_ref, elementwise."""
+    rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
+    d = np.abs(y_gpu - y_ref)
+    if rms == 0.0:
+        assert float(d.max(initial=0.0)) == 0.0, f"{tag}: reference is exactly 0"
+        return 0.0, 0.0
+    bound = Y_REL_TOL * rms + bf16_half_ulp(y_ref)
+    worst = int(np.argmax(d - bound))
+    assert np.all(d <= bound), (f"{tag}: |err| {d.flat[worst]:.3e} > bound {bound.flat[worst]:.3e} "
+                                f"at y_ref {y_ref.flat[worst]:.3e} (rms {rms:.3e})")
+    return float(d.max()), rms
 
 
 def oracle_all(x_u16, logits, bias, bank, k, tokens=None):

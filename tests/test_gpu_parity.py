@@ -21,6 +21,7 @@ from gpu_harness import (
     DEV,
     assert_buckets,
     assert_output,
+    assert_output_rounded,
     assert_route,
     collect,
     device_weights,
@@ -76,6 +77,40 @@ def test_ragged_token_counts(shape, T, path):
     assert_route(g, idx, w)
     assert_buckets(g, b)
     assert_output(g["y"][: y.shape[0]], y, f"{shape} T={T}")
+
+
+# Shapes whose row tiles run past the matrix: with H = 256 a gate/up tile
+# spans 128 rows of I and a down tile 512-1024 rows of H, so rows past I (or
+# H) must read as zeros and never be stored.  T picks the kernels: 8 tokens
+# the fused down/unroute kernel, 40 the per-expert down tiles (R > 128), 128
+# the MFMA tiles as well (experts with >= 16 routes; 128 weight rows per tile
+# against I = 64).
+RAGGED_TILE_SHAPES = [
+    # (H, I, E, k, T)
+    (256, 64, 16, 4, 8),
+    (256, 64, 16, 4, 40),
+    (256, 64, 16, 4, 128),
+    (128, 32, 8, 2, 70),
+    (32, 32, 4, 2, 10),
+    (32, 64, 6, 3, 50),
+]
+
+
+@pytest.mark.parametrize("shape", RAGGED_TILE_SHAPES, ids=lambda s: "H%d_I%d_E%d_k%d_T%d" % s)
+def test_ragged_row_tiles(shape):
+    from dataclasses import replace
+    from moe_inputs.configs import get_config
+    H, I, E, k, T = shape
+    cfg = replace(get_config("tiny"), name="ragged_tiles", H=H, I=I, E=E, k=k, T=T)
+    wl = make_workload(cfg, x_seed=11 + T)
+    print(f"[ragged tiles] H={H} I={I} E={E} k={k} T={T}", flush=True)
+    g = run_gpu(wl.x, wl.logits, wl.bias, wl.bank, wl.k)
+    idx, w, b, y = oracle_all(wl.x, wl.logits, wl.bias, wl.bank, wl.k)
+    assert_route(g, idx, w)
+    assert_buckets(g, b)
+    # shapes this small have max|y| up to ~5 * rms: the output's own bf16
+    # rounding is part of the bound here
+    assert_output_rounded(g["y"], y, f"ragged tiles {shape}")
 
 
 @pytest.mark.parametrize("path", PATHS)
