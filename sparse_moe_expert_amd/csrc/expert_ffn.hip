@@ -125,16 +125,23 @@ __device__ __forceinline__ void wait_vector_loads() { asm volatile("s_waitcnt vm
 
 // Activation rows staged per group of routes (16 KB of LDS).
 constexpr int kXStageBytes = 16384;
+// 16-byte activation pieces per thread when every token's row is staged up front.
+constexpr int kXLoads = kXStageBytes / 16 / kThreads;
 
 // Gate and up rows of one I tile for all routes of expert e.  Each wave holds
 // kGuUnits gate rows and the same up rows; with 64 lanes per row the four
-// units' sums are scattered so that lane row r ends with unit r.  Issue
-// order: the tile's scale bytes (2 KB gate + 2 KB up, one 16-byte load per
-// thread), the weight rows, then - through the scalar path - the expert's
-// routes, and the activation rows of its first routes straight into LDS.
-// Only then are the scale bytes written to LDS, so that store waits for the
-// scale loads alone, and nothing issued after the weights is needed before
-// they arrive.
+// units' sums are scattered so that lane row r ends with unit r.
+//
+// Issue order.  Small batches (every token's activation row fits the 16 KB
+// stage): all activation rows (into registers: they do not depend on the
+// routing), the tile's scale bytes (2 KB gate + 2 KB up, one 16-byte load
+// per thread), then the weight rows, unit by unit; the expert's route range
+// and first token come through the scalar path while the rows are in
+// flight.  Activations and scales go to LDS as soon as they land, and each
+// unit's products start as soon as its rows arrive, so only the last unit's
+// work is left when the stream ends.  Larger batches: scale bytes, weight
+// rows, then the activation rows of each group of routes straight into LDS
+// once the route range is known; all of them land before any product.
 template <int LG>
 __device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, kGuUnits>& g, uint8_t* s_sc,
                                              uint8_t* s_x, int e, int tile) {
@@ -142,7 +149,20 @@ __device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, k
   const uint32_t code_row = (uint32_t)p.H / 2, scale_row = (uint32_t)p.H / 16;
   const uint32_t mat_codes = (uint32_t)p.I * code_row, mat_scales = (uint32_t)p.I * scale_row;
   const uint32_t blk = (uint32_t)g.rpt * scale_row;            // 2048 bytes
-  const int half = (int)(tid >= kThreads / 2);
+  const int row_bytes = p.H * 2;
+  const int group = max(1, min(kXStageBytes / row_bytes, 64));   // x rows in the LDS stage (<= 16 KB)
+  const uint32_t x_bytes = (uint32_t)p.T * (uint32_t)row_bytes;
+  // small batches: every token's activation row is staged before the weights
+  const bool x_first = p.T <= group;
+  u32x4 xv[kXLoads];
+  if (x_first) {
+    const auto rx = make_rsrc(p.x, x_bytes);
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i)
+      xv[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(tid + i * kThreads) * 16, 0, 0);
+  }
+  compiler_fence();
+  const int half = (int)(g.wave >= kWavesPerBlock / 2);          // wave-uniform: waves 2, 3 load up scales
   const uint32_t sbyte = (uint32_t)(tid & (kThreads / 2 - 1)) * 16;
   const auto rs = make_rsrc((half ? p.su : p.sg) + (size_t)e * mat_scales, mat_scales);
   const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rs, sbyte + (uint32_t)tile * blk, 0, kStreamAux);
@@ -161,64 +181,84 @@ __device__ __forceinline__ void gate_up_tile(const FfnParams& p, const Geo<LG, k
   int off, cnt;
   expert_routes(p, e, off, cnt);
   const float Gg = sload(p.gsc, e * 3 + 0), Gu = sload(p.gsc, e * 3 + 1);
-  const int row_bytes = p.H * 2;
-  const int group = max(1, min(kXStageBytes / row_bytes, 64));
+  auto token_of = [&](int pos) { return min(max(sload(p.route_src, pos) / p.k, 0), p.T - 1); };
+
+  // h[pos, rows of this tile] for one route whose x row sits at s_x + xs*row_bytes.
+  // Each unit's weight rows are touched just before their own products, so
+  // on the first route the compiler waits for unit u's loads only.
+  auto route = [&](int pos, int xs) {
+    const float one = opaque_one();
+    uint32_t xr[16];
+    load_operand_chunk(reinterpret_cast<const uint16_t*>(s_x + (size_t)xs * row_bytes), g.sl, xr);
+    float ag[kGuUnits], au[kGuUnits];
+#pragma unroll
+    for (int u = 0; u < kGuUnits; ++u) {
+      const int rin = (u * kWavesPerBlock + g.wave) * g.rpw + g.sub;   // row within the tile
+      const uint32_t sg = *reinterpret_cast<const uint16_t*>(s_sc + rin * scale_row + g.sl * 2);
+      const uint32_t su = *reinterpret_cast<const uint16_t*>(s_sc + blk + rin * scale_row + g.sl * 2);
+      ag[u] = dot_chunk(cg[u], sg, xr, 0.0f, one);
+      au[u] = dot_chunk(cu[u], su, xr, 0.0f, one);
+    }
+    if constexpr (LG == 64) {
+      static_assert(kGuUnits == 4, "the row scatter maps 4 units to 4 lane rows");
+      const int row = g.row0(tile, lane >> 4);
+      const float gs = rows_scatter4(row16_sum(ag[0]), row16_sum(ag[1]), row16_sum(ag[2]), row16_sum(ag[3])) * Gg;
+      const float us = rows_scatter4(row16_sum(au[0]), row16_sum(au[1]), row16_sum(au[2]), row16_sum(au[3])) * Gu;
+      if ((lane & 15) == 0 && row < p.I) p.h[(size_t)pos * p.I + row] = (uint16_t)f32_to_bf16_rne(silu(gs) * us);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kGuUnits; ++u) {
+        const int row = g.row0(tile, u) + g.sub;
+        const float gs = group_sum(ag[u], g.lr) * Gg;
+        const float us = group_sum(au[u], g.lr) * Gu;
+        if (g.sl == 0 && row < p.I) p.h[(size_t)pos * p.I + row] = (uint16_t)f32_to_bf16_rne(silu(gs) * us);
+      }
+    }
+  };
+
+  if (x_first) {
+    // the first route's token comes through the scalar path while the rows
+    // are in flight; x and the scale bytes go to LDS as soon as they land
+    // (before the weight rows: the loads complete in order), and the waves
+    // meet at a barrier that does not wait for the weight rows
+    const int tok0 = cnt > 0 ? token_of(off) : 0;
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) {
+      const uint32_t q = (uint32_t)(tid + i * kThreads) * 16;
+      if (q < x_bytes) *reinterpret_cast<u32x4*>(s_x + q) = xv[i];
+    }
+    *reinterpret_cast<u32x4*>(s_sc + half * blk + sbyte) = sv;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    // the first route outside any loop: its unit-by-unit waits stay per use
+    // (before a loop the compiler would wait for every load)
+    if (cnt > 0) route(off, tok0);
+#pragma unroll 1
+    for (int i = 1; i < cnt; ++i) route(off + i, token_of(off + i));
+    return;
+  }
+
+  // larger batches: the activation rows of each group of routes go straight
+  // into LDS once the route range is known
   const int pieces = row_bytes / 16;                             // 16-byte pieces of one x row
-  bool scales_stored = false;
   for (int g0 = 0; g0 < cnt; g0 += group) {
     const int ng = min(group, cnt - g0);
     if (g0 > 0) __syncthreads();                                 // previous group's x reads done
-    // x rows of routes g0 .. g0+ng straight into LDS, one 1 KB wave load per step
     for (int i = 0; i < ng; ++i) {
-      const int tok = min(max(sload(p.route_src, off + g0 + i) / p.k, 0), p.T - 1);
-      const uint4* src = reinterpret_cast<const uint4*>(p.x + (size_t)tok * p.H);
-      for (int q0 = g.wave * kWave; q0 < pieces; q0 += kThreads) {
+      const uint4* src = reinterpret_cast<const uint4*>(p.x + (size_t)token_of(off + g0 + i) * p.H);
+      for (int q0 = g.wave * kWave; q0 < pieces; q0 += kThreads)
         if (q0 + lane < pieces)
           __builtin_amdgcn_global_load_lds(src + q0 + lane, s_x + (size_t)i * row_bytes + (size_t)q0 * 16, 16, 0, 0);
-      }
     }
-    if (!scales_stored) {
+    if (g0 == 0) {
       compiler_fence();
       *reinterpret_cast<u32x4*>(s_sc + half * blk + sbyte) = sv;
-      scales_stored = true;
     }
     wait_vector_loads();
     __syncthreads();
-    for (int i = 0; i < ng; ++i) {
-      const int pos = off + g0 + i;
-#pragma unroll
-      for (int u = 0; u < kGuUnits; ++u) {
-        opaque(cg[u]);
-        opaque(cu[u]);
-      }
-      uint32_t xr[16];
-      load_operand_chunk(reinterpret_cast<const uint16_t*>(s_x + (size_t)i * row_bytes), g.sl, xr);
-      float ag[kGuUnits], au[kGuUnits];
-#pragma unroll
-      for (int u = 0; u < kGuUnits; ++u) {
-        const int rin = (u * kWavesPerBlock + g.wave) * g.rpw + g.sub;   // row within the tile
-        const uint32_t sg = *reinterpret_cast<const uint16_t*>(s_sc + rin * scale_row + g.sl * 2);
-        const uint32_t su = *reinterpret_cast<const uint16_t*>(s_sc + blk + rin * scale_row + g.sl * 2);
-        ag[u] = dot_chunk(cg[u], sg, xr, 0.0f);
-        au[u] = dot_chunk(cu[u], su, xr, 0.0f);
-      }
-      if constexpr (LG == 64) {
-        static_assert(kGuUnits == 4, "the row scatter maps 4 units to 4 lane rows");
-        const int row = g.row0(tile, lane >> 4);
-        const float gs = rows_scatter4(row16_sum(ag[0]), row16_sum(ag[1]), row16_sum(ag[2]), row16_sum(ag[3])) * Gg;
-        const float us = rows_scatter4(row16_sum(au[0]), row16_sum(au[1]), row16_sum(au[2]), row16_sum(au[3])) * Gu;
-        if ((lane & 15) == 0 && row < p.I)
-          p.h[(size_t)pos * p.I + row] = (uint16_t)f32_to_bf16_rne(silu(gs) * us);
-      } else {
-#pragma unroll
-        for (int u = 0; u < kGuUnits; ++u) {
-          const int row = g.row0(tile, u) + g.sub;
-          const float gs = group_sum(ag[u], g.lr) * Gg;
-          const float us = group_sum(au[u], g.lr) * Gu;
-          if (g.sl == 0 && row < p.I) p.h[(size_t)pos * p.I + row] = (uint16_t)f32_to_bf16_rne(silu(gs) * us);
-        }
-      }
-    }
+#pragma unroll 1
+    for (int i = 0; i < ng; ++i) route(off + g0 + i, i);
   }
 }
 
@@ -227,13 +267,14 @@ __global__ __launch_bounds__(kThreads, 4) void gate_up_kernel(FfnParams p, int n
   __shared__ __align__(16) uint8_t s_sc[2 * kScaleTileBytes];
   extern __shared__ __align__(16) uint8_t s_x[];                // activation rows of a group of routes
   const Geo<LG, kGuUnits> g(p.lr_gu, p.I);
-  for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
-    const int a = task / g.tiles, tile = task - a * g.tiles;
-    const int e = slot_expert(p, a);
-    if (e < 0 || takes_mfma(p, e)) continue;
-    __syncthreads();                            // LDS of the previous task is free
-    gate_up_tile<LG>(p, g, s_sc, s_x, e, tile);
-  }
+  // one task per workgroup (the host launches exactly n_tasks): no loop
+  // around the tile, so the compiler's load waits stay per use
+  const int task = blockIdx.x;
+  if (task >= n_tasks) return;
+  const int a = task / g.tiles, tile = task - a * g.tiles;
+  const int e = slot_expert(p, a);
+  if (e < 0 || takes_mfma(p, e)) return;
+  gate_up_tile<LG>(p, g, s_sc, s_x, e, tile);
 }
 
 // ------------------------------------------------------------------ down
@@ -274,13 +315,12 @@ __device__ __forceinline__ void down_tile(const FfnParams& p, const Geo<LD, kDUn
   const float Gd = sload(p.gsc, e * 3 + 2);
   for (int t = 0; t < cnt; ++t) {
     const int pos = off + t;
-#pragma unroll
-    for (int u = 0; u < kDUnits; ++u) opaque(cd[u]);
+    const float one = opaque_one();
     uint32_t hr[16];
     load_operand_chunk(p.h + (size_t)pos * p.I, g.sl, hr);
     float ad[kDUnits];
 #pragma unroll
-    for (int u = 0; u < kDUnits; ++u) ad[u] = dot_chunk(cd[u], vd[u], hr, 0.0f);
+    for (int u = 0; u < kDUnits; ++u) ad[u] = dot_chunk(cd[u], vd[u], hr, 0.0f, one);
 #pragma unroll
     for (int u = 0; u < kDUnits; ++u) {
       const int row = g.row0(tile, u) + g.sub;
@@ -295,13 +335,12 @@ template <int LD>
 __global__ __launch_bounds__(kThreads, 4) void down_kernel(FfnParams p, int n_tasks) {
   __shared__ __align__(16) uint8_t s_sc[2 * kScaleTileBytes];
   const Geo<LD, kDUnits> g(p.lr_d, p.H);
-  for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
-    const int a = task / g.tiles, tile = task - a * g.tiles;
-    const int e = slot_expert(p, a);
-    if (e < 0 || takes_mfma(p, e)) continue;
-    __syncthreads();                            // LDS of the previous task is free
-    down_tile<LD>(p, g, s_sc, e, tile);
-  }
+  const int task = blockIdx.x;                  // one task per workgroup
+  if (task >= n_tasks) return;
+  const int a = task / g.tiles, tile = task - a * g.tiles;
+  const int e = slot_expert(p, a);
+  if (e < 0 || takes_mfma(p, e)) return;
+  down_tile<LD>(p, g, s_sc, e, tile);
 }
 
 // ------------------------------------------------------------------ MFMA tiles (experts with many routes)
@@ -724,10 +763,10 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
     if (e_u[u] < 0) continue;
     for (int t = 0; t < cnt_u[u]; ++t) {
       const int pos = off_u[u] + t;
-      opaque(cd[u]);
+      const float one = opaque_one();
       uint32_t hr[16];
       load_operand_chunk(s_h + (size_t)pos * p.I, sl, hr);
-      const float acc = dot_chunk(cd[u], vd[u], hr, 0.0f);
+      const float acc = dot_chunk(cd[u], vd[u], hr, 0.0f, one);
       const float v = (LD == 16 ? row16_sum(acc) : group_sum(acc, ld)) * gd_u[u];
       if (sl == 0 && row_ok) s_o[pos * rpw + sub] = v;
     }
@@ -771,13 +810,13 @@ WorkspaceLayout workspace_layout(int T, int H, int I, int k) {
   return L;
 }
 
-constexpr long long kMaxGrid = 1 << 20;
+constexpr long long kMaxGrid = 1 << 20;   // one workgroup per task; the shape limits keep tasks below this
 constexpr int kMfmaMinTokens = 64;      // batches from this size launch the MFMA kernels
 constexpr int kMfmaMinRoutes = 16;      // experts with this many routes use them
 
 template <int LG>
 void launch_gate_up(const FfnParams& p, long long tasks, hipStream_t s) {
-  const unsigned grid = (unsigned)std::max<long long>(1, std::min<long long>(tasks, kMaxGrid));
+  const unsigned grid = (unsigned)std::max<long long>(1, tasks);
   const int row_bytes = p.H * 2;
   const size_t x_lds = (size_t)std::max(1, std::min(kXStageBytes / row_bytes, 64)) * row_bytes;
   gate_up_kernel<LG><<<grid, kThreads, x_lds, s>>>(p, (int)tasks);
@@ -785,7 +824,7 @@ void launch_gate_up(const FfnParams& p, long long tasks, hipStream_t s) {
 
 template <int LD>
 void launch_down(const FfnParams& p, long long tasks, hipStream_t s) {
-  const unsigned grid = (unsigned)std::max<long long>(1, std::min<long long>(tasks, kMaxGrid));
+  const unsigned grid = (unsigned)std::max<long long>(1, tasks);
   down_kernel<LD><<<grid, kThreads, 0, s>>>(p, (int)tasks);
 }
 
@@ -855,6 +894,7 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
   const int rpt_d = kWavesPerBlock * (kWave / lr_d) * kDUnits;
   const long long tasks_gu = slots * ((I + rpt_gu - 1) / rpt_gu);
   const long long tasks_d = slots * ((H + rpt_d - 1) / rpt_d);
+  if (tasks_gu > kMaxGrid || tasks_d > kMaxGrid) return MOE_ERR_UNSUPPORTED;
 
   const long long slots8 = (slots + kXcds - 1) / kXcds * kXcds;   // slot count padded for the XCD numbering
   if (stage & 1) {

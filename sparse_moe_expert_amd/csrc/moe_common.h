@@ -32,8 +32,8 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) {
 // in one instruction.  Scale 1.0: the conversion is exact (e2m1 values have
 // at most 2 significant bits).
 template <int B>
-__device__ __forceinline__ bf16x2 fp4x2_to_bf16x2(uint32_t word) {
-  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, B);
+__device__ __forceinline__ bf16x2 fp4x2_to_bf16x2(uint32_t word, float one = 1.0f) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, one, B);
 }
 
 // FP8 E4M3FN scale byte -> fp32 value * 2^-8, exactly.  Shifting the 7

@@ -35,32 +35,41 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 __device__ __forceinline__ uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
-// Makes a register's value opaque to the optimiser (no instruction).  Used at
-// the top of per-route loops so the weight conversions are not hoisted out of
-// the loop, which would keep every converted value live at once.
-__device__ __forceinline__ void opaque(uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
+// 1.0f in a scalar register whose value the optimiser cannot see (no
+// instruction).  Per-route loops pass it as the scale operand of the weight
+// conversions, so those are not hoisted out of the loop (which would keep
+// every converted value live at once), while the weight registers
+// themselves stay untouched: an asm that rewrote them would make the
+// register allocator copy them, and each copy waits for its load.
+__device__ __forceinline__ float opaque_one() {
+  float v = 1.0f;
+  asm volatile("" : "+s"(v));
+  return v;
+}
 
 // One 16-byte chunk (32 NVFP4 values, two scale blocks) dotted with an
 // operand chunk xr (operand elements 2i, 2i+1 as bf16x2 in xr[i]); adds
-// sum_block(scale * sum(code * operand)) to acc.
-__device__ __forceinline__ float dot_chunk(const uint4 codes, uint32_t s2, const uint32_t (&xr)[16], float acc) {
+// sum_block(scale * sum(code * operand)) to acc.  `one` is 1.0f (see
+// opaque_one).
+__device__ __forceinline__ float dot_chunk(const uint4 codes, uint32_t s2, const uint32_t (&xr)[16], float acc,
+                                           float one) {
   const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 0);
   const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 1);
   const uint32_t c[4] = {codes.x, codes.y, codes.z, codes.w};
   float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<0>(c[q]), as_bf16x2(xr[4 * q + 0]), p0, false);
-    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<1>(c[q]), as_bf16x2(xr[4 * q + 1]), p0, false);
-    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<2>(c[q]), as_bf16x2(xr[4 * q + 2]), p0, false);
-    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<3>(c[q]), as_bf16x2(xr[4 * q + 3]), p0, false);
+    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<0>(c[q], one), as_bf16x2(xr[4 * q + 0]), p0, false);
+    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<1>(c[q], one), as_bf16x2(xr[4 * q + 1]), p0, false);
+    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<2>(c[q], one), as_bf16x2(xr[4 * q + 2]), p0, false);
+    p0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<3>(c[q], one), as_bf16x2(xr[4 * q + 3]), p0, false);
   }
 #pragma unroll
   for (int q = 2; q < 4; ++q) {
-    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<0>(c[q]), as_bf16x2(xr[4 * q + 0]), p1, false);
-    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<1>(c[q]), as_bf16x2(xr[4 * q + 1]), p1, false);
-    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<2>(c[q]), as_bf16x2(xr[4 * q + 2]), p1, false);
-    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<3>(c[q]), as_bf16x2(xr[4 * q + 3]), p1, false);
+    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<0>(c[q], one), as_bf16x2(xr[4 * q + 0]), p1, false);
+    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<1>(c[q], one), as_bf16x2(xr[4 * q + 1]), p1, false);
+    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<2>(c[q], one), as_bf16x2(xr[4 * q + 2]), p1, false);
+    p1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<3>(c[q], one), as_bf16x2(xr[4 * q + 3]), p1, false);
   }
   acc = fmaf(p0, s0, acc);
   return fmaf(p1, s1, acc);
