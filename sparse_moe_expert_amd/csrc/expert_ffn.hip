@@ -667,8 +667,8 @@ constexpr int kDcHLoads = kDcMaxLds / 16 / kDcThreads;   // 16-byte h pieces per
 // LDS, and each token's routes are finally summed in slot order.  No o round
 // trip through memory and no cross-workgroup ordering.
 //
-// Issue order: all routes' h rows (kDcHLoads 16-byte pieces per thread into
-// registers), the routes' positions and weights, the slots' expert ids
+// Issue order: all routes' h rows (up to kDcHLoads 16-byte pieces per thread
+// into registers), the routes' positions and weights, the slots' expert ids
 // (scalar path), then every slot's weight row, and then route ranges and
 // global scales through the scalar path.  Every vector load is issued
 // unconditionally - a piece or slot past the end reads out of range, which
@@ -698,8 +698,13 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
   const auto rh = make_rsrc(p.h, h_bytes);
   u32x4 hv[kDcHLoads];
 #pragma unroll
-  for (int i = 0; i < kDcHLoads; ++i)
-    hv[i] = __builtin_amdgcn_raw_buffer_load_b128(rh, (uint32_t)(tid + i * kDcThreads) * 16, 0, 0);
+  for (int i = 0; i < kDcHLoads; ++i) {
+    // a wave whose pieces all lie past h issues no load (address work is
+    // not free); a partly covered wave reads zeros past the end
+    hv[i] = u32x4{0u, 0u, 0u, 0u};
+    if ((uint32_t)(wave * kWave + i * kDcThreads) * 16 < h_bytes)
+      hv[i] = __builtin_amdgcn_raw_buffer_load_b128(rh, (uint32_t)(tid + i * kDcThreads) * 16, 0, 0);
+  }
   // route positions and gate weights (an index past R re-reads the last)
   const int rt = min(tid, R - 1);
   const int pos_r = p.route_pos[rt];
