@@ -75,4 +75,12 @@ inline int lanes_per_row(int chunks) {
   return l;
 }
 
+// Routing and bucketing as in moe_route_bucket; `scratch` (may be NULL) is
+// device memory the call may use until it returns (large batches bucket in
+// parallel with it; moe_step lends the FFN workspace, unused at that point).
+moe_status route_bucket(const float* logits, const float* bias, int T, int E, int k, int32_t* topk_idx,
+                        float* topk_w, int32_t* expert_count, int32_t* expert_offset, int32_t* active_experts,
+                        int32_t* n_active, int32_t* route_src, int32_t* route_pos, int32_t* scratch,
+                        size_t scratch_bytes, hipStream_t s);
+
 }  // namespace moe

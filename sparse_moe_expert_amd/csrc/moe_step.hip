@@ -48,8 +48,11 @@ extern "C" moe_status moe_step(const uint16_t* x, const float* logits, const flo
     if (!moe::aligned16(q)) return MOE_ERR_MISALIGNED;
   if (bias && !moe::aligned16(bias)) return MOE_ERR_MISALIGNED;
   if (workspace_bytes < moe_step_workspace_size(T, H, I, E, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  const moe_status st = moe_route_bucket(logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset,
-                                         active_experts, n_active, route_src, route_pos, stream);
+  // the FFN workspace is free until the expert kernels run: routing may use it
+  const moe_status st = moe::route_bucket(logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset,
+                                          active_experts, n_active, route_src, route_pos,
+                                          static_cast<int32_t*>(workspace), workspace_bytes,
+                                          static_cast<hipStream_t>(stream));
   if (st != MOE_OK) return st;
   return moe_expert_ffn(x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
                         expert_offset, active_experts, n_active, route_src, route_pos, T, H, I, E, k, workspace,

@@ -149,6 +149,94 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_routes_kernel(
                route_pos);
 }
 
+// Bucketing of large batches in parallel (three kernels over chunks of
+// kBucketThreads routes), with a caller-provided scratch array counts[C][E]:
+//   bucket_count_kernel    chunk c: per-expert route counts of the chunk
+//   bucket_scan_kernel     one workgroup: for every expert the exclusive
+//                          prefix of its counts over the chunks (in place),
+//                          its total, offset and active position
+//   bucket_scatter_kernel  chunk c: position = expert offset + prefix of
+//                          earlier chunks + rank inside the chunk (ballots)
+// The positions are the same as the one-workgroup bucketing's: a route's
+// rank among the routes of its expert in route order.
+constexpr int kChunkMinChunks = 8;             // batches of more chunks than this take the parallel path
+
+__global__ __launch_bounds__(kBucketThreads) void bucket_count_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                                      int32_t* __restrict__ counts) {
+  __shared__ int s_cnt[1024];
+  const int tid = threadIdx.x, c = blockIdx.x;
+  s_cnt[tid] = 0;
+  __syncthreads();
+  const int r = c * kBucketThreads + tid;
+  if (r < R) atomicAdd(&s_cnt[min(max(ids[r], 0), E - 1)], 1);    // integer counts: order-free
+  __syncthreads();
+  if (tid < E) counts[(size_t)c * E + tid] = s_cnt[tid];
+}
+
+__global__ __launch_bounds__(kBucketThreads) void bucket_scan_kernel(
+    int32_t* __restrict__ counts, int C, int E, int32_t* __restrict__ expert_count,
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active) {
+  __shared__ int s_wave[kBucketWaves + 1];
+  const int tid = threadIdx.x;
+  int run = 0;
+  if (tid < E) {
+    constexpr int kB = 8;                      // chunk counts fetched together
+    for (int c0 = 0; c0 < C; c0 += kB) {
+      int v[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) v[j] = c0 + j < C ? counts[(size_t)(c0 + j) * E + tid] : 0;
+#pragma unroll
+      for (int j = 0; j < kB; ++j)
+        if (c0 + j < C) {
+          counts[(size_t)(c0 + j) * E + tid] = run;
+          run += v[j];
+        }
+    }
+  }
+  int total_routes, total_active;
+  const int off = block_exclusive_scan(run, s_wave, &total_routes);
+  const int apos = block_exclusive_scan(run > 0 ? 1 : 0, s_wave, &total_active);
+  if (tid < E) {
+    expert_count[tid] = run;
+    expert_offset[tid] = off;
+    if (run > 0) active_experts[apos] = tid;
+    if (tid >= total_active) active_experts[tid] = -1;
+  }
+  if (tid == 0) {
+    expert_offset[E] = total_routes;
+    *n_active = total_active;
+  }
+}
+
+__global__ __launch_bounds__(kBucketThreads) void bucket_scatter_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int id_bits, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ expert_offset, int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos) {
+  __shared__ int s_base[1024];
+  __shared__ uint8_t s_wcnt[kBucketWaves][1024];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6, c = blockIdx.x;
+  if (tid < E) s_base[tid] = expert_offset[tid] + counts[(size_t)c * E + tid];
+  for (int i = tid; i < kBucketWaves * 1024 / 4; i += kBucketThreads) reinterpret_cast<int*>(&s_wcnt[0][0])[i] = 0;
+  const int r = c * kBucketThreads + tid;
+  const bool valid = r < R;
+  const int e = valid ? min(max(ids[r], 0), E - 1) : 0;
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < id_bits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    same &= bit ? bal : ~bal;
+  }
+  int rank = __popcll(same & ((1ull << lane) - 1ull));
+  __syncthreads();                             // s_wcnt cleared, s_base set
+  if (valid && rank == 0) s_wcnt[wave][e] = (uint8_t)__popcll(same);
+  __syncthreads();
+  if (valid) {
+    for (int w = 0; w < wave; ++w) rank += s_wcnt[w][e];
+    const int pos = s_base[e] + rank;
+    route_src[pos] = r;
+    route_pos[r] = pos;
+  }
+}
+
 // Route and bucket a small batch in one workgroup: wavefront w selects for
 // tokens w, w+16, ...; the ids stay in LDS for the bucketing.
 template <int V>
@@ -322,17 +410,16 @@ extern "C" moe_status moe_bucket_routes(const int32_t* topk_idx, int T, int E, i
   return launch_status();
 }
 
-extern "C" moe_status moe_route_bucket(const float* logits, const float* bias, int T, int E, int k,
-                                       int32_t* topk_idx, float* topk_w,
-                                       int32_t* expert_count, int32_t* expert_offset,
-                                       int32_t* active_experts, int32_t* n_active,
-                                       int32_t* route_src, int32_t* route_pos, void* stream) {
-  using namespace moe;
+namespace moe {
+
+moe_status route_bucket(const float* logits, const float* bias, int T, int E, int k, int32_t* topk_idx,
+                        float* topk_w, int32_t* expert_count, int32_t* expert_offset, int32_t* active_experts,
+                        int32_t* n_active, int32_t* route_src, int32_t* route_pos, int32_t* scratch,
+                        size_t scratch_bytes, hipStream_t s) {
   moe_status st = check_route_args(logits, bias, T, E, k, topk_idx, topk_w);
   if (st != MOE_OK) return st;
   st = check_bucket_args(T, E, k, expert_count, expert_offset, active_experts, n_active, route_src, route_pos);
   if (st != MOE_OK || T == 0) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   const int bits = id_bits_for(E);
   const int V = (E + kWave - 1) / kWave;
   if (T <= kSmallMaxTokens && T * k <= kSmallMaxRoutes) {
@@ -363,7 +450,30 @@ extern "C" moe_status moe_route_bucket(const float* logits, const float* bias, i
   }
   launch_route(logits, bias, T, E, k, topk_idx, topk_w, s);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
-  bucket_routes_kernel<<<1, kBucketThreads, 0, s>>>(topk_idx, T * k, E, bits, expert_count, expert_offset,
+  const long long R = (long long)T * k;
+  const long long C = (R + kBucketThreads - 1) / kBucketThreads;
+  if (scratch && C > kChunkMinChunks && (size_t)C * E * sizeof(int32_t) <= scratch_bytes) {
+    bucket_count_kernel<<<(unsigned)C, kBucketThreads, 0, s>>>(topk_idx, (int)R, E, scratch);
+    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+    bucket_scan_kernel<<<1, kBucketThreads, 0, s>>>(scratch, (int)C, E, expert_count, expert_offset, active_experts,
+                                                    n_active);
+    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+    bucket_scatter_kernel<<<(unsigned)C, kBucketThreads, 0, s>>>(topk_idx, (int)R, E, bits, scratch, expert_offset,
+                                                                 route_src, route_pos);
+    return launch_status();
+  }
+  bucket_routes_kernel<<<1, kBucketThreads, 0, s>>>(topk_idx, (int)R, E, bits, expert_count, expert_offset,
                                                      active_experts, n_active, route_src, route_pos);
   return launch_status();
+}
+
+}  // namespace moe
+
+extern "C" moe_status moe_route_bucket(const float* logits, const float* bias, int T, int E, int k,
+                                       int32_t* topk_idx, float* topk_w,
+                                       int32_t* expert_count, int32_t* expert_offset,
+                                       int32_t* active_experts, int32_t* n_active,
+                                       int32_t* route_src, int32_t* route_pos, void* stream) {
+  return moe::route_bucket(logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset, active_experts,
+                           n_active, route_src, route_pos, nullptr, 0, static_cast<hipStream_t>(stream));
 }
