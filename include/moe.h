@@ -239,6 +239,62 @@ moe_status moe_step(const uint16_t* x, const float* logits, const float* bias,
                     uint16_t* y,
                     void* stream);
 
+/*
+ * Bytes of the packed copy of all expert weights that moe_pack_weights
+ * writes for these sizes (0 when H or I is not a multiple of 64, or a size
+ * is not positive).
+ */
+size_t moe_packed_weights_size(int E, int H, int I);
+
+/*
+ * moe_pack_weights — the expert weights rearranged into the order in which
+ * the MFMA tiles of moe_step_packed read them (quantised bits rearranged
+ * offline to match the consumer's register fragments, as FLUTE does: page
+ * "Persistent execution for Flash-Next GGUF on SM70", section "Primary
+ * sources and transferable mechanisms", paragraph "FLUTE").  A pure byte
+ * permutation with zero padding: every code and scale byte is copied
+ * unchanged.  Done once when the weights are loaded; the packed copy is
+ * read instead of the standard layout by the MFMA tiles (experts with many
+ * routes), which then load one contiguous kilobyte per wavefront.
+ *   w_*, s_*   in   standard layout, as for moe_expert_ffn
+ *   packed     out  device buffer of moe_packed_weights_size(E,H,I) bytes,
+ *                   owned by the caller.  Layout per matrix and expert (N
+ *                   rows, reduction K; gate and up: N = I, K = H; down:
+ *                   N = H, K = I): 128-row tiles t, 64-wide reduction steps
+ *                   s, four 32-row groups w, 64 lanes l (row 128t + 32w +
+ *                   l%32, half h = l/32): 16 code bytes 32s+16h.. of the row
+ *                   at index ((t*S + s)*4 + w)*64 + l, then all scales (2
+ *                   bytes 4s+2h.. at the same index); rows past N are zero;
+ *                   each expert's matrix padded to 256 bytes; gate of all
+ *                   experts, then up, then down.
+ * Shapes: H and I multiples of 64 (else MOE_ERR_INVALID_SHAPE); envelope
+ * as for moe_expert_ffn.
+ */
+moe_status moe_pack_weights(const uint8_t* w_gate, const uint8_t* s_gate,
+                            const uint8_t* w_up, const uint8_t* s_up,
+                            const uint8_t* w_down, const uint8_t* s_down,
+                            int E, int H, int I, uint8_t* packed, void* stream);
+
+/*
+ * moe_step_packed — moe_step with the packed copy of the same weights
+ * (from moe_pack_weights; must not be NULL).  Results are identical to
+ * moe_step's; only the MFMA tiles' weight loads change.  H and I must be
+ * multiples of 64.
+ */
+moe_status moe_step_packed(const uint16_t* x, const float* logits, const float* bias,
+                           const uint8_t* w_gate, const uint8_t* s_gate,
+                           const uint8_t* w_up, const uint8_t* s_up,
+                           const uint8_t* w_down, const uint8_t* s_down,
+                           const float* g_scale, const uint8_t* packed,
+                           int T, int H, int I, int E, int k,
+                           int32_t* topk_idx, float* topk_w,
+                           int32_t* expert_count, int32_t* expert_offset,
+                           int32_t* active_experts, int32_t* n_active,
+                           int32_t* route_src, int32_t* route_pos,
+                           void* workspace, size_t workspace_bytes,
+                           uint16_t* y,
+                           void* stream);
+
 /* Static English description of a status code (never NULL). */
 const char* moe_status_string(moe_status s);
 

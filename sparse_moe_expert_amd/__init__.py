@@ -21,8 +21,10 @@ from ._lib import (
     moe_route_bucket,
     moe_route_topk,
     moe_status_string,
+    moe_packed_weights_size,
     moe_step,
     moe_step_workspace_size,
+    pack_weights,
 )
 from .step import MoeStep, expert_weights_from_numpy
 
@@ -41,8 +43,10 @@ __all__ = [
     "moe_route_bucket",
     "moe_route_topk",
     "moe_status_string",
+    "moe_packed_weights_size",
     "moe_step",
     "moe_step_workspace_size",
+    "pack_weights",
     "MoeStep",
     "expert_weights_from_numpy",
 ]

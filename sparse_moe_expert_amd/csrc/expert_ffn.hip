@@ -77,6 +77,7 @@ struct FfnParams {
   int lr_gu;     // lanes per gate/up row (power of two, <= 64)
   int lr_d;      // lanes per down row
   int mfma_min;  // experts with at least this many routes take the MFMA kernels (0: none do)
+  const uint8_t* packed;   // the weights also in MFMA tile order (moe_pack_weights), or null
 };
 
 constexpr int kGuUnits = 4;          // gate rows (and as many up rows) per wave per tile
@@ -382,6 +383,7 @@ constexpr int kMmK = 64;                     // reduction per step
 constexpr int kMmStages = 4;                 // operand-ring stages: three steps in flight
 constexpr int kMmStageBytes = kMmRoutes * kMmK * 2;   // 16 KB of operand rows per step
 constexpr int kXcds = 8;
+static_assert(kMmRows == kPackRows && kMmK == kPackK, "packed weights follow the MFMA tile");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -431,13 +433,14 @@ __device__ __forceinline__ void step_barrier() {
   compiler_fence();
 }
 
-template <bool GU>
+template <bool GU, bool PACKED>
 struct MmTile {
   static constexpr int NMAT = GU ? 2 : 1;
   static constexpr int kLoadsPerStep = 4 + 2 * NMAT;   // per thread: 4 operand chunks, codes + scales per matrix
   uint8_t* s_x[kMmStages];                             // one LDS array per stage
   __amdgpu_buffer_rsrc_t rc[NMAT], rs[NMAT], rb;
   uint32_t w_voff, s_voff;                             // this lane's weight row slice
+  uint32_t tile_step0;                                 // packed: tile index * steps
   uint32_t x_goff[4];                                  // operand chunk sources, per step add ks*128
   int wave, lane;
   uint4 wc[kMmStages][NMAT];
@@ -447,10 +450,17 @@ struct MmTile {
   __device__ __forceinline__ void issue(int ks) {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
-      // default cache policy: each load uses 32 of a row's 128 cached bytes,
-      // the next three K steps use the rest
-      wc[T][m] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rc[m], w_voff, (uint32_t)ks * (kMmK / 2), 0));
-      wsv[T][m] = __builtin_amdgcn_raw_buffer_load_b16(rs[m], s_voff, (uint32_t)ks * (kMmK / 16), 0);
+      if constexpr (PACKED) {
+        // one contiguous kilobyte of codes (and 128 bytes of scales) per wave, read once
+        const uint32_t slot = tile_step0 + (uint32_t)ks;
+        wc[T][m] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rc[m], w_voff, slot * 4096u, kStreamAux));
+        wsv[T][m] = __builtin_amdgcn_raw_buffer_load_b16(rs[m], s_voff, slot * 512u, kStreamAux);
+      } else {
+        // default cache policy: each load uses 32 of a row's 128 cached bytes,
+        // the next three K steps use the rest
+        wc[T][m] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rc[m], w_voff, (uint32_t)ks * (kMmK / 2), 0));
+        wsv[T][m] = __builtin_amdgcn_raw_buffer_load_b16(rs[m], s_voff, (uint32_t)ks * (kMmK / 16), 0);
+      }
     }
     uint8_t* stage = s_x[T];
 #pragma unroll
@@ -460,9 +470,9 @@ struct MmTile {
   }
 };
 
-template <bool GU>
+template <bool GU, bool PACKED>
 __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
-  using Tile = MmTile<GU>;
+  using Tile = MmTile<GU, PACKED>;
   constexpr int NMAT = Tile::NMAT;
   constexpr int LPS = Tile::kLoadsPerStep;
   // separate arrays per stage, so that reads of one stage are seen not to
@@ -497,19 +507,39 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
   t.lane = lane;
   const uint32_t code_row = (uint32_t)K / 2, scale_row = (uint32_t)K / 16;
   const uint32_t mat_codes = (uint32_t)N * code_row, mat_scales = (uint32_t)N * scale_row;
-  const uint8_t* wbase[2] = {GU ? p.wg : p.wd, p.wu};
-  const uint8_t* sbase[2] = {GU ? p.sg : p.sd, p.su};
+  if constexpr (PACKED) {
+    // packed matrices: gate and up of every expert, then down (tile order)
+    const size_t gu_mat = packed_matrix_bytes(p.I, p.H);
+    const size_t mat = packed_matrix_bytes(N, K), codes = packed_code_bytes(N, K);
+    const uint8_t* base[2] = {p.packed + (GU ? 0 : 2 * (size_t)p.E * gu_mat), p.packed + (size_t)p.E * gu_mat};
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m) {
-    t.rc[m] = make_rsrc(wbase[m] + (size_t)e * mat_codes, mat_codes);
-    t.rs[m] = make_rsrc(sbase[m] + (size_t)e * mat_scales, mat_scales);
+    for (int m = 0; m < NMAT; ++m) {
+      const uint8_t* me = base[m] + (size_t)e * mat;
+      t.rc[m] = make_rsrc(me, (uint32_t)codes);
+      t.rs[m] = make_rsrc(me + codes, (uint32_t)(mat - codes));
+    }
+  } else {
+    const uint8_t* wbase[2] = {GU ? p.wg : p.wd, p.wu};
+    const uint8_t* sbase[2] = {GU ? p.sg : p.sd, p.su};
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      t.rc[m] = make_rsrc(wbase[m] + (size_t)e * mat_codes, mat_codes);
+      t.rs[m] = make_rsrc(sbase[m] + (size_t)e * mat_scales, mat_scales);
+    }
   }
   const int R = p.T * p.k;
   t.rb = GU ? make_rsrc(p.x, (uint32_t)p.T * (uint32_t)p.H * 2u) : make_rsrc(p.h, (uint32_t)R * (uint32_t)p.I * 2u);
-  const int wrow = n0 + wave * 32 + l32;                     // this lane's weight row
-  t.w_voff = (uint32_t)wrow * code_row + (uint32_t)half * 16;
-  t.s_voff = (uint32_t)wrow * scale_row + (uint32_t)half * 2;
   const int steps = K / kMmK;
+  if constexpr (PACKED) {
+    t.w_voff = (uint32_t)(wave * 64 + lane) * 16;
+    t.s_voff = (uint32_t)(wave * 64 + lane) * 2;
+    t.tile_step0 = (uint32_t)(n0 / kMmRows) * (uint32_t)steps;
+  } else {
+    const int wrow = n0 + wave * 32 + l32;                   // this lane's weight row
+    t.w_voff = (uint32_t)wrow * code_row + (uint32_t)half * 16;
+    t.s_voff = (uint32_t)wrow * scale_row + (uint32_t)half * 2;
+    t.tile_step0 = 0;
+  }
 
   for (int m0 = 0; m0 < cnt; m0 += kMmRoutes) {
     const int mc = min(kMmRoutes, cnt - m0);
@@ -842,15 +872,14 @@ extern "C" size_t moe_expert_ffn_workspace_size(int T, int H, int I, int E, int 
   return moe::workspace_layout(T, H, I, k).total;
 }
 
-extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const uint8_t* w_gate, const uint8_t* s_gate,
-                                     const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,
-                                     const uint8_t* s_down, const float* g_scale, const float* topk_w,
-                                     const int32_t* expert_count, const int32_t* expert_offset,
-                                     const int32_t* active_experts, const int32_t* n_active,
-                                     const int32_t* route_src, const int32_t* route_pos, int T, int H,
-                                     int I, int E, int k, void* workspace, size_t workspace_bytes,
-                                     uint16_t* y, void* stream) {
-  using namespace moe;
+namespace moe {
+
+moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const uint8_t* s_gate,
+                      const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                      const float* g_scale, const float* topk_w, const int32_t* expert_count,
+                      const int32_t* expert_offset, const int32_t* active_experts, const int32_t* n_active,
+                      const int32_t* route_src, const int32_t* route_pos, const uint8_t* packed, int T, int H,
+                      int I, int E, int k, void* workspace, size_t workspace_bytes, uint16_t* y, hipStream_t s) {
   if (stage < 1 || stage > 3) return MOE_ERR_INVALID_SHAPE;
   if (T < 0 || k < 1 || E < 1 || k > E || H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
     return MOE_ERR_INVALID_SHAPE;
@@ -866,6 +895,7 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
     if (!q) return MOE_ERR_NULL_POINTER;
   for (const void* q : ptrs)
     if (!aligned16(q)) return MOE_ERR_MISALIGNED;
+  if (packed && !aligned16(packed)) return MOE_ERR_MISALIGNED;
   const WorkspaceLayout L = workspace_layout(T, H, I, k);
   if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
 
@@ -880,6 +910,7 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
   p.y = y;
   p.lr_gu = lr_gu;
   p.lr_d = lr_d;
+  p.packed = packed;
   const long long R = (long long)T * k;
   const size_t h_bytes = (size_t)R * I * 2;
   // one buffer resource spans all of W_down: its byte count must fit 31 bits
@@ -893,7 +924,6 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
   const bool mfma = !down_combine && T >= kMfmaMinTokens && H % kMmK == 0 && I % kMmK == 0;
   p.mfma_min = mfma ? kMfmaMinRoutes : 0;
 
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   const long long slots = std::min<long long>(E, (long long)T * k);
   const int rpt_gu = kWavesPerBlock * (kWave / lr_gu) * kGuUnits;
   const int rpt_d = kWavesPerBlock * (kWave / lr_d) * kDUnits;
@@ -908,7 +938,8 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
     if (mfma) {
       const unsigned grid = (unsigned)(slots8 * ((I + kMmRows - 1) / kMmRows));
-      ffn_mfma_kernel<true><<<grid, kMmThreads, 0, s>>>(p);
+      if (p.packed) ffn_mfma_kernel<true, true><<<grid, kMmThreads, 0, s>>>(p);
+      else ffn_mfma_kernel<true, false><<<grid, kMmThreads, 0, s>>>(p);
       if (launch_status() != MOE_OK) return MOE_ERR_HIP;
     }
   }
@@ -926,12 +957,28 @@ extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const u
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   if (mfma) {
     const unsigned grid = (unsigned)(slots8 * ((H + kMmRows - 1) / kMmRows));
-    ffn_mfma_kernel<false><<<grid, kMmThreads, 0, s>>>(p);
+    if (p.packed) ffn_mfma_kernel<false, true><<<grid, kMmThreads, 0, s>>>(p);
+    else ffn_mfma_kernel<false, false><<<grid, kMmThreads, 0, s>>>(p);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
   const long long cblocks = (long long)T * ((H + kCombineCols - 1) / kCombineCols);
   combine_kernel<<<(unsigned)cblocks, kThreads, 0, s>>>(p);
   return launch_status();
+}
+
+}  // namespace moe
+
+extern "C" moe_status moe_expert_ffn_stage(int stage, const uint16_t* x, const uint8_t* w_gate, const uint8_t* s_gate,
+                                           const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,
+                                           const uint8_t* s_down, const float* g_scale, const float* topk_w,
+                                           const int32_t* expert_count, const int32_t* expert_offset,
+                                           const int32_t* active_experts, const int32_t* n_active,
+                                           const int32_t* route_src, const int32_t* route_pos, int T, int H,
+                                           int I, int E, int k, void* workspace, size_t workspace_bytes,
+                                           uint16_t* y, void* stream) {
+  return moe::expert_ffn(stage, x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
+                         expert_offset, active_experts, n_active, route_src, route_pos, nullptr, T, H, I, E, k,
+                         workspace, workspace_bytes, y, static_cast<hipStream_t>(stream));
 }
 
 extern "C" moe_status moe_expert_ffn(const uint16_t* x, const uint8_t* w_gate, const uint8_t* s_gate,

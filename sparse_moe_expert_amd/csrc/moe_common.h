@@ -75,6 +75,28 @@ inline int lanes_per_row(int chunks) {
   return l;
 }
 
+// Packed (MFMA tile order) weights: tiles of kPackRows rows, steps of kPackK
+// along the reduction; per expert matrix the codes, then the scales, padded
+// to 256 bytes.
+constexpr int kPackRows = 128;
+constexpr int kPackK = 64;
+__host__ __device__ inline size_t packed_code_bytes(int N, int K) {
+  return (size_t)((N + kPackRows - 1) / kPackRows) * kPackRows * (size_t)(K / 2);
+}
+__host__ __device__ inline size_t packed_matrix_bytes(int N, int K) {
+  const size_t scales = (size_t)((N + kPackRows - 1) / kPackRows) * kPackRows * (size_t)(K / 16);
+  return (packed_code_bytes(N, K) + scales + 255) & ~(size_t)255;
+}
+
+// The expert FFN as in moe_expert_ffn_stage, with the packed weights (NULL:
+// none; the MFMA tiles then read the standard layout).
+moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const uint8_t* s_gate,
+                      const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                      const float* g_scale, const float* topk_w, const int32_t* expert_count,
+                      const int32_t* expert_offset, const int32_t* active_experts, const int32_t* n_active,
+                      const int32_t* route_src, const int32_t* route_pos, const uint8_t* packed, int T, int H,
+                      int I, int E, int k, void* workspace, size_t workspace_bytes, uint16_t* y, hipStream_t s);
+
 // Routing and bucketing as in moe_route_bucket; `scratch` (may be NULL) is
 // device memory the call may use until it returns (large batches bucket in
 // parallel with it; moe_step lends the FFN workspace, unused at that point).

@@ -23,14 +23,13 @@ extern "C" size_t moe_step_workspace_size(int T, int H, int I, int E, int k) {
   return moe_expert_ffn_workspace_size(T, H, I, E, k);
 }
 
-extern "C" moe_status moe_step(const uint16_t* x, const float* logits, const float* bias,
-                               const uint8_t* w_gate, const uint8_t* s_gate, const uint8_t* w_up,
-                               const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
-                               const float* g_scale, int T, int H, int I, int E, int k,
-                               int32_t* topk_idx, float* topk_w, int32_t* expert_count,
-                               int32_t* expert_offset, int32_t* active_experts, int32_t* n_active,
-                               int32_t* route_src, int32_t* route_pos, void* workspace,
-                               size_t workspace_bytes, uint16_t* y, void* stream) {
+// The step with optional packed weights (NULL: none).
+static moe_status step(const uint16_t* x, const float* logits, const float* bias, const uint8_t* w_gate,
+                       const uint8_t* s_gate, const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,
+                       const uint8_t* s_down, const float* g_scale, const uint8_t* packed, int T, int H, int I,
+                       int E, int k, int32_t* topk_idx, float* topk_w, int32_t* expert_count,
+                       int32_t* expert_offset, int32_t* active_experts, int32_t* n_active, int32_t* route_src,
+                       int32_t* route_pos, void* workspace, size_t workspace_bytes, uint16_t* y, void* stream) {
   // argument checks of the FFN call first, so that an invalid call launches nothing
   if (T < 0 || k < 1 || E < 1 || k > E || H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
     return MOE_ERR_INVALID_SHAPE;
@@ -38,6 +37,8 @@ extern "C" moe_status moe_step(const uint16_t* x, const float* logits, const flo
   const int chunks_h = H / 32, chunks_i = I / 32;
   if (chunks_h != moe::lanes_per_row(chunks_h) || chunks_i != moe::lanes_per_row(chunks_i))
     return MOE_ERR_UNSUPPORTED;
+  // packed weights exist only for H and I multiples of the MFMA step
+  if (packed && (H % moe::kPackK != 0 || I % moe::kPackK != 0)) return MOE_ERR_INVALID_SHAPE;
   if (T == 0) return MOE_OK;
   const void* ptrs[] = {x, logits, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_idx, topk_w,
                         expert_count, expert_offset, active_experts, n_active, route_src, route_pos,
@@ -46,15 +47,42 @@ extern "C" moe_status moe_step(const uint16_t* x, const float* logits, const flo
     if (!q) return MOE_ERR_NULL_POINTER;
   for (const void* q : ptrs)
     if (!moe::aligned16(q)) return MOE_ERR_MISALIGNED;
-  if (bias && !moe::aligned16(bias)) return MOE_ERR_MISALIGNED;
+  if ((bias && !moe::aligned16(bias)) || (packed && !moe::aligned16(packed))) return MOE_ERR_MISALIGNED;
   if (workspace_bytes < moe_step_workspace_size(T, H, I, E, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   // the FFN workspace is free until the expert kernels run: routing may use it
   const moe_status st = moe::route_bucket(logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset,
                                           active_experts, n_active, route_src, route_pos,
-                                          static_cast<int32_t*>(workspace), workspace_bytes,
-                                          static_cast<hipStream_t>(stream));
+                                          static_cast<int32_t*>(workspace), workspace_bytes, s);
   if (st != MOE_OK) return st;
-  return moe_expert_ffn(x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
-                        expert_offset, active_experts, n_active, route_src, route_pos, T, H, I, E, k, workspace,
-                        workspace_bytes, y, stream);
+  return moe::expert_ffn(3, x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
+                         expert_offset, active_experts, n_active, route_src, route_pos, packed, T, H, I, E, k,
+                         workspace, workspace_bytes, y, s);
+}
+
+extern "C" moe_status moe_step(const uint16_t* x, const float* logits, const float* bias,
+                               const uint8_t* w_gate, const uint8_t* s_gate, const uint8_t* w_up,
+                               const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                               const float* g_scale, int T, int H, int I, int E, int k,
+                               int32_t* topk_idx, float* topk_w, int32_t* expert_count,
+                               int32_t* expert_offset, int32_t* active_experts, int32_t* n_active,
+                               int32_t* route_src, int32_t* route_pos, void* workspace,
+                               size_t workspace_bytes, uint16_t* y, void* stream) {
+  return step(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, nullptr, T, H, I, E, k, topk_idx,
+              topk_w, expert_count, expert_offset, active_experts, n_active, route_src, route_pos, workspace,
+              workspace_bytes, y, stream);
+}
+
+extern "C" moe_status moe_step_packed(const uint16_t* x, const float* logits, const float* bias,
+                                      const uint8_t* w_gate, const uint8_t* s_gate, const uint8_t* w_up,
+                                      const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                                      const float* g_scale, const uint8_t* packed, int T, int H, int I, int E,
+                                      int k, int32_t* topk_idx, float* topk_w, int32_t* expert_count,
+                                      int32_t* expert_offset, int32_t* active_experts, int32_t* n_active,
+                                      int32_t* route_src, int32_t* route_pos, void* workspace,
+                                      size_t workspace_bytes, uint16_t* y, void* stream) {
+  if (!packed) return MOE_ERR_NULL_POINTER;
+  return step(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, packed, T, H, I, E, k, topk_idx,
+              topk_w, expert_count, expert_offset, active_experts, n_active, route_src, route_pos, workspace,
+              workspace_bytes, y, stream);
 }

@@ -39,11 +39,12 @@ def expert_weights_from_numpy(bank, device) -> ExpertWeights:
 class MoeStep:
     """Outputs and workspace for one step of fixed sizes, and the ways to run it.
 
-    path "step": moe_step (the whole step in one call).  "calls":
+    path "step": moe_step (the whole step in one call).  "packed":
+    moe_step_packed, with the weights' packed copy passed to run().  "calls":
     moe_route_bucket then moe_expert_ffn.  "calls_unfused": moe_route_topk,
-    moe_bucket_routes, moe_expert_ffn.  All three produce the same outputs."""
+    moe_bucket_routes, moe_expert_ffn.  All of them produce the same outputs."""
 
-    PATHS = ("step", "calls", "calls_unfused")
+    PATHS = ("step", "packed", "calls", "calls_unfused")
 
     def __init__(self, T: int, H: int, I: int, E: int, k: int, device, path: str = "step"):
         if path not in self.PATHS:
@@ -77,10 +78,12 @@ class MoeStep:
         moe_expert_ffn(x, weights, self.topk_w, self.buckets, self.workspace, self.y, stage=stage)
 
     def run(self, x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor],
-            weights: ExpertWeights) -> torch.Tensor:
-        if self.path == "step":
+            weights: ExpertWeights, packed: Optional[torch.Tensor] = None) -> torch.Tensor:
+        if self.path in ("step", "packed"):
+            if self.path == "packed" and packed is None:
+                raise ValueError('path "packed" needs the packed weights (pack_weights)')
             moe_step(x, logits, bias, weights, self.k, self.topk_idx, self.topk_w, self.buckets,
-                     self.workspace, self.y)
+                     self.workspace, self.y, packed=packed if self.path == "packed" else None)
         else:
             self.routing(logits, bias)
             self.ffn(x, weights)

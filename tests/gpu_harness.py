@@ -32,6 +32,17 @@ def device_weights(bank) -> sme.ExpertWeights:
     return _WEIGHTS[key][1]
 
 
+_PACKED = {}
+
+
+def device_packed(bank) -> torch.Tensor:
+    """The bank's weights packed in MFMA tile order (moe_pack_weights), cached."""
+    key = id(bank)
+    if key not in _PACKED:
+        _PACKED[key] = (bank, sme.pack_weights(device_weights(bank)))
+    return _PACKED[key][1]
+
+
 def to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
@@ -41,14 +52,15 @@ def x_bits(x_u16: np.ndarray) -> torch.Tensor:
 
 
 def run_gpu(x_u16, logits, bias, bank, k, step: sme.MoeStep = None, path: str = "step"):
-    """One step through the C ABI (moe_step, or the separate calls)."""
+    """One step through the C ABI (moe_step, moe_step_packed, or the separate calls)."""
     T, H = x_u16.shape
     E = logits.shape[1]
     W = device_weights(bank)
     I = W.shape[2]
     st = step or sme.MoeStep(T, H, I, E, k, DEV, path=path)
     st.run(x_bits(x_u16), to_dev(logits.astype(np.float32)),
-           None if bias is None else to_dev(bias.astype(np.float32)), W)
+           None if bias is None else to_dev(bias.astype(np.float32)), W,
+           packed=device_packed(bank) if st.path == "packed" else None)
     torch.cuda.synchronize()
     return collect(st)
 

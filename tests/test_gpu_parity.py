@@ -24,6 +24,7 @@ from gpu_harness import (
     assert_output_rounded,
     assert_route,
     collect,
+    device_packed,
     device_weights,
     oracle_all,
     run_gpu,
@@ -47,7 +48,7 @@ def _sample_tokens(wl, idx):
     return sorted(picks)
 
 
-PATHS = ["step", "calls"]
+PATHS = ["step", "packed", "calls"]
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -96,15 +97,18 @@ RAGGED_TILE_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("path", ["step", "packed"])
 @pytest.mark.parametrize("shape", RAGGED_TILE_SHAPES, ids=lambda s: "H%d_I%d_E%d_k%d_T%d" % s)
-def test_ragged_row_tiles(shape):
+def test_ragged_row_tiles(shape, path):
     from dataclasses import replace
     from moe_inputs.configs import get_config
     H, I, E, k, T = shape
     cfg = replace(get_config("tiny"), name="ragged_tiles", H=H, I=I, E=E, k=k, T=T)
     wl = make_workload(cfg, x_seed=11 + T)
-    print(f"[ragged tiles] H={H} I={I} E={E} k={k} T={T}", flush=True)
-    g = run_gpu(wl.x, wl.logits, wl.bias, wl.bank, wl.k)
+    if path == "packed" and (H % 64 or I % 64):
+        pytest.skip("packed weights need H and I multiples of 64")
+    print(f"[ragged tiles] H={H} I={I} E={E} k={k} T={T} path={path}", flush=True)
+    g = run_gpu(wl.x, wl.logits, wl.bias, wl.bank, wl.k, path=path)
     idx, w, b, y = oracle_all(wl.x, wl.logits, wl.bias, wl.bank, wl.k)
     assert_route(g, idx, w)
     assert_buckets(g, b)
@@ -182,7 +186,7 @@ def test_guard_regions_untouched(path):
     step.workspace = big_ws[256: 256 + ws_bytes]
     big_y = torch.full((T + 2, H), 3.0, dtype=torch.bfloat16, device=DEV)
     step.y = big_y[1: T + 1]
-    step.run(x_bits(wl.x), to_dev(wl.logits), None, W)
+    step.run(x_bits(wl.x), to_dev(wl.logits), None, W, packed=device_packed(wl.bank) if path == "packed" else None)
     torch.cuda.synchronize()
     assert torch.all(big_ws[:256] == 0xA5) and torch.all(big_ws[256 + ws_bytes:] == 0x5A)
     assert torch.all(big_y[0] == 3.0) and torch.all(big_y[T + 1] == 3.0)
@@ -210,13 +214,14 @@ def test_graph_replays_with_changed_inputs(path):
     T, H, I, E, k = A.T, A.H, A.I, A.E, A.k
     W = device_weights(A.bank)
     step = sme.MoeStep(T, H, I, E, k, DEV, path=path)
+    pk = device_packed(A.bank) if path == "packed" else None
     x_s = x_bits(A.x)
     l_s = to_dev(A.logits)
-    step.run(x_s, l_s, None, W)          # warm-up outside capture
+    step.run(x_s, l_s, None, W, packed=pk)          # warm-up outside capture
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        step.run(x_s, l_s, None, W)
+        step.run(x_s, l_s, None, W, packed=pk)
     torch.cuda.synchronize()
     refs = {}
     for wl in (A, B):
@@ -291,3 +296,45 @@ def test_stages_compose_to_full_call(name):
     st.ffn(x, W, stage=2)
     torch.cuda.synchronize()
     assert torch.equal(full.view(torch.int16), st.y.view(torch.int16))
+
+
+def _pack_reference(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """The packed layout of one matrix, written out in numpy from its
+    definition: 128-row tiles t, 64-wide steps s, 32-row groups w, lanes l
+    (row 128t + 32w + l%32, half l//32); 16 code bytes and 2 scale bytes per
+    (t, s, w, l) in that order, rows past N zero, each expert padded to 256."""
+    E, N, K2 = codes.shape
+    K = 2 * K2
+    tiles, steps = (N + 127) // 128, K // 64
+    out = []
+    for e in range(E):
+        c = np.zeros((tiles * 128, K2), np.uint8)
+        c[:N] = codes[e]
+        sc = np.zeros((tiles * 128, K // 16), np.uint8)
+        sc[:N] = scales[e]
+        cb, sb = [], []
+        for t in range(tiles):
+            for st in range(steps):
+                for w in range(4):
+                    for l in range(64):
+                        r, h = 128 * t + 32 * w + (l % 32), l // 32
+                        cb.append(c[r, 32 * st + 16 * h: 32 * st + 16 * h + 16])
+                        sb.append(sc[r, 4 * st + 2 * h: 4 * st + 2 * h + 2])
+        m = np.concatenate([np.concatenate(cb), np.concatenate(sb)])
+        out.append(np.concatenate([m, np.zeros((-m.size) % 256, np.uint8)]))
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("shape", [(3, 256, 128), (2, 128, 64), (2, 64, 192)])
+def test_packed_weights_layout(shape):
+    """moe_pack_weights is the byte permutation its header defines (bit-exact)."""
+    from dataclasses import replace
+    from moe_inputs.configs import get_config
+    E, H, I = shape
+    wl = make_workload(replace(get_config("tiny"), name="pack", H=H, I=I, E=E, k=1, T=1))
+    b = wl.bank
+    packed = device_packed(b).cpu().numpy()
+    ref = np.concatenate([_pack_reference(b.w_gate, b.s_gate), _pack_reference(b.w_up, b.s_up),
+                          _pack_reference(b.w_down, b.s_down)])
+    assert packed.shape == ref.shape
+    assert np.array_equal(packed, ref)
