@@ -847,7 +847,8 @@ WorkspaceLayout workspace_layout(int T, int H, int I, int k) {
 
 constexpr long long kMaxGrid = 1 << 20;   // one workgroup per task; the shape limits keep tasks below this
 constexpr int kMfmaMinTokens = 64;      // batches from this size launch the MFMA kernels
-constexpr int kMfmaMinRoutes = 16;      // experts with this many routes use them
+constexpr int kMfmaMinRoutes = 16;      // experts with this many routes use them (standard weight layout)
+constexpr int kMfmaMinRoutesPacked = 1; // with the packed copy: every expert of such a batch
 
 template <int LG>
 void launch_gate_up(const FfnParams& p, long long tasks, hipStream_t s) {
@@ -920,9 +921,13 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   // Experts with many routes go to the MFMA kernels; only batches large
   // enough to have such experts (and not small enough for the fused
   // down/unroute kernel) launch them.  K (H for gate/up, I for down) must be a
-  // multiple of the 64-wide step.
+  // multiple of the 64-wide step.  With the packed copy (one contiguous
+  // kilobyte per weight load) the tiles beat one row-dot pass per route from
+  // two routes on and match it at one (measured at decode_t256_zipf), so every
+  // expert takes them and the row-dot kernels are not launched at all.
   const bool mfma = !down_combine && T >= kMfmaMinTokens && H % kMmK == 0 && I % kMmK == 0;
-  p.mfma_min = mfma ? kMfmaMinRoutes : 0;
+  p.mfma_min = mfma ? (packed ? kMfmaMinRoutesPacked : kMfmaMinRoutes) : 0;
+  const bool row_dots = !mfma || p.mfma_min > 1;
 
   const long long slots = std::min<long long>(E, (long long)T * k);
   const int rpt_gu = kWavesPerBlock * (kWave / lr_gu) * kGuUnits;
@@ -933,9 +938,11 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
 
   const long long slots8 = (slots + kXcds - 1) / kXcds * kXcds;   // slot count padded for the XCD numbering
   if (stage & 1) {
-    if (lr_gu == 64) launch_gate_up<64>(p, tasks_gu, s);
-    else launch_gate_up<0>(p, tasks_gu, s);
-    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+    if (row_dots) {
+      if (lr_gu == 64) launch_gate_up<64>(p, tasks_gu, s);
+      else launch_gate_up<0>(p, tasks_gu, s);
+      if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+    }
     if (mfma) {
       const unsigned grid = (unsigned)(slots8 * ((I + kMmRows - 1) / kMmRows));
       if (p.packed) ffn_mfma_kernel<true, true><<<grid, kMmThreads, 0, s>>>(p);
@@ -952,9 +959,11 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
     else launch_down_combine<0>(p, grid, dyn, (int)slots, s);
     return launch_status();
   }
-  if (lr_d == 16) launch_down<16>(p, tasks_d, s);
-  else launch_down<0>(p, tasks_d, s);
-  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  if (row_dots) {
+    if (lr_d == 16) launch_down<16>(p, tasks_d, s);
+    else launch_down<0>(p, tasks_d, s);
+    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  }
   if (mfma) {
     const unsigned grid = (unsigned)(slots8 * ((H + kMmRows - 1) / kMmRows));
     if (p.packed) ffn_mfma_kernel<false, true><<<grid, kMmThreads, 0, s>>>(p);
