@@ -712,7 +712,7 @@ constexpr int kDcHLoads = kDcMaxLds / 16 / kDcThreads;   // 16-byte h pieces per
 template <int LD, int SLOTS>
 __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_kernel(FfnParams p) {
   extern __shared__ __align__(16) uint8_t s_dyn8[];   // [R, I] bf16 h, then [R, rpw] fp32 o
-  __shared__ int s_pos[kDcMaxRoutes];
+  __shared__ int s_src[kDcMaxRoutes];
   __shared__ float s_w[kDcMaxRoutes];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -737,7 +737,7 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
   }
   // route positions and gate weights (an index past R re-reads the last)
   const int rt = min(tid, R - 1);
-  const int pos_r = p.route_pos[rt];
+  const int src_r = p.route_src[rt];
   const float w_r = p.topk_w[rt];
   compiler_fence();
 
@@ -785,7 +785,7 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
     if (q < h_bytes) *reinterpret_cast<u32x4*>(s_dyn8 + q) = hv[i];
   }
   if (tid < R) {
-    s_pos[tid] = min(max(pos_r, 0), R - 1);
+    s_src[tid] = min(max(src_r, 0), R - 1);
     s_w[tid] = w_r;
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -803,7 +803,7 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
       load_operand_chunk(s_h + (size_t)pos * p.I, sl, hr);
       const float acc = dot_chunk(cd[u], vd[u], hr, 0.0f, one);
       const float v = (LD == 16 ? row16_sum(acc) : group_sum(acc, ld)) * gd_u[u];
-      if (sl == 0 && row_ok) s_o[pos * rpw + sub] = v;
+      if (sl == 0 && row_ok) s_o[s_src[pos] * rpw + sub] = v;
     }
   }
   __syncthreads();
@@ -813,7 +813,7 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
     const int t = i / rpw, r = i - t * rpw;
     if (row0 + r >= p.H) continue;
     float acc = 0.0f;
-    for (int j = 0; j < p.k; ++j) acc = fmaf(s_w[t * p.k + j], s_o[s_pos[t * p.k + j] * rpw + r], acc);
+    for (int j = 0; j < p.k; ++j) acc = fmaf(s_w[t * p.k + j], s_o[(t * p.k + j) * rpw + r], acc);
     p.y[(size_t)t * p.H + row0 + r] = (uint16_t)f32_to_bf16_rne(acc);
   }
 }

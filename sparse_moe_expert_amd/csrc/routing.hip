@@ -34,8 +34,12 @@ constexpr int kBucketThreads = 1024;
 constexpr int kBucketWaves = kBucketThreads / kWave;
 constexpr int kFusedMaxTokens = 64;        // one workgroup routes and buckets up to this many tokens
 constexpr int kFusedMaxRoutes = 2048;
+// The selecting kernels are also built with k fixed at this value (the
+// configured top-10), which unrolls the selection rounds; other k use the
+// loop.
+constexpr int kUnrolledK = 10;
 
-template <int V>
+template <int V, int KC>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
@@ -44,7 +48,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   if (t >= T) return;                           // whole wavefront leaves together
   int e;
   float w;
-  select_token<V>(logits + (size_t)t * E, bias, E, k, lane, e, w);
+  select_token<V, KC>(logits + (size_t)t * E, bias, E, k, lane, e, w);
   if (lane < k) {
     topk_idx[(size_t)t * k + lane] = e;
     topk_w[(size_t)t * k + lane] = w;
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_scatter_kernel(
 
 // Route and bucket a small batch in one workgroup: wavefront w selects for
 // tokens w, w+16, ...; the ids stay in LDS for the bucketing.
-template <int V>
+template <int V, int KC>
 __global__ __launch_bounds__(kBucketThreads) void route_bucket_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k, int id_bits,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(kBucketThreads) void route_bucket_kernel(
   for (int t = wave; t < T; t += kBucketWaves) {
     int e;
     float w;
-    select_token<V>(logits + (size_t)t * E, bias, E, k, lane, e, w);
+    select_token<V, KC>(logits + (size_t)t * E, bias, E, k, lane, e, w);
     if (lane < k) {
       topk_idx[(size_t)t * k + lane] = e;
       topk_w[(size_t)t * k + lane] = w;
@@ -273,9 +277,9 @@ __global__ __launch_bounds__(kBucketThreads) void route_bucket_kernel(
 constexpr int kSmallMaxTokens = 16;
 constexpr int kSmallMaxRoutes = 256;
 
-template <int V>
+template <int V, int KC>
 __global__ __launch_bounds__(kBucketThreads) void route_bucket_small_kernel(
-    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k, int id_bits,
+    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(kBucketThreads) void route_bucket_small_kernel(
   if (wave < T) {
     int e;
     float w;
-    select_token<V>(logits + (size_t)wave * E, bias, E, k, lane, e, w);
+    select_token<V, KC>(logits + (size_t)wave * E, bias, E, k, lane, e, w);
     if (lane < k) {
       topk_idx[(size_t)wave * k + lane] = e;
       topk_w[(size_t)wave * k + lane] = w;
@@ -299,11 +303,40 @@ __global__ __launch_bounds__(kBucketThreads) void route_bucket_small_kernel(
     }
   }
   __syncthreads();
-  if (tid < R) atomicAdd(&s_cnt[s_ids[tid]], 1);   // integer counts: order-free
+  // counts (LDS integer atomics: order-free) and, within each 64-route
+  // group, the stable rank of a route among the group's routes to the same
+  // expert (one ballot per id bit; ids are below 1024), both before the
+  // next barrier
+  const bool valid = tid < R;
+  int rank = 0, e = 0;
+  if (wave * kWave < R) {
+    e = valid ? s_ids[tid] : 0;
+    if (valid) atomicAdd(&s_cnt[e], 1);
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 10; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
+    }
+    rank = __popcll(same & ((1ull << lane) - 1ull));
+    if (valid && rank == 0) s_wcnt[wave][e] = (uint8_t)__popcll(same);
+  }
   __syncthreads();
   const int c = s_cnt[tid];                          // expert tid
-  int total;
-  const int scan = block_scan<kBucketWaves>(c + ((c > 0) << 16), s_wt, total);
+  // exclusive scan over the experts of (count, count > 0) packed in one int
+  const int v = c + ((c > 0) << 16);
+  const int inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) s_wt[wave] = inc;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kBucketWaves; ++w) {
+    const int t = s_wt[w];
+    base += (w < wave) ? t : 0;
+    total += t;
+  }
+  const int scan = base + inc - v;
   const int off = scan & 0xFFFF, apos = scan >> 16;
   const int total_active = total >> 16;
   if (tid < E) {
@@ -317,24 +350,8 @@ __global__ __launch_bounds__(kBucketThreads) void route_bucket_small_kernel(
     expert_offset[E] = total & 0xFFFF;
     *n_active = total_active;
   }
-  // stable rank among routes of the same expert: lanes of a 64-route group
-  // with the same id are found with one ballot per id bit; earlier groups
-  // contribute their per-expert counts
-  int rank = 0, e = 0;
-  if (wave * kWave < R) {
-    const bool valid = tid < R;
-    e = valid ? s_ids[tid] : 0;
-    uint64_t same = __ballot(valid);
-    for (int b = 0; b < id_bits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bal = __ballot(bit);
-      same &= bit ? bal : ~bal;
-    }
-    rank = __popcll(same & ((1ull << lane) - 1ull));
-    if (valid && rank == 0) s_wcnt[wave][e] = (uint8_t)__popcll(same);
-  }
   __syncthreads();
-  if (tid < R) {
+  if (valid) {
     for (int w = 0; w < wave; ++w) rank += s_wcnt[w][e];
     const int pos = s_cnt[e] + rank;
     route_src[pos] = tid;
@@ -375,11 +392,15 @@ void launch_route(const float* logits, const float* bias, int T, int E, int k, i
                   hipStream_t s) {
   const dim3 grid((T + 3) / 4), block(256);
   const int V = (E + kWave - 1) / kWave;
-  if (V <= 1) route_topk_kernel<1><<<grid, block, 0, s>>>(logits, bias, T, E, k, topk_idx, topk_w);
-  else if (V <= 2) route_topk_kernel<2><<<grid, block, 0, s>>>(logits, bias, T, E, k, topk_idx, topk_w);
-  else if (V <= 4) route_topk_kernel<4><<<grid, block, 0, s>>>(logits, bias, T, E, k, topk_idx, topk_w);
-  else if (V <= 8) route_topk_kernel<8><<<grid, block, 0, s>>>(logits, bias, T, E, k, topk_idx, topk_w);
-  else route_topk_kernel<16><<<grid, block, 0, s>>>(logits, bias, T, E, k, topk_idx, topk_w);
+#define MOE_RT(VV)                                                                                  \
+  if (k == kUnrolledK) route_topk_kernel<VV, kUnrolledK><<<grid, block, 0, s>>>(logits, bias, T, E, k, topk_idx, topk_w); \
+  else route_topk_kernel<VV, 0><<<grid, block, 0, s>>>(logits, bias, T, E, k, topk_idx, topk_w)
+  if (V <= 1) { MOE_RT(1); }
+  else if (V <= 2) { MOE_RT(2); }
+  else if (V <= 4) { MOE_RT(4); }
+  else if (V <= 8) { MOE_RT(8); }
+  else { MOE_RT(16); }
+#undef MOE_RT
 }
 
 }  // namespace
@@ -423,29 +444,35 @@ moe_status route_bucket(const float* logits, const float* bias, int T, int E, in
   const int bits = id_bits_for(E);
   const int V = (E + kWave - 1) / kWave;
   if (T <= kSmallMaxTokens && T * k <= kSmallMaxRoutes) {
-#define MOE_RBS(VV)                                                                                          \
-  route_bucket_small_kernel<VV><<<1, kBucketThreads, 0, s>>>(logits, bias, T, E, k, bits, topk_idx, topk_w, \
-                                                             expert_count, expert_offset, active_experts,     \
-                                                             n_active, route_src, route_pos)
-    if (V <= 1) MOE_RBS(1);
-    else if (V <= 2) MOE_RBS(2);
-    else if (V <= 4) MOE_RBS(4);
-    else if (V <= 8) MOE_RBS(8);
-    else MOE_RBS(16);
+#define MOE_RBS1(VV, KK)                                                                                       \
+  route_bucket_small_kernel<VV, KK><<<1, kBucketThreads, 0, s>>>(logits, bias, T, E, k, topk_idx, topk_w,       \
+                                                                 expert_count, expert_offset, active_experts,     \
+                                                                 n_active, route_src, route_pos)
+#define MOE_RBS(VV) \
+  if (k == kUnrolledK) MOE_RBS1(VV, kUnrolledK); else MOE_RBS1(VV, 0)
+    if (V <= 1) { MOE_RBS(1); }
+    else if (V <= 2) { MOE_RBS(2); }
+    else if (V <= 4) { MOE_RBS(4); }
+    else if (V <= 8) { MOE_RBS(8); }
+    else { MOE_RBS(16); }
 #undef MOE_RBS
+#undef MOE_RBS1
     return launch_status();
   }
   if (T <= kFusedMaxTokens && T * k <= kFusedMaxRoutes) {
-#define MOE_RB(VV)                                                                                          \
-  route_bucket_kernel<VV><<<1, kBucketThreads, 0, s>>>(logits, bias, T, E, k, bits, topk_idx, topk_w,       \
-                                                        expert_count, expert_offset, active_experts, n_active, \
-                                                        route_src, route_pos)
-    if (V <= 1) MOE_RB(1);
-    else if (V <= 2) MOE_RB(2);
-    else if (V <= 4) MOE_RB(4);
-    else if (V <= 8) MOE_RB(8);
-    else MOE_RB(16);
+#define MOE_RB1(VV, KK)                                                                                     \
+  route_bucket_kernel<VV, KK><<<1, kBucketThreads, 0, s>>>(logits, bias, T, E, k, bits, topk_idx, topk_w,   \
+                                                            expert_count, expert_offset, active_experts, n_active, \
+                                                            route_src, route_pos)
+#define MOE_RB(VV) \
+  if (k == kUnrolledK) MOE_RB1(VV, kUnrolledK); else MOE_RB1(VV, 0)
+    if (V <= 1) { MOE_RB(1); }
+    else if (V <= 2) { MOE_RB(2); }
+    else if (V <= 4) { MOE_RB(4); }
+    else if (V <= 8) { MOE_RB(8); }
+    else { MOE_RB(16); }
 #undef MOE_RB
+#undef MOE_RB1
     return launch_status();
   }
   launch_route(logits, bias, T, E, k, topk_idx, topk_w, s);

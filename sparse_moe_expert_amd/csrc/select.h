@@ -14,8 +14,9 @@ namespace {
 
 __device__ __forceinline__ uint32_t ordered_bits(float z) {
   uint32_t u = __float_as_uint(z);
-  if (u == 0x80000000u) u = 0;                 // -0.0 == +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  u = (u == 0x80000000u) ? 0u : u;             // -0.0 == +0.0
+  // negative: all bits flipped; otherwise the sign bit set
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float from_ordered(uint32_t o) {
@@ -72,7 +73,11 @@ constexpr uint32_t kIdMask = 1023;             // expert ids < 1024
 // lowest lane holding it (lanes own ascending id ranges, so that is the
 // lowest id among equal scores) and a one-step shift of that lane's list:
 // no per-round rescan and no divergent branch.
-template <int V>
+//
+// KC > 0 fixes k = KC at compile time: the rounds are then unrolled into one
+// straight-line block, so the shift of one round's winning list can fill the
+// wait states of the next round's reduction (k is then ignored).
+template <int V, int KC = 0>
 __device__ __forceinline__ void select_token(const float* __restrict__ row, const float* __restrict__ bias, int E,
                                              int k, int lane, int& my_e, float& my_w) {
   const int e0 = lane * V;
@@ -98,8 +103,11 @@ __device__ __forceinline__ void select_token(const float* __restrict__ row, cons
   }
   uint64_t K[V];
 #pragma unroll
-  for (int i = 0; i < V; ++i)
-    K[i] = (e0 + i < E) ? ((uint64_t)ordered_bits(zv[i]) << 32) | (kIdMask - (uint32_t)(e0 + i)) : 0ull;
+  for (int i = 0; i < V; ++i) {
+    const bool ok = e0 + i < E;
+    const uint32_t hi = ok ? ordered_bits(zv[i]) : 0u, lo = ok ? kIdMask - (uint32_t)(e0 + i) : 0u;
+    K[i] = ((uint64_t)hi << 32) | lo;
+  }
 #pragma unroll
   for (int size = 2; size <= V; size <<= 1) {
 #pragma unroll
@@ -110,16 +118,20 @@ __device__ __forceinline__ void select_token(const float* __restrict__ row, cons
         if (j > i) {
           const bool desc = (i & size) == 0;      // the last stage (size == V) is all descending
           const uint64_t a = K[i], b = K[j];
-          const bool swap = desc ? (b > a) : (a > b);
-          K[i] = swap ? b : a;
-          K[j] = swap ? a : b;
+          // one comparison per exchange: an opaque all-ones/zero mask and
+          // bitwise selects (plain selects become separate max and min)
+          uint32_t m = (desc ? (b > a) : (a > b)) ? 0xFFFFFFFFu : 0u;
+          asm("" : "+v"(m));
+          const uint64_t m64 = ((uint64_t)m << 32) | m;
+          K[i] = (b & m64) | (a & ~m64);
+          K[j] = (a & m64) | (b & ~m64);
         }
       }
     }
   }
   uint32_t my_key = 0, key0 = 0;
   my_e = 0;
-  for (int j = 0; j < k; ++j) {
+  auto round = [&](int j) {
     const uint32_t lead = (uint32_t)(K[0] >> 32);
     const uint32_t wbest = wave_max_u32(lead);
     const int wl = __builtin_ctzll(__ballot(lead == wbest));
@@ -137,10 +149,17 @@ __device__ __forceinline__ void select_token(const float* __restrict__ row, cons
 #pragma unroll
     for (int i = 0; i + 1 < V; ++i) K[i] = (K[i + 1] & m64) | (K[i] & ~m64);
     K[V - 1] &= ~m64;
+  };
+  if constexpr (KC > 0) {
+#pragma unroll
+    for (int j = 0; j < KC; ++j) round(j);
+  } else {
+    for (int j = 0; j < k; ++j) round(j);
   }
   // Renormalised softmax over the chosen set: w_j = exp(z_j - z_0) / sum.
   const float z0 = from_ordered(key0);
-  const float pj = (lane < k) ? __builtin_expf(from_ordered(my_key) - z0) : 0.0f;
+  const int kk = KC > 0 ? KC : k;
+  const float pj = (lane < kk) ? __builtin_expf(from_ordered(my_key) - z0) : 0.0f;
   my_w = pj / wave_sum_f32(pj);
 }
 

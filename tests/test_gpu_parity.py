@@ -280,6 +280,45 @@ def test_fused_routing_matches_two_calls(name):
             assert torch.equal(ta, tb)
 
 
+# (T, E, k, ties, bias): small batches through the fused routing kernels, at
+# 64 routes and past it, expert counts that are not a multiple of 64, k = E,
+# k = 32, k = 1, the unrolled k = 10 and other k, and heavy ties.
+ROUTING_EDGE_CASES = [
+    (1, 512, 10, False, False), (4, 512, 10, False, True), (6, 512, 10, True, False),
+    (16, 512, 4, False, False), (7, 100, 9, True, True), (13, 100, 5, False, False),
+    (16, 1000, 4, True, False), (3, 64, 10, False, False), (5, 8, 8, False, False),
+    (2, 1024, 32, True, False), (16, 1024, 1, False, False), (8, 200, 8, True, False),
+]
+
+
+@pytest.mark.parametrize("case", ROUTING_EDGE_CASES, ids=lambda c: "T%d_E%d_k%d_ties%d_bias%d" % c)
+def test_fused_routing_edges(case):
+    """moe_route_bucket against the oracle (bit-exact ids and buckets, weights
+    within 1e-6) and against the two separate calls, bit for bit."""
+    T, E, k, ties, with_bias = case
+    rng = np.random.default_rng(1000 + T * 7 + E + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    if ties:
+        logits = (np.round(logits * 2.0) / 2.0).astype(np.float32)   # few distinct scores
+    bias = (0.5 * rng.standard_normal(E)).astype(np.float32) if with_bias else None
+    idx_ref, w_ref = oracle.route_topk(logits, bias, k)
+    b_ref = oracle.bucket_routes(idx_ref, E)
+    ld = to_dev(logits)
+    bd = None if bias is None else to_dev(bias)
+    fused = sme.MoeStep(T, 64, 64, E, k, DEV, path="calls")
+    split = sme.MoeStep(T, 64, 64, E, k, DEV, path="calls_unfused")
+    fused.routing(ld, bd)
+    split.routing(ld, bd)
+    torch.cuda.synchronize()
+    g = collect(fused)
+    assert_route(g, idx_ref, w_ref)
+    assert_buckets(g, b_ref)
+    assert torch.equal(fused.topk_idx, split.topk_idx)
+    assert torch.equal(fused.topk_w.view(torch.int32), split.topk_w.view(torch.int32))
+    for ta, tb in zip(fused.buckets, split.buckets):
+        assert torch.equal(ta, tb)
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode_t4", "verify_t32"])
 def test_stages_compose_to_full_call(name):
     """moe_expert_ffn_stage 1 then 2 equals moe_expert_ffn bit for bit."""
