@@ -12,11 +12,15 @@
 // expert ids and scatter that follow top-k in the fused routing kernel,
 // exported as the compact expert-presence list plus original route positions
 // of the SM70 note (section "First implementation boundary", step 1).  The
-// same page paragraph describes one workgroup doing all of it for batches of
-// up to 64 tokens; moe_route_bucket does that here.
+// same page paragraph describes one workgroup doing all of it for small
+// batches; moe_route_bucket does that here up to 16 tokens.
 //
 // Selection (gfx950, select.h): one 64-lane wavefront per token, k rounds of
-// a wave-wide arg-max over order-preserving integer keys.
+// a wave-wide arg-max over order-preserving integer keys.  A selection is a
+// chain of dependent wave operations, so it runs at full speed only with
+// few waves per SIMD; batches of more than 16 tokens therefore select in a
+// kernel of four tokens per workgroup spread over the chip, and bucket in a
+// second one-workgroup kernel.
 //
 // Bucketing (one 1024-thread workgroup): LDS histogram of expert ids
 // (integer atomics: counts do not depend on their order), block-wide
@@ -32,8 +36,6 @@ namespace {
 
 constexpr int kBucketThreads = 1024;
 constexpr int kBucketWaves = kBucketThreads / kWave;
-constexpr int kFusedMaxTokens = 64;        // one workgroup routes and buckets up to this many tokens
-constexpr int kFusedMaxRoutes = 2048;
 // The selecting kernels are also built with k fixed at this value (the
 // configured top-10), which unrolls the selection rounds; other k use the
 // loop.
@@ -82,24 +84,34 @@ struct BucketShared {
 };
 
 // Bucket R routes whose expert ids are ids[0..R) (global or LDS).
-__device__ __forceinline__ void bucket_block(const int32_t* ids, int R, int E, int id_bits, BucketShared& sh,
+__device__ __forceinline__ void bucket_block(const int32_t* ids, int R, int E, BucketShared& sh,
                                              int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
                                              int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
                                              int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   for (int e = tid; e < 1024; e += kBucketThreads) sh.base[e] = 0;
-  for (int i = tid; i < kBucketWaves * 1024; i += kBucketThreads) (&sh.wcnt[0][0])[i] = 0;
+  for (int i = tid; i < kBucketWaves * 1024 / 4; i += kBucketThreads) reinterpret_cast<int*>(&sh.wcnt[0][0])[i] = 0;
   __syncthreads();
   // ids outside [0, E) violate the precondition; clamping keeps every access
   // in bounds
   for (int r = tid; r < R; r += kBucketThreads) atomicAdd(&sh.base[min(max(ids[r], 0), E - 1)], 1);
   __syncthreads();
 
-  // scans (E <= 1024: one expert per thread)
+  // scans (E <= 1024: one expert per thread) of the counts and of the
+  // count > 0 flags - one scan of both packed in one int while R < 2^16
   const int c = tid < E ? sh.base[tid] : 0;
-  int total_routes, total_active;
-  const int off = block_exclusive_scan(c, sh.wave_tot, &total_routes);
-  const int apos = block_exclusive_scan(c > 0 ? 1 : 0, sh.wave_tot, &total_active);
+  int off, apos, total_routes, total_active;
+  if (R < (1 << 16)) {
+    int total;
+    const int scan = block_exclusive_scan(c + ((c > 0) << 16), sh.wave_tot, &total);
+    off = scan & 0xFFFF;
+    apos = scan >> 16;
+    total_routes = total & 0xFFFF;
+    total_active = total >> 16;
+  } else {
+    off = block_exclusive_scan(c, sh.wave_tot, &total_routes);
+    apos = block_exclusive_scan(c > 0 ? 1 : 0, sh.wave_tot, &total_active);
+  }
   if (tid < E) {
     expert_count[tid] = c;
     expert_offset[tid] = off;
@@ -119,7 +131,8 @@ __device__ __forceinline__ void bucket_block(const int32_t* ids, int R, int E, i
     const bool valid = r < R;
     const int e = valid ? min(max(ids[r], 0), E - 1) : 0;
     uint64_t same = __ballot(valid);
-    for (int b = 0; b < id_bits; ++b) {
+#pragma unroll
+    for (int b = 0; b < 10; ++b) {                // ids are below 1024
       const bool bit = (e >> b) & 1;
       const uint64_t bal = __ballot(bit);
       same &= bit ? bal : ~bal;
@@ -134,6 +147,7 @@ __device__ __forceinline__ void bucket_block(const int32_t* ids, int R, int E, i
       route_src[pos] = r;
       route_pos[r] = pos;
     }
+    if (c0 + kBucketThreads >= R) break;          // last chunk: no bases to carry
     __syncthreads();
     if (valid && rank == 0) {
       atomicAdd(&sh.base[e], wcount);
@@ -144,12 +158,12 @@ __device__ __forceinline__ void bucket_block(const int32_t* ids, int R, int E, i
 }
 
 __global__ __launch_bounds__(kBucketThreads) void bucket_routes_kernel(
-    const int32_t* __restrict__ topk_idx, int R, int E, int id_bits,
+    const int32_t* __restrict__ topk_idx, int R, int E,
     int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
     int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos) {
   __shared__ BucketShared sh;
-  bucket_block(topk_idx, R, E, id_bits, sh, expert_count, expert_offset, active_experts, n_active, route_src,
+  bucket_block(topk_idx, R, E, sh, expert_count, expert_offset, active_experts, n_active, route_src,
                route_pos);
 }
 
@@ -239,33 +253,6 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_scatter_kernel(
     route_src[pos] = r;
     route_pos[r] = pos;
   }
-}
-
-// Route and bucket a small batch in one workgroup: wavefront w selects for
-// tokens w, w+16, ...; the ids stay in LDS for the bucketing.
-template <int V, int KC>
-__global__ __launch_bounds__(kBucketThreads) void route_bucket_kernel(
-    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k, int id_bits,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
-    int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
-    int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos) {
-  __shared__ BucketShared sh;
-  __shared__ int s_ids[kFusedMaxRoutes];
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  for (int t = wave; t < T; t += kBucketWaves) {
-    int e;
-    float w;
-    select_token<V, KC>(logits + (size_t)t * E, bias, E, k, lane, e, w);
-    if (lane < k) {
-      topk_idx[(size_t)t * k + lane] = e;
-      topk_w[(size_t)t * k + lane] = w;
-      s_ids[t * k + lane] = e;
-    }
-  }
-  __syncthreads();
-  bucket_block(s_ids, T * k, E, id_bits, sh, expert_count, expert_offset, active_experts, n_active, route_src,
-               route_pos);
 }
 
 // Route and bucket a batch of up to 16 tokens in one 1024-thread workgroup:
@@ -426,7 +413,7 @@ extern "C" moe_status moe_bucket_routes(const int32_t* topk_idx, int T, int E, i
   if (!topk_idx) return MOE_ERR_NULL_POINTER;
   if (!aligned16(topk_idx)) return MOE_ERR_MISALIGNED;
   bucket_routes_kernel<<<1, kBucketThreads, 0, static_cast<hipStream_t>(stream)>>>(
-      topk_idx, T * k, E, id_bits_for(E), expert_count, expert_offset, active_experts, n_active, route_src,
+      topk_idx, T * k, E, expert_count, expert_offset, active_experts, n_active, route_src,
       route_pos);
   return launch_status();
 }
@@ -459,22 +446,6 @@ moe_status route_bucket(const float* logits, const float* bias, int T, int E, in
 #undef MOE_RBS1
     return launch_status();
   }
-  if (T <= kFusedMaxTokens && T * k <= kFusedMaxRoutes) {
-#define MOE_RB1(VV, KK)                                                                                     \
-  route_bucket_kernel<VV, KK><<<1, kBucketThreads, 0, s>>>(logits, bias, T, E, k, bits, topk_idx, topk_w,   \
-                                                            expert_count, expert_offset, active_experts, n_active, \
-                                                            route_src, route_pos)
-#define MOE_RB(VV) \
-  if (k == kUnrolledK) MOE_RB1(VV, kUnrolledK); else MOE_RB1(VV, 0)
-    if (V <= 1) { MOE_RB(1); }
-    else if (V <= 2) { MOE_RB(2); }
-    else if (V <= 4) { MOE_RB(4); }
-    else if (V <= 8) { MOE_RB(8); }
-    else { MOE_RB(16); }
-#undef MOE_RB
-#undef MOE_RB1
-    return launch_status();
-  }
   launch_route(logits, bias, T, E, k, topk_idx, topk_w, s);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   const long long R = (long long)T * k;
@@ -489,7 +460,7 @@ moe_status route_bucket(const float* logits, const float* bias, int T, int E, in
                                                                  route_src, route_pos);
     return launch_status();
   }
-  bucket_routes_kernel<<<1, kBucketThreads, 0, s>>>(topk_idx, (int)R, E, bits, expert_count, expert_offset,
+  bucket_routes_kernel<<<1, kBucketThreads, 0, s>>>(topk_idx, (int)R, E, expert_count, expert_offset,
                                                      active_experts, n_active, route_src, route_pos);
   return launch_status();
 }

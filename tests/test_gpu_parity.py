@@ -280,14 +280,15 @@ def test_fused_routing_matches_two_calls(name):
             assert torch.equal(ta, tb)
 
 
-# (T, E, k, ties, bias): small batches through the fused routing kernels, at
-# 64 routes and past it, expert counts that are not a multiple of 64, k = E,
+# (T, E, k, ties, bias): batches on both sides of the one-workgroup routing
+# limit (16 tokens), expert counts that are not a multiple of 64, k = E,
 # k = 32, k = 1, the unrolled k = 10 and other k, and heavy ties.
 ROUTING_EDGE_CASES = [
     (1, 512, 10, False, False), (4, 512, 10, False, True), (6, 512, 10, True, False),
     (16, 512, 4, False, False), (7, 100, 9, True, True), (13, 100, 5, False, False),
     (16, 1000, 4, True, False), (3, 64, 10, False, False), (5, 8, 8, False, False),
     (2, 1024, 32, True, False), (16, 1024, 1, False, False), (8, 200, 8, True, False),
+    (17, 512, 10, False, True), (40, 100, 3, True, False), (64, 512, 10, False, False),
 ]
 
 
