@@ -350,7 +350,9 @@ __global__ __launch_bounds__(kThreads, 4) void down_kernel(FfnParams p, int n_ta
 // gate/up is [I x H] x [H x routes] twice, down is [H x I] x [I x routes].
 // A workgroup owns 128 weight rows of one expert (the same rows of W_gate
 // and W_up for gate/up) and the expert's routes in chunks of 128; each of
-// its four waves owns 32 of the rows and all of the chunk's routes.
+// its four waves owns 32 of the rows and all of the chunk's routes.  The
+// packed down kernel of prefill-sized batches gives each wave two 32-row
+// tiles (256 rows per workgroup), so every B fragment read feeds two MFMAs.
 //
 // v_mfma_f32_32x32x16_bf16 with the weights as A (32 rows x 16) and the
 // routes' operand rows as B (16 x 32 routes).  Lane layout (checked on the
@@ -433,33 +435,36 @@ __device__ __forceinline__ void step_barrier() {
   compiler_fence();
 }
 
-template <bool GU, bool PACKED>
+// NSUB: row tiles of W_down per wave (down only; gate/up always has two A
+// operands, the same rows of W_gate and W_up).  Two row tiles per wave halve
+// the workgroups of an expert, so each of its h rows is staged half as often
+// and each B fragment read from LDS feeds two MFMAs.
+template <bool GU, bool PACKED, int NSUB>
 struct MmTile {
-  static constexpr int NMAT = GU ? 2 : 1;
-  static constexpr int kLoadsPerStep = 4 + 2 * NMAT;   // per thread: 4 operand chunks, codes + scales per matrix
+  static constexpr int NA = GU ? 2 : NSUB;             // A operands per wave
+  static constexpr int kLoadsPerStep = 4 + 2 * NA;     // per thread: 4 operand chunks, codes + scales per operand
   uint8_t* s_x[kMmStages];                             // one LDS array per stage
-  __amdgpu_buffer_rsrc_t rc[NMAT], rs[NMAT], rb;
-  uint32_t w_voff, s_voff;                             // this lane's weight row slice
-  uint32_t tile_step0;                                 // packed: tile index * steps
+  __amdgpu_buffer_rsrc_t rc[NA], rs[NA], rb;
+  uint32_t w_voff[NA], s_voff[NA];                     // this lane's slice of each A operand (packed: from its tile)
   uint32_t x_goff[4];                                  // operand chunk sources, per step add ks*128
   int wave, lane;
-  uint4 wc[kMmStages][NMAT];
-  uint32_t wsv[kMmStages][NMAT];
+  uint4 wc[kMmStages][NA];
+  uint32_t wsv[kMmStages][NA];
 
   template <int T>
   __device__ __forceinline__ void issue(int ks) {
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
+    for (int m = 0; m < NA; ++m) {
       if constexpr (PACKED) {
-        // one contiguous kilobyte of codes (and 128 bytes of scales) per wave, read once
-        const uint32_t slot = tile_step0 + (uint32_t)ks;
-        wc[T][m] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rc[m], w_voff, slot * 4096u, kStreamAux));
-        wsv[T][m] = __builtin_amdgcn_raw_buffer_load_b16(rs[m], s_voff, slot * 512u, kStreamAux);
+        // one contiguous kilobyte of codes (and 128 bytes of scales) per wave,
+        // read once; the tile offset is in the range-checked vector offset
+        wc[T][m] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rc[m], w_voff[m], (uint32_t)ks * 4096u, kStreamAux));
+        wsv[T][m] = __builtin_amdgcn_raw_buffer_load_b16(rs[m], s_voff[m], (uint32_t)ks * 512u, kStreamAux);
       } else {
         // default cache policy: each load uses 32 of a row's 128 cached bytes,
         // the next three K steps use the rest
-        wc[T][m] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rc[m], w_voff, (uint32_t)ks * (kMmK / 2), 0));
-        wsv[T][m] = __builtin_amdgcn_raw_buffer_load_b16(rs[m], s_voff, (uint32_t)ks * (kMmK / 16), 0);
+        wc[T][m] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rc[m], w_voff[m], (uint32_t)ks * (kMmK / 2), 0));
+        wsv[T][m] = __builtin_amdgcn_raw_buffer_load_b16(rs[m], s_voff[m], (uint32_t)ks * (kMmK / 16), 0);
       }
     }
     uint8_t* stage = s_x[T];
@@ -470,10 +475,12 @@ struct MmTile {
   }
 };
 
-template <bool GU, bool PACKED>
+template <bool GU, bool PACKED, int NSUB>
 __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
-  using Tile = MmTile<GU, PACKED>;
-  constexpr int NMAT = Tile::NMAT;
+  static_assert(GU ? NSUB == 1 : (NSUB == 1 || PACKED), "several row tiles per wave: down on packed weights");
+  using Tile = MmTile<GU, PACKED, NSUB>;
+  constexpr int NMAT = Tile::NA;
+  constexpr int kWgRows = kMmRows * (GU ? 1 : NSUB);          // weight rows per workgroup
   constexpr int LPS = Tile::kLoadsPerStep;
   // separate arrays per stage, so that reads of one stage are seen not to
   // alias the buffer_load ... lds writes in flight to the others
@@ -487,10 +494,10 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
   const int l32 = lane & 31, half = lane >> 5;
   const int N = GU ? p.I : p.H;                              // weight rows
   const int K = GU ? p.H : p.I;                              // reduction length
-  const int tiles_n = (N + kMmRows - 1) / kMmRows;
+  const int tiles_n = (N + kWgRows - 1) / kWgRows;
   // workgroup b: XCD b % 8, j = b / 8; the tiles_n tiles of slot a share an XCD
   const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-  const int a = (j / tiles_n) * kXcds + xcd, n0 = (j % tiles_n) * kMmRows;
+  const int a = (j / tiles_n) * kXcds + xcd, n0 = (j % tiles_n) * kWgRows;
   if (a >= min(p.E, p.T * p.k)) return;
   const int e = slot_expert(p, a);
   if (e < 0) return;
@@ -507,6 +514,9 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
   t.lane = lane;
   const uint32_t code_row = (uint32_t)K / 2, scale_row = (uint32_t)K / 16;
   const uint32_t mat_codes = (uint32_t)N * code_row, mat_scales = (uint32_t)N * scale_row;
+  const int R = p.T * p.k;
+  t.rb = GU ? make_rsrc(p.x, (uint32_t)p.T * (uint32_t)p.H * 2u) : make_rsrc(p.h, (uint32_t)R * (uint32_t)p.I * 2u);
+  const int steps = K / kMmK;
   if constexpr (PACKED) {
     // packed matrices: gate and up of every expert, then down (tile order)
     const size_t gu_mat = packed_matrix_bytes(p.I, p.H);
@@ -514,31 +524,25 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
     const uint8_t* base[2] = {p.packed + (GU ? 0 : 2 * (size_t)p.E * gu_mat), p.packed + (size_t)p.E * gu_mat};
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
-      const uint8_t* me = base[m] + (size_t)e * mat;
+      const uint8_t* me = base[GU ? m : 0] + (size_t)e * mat;
       t.rc[m] = make_rsrc(me, (uint32_t)codes);
       t.rs[m] = make_rsrc(me + codes, (uint32_t)(mat - codes));
+      // gate/up: both operands from the workgroup's tile; down: tile m of it
+      const uint32_t tile_step0 = (uint32_t)(n0 / kMmRows + (GU ? 0 : m)) * (uint32_t)steps;
+      t.w_voff[m] = (uint32_t)(wave * 64 + lane) * 16 + tile_step0 * 4096u;
+      t.s_voff[m] = (uint32_t)(wave * 64 + lane) * 2 + tile_step0 * 512u;
     }
   } else {
     const uint8_t* wbase[2] = {GU ? p.wg : p.wd, p.wu};
     const uint8_t* sbase[2] = {GU ? p.sg : p.sd, p.su};
+    const int wrow = n0 + wave * 32 + l32;                   // this lane's weight row
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
       t.rc[m] = make_rsrc(wbase[m] + (size_t)e * mat_codes, mat_codes);
       t.rs[m] = make_rsrc(sbase[m] + (size_t)e * mat_scales, mat_scales);
+      t.w_voff[m] = (uint32_t)wrow * code_row + (uint32_t)half * 16;
+      t.s_voff[m] = (uint32_t)wrow * scale_row + (uint32_t)half * 2;
     }
-  }
-  const int R = p.T * p.k;
-  t.rb = GU ? make_rsrc(p.x, (uint32_t)p.T * (uint32_t)p.H * 2u) : make_rsrc(p.h, (uint32_t)R * (uint32_t)p.I * 2u);
-  const int steps = K / kMmK;
-  if constexpr (PACKED) {
-    t.w_voff = (uint32_t)(wave * 64 + lane) * 16;
-    t.s_voff = (uint32_t)(wave * 64 + lane) * 2;
-    t.tile_step0 = (uint32_t)(n0 / kMmRows) * (uint32_t)steps;
-  } else {
-    const int wrow = n0 + wave * 32 + l32;                   // this lane's weight row
-    t.w_voff = (uint32_t)wrow * code_row + (uint32_t)half * 16;
-    t.s_voff = (uint32_t)wrow * scale_row + (uint32_t)half * 2;
-    t.tile_step0 = 0;
   }
 
   for (int m0 = 0; m0 < cnt; m0 += kMmRoutes) {
@@ -633,9 +637,14 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
           *reinterpret_cast<uint2*>(p.h + (size_t)pos * p.I + n) = make_uint2(hv[0], hv[1]);
         } else {
           const float Gd = sload(p.gsc, e * 3 + 2);
-          *reinterpret_cast<float4*>(p.o + (size_t)pos * p.H + n) =
-              make_float4(acc[0][jt][4 * q] * Gd, acc[0][jt][4 * q + 1] * Gd, acc[0][jt][4 * q + 2] * Gd,
-                          acc[0][jt][4 * q + 3] * Gd);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) {
+            const int nm = n + m * kMmRows;
+            if (nm < N)
+              *reinterpret_cast<float4*>(p.o + (size_t)pos * p.H + nm) =
+                  make_float4(acc[m][jt][4 * q] * Gd, acc[m][jt][4 * q + 1] * Gd, acc[m][jt][4 * q + 2] * Gd,
+                              acc[m][jt][4 * q + 3] * Gd);
+          }
         }
       }
     }
@@ -849,6 +858,11 @@ constexpr long long kMaxGrid = 1 << 20;   // one workgroup per task; the shape l
 constexpr int kMfmaMinTokens = 64;      // batches from this size launch the MFMA kernels
 constexpr int kMfmaMinRoutes = 16;      // experts with this many routes use them (standard weight layout)
 constexpr int kMfmaMinRoutesPacked = 1; // with the packed copy: every expert of such a batch
+// Packed down kernel: two row tiles per wave when the batch averages at
+// least this many routes per expert slot (prefill-sized: each expert's h
+// rows are then staged half as often; with fewer, halving the workgroups
+// leaves too few of them in flight).
+constexpr int kDownSubMinRoutes = 16;
 
 template <int LG>
 void launch_gate_up(const FfnParams& p, long long tasks, hipStream_t s) {
@@ -945,8 +959,8 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
     }
     if (mfma) {
       const unsigned grid = (unsigned)(slots8 * ((I + kMmRows - 1) / kMmRows));
-      if (p.packed) ffn_mfma_kernel<true, true><<<grid, kMmThreads, 0, s>>>(p);
-      else ffn_mfma_kernel<true, false><<<grid, kMmThreads, 0, s>>>(p);
+      if (p.packed) ffn_mfma_kernel<true, true, 1><<<grid, kMmThreads, 0, s>>>(p);
+      else ffn_mfma_kernel<true, false, 1><<<grid, kMmThreads, 0, s>>>(p);
       if (launch_status() != MOE_OK) return MOE_ERR_HIP;
     }
   }
@@ -965,9 +979,16 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
   if (mfma) {
-    const unsigned grid = (unsigned)(slots8 * ((H + kMmRows - 1) / kMmRows));
-    if (p.packed) ffn_mfma_kernel<false, true><<<grid, kMmThreads, 0, s>>>(p);
-    else ffn_mfma_kernel<false, false><<<grid, kMmThreads, 0, s>>>(p);
+    if (p.packed && R >= (long long)kDownSubMinRoutes * slots) {
+      const unsigned grid = (unsigned)(slots8 * ((H + 2 * kMmRows - 1) / (2 * kMmRows)));
+      ffn_mfma_kernel<false, true, 2><<<grid, kMmThreads, 0, s>>>(p);
+    } else if (p.packed) {
+      const unsigned grid = (unsigned)(slots8 * ((H + kMmRows - 1) / kMmRows));
+      ffn_mfma_kernel<false, true, 1><<<grid, kMmThreads, 0, s>>>(p);
+    } else {
+      const unsigned grid = (unsigned)(slots8 * ((H + kMmRows - 1) / kMmRows));
+      ffn_mfma_kernel<false, false, 1><<<grid, kMmThreads, 0, s>>>(p);
+    }
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
   const long long cblocks = (long long)T * ((H + kCombineCols - 1) / kCombineCols);
