@@ -83,9 +83,9 @@ def test_ragged_token_counts(shape, T, path):
 # Shapes whose row tiles run past the matrix: with H = 256 a gate/up tile
 # spans 128 rows of I and a down tile 512-1024 rows of H, so rows past I (or
 # H) must read as zeros and never be stored.  T picks the kernels: 8 tokens
-# the fused down/unroute kernel, 40 the per-expert down tiles (R > 128), 128
-# the MFMA tiles as well (experts with >= 16 routes; 128 weight rows per tile
-# against I = 64).
+# the fused down/unroute kernel, 40 the per-expert down tiles (R > 128; with
+# E = 4 each expert's row tiles loop over ~40 routes), 128 the MFMA tiles as
+# well (128 weight rows per tile against I = 64).
 RAGGED_TILE_SHAPES = [
     # (H, I, E, k, T)
     (256, 64, 16, 4, 8),
@@ -94,6 +94,7 @@ RAGGED_TILE_SHAPES = [
     (128, 32, 8, 2, 70),
     (32, 32, 4, 2, 10),
     (32, 64, 6, 3, 50),
+    (256, 64, 4, 4, 40),     # ~40 routes per expert in a batch under 64 tokens
 ]
 
 
@@ -127,17 +128,18 @@ def test_k_equals_E(path):
     assert_output(g["y"], y, "k=E")
 
 
+@pytest.mark.parametrize("path", ["step", "packed"])
 @pytest.mark.parametrize("T", [12, 33])
-def test_all_tokens_on_same_experts(T):
+def test_all_tokens_on_same_experts(T, path):
     """Every token routed to the same 10 experts: T routes per expert, so the
     kernels loop over the expert's tokens (T = 12: the small-batch routing
     kernel and the fused down/unroute kernel; T = 33: the larger-batch
-    kernels)."""
+    kernels), on both weight layouts."""
     wl = make_workload("decode_t4", T=T, x_seed=3)
     chosen = [7, 100, 101, 250, 311, 312, 400, 450, 500, 511]
     bias = np.zeros(wl.E, np.float32)
     bias[chosen] = 50.0
-    g = run_gpu(wl.x, wl.logits, bias, wl.bank, wl.k)
+    g = run_gpu(wl.x, wl.logits, bias, wl.bank, wl.k, path=path)
     toks = [0, T // 2, T - 1]
     idx, w, b, y = oracle_all(wl.x, wl.logits, bias, wl.bank, wl.k, tokens=toks)
     assert int(b["n_active"]) == 10 and sorted(np.unique(idx)) == chosen
@@ -146,8 +148,9 @@ def test_all_tokens_on_same_experts(T):
     assert_output(g["y"][toks], y, "all-equal experts")
 
 
+@pytest.mark.parametrize("path", ["step", "packed"])
 @pytest.mark.parametrize("T", [12, 40])
-def test_all_routes_on_distinct_experts(T):
+def test_all_routes_on_distinct_experts(T, path):
     wl = make_workload("decode_t4", T=T, x_seed=4)
     k, E = 10, 512
     logits = np.zeros((T, E), np.float32)
@@ -155,7 +158,7 @@ def test_all_routes_on_distinct_experts(T):
     perm = rng.permutation(E)[: T * k].reshape(T, k)
     for t in range(T):
         logits[t, perm[t]] = 10.0 - np.arange(k, dtype=np.float32) * 0.5
-    g = run_gpu(wl.x, logits, None, wl.bank, k)
+    g = run_gpu(wl.x, logits, None, wl.bank, k, path=path)
     idx, w, b, y = oracle_all(wl.x, logits, None, wl.bank, k, tokens=[0, T - 1])
     assert np.all(b["expert_count"][b["expert_count"] > 0] == 1) and int(b["n_active"]) == T * k
     assert_route(g, idx, w)
