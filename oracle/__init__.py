@@ -7,6 +7,7 @@ it.  It is plain and slow on purpose: fp64 NumPy, per-route loops, one
 library matmul per projection, no blocking or fusion.
 
 What it computes (one routed-MoE step of a decode/verify batch):
+  router_logits   the router projection that produces the routing logits
   route_topk      softmax top-k routing with renormalised gate weights
   bucket_routes   per-expert route counts, offsets, active list, stable order
   moe_output      per route: SiLU(W_gate x) * (W_up x), then W_down; weighted
@@ -31,6 +32,7 @@ from .formats import (
     dequant_nvfp4,
 )
 from .route import route_topk, selection_order, renormalised_weights
+from .router import router_logits
 from .buckets import bucket_routes
 from .ffn import expert_route_output, moe_output, ExpertDecoder
 
@@ -40,6 +42,7 @@ __all__ = [
     "bf16_bits_to_f64",
     "unpack_nibbles",
     "dequant_nvfp4",
+    "router_logits",
     "route_topk",
     "selection_order",
     "renormalised_weights",

@@ -307,10 +307,57 @@ def check_symmetries():
     assert np.array_equal(yd[-1], yd[0])
 
 
+# ---------------------------------------------------------------- router projection
+
+def check_router_integers_exact():
+    """Integer activations (exact in bf16) and integer weights: every sum is an
+    integer below 2^24, so the logits are those integers exactly; T, E and H
+    all differ, so a transposed operand cannot pass."""
+    rng = np.random.default_rng(20)
+    T, E, H = 3, 5, 64
+    xi = rng.integers(-8, 9, size=(T, H))
+    wi = rng.integers(-100, 101, size=(E, H))
+    x_bits = (xi.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(bf16_values(x_bits), xi.astype(np.float64))
+    got = oracle.router_logits(x_bits, wi.astype(np.float32))
+    want = np.array([[int(np.dot(xi[t], wi[e])) for e in range(E)] for t in range(T)], dtype=np.float32)
+    assert got.dtype == np.float32 and got.shape == (T, E)
+    assert np.array_equal(got, want)
+
+
+def _round_f32_exact(q):
+    """Round a Fraction to the nearest float32, ties to even mantissa."""
+    from fractions import Fraction
+    if q == 0:
+        return np.float32(0.0)
+    c = np.float32(float(q))
+    cands = [np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))]
+    return min(cands, key=lambda f: (abs(Fraction(float(f)) - q), int(np.float32(f).view(np.uint32)) & 1))
+
+
+def check_router_exact_rounding():
+    """Random bf16 activations and fp32 weights: each logit is the float32
+    nearest the exact rational sum (fractions.Fraction), i.e. one rounding."""
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    for _ in range(6):
+        T, E, H = 3, 4, 48
+        xf = rng.standard_normal((T, H)).astype(np.float32)
+        x_bits = (xf.view(np.uint32) >> 16).astype(np.uint16)
+        w = (rng.standard_normal((E, H)) / np.sqrt(H)).astype(np.float32)
+        got = oracle.router_logits(x_bits, w)
+        xv = bf16_values(x_bits)
+        for t in range(T):
+            for e in range(E):
+                q = sum((Fraction(float(xv[t, h])) * Fraction(float(w[e, h])) for h in range(H)), Fraction(0))
+                assert got[t, e] == _round_f32_exact(q), (t, e, got[t, e], float(q))
+
+
 ALL_PINS = [
     check_e2m1, check_e4m3, check_products_exact_in_bf16, check_dequant_layout,
     check_routing_golden, check_topk_bruteforce, check_weight_invariants,
     check_buckets, check_ffn_golden, check_single_expert_is_dense,
     check_mixture_matches_dense, check_zero_input, check_all_equal_experts,
     check_all_disjoint_experts, check_symmetries,
+    check_router_integers_exact, check_router_exact_rounding,
 ]

@@ -15,6 +15,7 @@ import oracle.buckets
 import oracle.ffn
 import oracle.formats
 import oracle.route
+import oracle.router
 import pins
 
 
@@ -94,3 +95,26 @@ def test_wrong_scale_block(monkeypatch):
     monkeypatch.setattr(oracle.ffn, "dequant_nvfp4", shifted)
     _expect_failure([pins.check_ffn_golden, pins.check_dequant_layout,
                      pins.check_single_expert_is_dense])
+
+
+def test_router_summed_in_fp32(monkeypatch):
+    def fp32_sum(x_bf16, w_router):
+        x = oracle.formats.bf16_bits_to_f64(np.asarray(x_bf16, np.uint16)).astype(np.float32)
+        w = np.asarray(w_router, np.float32)
+        out = np.zeros((x.shape[0], w.shape[0]), np.float32)
+        for h in range(x.shape[1]):                     # one fp32 rounding per term
+            out = (out + np.outer(x[:, h], w[:, h])).astype(np.float32)
+        return out
+    monkeypatch.setattr(oracle.router, "router_logits", fp32_sum)
+    monkeypatch.setattr(oracle, "router_logits", fp32_sum)
+    _expect_failure([pins.check_router_exact_rounding])
+
+
+def test_router_transposed(monkeypatch):
+    def transposed(x_bf16, w_router):
+        x = oracle.formats.bf16_bits_to_f64(np.asarray(x_bf16, np.uint16))
+        w = np.asarray(w_router, np.float32).astype(np.float64)
+        return (x @ w.reshape(w.shape[1], w.shape[0])).astype(np.float32)
+    monkeypatch.setattr(oracle.router, "router_logits", transposed)
+    monkeypatch.setattr(oracle, "router_logits", transposed)
+    _expect_failure([pins.check_router_integers_exact])
