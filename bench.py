@@ -21,6 +21,11 @@ measured step time; `us_per_step` is the step time.  `roofline` covers the
 dominant kernel, the gate/up projection: HIP events on its stream around a
 graph of back-to-back launches of that kernel alone.
 `cpu_baseline` is the fp64 CPU oracle timed on this host on a bounded sample.
+`router` times the router projection that produces the logits
+(moe_router_logits, outside the step) on the workload's tokens, over
+rotating copies of the router weights so they are read from HBM, against
+its own roofline (HBM for small batches, fp64 arithmetic for large ones),
+with the oracle's projection timed on the host beside it.
 """
 
 from __future__ import annotations
@@ -58,6 +63,9 @@ def parse():
                     help="launches of the dominant kernel timed with events for the roofline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle sample budget (0 disables the cpu_baseline leg)")
+    ap.add_argument("--router-copies", type=int, default=80,
+                    help="router weight copies rotated in the router leg (80 x 4 MB: beyond the 256 MB "
+                         "Infinity Cache, so each call reads its weights from HBM); 0 skips the leg")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the bench, run a plain device-to-device copy of this many MiB three times "
                          "(the known-size kernel that calibrates FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -90,6 +98,67 @@ def measured_traffic(workload: str):
     if rec.get("workload") != workload or rec.get("sources_sha256") != kernel_sources_digest():
         return None
     return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
+
+
+FP64_PEAK_TFLOPS = 78.6
+
+
+def router_leg(args, cfg, wl, dev):
+    """The router projection (moe_router_logits) on the workload's tokens:
+    graph-replayed calls over rotating copies of the router weights, HIP
+    events on the library's stream; the bound is HBM for small batches (the
+    weights, E*H*4 bytes, dominate) and fp64 arithmetic for large ones
+    (2*T*H*E flop).  The oracle's router projection is timed on the host
+    beside it."""
+    import numpy as np
+    import torch
+    import oracle
+    import sparse_moe_expert_amd as sme
+    T, H, E = cfg.T, cfg.H, cfg.E
+    n = args.router_copies
+    x = torch.from_numpy(wl.x.view(np.int16)).to(dev)
+    w0 = torch.from_numpy(wl.w_router).to(dev)
+    ws = [w0] + [torch.roll(w0, shifts=131 * i, dims=0).contiguous() for i in range(1, n)]
+    outs = [torch.empty((T, E), dtype=torch.float32, device=dev) for _ in range(2)]
+    for i in range(n):
+        sme.moe_router_logits(x, ws[i], outs[i % 2])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            sme.moe_router_logits(x, ws[i], outs[i % 2])
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, 200 // n) if T <= 64 else 1
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * n)
+    wbytes = E * H * 4 + T * H * 2 + T * E * 4
+    flop = 2.0 * T * H * E
+    gbps = wbytes / us / 1e3
+    tflops = flop / us / 1e6
+    kernel = "router_rows_kernel" if T <= 64 else "router_logits_kernel"
+    bound = "hbm" if T <= 64 else "fp64"
+    # the oracle's projection on the same tokens (a few calls, host cores)
+    t0 = time.perf_counter()
+    calls = 0
+    while calls == 0 or time.perf_counter() - t0 < 0.5:
+        oracle.router_logits(wl.x, wl.w_router)
+        calls += 1
+    cpu_us = (time.perf_counter() - t0) / calls * 1e6
+    return {"kernel": kernel, "us_per_call": round(us, 3), "bound": bound,
+            "achieved": round(gbps, 1) if bound == "hbm" else round(tflops, 3),
+            "peak": HBM_PEAK_GBPS if bound == "hbm" else FP64_PEAK_TFLOPS,
+            "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4) if bound == "hbm" else round(tflops / FP64_PEAK_TFLOPS, 4),
+            "bytes_per_call": int(wbytes), "flop_per_call": int(flop), "calls": reps * n,
+            "weight_copies": n, "cpu_oracle_us_per_call": round(cpu_us, 1)}
 
 
 def cpu_baseline(cfg, budget_s: float, expert_bytes: int):
@@ -260,6 +329,9 @@ def main():
                      "avg_launch_us": round(avg * 1e6, 3),
                      "bytes_per_launch": int(dom_bytes), "launches": n_dom},
     }
+    if args.router_copies > 0:
+        log(f"[bench] router projection leg ({args.router_copies} weight copies)")
+        out["router"] = router_leg(args, cfg, wls[0], dev)
     if args.copy_mb > 0:
         nbytes = args.copy_mb << 20
         src = torch.ones(nbytes, dtype=torch.uint8, device=dev)

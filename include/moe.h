@@ -11,7 +11,8 @@
  * these calls (the MonoMoE host wrapper takes precomputed router logits and
  * the SM70 design note keeps the router GEMV as an explicit prerequisite:
  * page "Persistent execution for Flash-Next GGUF on SM70", sections "MonoMoE"
- * and "First implementation boundary").
+ * and "First implementation boundary"); moe_router_logits computes it on the
+ * GPU for callers that start from the tokens.
  *
  * Conventions for every call
  *  - Tensor pointers are DEVICE pointers owned by the caller, row-major and
@@ -51,6 +52,32 @@ typedef enum {
   MOE_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < moe_expert_ffn_workspace_size() */
   MOE_ERR_HIP = 6                  /* a HIP runtime call failed (launch or device query) */
 } moe_status;
+
+/*
+ * moe_router_logits — the router projection: tokens -> routing logits.
+ *
+ * Defines logits[t,e] = fl32( sum_h x[t,h] * w_router[e,h] ): every bf16
+ * activation and fp32 weight is exact in fp64, so is each product; the sum
+ * is accumulated in fp64 and rounded once to fp32.  The router is this
+ * projection followed by the selection of moe_route_topk (page "Persistent
+ * execution for Flash-Next GGUF on SM70", section "Router: selection and
+ * expert-task production", which also notes that the projection's results
+ * span many workgroups and need an explicit hand-off to the selection: here
+ * the boundary between this call and the next on the stream).  The fp64 sum
+ * is taken in a fixed order, so results are bitwise reproducible; against
+ * the exactly rounded value a logit can differ by one fp32 ulp, when the
+ * exact sum lies within the fp64 accumulation error of a rounding boundary.
+ *
+ *   x         [T, H] bf16 bits     in
+ *   w_router  [E, H] fp32          in
+ *   logits    [T, E] fp32          out
+ * Shapes: T >= 0 (T = 0 launches nothing), E >= 1, H >= 8 and a multiple of
+ * 8 (else MOE_ERR_INVALID_SHAPE).  Envelope: H <= 4096, E <= 1024,
+ * T <= 524280 (else MOE_ERR_UNSUPPORTED).
+ */
+moe_status moe_router_logits(const uint16_t* x, const float* w_router,
+                             int T, int H, int E, float* logits,
+                             void* stream);
 
 /*
  * moe_route_topk — softmax top-k routing with renormalised gate weights.

@@ -19,6 +19,7 @@ from ._lib import (
     moe_expert_ffn,
     moe_expert_ffn_workspace_size,
     moe_route_bucket,
+    moe_router_logits,
     moe_route_topk,
     moe_status_string,
     moe_packed_weights_size,
@@ -41,6 +42,7 @@ __all__ = [
     "moe_expert_ffn",
     "moe_expert_ffn_workspace_size",
     "moe_route_bucket",
+    "moe_router_logits",
     "moe_route_topk",
     "moe_status_string",
     "moe_packed_weights_size",

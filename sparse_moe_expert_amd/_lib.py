@@ -31,6 +31,7 @@ MOE_STATUS = {
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 SIGNATURES = {
+    "moe_router_logits": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "moe_route_topk": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
     "moe_bucket_routes": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "moe_route_bucket": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -100,6 +101,23 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def moe_router_logits(x: torch.Tensor, w_router: torch.Tensor,
+                      logits: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Router logits fp32 [T,E] = fl32(x @ w_router^T) from bf16 x [T,H] (or its
+    uint16 bits) and fp32 w_router [E,H], summed in fp64 on the GPU."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    x = _check_x(x)
+    _need(w_router, "w_router", torch.float32, (E, H), dev)
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    _need(logits, "logits", torch.float32, (T, E), dev)
+    st = load_library().moe_router_logits(_ptr(x), _ptr(w_router), T, H, E, _ptr(logits), _stream(dev))
+    _check("moe_router_logits", st)
+    return logits
 
 
 def moe_route_topk(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int,

@@ -1,0 +1,209 @@
+// moe_router_logits: the router projection that produces the routing logits.
+//
+// logits[t, e] = fl32( sum_h x[t, h] * W_r[e, h] ).  The router is a
+// projection followed by the selection (page "Persistent execution for
+// Flash-Next GGUF on SM70", section "Router: selection and expert-task
+// production"); its projection results span many workgroups, and the
+// kernel boundary before moe_route_topk / moe_route_bucket is the hand-off
+// to the selection.  Each bf16 x fp32 product is exact in fp64 (8 + 24
+// significant bits), the sum is accumulated in fp64 and rounded once.
+//
+// gfx950 layout (larger batches): wavefront w of workgroup (b, c) owns expert
+// row e = 4b + w and the workgroup's chunk of up to 8 tokens (rows staged in
+// LDS).  Lane l
+// holds the row's values h = 4(l + 64j) as fp64, converted once; per token it
+// forms a partial sum over those 4*NCH values with v_fma_f64, and a
+// fixed-order butterfly over the wavefront adds the 64 partials (every lane
+// ends with the same bits).
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRtThreads = 256;
+constexpr int kRtWaves = kRtThreads / kWave;
+constexpr int kRtTokens = 8;           // tokens per workgroup
+constexpr int kRtMaxH = 4096;          // 16 four-value pieces per lane
+constexpr int kRsMaxTokens = 64;       // batches up to this size: one workgroup per expert row
+
+__device__ __forceinline__ double bf16_lo(uint32_t v) { return (double)__uint_as_float(v << 16); }
+__device__ __forceinline__ double bf16_hi(uint32_t v) { return (double)__uint_as_float(v & 0xFFFF0000u); }
+
+// fp64 value moved by one DPP pattern (each 32-bit half with the same control).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the wavefront in a fixed order; every lane gets the same bits.
+// DPP steps sum each 16-lane row into all of its lanes; v_permlane16_swap and
+// v_permlane32_swap (each applied to both halves) then add the rows pairwise:
+// ((row0 + row1) + (row2 + row3)) - lanes of the other half form the same
+// sums with the operands swapped, which fp64 addition does not distinguish.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f64<0x124>(v);   // row_ror:4
+  v += dpp_f64<0x128>(v);   // row_ror:8
+  auto swap_add = [](double a, bool rows32) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, a);
+    const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+    const auto l = rows32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                          : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = rows32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                          : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const double x0 = __builtin_bit_cast(double, ((uint64_t)h[0] << 32) | l[0]);
+    const double x1 = __builtin_bit_cast(double, ((uint64_t)h[1] << 32) | l[1]);
+    return x0 + x1;
+  };
+  v = swap_add(v, false);   // rows (0+1), (2+3) in every lane of their pair
+  return swap_add(v, true); // (0+1) + (2+3)
+}
+
+// Small batches (T <= 64): one workgroup per expert row, so the row's loads
+// and products spread over 256 lanes.  Thread i holds the row's values
+// h = 8(i + 256c) .. +8 as fp64 and reads the same 16 bytes of each token's
+// activation row directly (cached: every workgroup reads the same x), eight
+// tokens at a time; wavefront sums go to LDS and are added in wave order.
+constexpr int kRsGroup = 8;
+
+template <int NCH>
+__global__ __launch_bounds__(kRtThreads) void router_rows_kernel(const uint16_t* __restrict__ x,
+                                                                 const float* __restrict__ w, int T, int H, int E,
+                                                                 float* __restrict__ logits) {
+  __shared__ double s_part[kRtWaves][kRsGroup];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int e = blockIdx.x;
+  double wd[NCH][8];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int h0 = 8 * (tid + kRtThreads * c);
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f), b = a;
+    if (h0 < H) {
+      a = *reinterpret_cast<const float4*>(w + (size_t)e * H + h0);
+      b = *reinterpret_cast<const float4*>(w + (size_t)e * H + h0 + 4);
+    }
+    wd[c][0] = a.x; wd[c][1] = a.y; wd[c][2] = a.z; wd[c][3] = a.w;
+    wd[c][4] = b.x; wd[c][5] = b.y; wd[c][6] = b.z; wd[c][7] = b.w;
+  }
+  for (int t0 = 0; t0 < T; t0 += kRsGroup) {
+    const int nt = min(kRsGroup, T - t0);
+    uint4 xv[kRsGroup][NCH];
+#pragma unroll
+    for (int g = 0; g < kRsGroup; ++g)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int h0 = 8 * (tid + kRtThreads * c);
+        xv[g][c] = make_uint4(0u, 0u, 0u, 0u);
+        if (g < nt && h0 < H) xv[g][c] = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + g) * H + h0);
+      }
+    double acc[kRsGroup];
+#pragma unroll
+    for (int g = 0; g < kRsGroup; ++g) {
+      double a = 0.0;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t q[4] = {xv[g][c].x, xv[g][c].y, xv[g][c].z, xv[g][c].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a = fma(wd[c][2 * i], bf16_lo(q[i]), a);
+          a = fma(wd[c][2 * i + 1], bf16_hi(q[i]), a);
+        }
+      }
+      acc[g] = wave_sum_f64(a);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < kRsGroup; ++g) s_part[wave][g] = acc[g];
+    }
+    __syncthreads();
+    if (tid < nt) {
+      static_assert(kRtWaves == 4, "the wave partials are added pairwise");
+      const double sum = (s_part[0][tid] + s_part[1][tid]) + (s_part[2][tid] + s_part[3][tid]);
+      logits[(size_t)(t0 + tid) * E + e] = (float)sum;
+    }
+    __syncthreads();                                   // s_part reused by the next group
+  }
+}
+
+template <int NCH>
+__global__ __launch_bounds__(kRtThreads) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                                   const float* __restrict__ w, int T, int H, int E,
+                                                                   float* __restrict__ logits) {
+  extern __shared__ __align__(16) uint16_t s_x[];   // [kRtTokens][H] bf16
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = blockIdx.y * kRtTokens;
+  const int nt = min(kRtTokens, T - t0);
+  const int e = blockIdx.x * kRtWaves + wave;
+  const int nq = H / 4;                              // four-value pieces of a row
+  // the wave's weight row (loads issued before the x staging completes)
+  double wd[NCH][4];
+  if (e < E) {
+    const float4* wr = reinterpret_cast<const float4*>(w + (size_t)e * H);
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int q = lane + kWave * j;
+      const float4 v = q < nq ? wr[q] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      wd[j][0] = v.x; wd[j][1] = v.y; wd[j][2] = v.z; wd[j][3] = v.w;
+    }
+  }
+  const int pieces = nt * (H / 8);                   // 16-byte pieces of the chunk's x rows
+  const uint4* xs = reinterpret_cast<const uint4*>(x + (size_t)t0 * H);
+  for (int i = threadIdx.x; i < pieces; i += kRtThreads) reinterpret_cast<uint4*>(s_x)[i] = xs[i];
+  __syncthreads();
+  if (e >= E) return;
+  for (int t = 0; t < nt; ++t) {
+    const uint16_t* xr = s_x + (size_t)t * H;
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int q = lane + kWave * j;
+      if (q < nq) {
+        const uint2 b = *reinterpret_cast<const uint2*>(xr + 4 * q);
+        acc = fma(wd[j][0], bf16_lo(b.x), acc);
+        acc = fma(wd[j][1], bf16_hi(b.x), acc);
+        acc = fma(wd[j][2], bf16_lo(b.y), acc);
+        acc = fma(wd[j][3], bf16_hi(b.y), acc);
+      }
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) logits[(size_t)(t0 + t) * E + e] = (float)acc;
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_router_logits(const uint16_t* x, const float* w_router, int T, int H, int E,
+                                        float* logits, void* stream) {
+  using namespace moe;
+  if (T < 0 || E < 1 || H < 8 || H % 8 != 0) return MOE_ERR_INVALID_SHAPE;
+  if (H > kRtMaxH || E > 1024) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !logits) return MOE_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits)) return MOE_ERR_MISALIGNED;
+  const long long chunks = ((long long)T + kRtTokens - 1) / kRtTokens;
+  if (chunks > 65535) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T <= kRsMaxTokens) {
+    const int nc = (H / 8 + kRtThreads - 1) / kRtThreads;   // 16-byte pieces per thread
+    if (nc <= 1) router_rows_kernel<1><<<E, kRtThreads, 0, s>>>(x, w_router, T, H, E, logits);
+    else router_rows_kernel<2><<<E, kRtThreads, 0, s>>>(x, w_router, T, H, E, logits);
+    return launch_status();
+  }
+  const dim3 grid((unsigned)((E + kRtWaves - 1) / kRtWaves), (unsigned)chunks);
+  const size_t dyn = (size_t)kRtTokens * H * 2;
+  const int nch = (H / 4 + kWave - 1) / kWave;       // pieces per lane
+  if (nch <= 1) router_logits_kernel<1><<<grid, kRtThreads, dyn, s>>>(x, w_router, T, H, E, logits);
+  else if (nch <= 2) router_logits_kernel<2><<<grid, kRtThreads, dyn, s>>>(x, w_router, T, H, E, logits);
+  else if (nch <= 4) router_logits_kernel<4><<<grid, kRtThreads, dyn, s>>>(x, w_router, T, H, E, logits);
+  else if (nch <= 8) router_logits_kernel<8><<<grid, kRtThreads, dyn, s>>>(x, w_router, T, H, E, logits);
+  else router_logits_kernel<16><<<grid, kRtThreads, dyn, s>>>(x, w_router, T, H, E, logits);
+  return launch_status();
+}

@@ -59,6 +59,20 @@ def test_route_topk_host_checks(lib):
     assert f(P(258), None, 4, 8, 2, A, A, None) == 4
 
 
+def test_router_logits_host_checks(lib):
+    f = lib.moe_router_logits
+    assert f(A, A, -1, 64, 8, A, None) == 2         # T < 0
+    assert f(A, A, 4, 60, 8, A, None) == 2          # H not a multiple of 8
+    assert f(A, A, 4, 0, 8, A, None) == 2           # H < 8
+    assert f(A, A, 4, 64, 0, A, None) == 2          # E < 1
+    assert f(A, A, 4, 8192, 8, A, None) == 3        # H beyond envelope
+    assert f(A, A, 4, 64, 2048, A, None) == 3       # E beyond envelope
+    assert f(A, A, 0, 64, 8, A, None) == 0          # T = 0: nothing launched
+    assert f(None, A, 4, 64, 8, A, None) == 1
+    assert f(A, A, 4, 64, 8, None, None) == 1
+    assert f(A, P(258), 4, 64, 8, A, None) == 4
+
+
 def test_bucket_routes_host_checks(lib):
     f = lib.moe_bucket_routes
     assert f(A, 4, 8, 9, A, A, A, A, A, A, None) == 2
