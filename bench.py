@@ -25,7 +25,10 @@ graph of back-to-back launches of that kernel alone.
 (moe_router_logits, outside the step) on the workload's tokens, over
 rotating copies of the router weights so they are read from HBM, against
 its own roofline (HBM for small batches, fp64 arithmetic for large ones),
-with the oracle's projection timed on the host beside it.
+with the oracle's projection timed on the host beside it.  `layers` chains
+L layers (router projection + step per layer, each on its own weight bank
+and router weights) in one graph, each layer's input the previous input
+plus the previous output (a residual stream).
 """
 
 from __future__ import annotations
@@ -66,6 +69,9 @@ def parse():
     ap.add_argument("--router-copies", type=int, default=80,
                     help="router weight copies rotated in the router leg (80 x 4 MB: beyond the 256 MB "
                          "Infinity Cache, so each call reads its weights from HBM); 0 skips the leg")
+    ap.add_argument("--layers", type=int, default=8,
+                    help="layers of the chained leg: router projection + routed step per layer, layer l+1's "
+                         "input = layer l's input + its output, layer l on weight bank l (0 skips the leg)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the bench, run a plain device-to-device copy of this many MiB three times "
                          "(the known-size kernel that calibrates FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -159,6 +165,62 @@ def router_leg(args, cfg, wl, dev):
             "frac": round(gbps / HBM_PEAK_GBPS, 4) if bound == "hbm" else round(tflops / FP64_PEAK_TFLOPS, 4),
             "bytes_per_call": int(wbytes), "flop_per_call": int(flop), "calls": reps * n,
             "weight_copies": n, "cpu_oracle_us_per_call": round(cpu_us, 1)}
+
+
+def layers_leg(args, cfg, x0, banks, pks, bias, dev, expert_bytes: int):
+    """L routed-MoE layers chained in one graph: per layer the router
+    projection (its own router weights) and one step on weight bank l; the
+    input of layer l+1 is layer l's input plus its bf16 output.
+    Timed per pass with HIP events; bytes are the unique expert bytes of
+    every layer plus its router weights."""
+    import numpy as np
+    import torch
+    import sparse_moe_expert_amd as sme
+    from moe_inputs import make_workload
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    L = min(args.layers, len(banks))
+    w_rs = [torch.from_numpy(make_workload(cfg.name, seed=cfg.seed + 100 + l, with_bank=False).w_router).to(dev)
+            for l in range(L)]
+    steps = [sme.MoeStep(T, H, I, E, k, dev, path=args.path) for _ in range(L)]
+    logits = [torch.empty((T, E), dtype=torch.float32, device=dev) for _ in range(L)]
+
+    # the residual stream: layer l's input is the sum of the first input and
+    # the outputs of layers 0..l-1 (a bf16 add by torch, outside the library);
+    # without it the outputs shrink layer by layer until the routing degenerates
+    xs_l = [x0.view(torch.bfloat16)] + [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(L - 1)]
+
+    def one_pass():
+        for l in range(L):
+            sme.moe_router_logits(xs_l[l], w_rs[l], logits[l])
+            steps[l].run(xs_l[l], logits[l], bias, banks[l], packed=pks[l])
+            if l + 1 < L:
+                torch.add(xs_l[l], steps[l].y, out=xs_l[l + 1])
+
+    one_pass()
+    torch.cuda.synchronize()
+    n_unique = [int(st.buckets.n_active.item()) for st in steps]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        one_pass()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // (4 * L))
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = float(np.sum(n_unique)) * expert_bytes + L * E * H * 4
+    return {"layers": L, "us_per_pass": round(us, 2), "us_per_layer": round(us / L, 3),
+            "effective_TBps": round(nbytes / us / 1e6, 4), "unique_experts_per_layer": n_unique,
+            "bytes_per_pass": int(nbytes), "passes": reps,
+            "per_layer": "router projection + route/bucket + expert FFN (library) + residual add (torch, bf16); "
+                         "the input of layer l+1 is the input of layer l plus its output"}
 
 
 def cpu_baseline(cfg, budget_s: float, expert_bytes: int):
@@ -332,6 +394,9 @@ def main():
     if args.router_copies > 0:
         log(f"[bench] router projection leg ({args.router_copies} weight copies)")
         out["router"] = router_leg(args, cfg, wls[0], dev)
+    if args.layers > 0:
+        log(f"[bench] chained layers leg ({min(args.layers, NB)} layers)")
+        out["layers"] = layers_leg(args, cfg, xs[0], banks, pks, bias, dev, expert_bytes)
     if args.copy_mb > 0:
         nbytes = args.copy_mb << 20
         src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
