@@ -73,7 +73,7 @@ typedef enum {
  *   logits    [T, E] fp32          out
  * Shapes: T >= 0 (T = 0 launches nothing), E >= 1, H >= 8 and a multiple of
  * 8 (else MOE_ERR_INVALID_SHAPE).  Envelope: H <= 4096, E <= 1024,
- * T <= 524280 (else MOE_ERR_UNSUPPORTED).
+ * T <= 4194240 (else MOE_ERR_UNSUPPORTED).
  */
 moe_status moe_router_logits(const uint16_t* x, const float* w_router,
                              int T, int H, int E, float* logits,

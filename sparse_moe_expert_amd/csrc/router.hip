@@ -8,13 +8,10 @@
 // to the selection.  Each bf16 x fp32 product is exact in fp64 (8 + 24
 // significant bits), the sum is accumulated in fp64 and rounded once.
 //
-// gfx950 layout (larger batches): wavefront w of workgroup (b, c) owns expert
-// row e = 4b + w and the workgroup's chunk of up to 8 tokens (rows staged in
-// LDS).  Lane l
-// holds the row's values h = 4(l + 64j) as fp64, converted once; per token it
-// forms a partial sum over those 4*NCH values with v_fma_f64, and a
-// fixed-order butterfly over the wavefront adds the 64 partials (every lane
-// ends with the same bits).
+// Three kernels (gfx950): batches up to 64 tokens spread each expert row over
+// one 256-lane workgroup (the router weights dominate the bytes); mid-size
+// batches give each expert row one wavefront and chunks of 8 tokens; from
+// 1024 tokens a register-tiled fp64 product (the arithmetic dominates).
 #include "moe_common.h"
 
 namespace moe {
@@ -22,8 +19,7 @@ namespace {
 
 constexpr int kRtThreads = 256;
 constexpr int kRtWaves = kRtThreads / kWave;
-constexpr int kRtTokens = 8;           // tokens per workgroup
-constexpr int kRtMaxH = 4096;          // 16 four-value pieces per lane
+constexpr int kRtMaxH = 4096;          // the small-batch kernel: two 8-value pieces per thread
 constexpr int kRsMaxTokens = 64;       // batches up to this size: one workgroup per expert row
 
 __device__ __forceinline__ double bf16_lo(uint32_t v) { return (double)__uint_as_float(v << 16); }
@@ -130,6 +126,13 @@ __global__ __launch_bounds__(kRtThreads) void router_rows_kernel(const uint16_t*
   }
 }
 
+// Mid-size batches (64 < T < 1024): wavefront w of workgroup (b, c) owns
+// expert row e = 4b + w and the workgroup's chunk of up to 8 tokens (rows
+// staged in LDS); lane l holds the row's values h = 4(l + 64j) as fp64,
+// converted once, forms a partial sum per token with v_fma_f64, and a
+// fixed-order butterfly over the wavefront adds the 64 partials.
+constexpr int kRtTokens = 8;           // tokens per workgroup of the chunked kernel
+
 template <int NCH>
 __global__ __launch_bounds__(kRtThreads) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                                    const float* __restrict__ w, int T, int H, int E,
@@ -177,6 +180,80 @@ __global__ __launch_bounds__(kRtThreads) void router_logits_kernel(const uint16_
   }
 }
 
+// Large batches (T >= 1024): a register-tiled fp64 product.  A workgroup owns 64 tokens x
+// 128 experts; thread (g, f) = (tid / 16, tid % 16) accumulates tokens
+// 4g..4g+3 x experts 8f..8f+7 in 32 fp64 registers.  K advances 16 at a
+// time: the chunk's activations and weights are converted to fp64 into LDS
+// (k-major, so a thread's 4 tokens and 8 experts are contiguous), then each
+// k adds 32 products per thread.  Each output is summed in k order.
+constexpr int kRgTokens = 64, kRgExperts = 128, kRgK = 16;
+constexpr int kRgMinTokens = 1024;     // from here the tiled product has enough workgroups
+
+__global__ __launch_bounds__(kRtThreads) void router_gemm_kernel(const uint16_t* __restrict__ x,
+                                                                 const float* __restrict__ w, int T, int H, int E,
+                                                                 float* __restrict__ logits) {
+  __shared__ __align__(16) double s_x[kRgK][kRgTokens];
+  __shared__ __align__(16) double s_w[kRgK][kRgExperts];
+  const int tid = threadIdx.x;
+  const int g = tid / 16, f = tid % 16;
+  const int t0 = blockIdx.y * kRgTokens, e0 = blockIdx.x * kRgExperts;
+  // staging roles: x piece (token tid/4, k 4*(tid%4)..+4), w piece (expert tid/2, k 8*(tid%2)..+8)
+  const int xt = tid / 4, xk = 4 * (tid % 4);
+  const int we = tid / 2, wk = 8 * (tid % 2);
+  double acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+  // global reads of one chunk (zeros past T, E or H; H is a multiple of 8)
+  uint2 xb;
+  float4 wa, wb;
+  auto fetch = [&](int k0) {
+    xb = make_uint2(0u, 0u);
+    if (t0 + xt < T && k0 + xk < H) xb = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + xt) * H + k0 + xk);
+    wa = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    wb = wa;
+    if (e0 + we < E && k0 + wk < H) {
+      wa = *reinterpret_cast<const float4*>(w + (size_t)(e0 + we) * H + k0 + wk);
+      wb = *reinterpret_cast<const float4*>(w + (size_t)(e0 + we) * H + k0 + wk + 4);
+    }
+  };
+  fetch(0);
+  for (int k0 = 0; k0 < H; k0 += kRgK) {
+    __syncthreads();                                   // the previous chunk is consumed
+    s_x[xk + 0][xt] = bf16_lo(xb.x);
+    s_x[xk + 1][xt] = bf16_hi(xb.x);
+    s_x[xk + 2][xt] = bf16_lo(xb.y);
+    s_x[xk + 3][xt] = bf16_hi(xb.y);
+    s_w[wk + 0][we] = wa.x; s_w[wk + 1][we] = wa.y; s_w[wk + 2][we] = wa.z; s_w[wk + 3][we] = wa.w;
+    s_w[wk + 4][we] = wb.x; s_w[wk + 5][we] = wb.y; s_w[wk + 6][we] = wb.z; s_w[wk + 7][we] = wb.w;
+    __syncthreads();
+    if (k0 + kRgK < H) fetch(k0 + kRgK);               // in flight while this chunk is summed
+#pragma unroll
+    for (int k = 0; k < kRgK; ++k) {
+      double a[4], b[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = s_x[k][4 * g + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[j] = s_w[k][8 * f + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * g + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + 8 * f + j;
+      if (e < E) logits[(size_t)t * E + e] = (float)acc[i][j];
+    }
+  }
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -188,8 +265,7 @@ extern "C" moe_status moe_router_logits(const uint16_t* x, const float* w_router
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !logits) return MOE_ERR_NULL_POINTER;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits)) return MOE_ERR_MISALIGNED;
-  const long long chunks = ((long long)T + kRtTokens - 1) / kRtTokens;
-  if (chunks > 65535) return MOE_ERR_UNSUPPORTED;
+  if (((long long)T + kRgTokens - 1) / kRgTokens > 65535) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T <= kRsMaxTokens) {
     const int nc = (H / 8 + kRtThreads - 1) / kRtThreads;   // 16-byte pieces per thread
@@ -197,7 +273,12 @@ extern "C" moe_status moe_router_logits(const uint16_t* x, const float* w_router
     else router_rows_kernel<2><<<E, kRtThreads, 0, s>>>(x, w_router, T, H, E, logits);
     return launch_status();
   }
-  const dim3 grid((unsigned)((E + kRtWaves - 1) / kRtWaves), (unsigned)chunks);
+  if (T >= kRgMinTokens) {
+    const dim3 grid((unsigned)((E + kRgExperts - 1) / kRgExperts), (unsigned)((T + kRgTokens - 1) / kRgTokens));
+    router_gemm_kernel<<<grid, kRtThreads, 0, s>>>(x, w_router, T, H, E, logits);
+    return launch_status();
+  }
+  const dim3 grid((unsigned)((E + kRtWaves - 1) / kRtWaves), (unsigned)((T + kRtTokens - 1) / kRtTokens));
   const size_t dyn = (size_t)kRtTokens * H * 2;
   const int nch = (H / 4 + kWave - 1) / kWave;       // pieces per lane
   if (nch <= 1) router_logits_kernel<1><<<grid, kRtThreads, dyn, s>>>(x, w_router, T, H, E, logits);

@@ -39,10 +39,11 @@ def _check_logits(got, x_u16, w):
 
 
 # (T, H, E): decode, one token, ragged token groups, small and odd sizes, the
-# largest row, both sides of the 64-token switch between the two kernels, a
-# prefill chunk
+# largest row, both sides of the 64- and 1024-token switches between the three
+# kernels (a K tail at H = 520, ragged token and expert tiles), a prefill chunk
 ROUTER_SHAPES = [(4, 2048, 512), (1, 2048, 512), (33, 2048, 512), (5, 256, 100), (9, 8, 3), (17, 4096, 64),
-                 (3, 520, 1000), (64, 2048, 512), (65, 1024, 40), (100, 4096, 33), (4096, 2048, 512)]
+                 (3, 520, 1000), (64, 2048, 512), (65, 1024, 40), (100, 4096, 33), (1023, 256, 70),
+                 (1024, 520, 130), (1500, 64, 1000), (4096, 2048, 512)]
 
 
 @pytest.mark.parametrize("shape", ROUTER_SHAPES, ids=lambda s: "T%d_H%d_E%d" % s)
