@@ -255,8 +255,9 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_scatter_kernel(
   }
 }
 
-// Route and bucket a batch of up to 16 tokens in one 1024-thread workgroup:
-// wavefront w selects token w; bucketing is an LDS histogram, one packed
+// Route and bucket a batch of up to 16 tokens in one workgroup of NT threads
+// (512 when E <= 512 and T <= 8: fewer waves to meet at each barrier, else
+// 1024): wavefront w selects token w; bucketing is an LDS histogram, one packed
 // scan over one expert per thread (route offsets in the low half,
 // active-expert positions in the high half), and a stable scatter whose rank
 // is the number of earlier routes to the same expert (ballots per id bit
@@ -264,21 +265,22 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_scatter_kernel(
 constexpr int kSmallMaxTokens = 16;
 constexpr int kSmallMaxRoutes = 256;
 
-template <int V, int KC>
-__global__ __launch_bounds__(kBucketThreads) void route_bucket_small_kernel(
+template <int V, int KC, int NT>
+__global__ __launch_bounds__(NT) void route_bucket_small_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
     int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos) {
-  __shared__ int s_cnt[1024];
+  __shared__ int s_cnt[NT];
   __shared__ int s_ids[kSmallMaxRoutes];
-  __shared__ int s_wt[kBucketWaves];
-  __shared__ uint8_t s_wcnt[kSmallMaxRoutes / kWave][1024];   // routes per expert in each 64-route group
+  constexpr int NW = NT / kWave;
+  __shared__ int s_wt[NW];
+  __shared__ uint8_t s_wcnt[kSmallMaxRoutes / kWave][NT];     // routes per expert in each 64-route group
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int R = T * k;
   s_cnt[tid] = 0;
-  reinterpret_cast<int*>(&s_wcnt[0][0])[tid] = 0;
+  for (int i = tid; i < kSmallMaxRoutes / kWave * NT / 4; i += NT) reinterpret_cast<int*>(&s_wcnt[0][0])[i] = 0;
   if (wave < T) {
     int e;
     float w;
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(kBucketThreads) void route_bucket_small_kernel(
   __syncthreads();
   int base = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < kBucketWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int t = s_wt[w];
     base += (w < wave) ? t : 0;
     total += t;
@@ -432,7 +434,10 @@ moe_status route_bucket(const float* logits, const float* bias, int T, int E, in
   const int V = (E + kWave - 1) / kWave;
   if (T <= kSmallMaxTokens && T * k <= kSmallMaxRoutes) {
 #define MOE_RBS1(VV, KK)                                                                                       \
-  route_bucket_small_kernel<VV, KK><<<1, kBucketThreads, 0, s>>>(logits, bias, T, E, k, topk_idx, topk_w,       \
+  if (E <= 512 && T <= 8) route_bucket_small_kernel<VV, KK, 512><<<1, 512, 0, s>>>(logits, bias, T, E, k, topk_idx, topk_w, \
+                                                                 expert_count, expert_offset, active_experts,     \
+                                                                 n_active, route_src, route_pos); else \
+  route_bucket_small_kernel<VV, KK, 1024><<<1, 1024, 0, s>>>(logits, bias, T, E, k, topk_idx, topk_w,       \
                                                                  expert_count, expert_offset, active_experts,     \
                                                                  n_active, route_src, route_pos)
 #define MOE_RBS(VV) \
