@@ -78,6 +78,8 @@ struct FfnParams {
   int lr_d;      // lanes per down row
   int mfma_min;  // experts with at least this many routes take the MFMA kernels (0: none do)
   const uint8_t* packed;   // the weights also in MFMA tile order (moe_pack_weights), or null
+  int32_t* plan;           // workspace: MFMA work items (plan_kernel), see there
+  int plan_max;            // capacity of the item list
 };
 
 constexpr int kGuUnits = 4;          // gate rows (and as many up rows) per wave per tile
@@ -349,8 +351,10 @@ __global__ __launch_bounds__(kThreads, 4) void down_kernel(FfnParams p, int n_ta
 // For an expert with many routes the projections are dense contractions:
 // gate/up is [I x H] x [H x routes] twice, down is [H x I] x [I x routes].
 // A workgroup owns 128 weight rows of one expert (the same rows of W_gate
-// and W_up for gate/up) and the expert's routes in chunks of 128; each of
-// its four waves owns 32 of the rows and all of the chunk's routes.  The
+// and W_up for gate/up) and one chunk of up to 128 of its routes (one item
+// of the work plan below: an expert with more routes has one workgroup per
+// chunk, running side by side); each of its four waves owns 32 of the rows
+// and all of the chunk's routes.  The
 // packed down kernel of prefill-sized batches gives each wave two 32-row
 // tiles (256 rows per workgroup), so every B fragment read feeds two MFMAs.
 //
@@ -495,15 +499,19 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
   const int N = GU ? p.I : p.H;                              // weight rows
   const int K = GU ? p.H : p.I;                              // reduction length
   const int tiles_n = (N + kWgRows - 1) / kWgRows;
-  // workgroup b: XCD b % 8, j = b / 8; the tiles_n tiles of slot a share an XCD
+  // workgroup b: XCD b % 8, j = b / 8, item (j / tiles_n) * 8 + XCD, n-tile
+  // j % tiles_n: the tiles of one item share an XCD, and the items (longest
+  // first) start in plan order
   const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-  const int a = (j / tiles_n) * kXcds + xcd, n0 = (j % tiles_n) * kWgRows;
-  if (a >= min(p.E, p.T * p.k)) return;
-  const int e = slot_expert(p, a);
-  if (e < 0) return;
-  int off, cnt;
-  expert_routes(p, e, off, cnt);
-  if (p.mfma_min <= 0 || cnt < p.mfma_min) return;
+  const int it = (j / tiles_n) * kXcds + xcd, n0 = (j % tiles_n) * kWgRows;
+  // the item is read together with the count (the list has room for every
+  // item index of the grid), so the head costs one round of scalar loads
+  const int n_items = min(sload(p.plan, 0), p.plan_max);
+  const int R = p.T * p.k;
+  const int e = min(max(sload(p.plan, 4 + 4 * it), 0), p.E - 1);
+  const int off = min(max(sload(p.plan, 5 + 4 * it), 0), R);
+  const int cnt = min(max(sload(p.plan, 6 + 4 * it), 0), min(kMmRoutes, R - off));
+  if (it >= n_items || cnt <= 0) return;
 
   Tile t;
   t.s_x[0] = s_x0;
@@ -514,7 +522,6 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
   t.lane = lane;
   const uint32_t code_row = (uint32_t)K / 2, scale_row = (uint32_t)K / 16;
   const uint32_t mat_codes = (uint32_t)N * code_row, mat_scales = (uint32_t)N * scale_row;
-  const int R = p.T * p.k;
   t.rb = GU ? make_rsrc(p.x, (uint32_t)p.T * (uint32_t)p.H * 2u) : make_rsrc(p.h, (uint32_t)R * (uint32_t)p.I * 2u);
   const int steps = K / kMmK;
   if constexpr (PACKED) {
@@ -545,8 +552,9 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
     }
   }
 
-  for (int m0 = 0; m0 < cnt; m0 += kMmRoutes) {
-    const int mc = min(kMmRoutes, cnt - m0);
+  {
+    // one chunk of at most kMmRoutes routes: bucket positions off .. off + cnt - 1
+    const int m0 = 0, mc = cnt;
     const int mtiles = (mc + 31) >> 5;
     __syncthreads();                                         // previous chunk done with LDS
     if (tid < kMmRoutes) {
@@ -648,6 +656,57 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
         }
       }
     }
+  }
+}
+
+// ------------------------------------------------------------------ MFMA work plan
+
+constexpr int kPlanThreads = 1024;
+
+// The MFMA kernels' work items: every expert that takes them (at least
+// mfma_min routes) contributes one item per chunk of up to kMmRoutes routes,
+// {expert, first bucket position, route count, 0}.  Items are grouped by
+// route tiles, the full chunks first: workgroups start in that order, so the
+// longest items are not left for the end, and an expert with more than one
+// chunk has them side by side.  The order inside a group is that of the LDS
+// counters (it affects only which workgroup computes an item, not what is
+// computed).  plan[0] = item count; items from plan[4].
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(FfnParams p) {
+  __shared__ int s_cnt[4], s_base[4];
+  const int tid = threadIdx.x;
+  const int S = min(p.E, p.T * p.k);
+  const int n_act = min(max(sload(p.n_active_ptr, 0), 0), S);
+  if (tid < 4) s_cnt[tid] = 0;
+  __syncthreads();
+  // slot a = tid (S <= 1024 slots)
+  int e = -1, off = 0, cnt = 0;
+  if (tid < n_act) {
+    e = slot_expert(p, tid);
+    if (e >= 0) {
+      expert_routes(p, e, off, cnt);
+      if (p.mfma_min <= 0 || cnt < p.mfma_min) cnt = 0;
+    }
+  }
+  const int full = cnt / kMmRoutes, rest = cnt - full * kMmRoutes;
+  const int rest_cls = rest > 0 ? 4 - ((rest + 31) >> 5) : -1;   // 0: four route tiles .. 3: one
+  if (full > 0) atomicAdd(&s_cnt[0], full);
+  if (rest_cls >= 0) atomicAdd(&s_cnt[rest_cls], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int t = 0;
+    for (int c = 0; c < 4; ++c) { s_base[c] = t; t += s_cnt[c]; }
+    p.plan[0] = min(t, p.plan_max);
+  }
+  __syncthreads();
+  if (full > 0) {
+    const int b = atomicAdd(&s_base[0], full);
+    for (int c = 0; c < full; ++c)
+      if (b + c < p.plan_max)
+        reinterpret_cast<int4*>(p.plan + 4)[b + c] = make_int4(e, off + c * kMmRoutes, kMmRoutes, 0);
+  }
+  if (rest_cls >= 0) {
+    const int b = atomicAdd(&s_base[rest_cls], 1);
+    if (b < p.plan_max) reinterpret_cast<int4*>(p.plan + 4)[b] = make_int4(e, off + full * kMmRoutes, rest, 0);
   }
 }
 
@@ -842,15 +901,21 @@ void launch_down_combine(const FfnParams& p, unsigned grid, size_t dyn, int slot
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WorkspaceLayout {
-  size_t h_off, o_off, total;
+  size_t h_off, o_off, plan_off, total;   // h [R, I] bf16, o [R, H] fp32, MFMA work plan
+  int plan_max;
 };
 
-WorkspaceLayout workspace_layout(int T, int H, int I, int k) {
+WorkspaceLayout workspace_layout(int T, int H, int I, int E, int k) {
   WorkspaceLayout L;
   const size_t R = (size_t)T * (size_t)k;
   L.h_off = 0;
   L.o_off = align256(R * (size_t)I * 2);
-  L.total = L.o_off + align256(R * (size_t)H * 4);
+  L.plan_off = L.o_off + align256(R * (size_t)H * 4);
+  // at most one partial chunk per expert slot plus R / kMmRoutes full ones;
+  // the list has room for a multiple of 8 items (the MFMA grids' bound)
+  L.plan_max = (int)(std::min<size_t>((size_t)E, R) + R / kMmRoutes);
+  const size_t cap = ((size_t)L.plan_max + kXcds - 1) / kXcds * kXcds;
+  L.total = L.plan_off + align256((4 + 4 * cap) * 4);
   return L;
 }
 
@@ -882,9 +947,8 @@ void launch_down(const FfnParams& p, long long tasks, hipStream_t s) {
 }  // namespace moe
 
 extern "C" size_t moe_expert_ffn_workspace_size(int T, int H, int I, int E, int k) {
-  (void)E;
-  if (T <= 0 || k <= 0 || H <= 0 || I <= 0) return 0;
-  return moe::workspace_layout(T, H, I, k).total;
+  if (T <= 0 || k <= 0 || H <= 0 || I <= 0 || E <= 0) return 0;
+  return moe::workspace_layout(T, H, I, E, k).total;
 }
 
 namespace moe {
@@ -911,7 +975,7 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   for (const void* q : ptrs)
     if (!aligned16(q)) return MOE_ERR_MISALIGNED;
   if (packed && !aligned16(packed)) return MOE_ERR_MISALIGNED;
-  const WorkspaceLayout L = workspace_layout(T, H, I, k);
+  const WorkspaceLayout L = workspace_layout(T, H, I, E, k);
   if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
 
   FfnParams p;
@@ -922,6 +986,8 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   char* ws = static_cast<char*>(workspace);
   p.h = reinterpret_cast<uint16_t*>(ws + L.h_off);
   p.o = reinterpret_cast<float*>(ws + L.o_off);
+  p.plan = reinterpret_cast<int32_t*>(ws + L.plan_off);
+  p.plan_max = L.plan_max;
   p.y = y;
   p.lr_gu = lr_gu;
   p.lr_d = lr_d;
@@ -950,7 +1016,12 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   const long long tasks_d = slots * ((H + rpt_d - 1) / rpt_d);
   if (tasks_gu > kMaxGrid || tasks_d > kMaxGrid) return MOE_ERR_UNSUPPORTED;
 
-  const long long slots8 = (slots + kXcds - 1) / kXcds * kXcds;   // slot count padded for the XCD numbering
+  const long long items8 = ((long long)L.plan_max + kXcds - 1) / kXcds * kXcds;   // MFMA item bound, padded
+  if (mfma) {
+    // the MFMA kernels' work list (both stages use it; stage 2 alone rebuilds it)
+    plan_kernel<<<1, kPlanThreads, 0, s>>>(p);
+    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  }
   if (stage & 1) {
     if (row_dots) {
       if (lr_gu == 64) launch_gate_up<64>(p, tasks_gu, s);
@@ -958,7 +1029,7 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
       if (launch_status() != MOE_OK) return MOE_ERR_HIP;
     }
     if (mfma) {
-      const unsigned grid = (unsigned)(slots8 * ((I + kMmRows - 1) / kMmRows));
+      const unsigned grid = (unsigned)(items8 * ((I + kMmRows - 1) / kMmRows));
       if (p.packed) ffn_mfma_kernel<true, true, 1><<<grid, kMmThreads, 0, s>>>(p);
       else ffn_mfma_kernel<true, false, 1><<<grid, kMmThreads, 0, s>>>(p);
       if (launch_status() != MOE_OK) return MOE_ERR_HIP;
@@ -980,13 +1051,13 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   }
   if (mfma) {
     if (p.packed && R >= (long long)kDownSubMinRoutes * slots) {
-      const unsigned grid = (unsigned)(slots8 * ((H + 2 * kMmRows - 1) / (2 * kMmRows)));
+      const unsigned grid = (unsigned)(items8 * ((H + 2 * kMmRows - 1) / (2 * kMmRows)));
       ffn_mfma_kernel<false, true, 2><<<grid, kMmThreads, 0, s>>>(p);
     } else if (p.packed) {
-      const unsigned grid = (unsigned)(slots8 * ((H + kMmRows - 1) / kMmRows));
+      const unsigned grid = (unsigned)(items8 * ((H + kMmRows - 1) / kMmRows));
       ffn_mfma_kernel<false, true, 1><<<grid, kMmThreads, 0, s>>>(p);
     } else {
-      const unsigned grid = (unsigned)(slots8 * ((H + kMmRows - 1) / kMmRows));
+      const unsigned grid = (unsigned)(items8 * ((H + kMmRows - 1) / kMmRows));
       ffn_mfma_kernel<false, false, 1><<<grid, kMmThreads, 0, s>>>(p);
     }
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;

@@ -149,6 +149,25 @@ def test_step_host_checks(lib):
     assert _step(lib, ws=need - 1) == 5
 
 
+def _workspace_formula(T, H, I, E, k):
+    """moe_expert_ffn_workspace_size as the header states it: h (2*I bytes
+    per route), o (4*H bytes per route), and a work list of 16 bytes per item
+    for min(E, T*k) + T*k // 128 items rounded up to 8, plus 16; each region
+    rounded up to 256 bytes."""
+    up = lambda v: (v + 255) // 256 * 256
+    R = T * k
+    items = min(E, R) + R // 128
+    items = (items + 7) // 8 * 8
+    return up(R * I * 2) + up(R * H * 4) + up(16 + 16 * items)
+
+
+def test_workspace_size_formula(lib):
+    for shape in [(4, 256, 128, 8, 2), (4, 2048, 512, 512, 10), (32, 2048, 512, 512, 10),
+                  (256, 2048, 512, 512, 10), (4096, 2048, 512, 512, 10), (1, 32, 32, 1, 1)]:
+        assert lib.moe_expert_ffn_workspace_size(*shape) == _workspace_formula(*shape), shape
+    assert lib.moe_expert_ffn_workspace_size(4, 256, 128, 0, 2) == 0
+
+
 def test_step_workspace_size(lib):
     for shape in [(4, 2048, 512, 512, 10), (4, 256, 128, 8, 2), (33, 2048, 512, 512, 10), (1, 32, 32, 2, 1)]:
         assert lib.moe_step_workspace_size(*shape) == lib.moe_expert_ffn_workspace_size(*shape)

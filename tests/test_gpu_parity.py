@@ -129,12 +129,14 @@ def test_k_equals_E(path):
 
 
 @pytest.mark.parametrize("path", ["step", "packed"])
-@pytest.mark.parametrize("T", [12, 33])
+@pytest.mark.parametrize("T", [12, 33, 300])
 def test_all_tokens_on_same_experts(T, path):
     """Every token routed to the same 10 experts: T routes per expert, so the
     kernels loop over the expert's tokens (T = 12: the small-batch routing
     kernel and the fused down/unroute kernel; T = 33: the larger-batch
-    kernels), on both weight layouts."""
+    kernels; T = 300: the matrix-core kernels with two full 128-route chunks
+    and a partial one per expert, each chunk its own work item), on both
+    weight layouts."""
     wl = make_workload("decode_t4", T=T, x_seed=3)
     chosen = [7, 100, 101, 250, 311, 312, 400, 450, 500, 511]
     bias = np.zeros(wl.E, np.float32)
@@ -323,9 +325,11 @@ def test_fused_routing_edges(case):
         assert torch.equal(ta, tb)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode_t4", "verify_t32"])
+@pytest.mark.parametrize("name", ["tiny", "decode_t4", "verify_t32", "decode_t256_zipf"])
 def test_stages_compose_to_full_call(name):
-    """moe_expert_ffn_stage 1 then 2 equals moe_expert_ffn bit for bit."""
+    """moe_expert_ffn_stage 1 then 2 equals moe_expert_ffn bit for bit
+    (decode_t256_zipf: the matrix-core kernels, whose work list stage 2
+    rebuilds on its own)."""
     wl = make_workload(name)
     W = device_weights(wl.bank)
     st = sme.MoeStep(wl.T, wl.H, wl.I, wl.E, wl.k, DEV)
