@@ -153,9 +153,10 @@ moe_status moe_route_bucket(const float* logits, const float* bias,
 /*
  * Bytes of device workspace moe_expert_ffn needs for these sizes (0 when
  * T == 0 or a size is not positive): the per-route intermediates, 2*I + 4*H
- * bytes per route, and the dense kernels' work list, 16 bytes for each of
- * at most min(E, T*k) + T*k/128 items (rounded up to a multiple of 8) plus
- * 16; each region rounded up to 256 bytes.
+ * bytes per route; the dense kernels' work list, 16 bytes for each of at
+ * most min(E, T*k) + T*k/128 items (rounded up to a multiple of 8) plus 16;
+ * and the row-dot kernels' expert list, 4 bytes for each of min(E, T*k)
+ * experts plus 4; each region rounded up to 256 bytes.
  */
 size_t moe_expert_ffn_workspace_size(int T, int H, int I, int E, int k);
 
@@ -187,9 +188,9 @@ size_t moe_expert_ffn_workspace_size(int T, int H, int I, int E, int k);
  *   route_pos                           in   (from moe_bucket_routes)
  *   workspace   device buffer of workspace_bytes >= moe_expert_ffn_workspace_size(T,H,I,E,k),
  *               owned by the caller; holds the per-route intermediates h
- *               (bf16 [T*k, I]) and o (fp32 [T*k, H]) and the work list of
- *               the dense (matrix-core) kernels.  Its contents before and
- *               after a call are unspecified and never need a reset.
+ *               (bf16 [T*k, I]) and o (fp32 [T*k, H]) and the work lists
+ *               of the expert kernels.  Its contents before and after a
+ *               call are unspecified and never need a reset.
  *   y           [T, H] bf16 bits        out
  * Shapes: T >= 0 (T = 0 launches nothing), 1 <= k <= E, H and I multiples of
  * 32.  Envelope: E <= 1024, k <= 32, H and I powers of two from 32 to 4096

@@ -80,6 +80,8 @@ struct FfnParams {
   const uint8_t* packed;   // the weights also in MFMA tile order (moe_pack_weights), or null
   int32_t* plan;           // workspace: MFMA work items (plan_kernel), see there
   int plan_max;            // capacity of the item list
+  int32_t* rd_list;        // workspace: row-dot experts, most routes first (plan_kernel)
+  int rd_plan;             // the row-dot kernels take their experts from rd_list
 };
 
 constexpr int kGuUnits = 4;          // gate rows (and as many up rows) per wave per tile
@@ -119,6 +121,20 @@ __device__ __forceinline__ bool takes_mfma(const FfnParams& p, int e) {
   int off, cnt;
   expert_routes(p, e, off, cnt);
   return cnt >= p.mfma_min;
+}
+
+// Expert of the a-th row-dot workgroup group, or -1 when there is none.
+// With the plan (batches above 16 tokens) the experts come most routes first
+// (rd_list[0] = their count, then the list), so the longest workgroups start
+// first; otherwise in active-slot order, skipping the experts the MFMA
+// kernels take.
+__device__ __forceinline__ int row_dot_expert(const FfnParams& p, int a) {
+  if (p.rd_plan) {
+    const int n = sload(p.rd_list, 0), e = sload(p.rd_list, 1 + a);   // a < min(E, T*k): in the list
+    return a < n ? min(max(e, 0), p.E - 1) : -1;
+  }
+  const int e = slot_expert(p, a);
+  return (e < 0 || takes_mfma(p, e)) ? -1 : e;
 }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -275,8 +291,8 @@ __global__ __launch_bounds__(kThreads, 4) void gate_up_kernel(FfnParams p, int n
   const int task = blockIdx.x;
   if (task >= n_tasks) return;
   const int a = task / g.tiles, tile = task - a * g.tiles;
-  const int e = slot_expert(p, a);
-  if (e < 0 || takes_mfma(p, e)) return;
+  const int e = row_dot_expert(p, a);
+  if (e < 0) return;
   gate_up_tile<LG>(p, g, s_sc, s_x, e, tile);
 }
 
@@ -341,8 +357,8 @@ __global__ __launch_bounds__(kThreads, 4) void down_kernel(FfnParams p, int n_ta
   const int task = blockIdx.x;                  // one task per workgroup
   if (task >= n_tasks) return;
   const int a = task / g.tiles, tile = task - a * g.tiles;
-  const int e = slot_expert(p, a);
-  if (e < 0 || takes_mfma(p, e)) return;
+  const int e = row_dot_expert(p, a);
+  if (e < 0) return;
   down_tile<LD>(p, g, s_sc, e, tile);
 }
 
@@ -671,33 +687,60 @@ constexpr int kPlanThreads = 1024;
 // chunk has them side by side.  The order inside a group is that of the LDS
 // counters (it affects only which workgroup computes an item, not what is
 // computed).  plan[0] = item count; items from plan[4].
+//
+// With rd_plan it also lists the experts of the row-dot kernels (fewer than
+// mfma_min routes, or all when no expert takes the MFMA kernels) by route
+// count, most first (a counting sort over 64 bins; counts of 63 and more
+// share the first): rd_list[0] = their number, rd_list[1 + i] = expert.
+constexpr int kRdBins = 64;
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(FfnParams p) {
   __shared__ int s_cnt[4], s_base[4];
+  __shared__ int s_rh[kRdBins];
   const int tid = threadIdx.x;
   const int S = min(p.E, p.T * p.k);
   const int n_act = min(max(sload(p.n_active_ptr, 0), 0), S);
   if (tid < 4) s_cnt[tid] = 0;
+  if (tid < kRdBins) s_rh[tid] = 0;
   __syncthreads();
   // slot a = tid (S <= 1024 slots)
-  int e = -1, off = 0, cnt = 0;
+  int e = -1, off = 0, cnt = 0, rcnt = 0;
   if (tid < n_act) {
     e = slot_expert(p, tid);
     if (e >= 0) {
       expert_routes(p, e, off, cnt);
-      if (p.mfma_min <= 0 || cnt < p.mfma_min) cnt = 0;
+      if (p.mfma_min <= 0 || cnt < p.mfma_min) {
+        rcnt = cnt;
+        cnt = 0;
+      }
     }
   }
   const int full = cnt / kMmRoutes, rest = cnt - full * kMmRoutes;
   const int rest_cls = rest > 0 ? 4 - ((rest + 31) >> 5) : -1;   // 0: four route tiles .. 3: one
   if (full > 0) atomicAdd(&s_cnt[0], full);
   if (rest_cls >= 0) atomicAdd(&s_cnt[rest_cls], 1);
+  const int rbin = kRdBins - 1 - min(rcnt, kRdBins - 1);          // 0: most routes
+  if (p.rd_plan && rcnt > 0) atomicAdd(&s_rh[rbin], 1);
   __syncthreads();
   if (tid == 0) {
     int t = 0;
     for (int c = 0; c < 4; ++c) { s_base[c] = t; t += s_cnt[c]; }
     p.plan[0] = min(t, p.plan_max);
   }
+  if (p.rd_plan && tid < kWave) {
+    // exclusive scan of the 64 bins, one per lane
+    const int v = s_rh[tid];
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int u = __shfl_up(incl, d, kWave);
+      if (tid >= d) incl += u;
+    }
+    s_rh[tid] = incl - v;
+    if (tid == kWave - 1) p.rd_list[0] = incl;
+  }
   __syncthreads();
+  if (p.rd_plan && rcnt > 0) p.rd_list[1 + atomicAdd(&s_rh[rbin], 1)] = e;
   if (full > 0) {
     const int b = atomicAdd(&s_base[0], full);
     for (int c = 0; c < full; ++c)
@@ -901,7 +944,7 @@ void launch_down_combine(const FfnParams& p, unsigned grid, size_t dyn, int slot
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WorkspaceLayout {
-  size_t h_off, o_off, plan_off, total;   // h [R, I] bf16, o [R, H] fp32, MFMA work plan
+  size_t h_off, o_off, plan_off, rd_off, total;   // h [R, I] bf16, o [R, H] fp32, MFMA work plan, row-dot list
   int plan_max;
 };
 
@@ -915,12 +958,15 @@ WorkspaceLayout workspace_layout(int T, int H, int I, int E, int k) {
   // the list has room for a multiple of 8 items (the MFMA grids' bound)
   L.plan_max = (int)(std::min<size_t>((size_t)E, R) + R / kMmRoutes);
   const size_t cap = ((size_t)L.plan_max + kXcds - 1) / kXcds * kXcds;
-  L.total = L.plan_off + align256((4 + 4 * cap) * 4);
+  L.rd_off = L.plan_off + align256((4 + 4 * cap) * 4);
+  // the row-dot list: its length and one expert per slot
+  L.total = L.rd_off + align256((1 + std::min<size_t>((size_t)E, R)) * 4);
   return L;
 }
 
 constexpr long long kMaxGrid = 1 << 20;   // one workgroup per task; the shape limits keep tasks below this
 constexpr int kMfmaMinTokens = 64;      // batches from this size launch the MFMA kernels
+constexpr int kRowPlanMinTokens = 16;   // batches above this size order the row-dot experts by count
 constexpr int kMfmaMinRoutes = 16;      // experts with this many routes use them (standard weight layout)
 constexpr int kMfmaMinRoutesPacked = 1; // with the packed copy: every expert of such a batch
 // Packed down kernel: two row tiles per wave when the batch averages at
@@ -988,6 +1034,7 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   p.o = reinterpret_cast<float*>(ws + L.o_off);
   p.plan = reinterpret_cast<int32_t*>(ws + L.plan_off);
   p.plan_max = L.plan_max;
+  p.rd_list = reinterpret_cast<int32_t*>(ws + L.rd_off);
   p.y = y;
   p.lr_gu = lr_gu;
   p.lr_d = lr_d;
@@ -1008,6 +1055,9 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   const bool mfma = !down_combine && T >= kMfmaMinTokens && H % kMmK == 0 && I % kMmK == 0;
   p.mfma_min = mfma ? (packed ? kMfmaMinRoutesPacked : kMfmaMinRoutes) : 0;
   const bool row_dots = !mfma || p.mfma_min > 1;
+  // above the small-batch size the row-dot kernels take their experts most
+  // routes first from the plan (their workgroups' lengths grow with the count)
+  p.rd_plan = row_dots && T > kRowPlanMinTokens ? 1 : 0;
 
   const long long slots = std::min<long long>(E, (long long)T * k);
   const int rpt_gu = kWavesPerBlock * (kWave / lr_gu) * kGuUnits;
@@ -1017,8 +1067,8 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   if (tasks_gu > kMaxGrid || tasks_d > kMaxGrid) return MOE_ERR_UNSUPPORTED;
 
   const long long items8 = ((long long)L.plan_max + kXcds - 1) / kXcds * kXcds;   // MFMA item bound, padded
-  if (mfma) {
-    // the MFMA kernels' work list (both stages use it; stage 2 alone rebuilds it)
+  if (mfma || p.rd_plan) {
+    // the work lists (both stages use them; stage 2 alone rebuilds them)
     plan_kernel<<<1, kPlanThreads, 0, s>>>(p);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
