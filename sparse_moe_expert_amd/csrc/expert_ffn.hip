@@ -370,9 +370,9 @@ __global__ __launch_bounds__(kThreads, 4) void down_kernel(FfnParams p, int n_ta
 // and W_up for gate/up) and one chunk of up to 128 of its routes (one item
 // of the work plan below: an expert with more routes has one workgroup per
 // chunk, running side by side); each of its four waves owns 32 of the rows
-// and all of the chunk's routes.  The
-// packed down kernel of prefill-sized batches gives each wave two 32-row
-// tiles (256 rows per workgroup), so every B fragment read feeds two MFMAs.
+// and all of the chunk's routes.  The packed down kernel gives each wave two
+// 32-row tiles (256 rows per workgroup), so every B fragment read feeds two
+// MFMAs.
 //
 // v_mfma_f32_32x32x16_bf16 with the weights as A (32 rows x 16) and the
 // routes' operand rows as B (16 x 32 routes).  Lane layout (checked on the
@@ -699,13 +699,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(FfnParams p) {
   __shared__ int s_rh[kRdBins];
   const int tid = threadIdx.x;
   const int S = min(p.E, p.T * p.k);
-  const int n_act = min(max(sload(p.n_active_ptr, 0), 0), S);
   if (tid < 4) s_cnt[tid] = 0;
   if (tid < kRdBins) s_rh[tid] = 0;
   __syncthreads();
-  // slot a = tid (S <= 1024 slots)
+  // slot a = tid (S <= 1024 slots); the active list holds -1 past its end,
+  // so n_active is not needed
   int e = -1, off = 0, cnt = 0, rcnt = 0;
-  if (tid < n_act) {
+  if (tid < S) {
     e = slot_expert(p, tid);
     if (e >= 0) {
       expert_routes(p, e, off, cnt);
@@ -969,11 +969,6 @@ constexpr int kMfmaMinTokens = 64;      // batches from this size launch the MFM
 constexpr int kRowPlanMinTokens = 16;   // batches above this size order the row-dot experts by count
 constexpr int kMfmaMinRoutes = 16;      // experts with this many routes use them (standard weight layout)
 constexpr int kMfmaMinRoutesPacked = 1; // with the packed copy: every expert of such a batch
-// Packed down kernel: two row tiles per wave when the batch averages at
-// least this many routes per expert slot (prefill-sized: each expert's h
-// rows are then staged half as often; with fewer, halving the workgroups
-// leaves too few of them in flight).
-constexpr int kDownSubMinRoutes = 16;
 
 template <int LG>
 void launch_gate_up(const FfnParams& p, long long tasks, hipStream_t s) {
@@ -1100,12 +1095,11 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
   if (mfma) {
-    if (p.packed && R >= (long long)kDownSubMinRoutes * slots) {
+    if (p.packed) {
+      // two row tiles per wave: each item's h rows are staged half as often
+      // and every B fragment feeds two MFMAs
       const unsigned grid = (unsigned)(items8 * ((H + 2 * kMmRows - 1) / (2 * kMmRows)));
       ffn_mfma_kernel<false, true, 2><<<grid, kMmThreads, 0, s>>>(p);
-    } else if (p.packed) {
-      const unsigned grid = (unsigned)(items8 * ((H + kMmRows - 1) / kMmRows));
-      ffn_mfma_kernel<false, true, 1><<<grid, kMmThreads, 0, s>>>(p);
     } else {
       const unsigned grid = (unsigned)(items8 * ((H + kMmRows - 1) / kMmRows));
       ffn_mfma_kernel<false, false, 1><<<grid, kMmThreads, 0, s>>>(p);

@@ -92,6 +92,7 @@ RAGGED_TILE_SHAPES = [
     (256, 64, 16, 4, 40),
     (256, 64, 16, 4, 128),
     (128, 32, 8, 2, 70),
+    (128, 64, 8, 2, 70),     # the packed down kernel's second 128-row tile lies past H
     (32, 32, 4, 2, 10),
     (32, 64, 6, 3, 50),
     (256, 64, 4, 4, 40),     # ~40 routes per expert in a batch under 64 tokens
