@@ -50,6 +50,7 @@
 #include <type_traits>
 
 #include "row_dot.h"
+#include "work_list.h"
 
 namespace moe {
 namespace {
@@ -675,82 +676,30 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
   }
 }
 
-// ------------------------------------------------------------------ MFMA work plan
+// ------------------------------------------------------------------ work lists
 
-constexpr int kPlanThreads = 1024;
+static_assert(kMmRoutes == kWlRoutes, "an MFMA item is one route chunk of the MFMA kernels");
 
-// The MFMA kernels' work items: every expert that takes them (at least
-// mfma_min routes) contributes one item per chunk of up to kMmRoutes routes,
-// {expert, first bucket position, route count, 0}.  Items are grouped by
-// route tiles, the full chunks first: workgroups start in that order, so the
-// longest items are not left for the end, and an expert with more than one
-// chunk has them side by side.  The order inside a group is that of the LDS
-// counters (it affects only which workgroup computes an item, not what is
-// computed).  plan[0] = item count; items from plan[4].
-//
-// With rd_plan it also lists the experts of the row-dot kernels (fewer than
-// mfma_min routes, or all when no expert takes the MFMA kernels) by route
-// count, most first (a counting sort over 64 bins; counts of 63 and more
-// share the first): rd_list[0] = their number, rd_list[1 + i] = expert.
-constexpr int kRdBins = 64;
-
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(FfnParams p) {
-  __shared__ int s_cnt[4], s_base[4];
-  __shared__ int s_rh[kRdBins];
+// The work lists (work_list.h) from the bucket arrays, one expert slot per
+// thread (S <= 1024 slots); the active list holds -1 past its end, so
+// n_active is not needed.  moe_step builds the same lists in its bucketing
+// kernel and skips this one.
+__global__ __launch_bounds__(kWlThreads) void plan_kernel(FfnParams p) {
+  __shared__ WorkListShared sh;
   const int tid = threadIdx.x;
   const int S = min(p.E, p.T * p.k);
-  if (tid < 4) s_cnt[tid] = 0;
-  if (tid < kRdBins) s_rh[tid] = 0;
-  __syncthreads();
-  // slot a = tid (S <= 1024 slots); the active list holds -1 past its end,
-  // so n_active is not needed
-  int e = -1, off = 0, cnt = 0, rcnt = 0;
+  int e = -1, off = 0, cnt = 0;
   if (tid < S) {
     e = slot_expert(p, tid);
-    if (e >= 0) {
-      expert_routes(p, e, off, cnt);
-      if (p.mfma_min <= 0 || cnt < p.mfma_min) {
-        rcnt = cnt;
-        cnt = 0;
-      }
-    }
+    if (e >= 0) expert_routes(p, e, off, cnt);
   }
-  const int full = cnt / kMmRoutes, rest = cnt - full * kMmRoutes;
-  const int rest_cls = rest > 0 ? 4 - ((rest + 31) >> 5) : -1;   // 0: four route tiles .. 3: one
-  if (full > 0) atomicAdd(&s_cnt[0], full);
-  if (rest_cls >= 0) atomicAdd(&s_cnt[rest_cls], 1);
-  const int rbin = kRdBins - 1 - min(rcnt, kRdBins - 1);          // 0: most routes
-  if (p.rd_plan && rcnt > 0) atomicAdd(&s_rh[rbin], 1);
-  __syncthreads();
-  if (tid == 0) {
-    int t = 0;
-    for (int c = 0; c < 4; ++c) { s_base[c] = t; t += s_cnt[c]; }
-    p.plan[0] = min(t, p.plan_max);
-  }
-  if (p.rd_plan && tid < kWave) {
-    // exclusive scan of the 64 bins, one per lane
-    const int v = s_rh[tid];
-    int incl = v;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int u = __shfl_up(incl, d, kWave);
-      if (tid >= d) incl += u;
-    }
-    s_rh[tid] = incl - v;
-    if (tid == kWave - 1) p.rd_list[0] = incl;
-  }
-  __syncthreads();
-  if (p.rd_plan && rcnt > 0) p.rd_list[1 + atomicAdd(&s_rh[rbin], 1)] = e;
-  if (full > 0) {
-    const int b = atomicAdd(&s_base[0], full);
-    for (int c = 0; c < full; ++c)
-      if (b + c < p.plan_max)
-        reinterpret_cast<int4*>(p.plan + 4)[b + c] = make_int4(e, off + c * kMmRoutes, kMmRoutes, 0);
-  }
-  if (rest_cls >= 0) {
-    const int b = atomicAdd(&s_base[rest_cls], 1);
-    if (b < p.plan_max) reinterpret_cast<int4*>(p.plan + 4)[b] = make_int4(e, off + full * kMmRoutes, rest, 0);
-  }
+  WorkLists wl;
+  wl.plan = p.plan;
+  wl.rd_list = p.rd_list;
+  wl.plan_max = p.plan_max;
+  wl.mfma_min = p.mfma_min;
+  wl.rd_plan = p.rd_plan;
+  build_work_lists(wl, sh, e, cnt, off);
 }
 
 // ------------------------------------------------------------------ combine
@@ -994,12 +943,63 @@ extern "C" size_t moe_expert_ffn_workspace_size(int T, int H, int I, int E, int 
 
 namespace moe {
 
+// Which kernels a call of these sizes launches (shared by expert_ffn and the
+// work-list set-up of moe_step, so that both agree).
+struct FfnPolicy {
+  bool down_combine;   // fused down/unroute kernel (small batches)
+  bool mfma;           // MFMA kernels launched
+  int mfma_min;        // experts with at least this many routes take them (0: none)
+  bool row_dots;       // row-dot kernels launched
+  bool rd_plan;        // row-dot kernels read the sorted expert list
+};
+
+FfnPolicy ffn_policy(int T, int H, int I, int E, int k, bool packed) {
+  FfnPolicy f;
+  const long long R = (long long)T * k;
+  const int lr_d = lanes_per_row(I / 32);
+  const size_t h_bytes = (size_t)R * I * 2;
+  // one buffer resource spans all of W_down: its byte count must fit 31 bits
+  const bool dc_fits = (size_t)E * H * (I / 2) < (size_t)0x7FFFFFFF;
+  const size_t dc_lds = h_bytes + (size_t)R * (kWave / lr_d) * 4;   // h and o of the fused down/unroute kernel
+  f.down_combine = R <= kDcMaxRoutes && dc_lds <= (size_t)kDcMaxLds && dc_fits;
+  // Experts with many routes go to the MFMA kernels; only batches large
+  // enough to have such experts (and not small enough for the fused
+  // down/unroute kernel) launch them.  K (H for gate/up, I for down) must be a
+  // multiple of the 64-wide step.  With the packed copy (one contiguous
+  // kilobyte per weight load) the tiles beat one row-dot pass per route from
+  // two routes on and match it at one (measured at decode_t256_zipf), so every
+  // expert takes them and the row-dot kernels are not launched at all.
+  f.mfma = !f.down_combine && T >= kMfmaMinTokens && H % kMmK == 0 && I % kMmK == 0;
+  f.mfma_min = f.mfma ? (packed ? kMfmaMinRoutesPacked : kMfmaMinRoutes) : 0;
+  f.row_dots = !f.mfma || f.mfma_min > 1;
+  // above the small-batch size the row-dot kernels take their experts most
+  // routes first from the list (their workgroups' lengths grow with the count)
+  f.rd_plan = f.row_dots && T > kRowPlanMinTokens;
+  return f;
+}
+
+bool ffn_work_lists(int T, int H, int I, int E, int k, bool packed, void* workspace, WorkLists* wl,
+                    size_t* scratch_bytes) {
+  if (T <= 0 || k < 1 || E < 1 || H < 32 || I < 32) return false;
+  const FfnPolicy f = ffn_policy(T, H, I, E, k, packed);
+  const WorkspaceLayout L = workspace_layout(T, H, I, E, k);
+  char* ws = static_cast<char*>(workspace);
+  wl->plan = reinterpret_cast<int32_t*>(ws + L.plan_off);
+  wl->rd_list = reinterpret_cast<int32_t*>(ws + L.rd_off);
+  wl->plan_max = L.plan_max;
+  wl->mfma_min = f.mfma_min;
+  wl->rd_plan = f.rd_plan ? 1 : 0;
+  *scratch_bytes = L.plan_off;
+  return f.mfma || f.rd_plan;
+}
+
 moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const uint8_t* s_gate,
                       const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
                       const float* g_scale, const float* topk_w, const int32_t* expert_count,
                       const int32_t* expert_offset, const int32_t* active_experts, const int32_t* n_active,
                       const int32_t* route_src, const int32_t* route_pos, const uint8_t* packed, int T, int H,
-                      int I, int E, int k, void* workspace, size_t workspace_bytes, uint16_t* y, hipStream_t s) {
+                      int I, int E, int k, void* workspace, size_t workspace_bytes, uint16_t* y, hipStream_t s,
+                      bool lists_ready) {
   if (stage < 1 || stage > 3) return MOE_ERR_INVALID_SHAPE;
   if (T < 0 || k < 1 || E < 1 || k > E || H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
     return MOE_ERR_INVALID_SHAPE;
@@ -1036,23 +1036,10 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   p.packed = packed;
   const long long R = (long long)T * k;
   const size_t h_bytes = (size_t)R * I * 2;
-  // one buffer resource spans all of W_down: its byte count must fit 31 bits
-  const bool dc_fits = (size_t)E * H * (I / 2) < (size_t)0x7FFFFFFF;
-  const size_t dc_lds = h_bytes + (size_t)R * (kWave / lr_d) * 4;   // h and o of the fused down/unroute kernel
-  const bool down_combine = R <= kDcMaxRoutes && dc_lds <= (size_t)kDcMaxLds && dc_fits;
-  // Experts with many routes go to the MFMA kernels; only batches large
-  // enough to have such experts (and not small enough for the fused
-  // down/unroute kernel) launch them.  K (H for gate/up, I for down) must be a
-  // multiple of the 64-wide step.  With the packed copy (one contiguous
-  // kilobyte per weight load) the tiles beat one row-dot pass per route from
-  // two routes on and match it at one (measured at decode_t256_zipf), so every
-  // expert takes them and the row-dot kernels are not launched at all.
-  const bool mfma = !down_combine && T >= kMfmaMinTokens && H % kMmK == 0 && I % kMmK == 0;
-  p.mfma_min = mfma ? (packed ? kMfmaMinRoutesPacked : kMfmaMinRoutes) : 0;
-  const bool row_dots = !mfma || p.mfma_min > 1;
-  // above the small-batch size the row-dot kernels take their experts most
-  // routes first from the plan (their workgroups' lengths grow with the count)
-  p.rd_plan = row_dots && T > kRowPlanMinTokens ? 1 : 0;
+  const FfnPolicy pol = ffn_policy(T, H, I, E, k, packed != nullptr);
+  const bool down_combine = pol.down_combine, mfma = pol.mfma, row_dots = pol.row_dots;
+  p.mfma_min = pol.mfma_min;
+  p.rd_plan = pol.rd_plan ? 1 : 0;
 
   const long long slots = std::min<long long>(E, (long long)T * k);
   const int rpt_gu = kWavesPerBlock * (kWave / lr_gu) * kGuUnits;
@@ -1062,9 +1049,9 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   if (tasks_gu > kMaxGrid || tasks_d > kMaxGrid) return MOE_ERR_UNSUPPORTED;
 
   const long long items8 = ((long long)L.plan_max + kXcds - 1) / kXcds * kXcds;   // MFMA item bound, padded
-  if (mfma || p.rd_plan) {
+  if ((mfma || p.rd_plan) && !lists_ready) {
     // the work lists (both stages use them; stage 2 alone rebuilds them)
-    plan_kernel<<<1, kPlanThreads, 0, s>>>(p);
+    plan_kernel<<<1, kWlThreads, 0, s>>>(p);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
   if (stage & 1) {

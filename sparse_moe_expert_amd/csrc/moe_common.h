@@ -88,21 +88,41 @@ __host__ __device__ inline size_t packed_matrix_bytes(int N, int K) {
   return (packed_code_bytes(N, K) + scales + 255) & ~(size_t)255;
 }
 
+// Work lists of the expert kernels in the FFN workspace (see work_list.h).
+struct WorkLists {
+  int32_t* plan;      // MFMA items: [0] count, int4 items from [4]
+  int32_t* rd_list;   // row-dot experts: [0] count, then the experts
+  int plan_max;       // capacity of the MFMA item list
+  int mfma_min;       // experts with at least this many routes take the MFMA kernels (0: none do)
+  int rd_plan;        // the row-dot kernels read rd_list
+};
+
+// Whether moe_expert_ffn for these sizes reads work lists, and where they go
+// in its workspace (*wl); *scratch_bytes = the workspace bytes in front of
+// them, free until the expert kernels run.
+bool ffn_work_lists(int T, int H, int I, int E, int k, bool packed, void* workspace, WorkLists* wl,
+                    size_t* scratch_bytes);
+
 // The expert FFN as in moe_expert_ffn_stage, with the packed weights (NULL:
-// none; the MFMA tiles then read the standard layout).
+// none; the MFMA tiles then read the standard layout).  lists_ready: the
+// work lists were built by the bucketing (moe_step) for these buckets.
 moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const uint8_t* s_gate,
                       const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
                       const float* g_scale, const float* topk_w, const int32_t* expert_count,
                       const int32_t* expert_offset, const int32_t* active_experts, const int32_t* n_active,
                       const int32_t* route_src, const int32_t* route_pos, const uint8_t* packed, int T, int H,
-                      int I, int E, int k, void* workspace, size_t workspace_bytes, uint16_t* y, hipStream_t s);
+                      int I, int E, int k, void* workspace, size_t workspace_bytes, uint16_t* y, hipStream_t s,
+                      bool lists_ready = false);
 
 // Routing and bucketing as in moe_route_bucket; `scratch` (may be NULL) is
 // device memory the call may use until it returns (large batches bucket in
 // parallel with it; moe_step lends the FFN workspace, unused at that point).
+// With `wl` (may be NULL) the one-workgroup bucketing kernels also build the
+// expert kernels' work lists; *lists_built says whether they did.
 moe_status route_bucket(const float* logits, const float* bias, int T, int E, int k, int32_t* topk_idx,
                         float* topk_w, int32_t* expert_count, int32_t* expert_offset, int32_t* active_experts,
                         int32_t* n_active, int32_t* route_src, int32_t* route_pos, int32_t* scratch,
-                        size_t scratch_bytes, hipStream_t s);
+                        size_t scratch_bytes, hipStream_t s, const WorkLists* wl = nullptr,
+                        bool* lists_built = nullptr);
 
 }  // namespace moe

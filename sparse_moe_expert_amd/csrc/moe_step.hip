@@ -50,14 +50,23 @@ static moe_status step(const uint16_t* x, const float* logits, const float* bias
   if ((bias && !moe::aligned16(bias)) || (packed && !moe::aligned16(packed))) return MOE_ERR_MISALIGNED;
   if (workspace_bytes < moe_step_workspace_size(T, H, I, E, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  // the FFN workspace is free until the expert kernels run: routing may use it
+  // The expert kernels' work lists, when they read any, are built by the
+  // one-workgroup bucketing kernel, which holds the counts already (one
+  // launch less than building them in the FFN call).  The FFN workspace in
+  // front of the lists is free until the expert kernels run: routing may use
+  // it as scratch.
+  moe::WorkLists wl;
+  size_t scratch_bytes = workspace_bytes;
+  const bool want_lists = moe::ffn_work_lists(T, H, I, E, k, packed != nullptr, workspace, &wl, &scratch_bytes);
+  bool lists_built = false;
   const moe_status st = moe::route_bucket(logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset,
                                           active_experts, n_active, route_src, route_pos,
-                                          static_cast<int32_t*>(workspace), workspace_bytes, s);
+                                          static_cast<int32_t*>(workspace), scratch_bytes, s,
+                                          want_lists ? &wl : nullptr, &lists_built);
   if (st != MOE_OK) return st;
   return moe::expert_ffn(3, x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
                          expert_offset, active_experts, n_active, route_src, route_pos, packed, T, H, I, E, k,
-                         workspace, workspace_bytes, y, s);
+                         workspace, workspace_bytes, y, s, lists_built);
 }
 
 extern "C" moe_status moe_step(const uint16_t* x, const float* logits, const float* bias,

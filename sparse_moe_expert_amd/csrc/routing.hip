@@ -30,6 +30,7 @@
 // wavefronts in the chunk + the expert's running base gives the position.
 // Positions never depend on timing, so the result is exact and reproducible.
 #include "select.h"
+#include "work_list.h"
 
 namespace moe {
 namespace {
@@ -81,13 +82,17 @@ struct BucketShared {
   int base[1024];                    // counts, then running bases
   uint8_t wcnt[kBucketWaves][1024];  // per-wavefront counts inside a chunk
   int wave_tot[kBucketWaves + 1];
+  WorkListShared wl;
 };
+static_assert(kBucketThreads == kWlThreads, "the bucketing workgroup builds the work lists");
 
 // Bucket R routes whose expert ids are ids[0..R) (global or LDS).
+// With wl.plan set it also builds the expert kernels' work lists.
 __device__ __forceinline__ void bucket_block(const int32_t* ids, int R, int E, BucketShared& sh,
                                              int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
                                              int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
-                                             int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos) {
+                                             int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos,
+                                             const WorkLists& wl) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   for (int e = tid; e < 1024; e += kBucketThreads) sh.base[e] = 0;
   for (int i = tid; i < kBucketWaves * 1024 / 4; i += kBucketThreads) reinterpret_cast<int*>(&sh.wcnt[0][0])[i] = 0;
@@ -123,6 +128,7 @@ __device__ __forceinline__ void bucket_block(const int32_t* ids, int R, int E, B
     expert_offset[E] = total_routes;
     *n_active = total_active;
   }
+  if (wl.plan) build_work_lists(wl, sh.wl, tid < E ? tid : -1, c, off);   // uniform: a kernel argument
   __syncthreads();
 
   const uint64_t below = (1ull << lane) - 1ull;
@@ -161,10 +167,10 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_routes_kernel(
     const int32_t* __restrict__ topk_idx, int R, int E,
     int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
-    int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos) {
+    int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos, WorkLists wl) {
   __shared__ BucketShared sh;
   bucket_block(topk_idx, R, E, sh, expert_count, expert_offset, active_experts, n_active, route_src,
-               route_pos);
+               route_pos, wl);
 }
 
 // Bucketing of large batches in parallel (three kernels over chunks of
@@ -193,8 +199,10 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_count_kernel(const int3
 
 __global__ __launch_bounds__(kBucketThreads) void bucket_scan_kernel(
     int32_t* __restrict__ counts, int C, int E, int32_t* __restrict__ expert_count,
-    int32_t* __restrict__ expert_offset, int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active) {
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
+    WorkLists wl) {
   __shared__ int s_wave[kBucketWaves + 1];
+  __shared__ WorkListShared s_wl;
   const int tid = threadIdx.x;
   int run = 0;
   if (tid < E) {
@@ -224,6 +232,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_scan_kernel(
     expert_offset[E] = total_routes;
     *n_active = total_active;
   }
+  if (wl.plan) build_work_lists(wl, s_wl, tid < E ? tid : -1, run, off);   // uniform: a kernel argument
 }
 
 __global__ __launch_bounds__(kBucketThreads) void bucket_scatter_kernel(
@@ -416,7 +425,7 @@ extern "C" moe_status moe_bucket_routes(const int32_t* topk_idx, int T, int E, i
   if (!aligned16(topk_idx)) return MOE_ERR_MISALIGNED;
   bucket_routes_kernel<<<1, kBucketThreads, 0, static_cast<hipStream_t>(stream)>>>(
       topk_idx, T * k, E, expert_count, expert_offset, active_experts, n_active, route_src,
-      route_pos);
+      route_pos, WorkLists{});
   return launch_status();
 }
 
@@ -425,7 +434,9 @@ namespace moe {
 moe_status route_bucket(const float* logits, const float* bias, int T, int E, int k, int32_t* topk_idx,
                         float* topk_w, int32_t* expert_count, int32_t* expert_offset, int32_t* active_experts,
                         int32_t* n_active, int32_t* route_src, int32_t* route_pos, int32_t* scratch,
-                        size_t scratch_bytes, hipStream_t s) {
+                        size_t scratch_bytes, hipStream_t s, const WorkLists* wl, bool* lists_built) {
+  if (lists_built) *lists_built = false;
+  const WorkLists lists = wl ? *wl : WorkLists{};
   moe_status st = check_route_args(logits, bias, T, E, k, topk_idx, topk_w);
   if (st != MOE_OK) return st;
   st = check_bucket_args(T, E, k, expert_count, expert_offset, active_experts, n_active, route_src, route_pos);
@@ -459,15 +470,19 @@ moe_status route_bucket(const float* logits, const float* bias, int T, int E, in
     bucket_count_kernel<<<(unsigned)C, kBucketThreads, 0, s>>>(topk_idx, (int)R, E, scratch);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
     bucket_scan_kernel<<<1, kBucketThreads, 0, s>>>(scratch, (int)C, E, expert_count, expert_offset, active_experts,
-                                                    n_active);
+                                                    n_active, lists);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
     bucket_scatter_kernel<<<(unsigned)C, kBucketThreads, 0, s>>>(topk_idx, (int)R, E, bits, scratch, expert_offset,
                                                                  route_src, route_pos);
-    return launch_status();
+    st = launch_status();
+    if (lists_built) *lists_built = st == MOE_OK && wl != nullptr;
+    return st;
   }
   bucket_routes_kernel<<<1, kBucketThreads, 0, s>>>(topk_idx, (int)R, E, expert_count, expert_offset,
-                                                     active_experts, n_active, route_src, route_pos);
-  return launch_status();
+                                                     active_experts, n_active, route_src, route_pos, lists);
+  st = launch_status();
+  if (lists_built) *lists_built = st == MOE_OK && wl != nullptr;
+  return st;
 }
 
 }  // namespace moe
