@@ -704,18 +704,19 @@ __global__ __launch_bounds__(kWlThreads) void plan_kernel(FfnParams p) {
 
 // ------------------------------------------------------------------ combine
 
-constexpr int kCombineCols = 2 * kThreads;   // output columns per workgroup
+constexpr int kCombineCols = 4 * kThreads;   // output columns per workgroup
 constexpr int kMaxK = 32;
 
-// y[t, c..c+1] = sum over slots j in order of w[t,j] * o[route_pos[t*k+j], c..c+1].
-// One workgroup per (token, 512 columns): the token's weights and route
-// positions are staged once, then every o load is issued before the sum.
+// y[t, c..c+3] = sum over slots j in order of w[t,j] * o[route_pos[t*k+j], c..c+3].
+// One workgroup per (token, 1024 columns): the token's weights and route
+// positions are staged once, then every o load (16 bytes per thread) is
+// issued before the sum.
 __global__ __launch_bounds__(kThreads) void combine_kernel(FfnParams p) {
   __shared__ float s_w[kMaxK];
   __shared__ int s_pos[kMaxK];
   const int col_blocks = (p.H + kCombineCols - 1) / kCombineCols;
   const int t = blockIdx.x / col_blocks;
-  const int c = (blockIdx.x - t * col_blocks) * kCombineCols + 2 * threadIdx.x;
+  const int c = (blockIdx.x - t * col_blocks) * kCombineCols + 4 * threadIdx.x;
   const int R = p.T * p.k;
   if (threadIdx.x < p.k) {
     s_w[threadIdx.x] = p.topk_w[(size_t)t * p.k + threadIdx.x];
@@ -723,19 +724,22 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(FfnParams p) {
   }
   __syncthreads();
   if (c >= p.H) return;
-  float2 ov[kMaxK];
+  float4 ov[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j)
-    if (j < p.k) ov[j] = *reinterpret_cast<const float2*>(p.o + (size_t)s_pos[j] * p.H + c);
-  float y0 = 0.0f, y1 = 0.0f;
+    if (j < p.k) ov[j] = *reinterpret_cast<const float4*>(p.o + (size_t)s_pos[j] * p.H + c);
+  float y0 = 0.0f, y1 = 0.0f, y2 = 0.0f, y3 = 0.0f;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j < p.k) {
       y0 = fmaf(s_w[j], ov[j].x, y0);
       y1 = fmaf(s_w[j], ov[j].y, y1);
+      y2 = fmaf(s_w[j], ov[j].z, y2);
+      y3 = fmaf(s_w[j], ov[j].w, y3);
     }
   }
-  reinterpret_cast<uint32_t*>(p.y)[((size_t)t * p.H + c) >> 1] = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
+  reinterpret_cast<uint2*>(p.y)[((size_t)t * p.H + c) >> 2] =
+      make_uint2(f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16), f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16));
 }
 
 // ------------------------------------------------------------------ down + combine (small batches)
