@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=8,
                     help="layers of the chained leg: router projection + routed step per layer, layer l+1's "
                          "input = layer l's input + its output, layer l on weight bank l (0 skips the leg)")
+    ap.add_argument("--protocol", type=int, default=1,
+                    help="1: add the protocol figures (timed rounds, cache-resident step, FFN alone, copy ceiling); "
+                         "0: skip them (counter runs)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the bench, run a plain device-to-device copy of this many MiB three times "
                          "(the known-size kernel that calibrates FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -274,6 +277,82 @@ def cpu_baseline(cfg, budget_s: float, expert_bytes: int):
     return out
 
 
+def protocol_leg(step, full, gu_steps, xs, ls, bias, banks, pks, stream, dev, NB, eff_tbps, route_bytes,
+                 bytes_per_step):
+    """Measurement protocol figures beside the contract's single timed region:
+    seven timed rounds of about 100 steps each (median, min, max), the same
+    step replayed on one bank and routing set (cache-resident: the MALL holds
+    its experts), the expert FFN alone (moe_expert_ffn over the NB pairs, HIP
+    events), a plain device-to-device copy as the box's practical bandwidth
+    ceiling, and the bytes a per-route kernel would stream."""
+    import numpy as np
+    import torch
+    log("[bench] protocol figures")
+    rounds = []
+    per_round = max(1, 100 // NB)
+    for _ in range(7):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(per_round):
+            full.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rounds.append(e0.elapsed_time(e1) * 1e3 / (per_round * NB))
+    g_hot = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_hot):
+        for _ in range(NB):
+            step.run(xs[0], ls[0], bias, banks[0], packed=pks[0])
+    g_hot.replay()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(per_round):
+        g_hot.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    hot_us = e0.elapsed_time(e1) * 1e3 / (per_round * NB)
+    g_ffn = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_ffn):
+        for b in range(NB):
+            gu_steps[b].ffn(xs[b], banks[b], stage=3)
+    g_ffn.replay()
+    e0.record(stream)
+    for _ in range(per_round):
+        g_ffn.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ffn_us = e0.elapsed_time(e1) * 1e3 / (per_round * NB)
+    cbytes = 1 << 30
+    csrc = torch.ones(cbytes, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    e0.record(stream)
+    for _ in range(5):
+        cdst.copy_(csrc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_tbps = 2 * cbytes * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del csrc, cdst
+    protocol = {
+        "rounds_us_per_step": {"median": round(float(np.median(rounds)), 3), "min": round(min(rounds), 3),
+                               "max": round(max(rounds), 3), "rounds": 7, "steps_per_round": per_round * NB},
+        "hot_us_per_step": round(hot_us, 3),
+        "hot_note": "one bank and routing set replayed: its experts stay in the 256 MB Infinity Cache",
+        "ffn_only_us": round(ffn_us, 3),
+        "ffn_only_note": "moe_expert_ffn alone on the standard weight layout (routing prepared), HIP events over "
+                         "the NB pairs; only moe_step_packed's MFMA tiles read the packed copy, so at decode sizes "
+                         "the kernels are the step's",
+        "copy_ceiling_TBps": round(copy_tbps, 3),
+        "value_frac_of_copy": round(eff_tbps / copy_tbps, 4),
+        "route_issued_bytes_per_step": int(route_bytes),
+        "reuse_factor": round(route_bytes / bytes_per_step, 3),
+    }
+    log(f"[bench] rounds median {protocol['rounds_us_per_step']['median']} us, hot {hot_us:.2f} us, "
+        f"ffn {ffn_us:.2f} us, copy {copy_tbps:.2f} TB/s")
+
+    return protocol
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -384,76 +463,10 @@ def main():
     achieved = dom_bytes / avg / 1e9
     log(f"[bench] {kname} avg {avg * 1e6:.2f} us over {n_dom} launches -> {achieved:.1f} GB/s")
 
-    # Measurement protocol figures beside the contract's single timed region:
-    # seven timed rounds of about 100 steps each (median, min, max), the same
-    # step replayed on one bank and routing set (cache-resident: the MALL
-    # holds its experts), the expert FFN alone (moe_expert_ffn over the NB
-    # pairs, HIP events), a plain device-to-device copy as the box's practical
-    # bandwidth ceiling, and the bytes a per-route kernel would stream.
-    log("[bench] protocol figures")
-    rounds = []
-    per_round = max(1, 100 // NB)
-    for _ in range(7):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(per_round):
-            full.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        rounds.append(e0.elapsed_time(e1) * 1e3 / (per_round * NB))
-    g_hot = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_hot):
-        for _ in range(NB):
-            step.run(xs[0], ls[0], bias, banks[0], packed=pks[0])
-    g_hot.replay()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(per_round):
-        g_hot.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    hot_us = e0.elapsed_time(e1) * 1e3 / (per_round * NB)
-    g_ffn = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_ffn):
-        for b in range(NB):
-            gu_steps[b].ffn(xs[b], banks[b], stage=3)
-    g_ffn.replay()
-    e0.record(stream)
-    for _ in range(per_round):
-        g_ffn.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ffn_us = e0.elapsed_time(e1) * 1e3 / (per_round * NB)
-    cbytes = 1 << 30
-    csrc = torch.ones(cbytes, dtype=torch.uint8, device=dev)
-    cdst = torch.empty_like(csrc)
-    cdst.copy_(csrc)
-    e0.record(stream)
-    for _ in range(5):
-        cdst.copy_(csrc)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_tbps = 2 * cbytes * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12
-    del csrc, cdst
-    route_bytes = n_routes * expert_bytes
-    protocol = {
-        "rounds_us_per_step": {"median": round(float(np.median(rounds)), 3), "min": round(min(rounds), 3),
-                               "max": round(max(rounds), 3), "rounds": 7, "steps_per_round": per_round * NB},
-        "hot_us_per_step": round(hot_us, 3),
-        "hot_note": "one bank and routing set replayed: its experts stay in the 256 MB Infinity Cache",
-        "ffn_only_us": round(ffn_us, 3),
-        "ffn_only_note": "moe_expert_ffn alone on the standard weight layout (routing prepared), HIP events over "
-                         "the NB pairs; only moe_step_packed's MFMA tiles read the packed copy, so at decode sizes "
-                         "the kernels are the step's",
-        "copy_ceiling_TBps": round(copy_tbps, 3),
-        "value_frac_of_copy": round(eff_tbps / copy_tbps, 4),
-        "route_issued_bytes_per_step": int(route_bytes),
-        "reuse_factor": round(route_bytes / bytes_per_step, 3),
-    }
-    log(f"[bench] rounds median {protocol['rounds_us_per_step']['median']} us, hot {hot_us:.2f} us, "
-        f"ffn {ffn_us:.2f} us, copy {copy_tbps:.2f} TB/s")
+    protocol = None
+    if args.protocol:
+        protocol = protocol_leg(step, full, gu_steps, xs, ls, bias, banks, pks, stream, dev, NB, eff_tbps,
+                                n_routes * expert_bytes, bytes_per_step)
 
     out = {
         "metric": METRIC,
@@ -479,8 +492,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg.name),
                      "avg_launch_us": round(avg * 1e6, 3),
                      "bytes_per_launch": int(dom_bytes), "launches": n_dom},
-        "protocol": protocol,
     }
+    if protocol is not None:
+        out["protocol"] = protocol
     if args.router_copies > 0:
         log(f"[bench] router projection leg ({args.router_copies} weight copies)")
         out["router"] = router_leg(args, cfg, wls[0], dev)
