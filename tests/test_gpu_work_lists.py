@@ -100,3 +100,24 @@ def test_wide_expert_count(T, path):
     assert_route(g, idx, w)
     assert_buckets(g, b)
     assert_output(g["y"][toks], y, f"E=1000 T={T}")
+
+
+@pytest.mark.parametrize("path", ["step", "packed", "calls"])
+@pytest.mark.parametrize("T,E,k", [(17, 1, 1), (200, 1, 1), (70, 8, 8)])
+def test_every_token_on_every_expert(T, E, k, path):
+    """k = E: every expert takes every token.  E = 1 at T = 17 (one row-dot
+    expert in the sorted list) and T = 200 (one expert, a full 128-route
+    chunk and a 72-route one on the MFMA path); E = k = 8 at T = 70 (eight
+    MFMA items of 70 routes)."""
+    from dataclasses import replace
+    from moe_inputs.configs import get_config
+    cfg = replace(get_config("tiny"), name="work_list_all", H=256, I=128, E=E, k=k, T=T)
+    wl = make_workload(cfg, x_seed=9)
+    st = _run(wl, wl.logits, None, path)
+    g = collect(st)
+    toks = [0, T // 2, T - 1]
+    idx, w, b, y = oracle_all(wl.x, wl.logits, None, wl.bank, wl.k, tokens=toks)
+    assert np.all(b["expert_count"] == T)
+    assert_route(g, idx, w)
+    assert_buckets(g, b)
+    assert_output(g["y"][toks], y, f"k=E={E} T={T}")
