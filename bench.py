@@ -356,7 +356,7 @@ def protocol_leg(step, full, gu_steps, xs, ls, bias, banks, pks, stream, dev, NB
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
