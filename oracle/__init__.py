@@ -12,6 +12,7 @@ What it computes (one routed-MoE step of a decode/verify batch):
   bucket_routes   per-expert route counts, offsets, active list, stable order
   moe_output      per route: SiLU(W_gate x) * (W_up x), then W_down; weighted
                   sum over each token's k routes in slot order
+  shared_expert_output  the dense BF16 shared expert for every token
 
 Sources: the routing rule of the fused MoE routing kernel (page "How I forked
 vLLM and made Qwen3.8-Flash-Next decode 1.6x faster on one GPU", section
@@ -35,8 +36,10 @@ from .route import route_topk, selection_order, renormalised_weights
 from .router import router_logits
 from .buckets import bucket_routes
 from .ffn import expert_route_output, moe_output, ExpertDecoder
+from .shared import shared_expert_output
 
 __all__ = [
+    "shared_expert_output",
     "E2M1_VALUES",
     "e4m3_table",
     "bf16_bits_to_f64",
