@@ -326,6 +326,40 @@ moe_status moe_step_packed(const uint16_t* x, const float* logits, const float* 
                            uint16_t* y,
                            void* stream);
 
+/*
+ * Bytes of device workspace moe_shared_expert needs (0 when T <= 0): the
+ * intermediate h, T*Is bf16 values, rounded up to 256 bytes.
+ */
+size_t moe_shared_expert_workspace_size(int T, int H, int Is);
+
+/*
+ * moe_shared_expert — the dense shared expert that every token goes through,
+ * beside the routed ones, with BF16 weights (page "How I forked vLLM and made
+ * Qwen3.8-Flash-Next decode 1.6x faster on one GPU", section "2. FP8 for the
+ * dense layers"; page "Persistent execution for Flash-Next GGUF on SM70",
+ * section "Opportunity sized from the actual routes", on running it beside
+ * the routed work):
+ *   h_t = bf16(SiLU(W_gate x_t) * (W_up x_t)),   y_t = bf16(W_down h_t)
+ * with fp32 accumulation, sums in a fixed order (bitwise reproducible).  The
+ * caller adds y to the routed output; to overlap the two, enqueue this call
+ * on a second stream.
+ *   x          [T, H] bf16 bits         in
+ *   w_gate     [Is, H] bf16 bits        in   (rows = outputs)
+ *   w_up       [Is, H] bf16 bits        in
+ *   w_down     [H, Is] bf16 bits        in
+ *   workspace  >= moe_shared_expert_workspace_size(T, H, Is) bytes, owned by
+ *              the caller, contents unspecified before and after
+ *   y          [T, H] bf16 bits         out
+ * Shapes: T >= 0 (T = 0 launches nothing), H and Is multiples of 32 (else
+ * MOE_ERR_INVALID_SHAPE).  Envelope: H and Is multiples of 512 up to 4096,
+ * T <= 2^20 (else MOE_ERR_UNSUPPORTED).  Decode-sized batches: the tokens
+ * are taken four at a time by every weight row.
+ */
+moe_status moe_shared_expert(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up,
+                             const uint16_t* w_down, int T, int H, int Is,
+                             void* workspace, size_t workspace_bytes,
+                             uint16_t* y, void* stream);
+
 /* Static English description of a status code (never NULL). */
 const char* moe_status_string(moe_status s);
 

@@ -21,6 +21,7 @@ from ._lib import (
     moe_route_bucket,
     moe_router_logits,
     moe_route_topk,
+    moe_shared_expert,
     moe_status_string,
     moe_packed_weights_size,
     moe_step,
@@ -44,6 +45,7 @@ __all__ = [
     "moe_route_bucket",
     "moe_router_logits",
     "moe_route_topk",
+    "moe_shared_expert",
     "moe_status_string",
     "moe_packed_weights_size",
     "moe_step",

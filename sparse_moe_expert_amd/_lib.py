@@ -43,6 +43,8 @@ SIGNATURES = {
     "moe_packed_weights_size": (ctypes.c_size_t, [_I, _I, _I]),
     "moe_pack_weights": (_I, [_P] * 6 + [_I] * 3 + [_P, _P]),
     "moe_step_packed": (_I, [_P, _P, _P] + [_P] * 7 + [_P] + [_I] * 5 + [_P] * 8 + [_P, ctypes.c_size_t, _P, _P]),
+    "moe_shared_expert_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
+    "moe_shared_expert": (_I, [_P] * 4 + [_I] * 3 + [_P, ctypes.c_size_t, _P, _P]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -118,6 +120,29 @@ def moe_router_logits(x: torch.Tensor, w_router: torch.Tensor,
     st = load_library().moe_router_logits(_ptr(x), _ptr(w_router), T, H, E, _ptr(logits), _stream(dev))
     _check("moe_router_logits", st)
     return logits
+
+
+def moe_shared_expert(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                      y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The dense shared expert: bf16 y [T,H] = W_down (SiLU(W_gate x) * (W_up x))
+    for every token, bf16 weights w_gate/w_up [Is,H] and w_down [H,Is]."""
+    T, H = x.shape
+    Is = w_gate.shape[0]
+    dev = x.device
+    x = _check_x(x)
+    for t, name, shape in ((w_gate, "w_gate", (Is, H)), (w_up, "w_up", (Is, H)), (w_down, "w_down", (H, Is))):
+        _need(t, name, torch.bfloat16, shape, dev)
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, (T, H), dev)
+    lib = load_library()
+    ws_bytes = lib.moe_shared_expert_workspace_size(T, H, Is)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    st = lib.moe_shared_expert(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), T, H, Is, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _ptr(y), _stream(dev))
+    _check("moe_shared_expert", st)
+    return y
 
 
 def moe_route_topk(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int,

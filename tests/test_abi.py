@@ -173,3 +173,24 @@ def test_step_workspace_size(lib):
     for shape in [(4, 2048, 512, 512, 10), (4, 256, 128, 8, 2), (33, 2048, 512, 512, 10), (1, 32, 32, 2, 1)]:
         assert lib.moe_step_workspace_size(*shape) == lib.moe_expert_ffn_workspace_size(*shape)
     assert lib.moe_step_workspace_size(0, 2048, 512, 512, 10) == 0
+
+
+def test_shared_expert_host_checks(lib):
+    """Shape, envelope, pointer and workspace checks of moe_shared_expert
+    before any launch (no device work: every case fails on the host)."""
+    import ctypes
+    buf = (ctypes.c_uint8 * 64)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    al = ctypes.c_void_p((ctypes.addressof(buf) + 15) & ~15)
+    f = lib.moe_shared_expert
+    assert f(al, al, al, al, -1, 512, 512, al, 1 << 20, al, None) == 2          # T < 0
+    assert f(al, al, al, al, 4, 48, 512, al, 1 << 20, al, None) == 2           # H not a multiple of 32
+    assert f(al, al, al, al, 4, 256, 512, al, 1 << 20, al, None) == 3          # H not a multiple of 512
+    assert f(al, al, al, al, 4, 8192, 512, al, 1 << 20, al, None) == 3         # H > 4096
+    assert f(al, al, al, al, 0, 512, 512, None, 0, None, None) == 0            # T = 0: nothing to do
+    assert f(None, al, al, al, 4, 512, 512, al, 1 << 20, al, None) == 1        # null x
+    assert f(al, al, al, al, 4, 512, 512, al, 16, al, None) == 5               # workspace too small
+    mis = ctypes.c_void_p(al.value + 4)
+    assert f(mis, al, al, al, 4, 512, 512, al, 1 << 20, al, None) == 4        # misaligned x
+    assert lib.moe_shared_expert_workspace_size(4, 2048, 512) == 4096
+    assert lib.moe_shared_expert_workspace_size(0, 2048, 512) == 0
