@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=8,
                     help="layers of the chained leg: router projection + routed step per layer, layer l+1's "
                          "input = layer l's input + its output, layer l on weight bank l (0 skips the leg)")
+    ap.add_argument("--shared", type=int, default=1,
+                    help="1: the chained layers again with a dense bf16 shared expert per layer, after and beside "
+                         "the routed step (0 skips the leg)")
     ap.add_argument("--protocol", type=int, default=1,
                     help="1: add the protocol figures (timed rounds, cache-resident step, FFN alone, copy ceiling); "
                          "0: skip them (counter runs)")
@@ -228,6 +231,85 @@ def layers_leg(args, cfg, x0, banks, pks, bias, dev, expert_bytes: int):
             "bytes_per_pass": int(nbytes), "passes": reps,
             "per_layer": "router projection + route/bucket + expert FFN (library) + residual add (torch, bf16); "
                          "the input of layer l+1 is the input of layer l plus its output"}
+
+
+def shared_expert_weights(L, H, Is, dev, seed=500):
+    """Per layer a dense bf16 SwiGLU shared expert: W_g, W_u [Is, H] and W_d
+    [H, Is], drawn N(0, 1/fan_in) and rounded to bf16."""
+    import numpy as np
+    import torch
+    out = []
+    for l in range(L):
+        rng = np.random.default_rng([seed, l])
+        wg = rng.standard_normal((Is, H)) / np.sqrt(H)
+        wu = rng.standard_normal((Is, H)) / np.sqrt(H)
+        wd = rng.standard_normal((H, Is)) / np.sqrt(Is)
+        out.append(tuple(torch.from_numpy(w.astype(np.float32)).to(dev).to(torch.bfloat16) for w in (wg, wu, wd)))
+    return out
+
+
+def shared_leg(args, cfg, x0, banks, pks, bias, dev, expert_bytes: int):
+    """The chained layers with a dense shared expert per layer (bf16 weights,
+    Is = I, moe_shared_expert), its output added to the routed one.  Timed
+    twice, one graph each: the shared expert on the routed step's stream
+    after it, and on a second stream beside it (forked after the router
+    projection, joined before the residual add)."""
+    import numpy as np
+    import torch
+    import sparse_moe_expert_amd as sme
+    from moe_inputs import make_workload
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    L = min(args.layers, len(banks))
+    w_rs = [torch.from_numpy(make_workload(cfg.name, seed=cfg.seed + 100 + l, with_bank=False).w_router).to(dev)
+            for l in range(L)]
+    w_sh = shared_expert_weights(L, H, I, dev)
+    steps = [sme.MoeStep(T, H, I, E, k, dev, path=args.path) for _ in range(L)]
+    logits = [torch.empty((T, E), dtype=torch.float32, device=dev) for _ in range(L)]
+    xs_l = [x0.view(torch.bfloat16)] + [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    ys = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    ws = [torch.empty(max(16, sme.load_library().moe_shared_expert_workspace_size(T, H, I)), dtype=torch.uint8,
+                      device=dev) for _ in range(L)]
+    side = torch.cuda.Stream(dev)      # default priority
+
+    def one_pass(overlap):
+        main = torch.cuda.current_stream(dev)
+        for l in range(L):
+            sme.moe_router_logits(xs_l[l], w_rs[l], logits[l])
+            if overlap:
+                side.wait_stream(main)
+                with torch.cuda.stream(side):
+                    sme.moe_shared_expert(xs_l[l], *w_sh[l], y=ys[l], workspace=ws[l])
+                steps[l].run(xs_l[l], logits[l], bias, banks[l], packed=pks[l])
+                main.wait_stream(side)
+            else:
+                steps[l].run(xs_l[l], logits[l], bias, banks[l], packed=pks[l])
+                sme.moe_shared_expert(xs_l[l], *w_sh[l], y=ys[l], workspace=ws[l])
+            torch.add(torch.add(xs_l[l], steps[l].y), ys[l], out=xs_l[l + 1])
+
+    res = {}
+    for overlap in (False, True):
+        one_pass(overlap)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one_pass(overlap)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // (4 * L))
+        stream = torch.cuda.current_stream(dev)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["overlapped" if overlap else "sequential"] = round(e0.elapsed_time(e1) * 1e3 / reps / L, 3)
+    return {"layers": L, "us_per_layer_sequential": res["sequential"], "us_per_layer_overlapped": res["overlapped"],
+            "shared_expert": f"dense SwiGLU, bf16 weights, H={H}, Is={I} ({3 * H * I * 2} bytes per layer), "
+                             "moe_shared_expert",
+            "per_layer": "router projection + routed step + shared expert (library) + residual add (torch)"}
 
 
 def cpu_baseline(cfg, budget_s: float, expert_bytes: int):
@@ -501,6 +583,9 @@ def main():
     if args.layers > 0:
         log(f"[bench] chained layers leg ({min(args.layers, NB)} layers)")
         out["layers"] = layers_leg(args, cfg, xs[0], banks, pks, bias, dev, expert_bytes)
+    if args.layers > 0 and args.shared:
+        log("[bench] shared-expert leg")
+        out["shared"] = shared_leg(args, cfg, xs[0], banks, pks, bias, dev, expert_bytes)
     if args.copy_mb > 0:
         nbytes = args.copy_mb << 20
         src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
