@@ -250,10 +250,12 @@ def shared_expert_weights(L, H, Is, dev, seed=500):
 
 def shared_leg(args, cfg, x0, banks, pks, bias, dev, expert_bytes: int):
     """The chained layers with a dense shared expert per layer (bf16 weights,
-    Is = I, moe_shared_expert), its output added to the routed one.  Timed
-    twice, one graph each: the shared expert on the routed step's stream
-    after it, and on a second stream beside it (forked after the router
-    projection, joined before the residual add)."""
+    Is = I), its output added to the routed one.  Timed three ways, one graph
+    each: moe_shared_expert on the routed step's stream after it; on a second
+    stream beside it (forked after the router projection, joined before the
+    residual add); and moe_step_shared, whose launches carry the shared
+    expert's rows.  Then moe_shared_expert alone, cycling over enough weight
+    copies that each call reads its weights from HBM."""
     import numpy as np
     import torch
     import sparse_moe_expert_amd as sme
@@ -271,11 +273,15 @@ def shared_leg(args, cfg, x0, banks, pks, bias, dev, expert_bytes: int):
                       device=dev) for _ in range(L)]
     side = torch.cuda.Stream(dev)      # default priority
 
-    def one_pass(overlap):
+    def one_pass(mode):
         main = torch.cuda.current_stream(dev)
         for l in range(L):
             sme.moe_router_logits(xs_l[l], w_rs[l], logits[l])
-            if overlap:
+            if mode == "fused":
+                s = steps[l]
+                sme.moe_step_shared(xs_l[l], logits[l], bias, banks[l], k, s.topk_idx, s.topk_w, s.buckets,
+                                    s.workspace, s.y, w_sh[l], ys[l], ws[l], packed=pks[l])
+            elif mode == "overlapped":
                 side.wait_stream(main)
                 with torch.cuda.stream(side):
                     sme.moe_shared_expert(xs_l[l], *w_sh[l], y=ys[l], workspace=ws[l])
@@ -287,12 +293,12 @@ def shared_leg(args, cfg, x0, banks, pks, bias, dev, expert_bytes: int):
             torch.add(torch.add(xs_l[l], steps[l].y), ys[l], out=xs_l[l + 1])
 
     res = {}
-    for overlap in (False, True):
-        one_pass(overlap)
+    for mode in ("sequential", "overlapped", "fused"):
+        one_pass(mode)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            one_pass(overlap)
+            one_pass(mode)
         for _ in range(3):
             g.replay()
         torch.cuda.synchronize()
@@ -305,11 +311,43 @@ def shared_leg(args, cfg, x0, banks, pks, bias, dev, expert_bytes: int):
             g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        res["overlapped" if overlap else "sequential"] = round(e0.elapsed_time(e1) * 1e3 / reps / L, 3)
+        res[mode] = round(e0.elapsed_time(e1) * 1e3 / reps / L, 3)
+    # alone: 3 * H * Is * 2 weight bytes per call, 96 copies (> the 256 MB Infinity Cache)
+    n_cp = 96
+    cps = [tuple((torch.randn(shp, device=dev) / shp[1] ** 0.5).to(torch.bfloat16)
+                 for shp in ((I, H), (I, H), (H, I))) for _ in range(n_cp)]
+    y1, w1 = ys[0], ws[0]
+    for c in cps[:4]:
+        sme.moe_shared_expert(xs_l[0], *c, y=y1, workspace=w1)
+    torch.cuda.synchronize()
+    ga = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ga):
+        for c in cps:
+            sme.moe_shared_expert(xs_l[0], *c, y=y1, workspace=w1)
+    ga.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record(stream)
+    for _ in range(reps):
+        ga.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_alone = e0.elapsed_time(e1) * 1e3 / reps / n_cp
+    wbytes = 3 * H * I * 2
+    del cps
     return {"layers": L, "us_per_layer_sequential": res["sequential"], "us_per_layer_overlapped": res["overlapped"],
+            "us_per_layer_fused": res["fused"],
+            "alone": {"us_per_call": round(us_alone, 3), "weight_bytes": wbytes,
+                      "achieved_GBps": round(wbytes / us_alone / 1e3, 1),
+                      "frac_of_8TBps": round(wbytes / us_alone / 1e3 / 8000.0, 4),
+                      "note": "moe_shared_expert alone (two kernels), 96 weight copies in turn, HIP events"},
             "shared_expert": f"dense SwiGLU, bf16 weights, H={H}, Is={I} ({3 * H * I * 2} bytes per layer), "
                              "moe_shared_expert",
-            "per_layer": "router projection + routed step + shared expert (library) + residual add (torch)"}
+            "per_layer": "router projection + routed step + shared expert (library) + residual add (torch); "
+                         "fused: moe_step_shared in place of the step and the shared-expert call"}
 
 
 def cpu_baseline(cfg, budget_s: float, expert_bytes: int):

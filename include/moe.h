@@ -360,6 +360,44 @@ moe_status moe_shared_expert(const uint16_t* x, const uint16_t* w_gate, const ui
                              void* workspace, size_t workspace_bytes,
                              uint16_t* y, void* stream);
 
+/*
+ * moe_step_shared — one routed step and the dense shared expert of the same
+ * tokens in one call (page "Persistent execution for Flash-Next GGUF on
+ * SM70", section "Opportunity sized from the actual routes": the shared
+ * expert's work runs beside the routed experts'; page "How I forked vLLM and
+ * made Qwen3.8-Flash-Next decode 1.6x faster on one GPU", section "2. FP8
+ * for the dense layers": its weights stay BF16).
+ *   Arguments up to y: as moe_step, plus `packed` (NULL: none) as in
+ *              moe_step_packed.  y receives the routed output, bit for bit
+ *              what moe_step / moe_step_packed writes.
+ *   se_gate, se_up [Is, H], se_down [H, Is], se_workspace, y_shared: as
+ *              w_gate, w_up, w_down, workspace and y of moe_shared_expert;
+ *              y_shared receives bit for bit what moe_shared_expert writes.
+ *              The caller adds y and y_shared.  No output may overlap
+ *              another output or an input.
+ * The shared expert's argument checks come first, then the step's; a
+ * failing check launches nothing.  At decode sizes (at most 8 tokens with at
+ * most 512 experts, or 16 tokens with at most 1024; H of 512, 1024 or 2048
+ * for the gate/up rows, Is of 512 or 1024 for the down rows) the shared
+ * expert's rows run as extra workgroups of the step's routing and gate/up
+ * launches; otherwise its own two kernels run on the same stream.
+ */
+moe_status moe_step_shared(const uint16_t* x, const float* logits, const float* bias,
+                           const uint8_t* w_gate, const uint8_t* s_gate,
+                           const uint8_t* w_up, const uint8_t* s_up,
+                           const uint8_t* w_down, const uint8_t* s_down,
+                           const float* g_scale, const uint8_t* packed,
+                           int T, int H, int I, int E, int k,
+                           int32_t* topk_idx, float* topk_w,
+                           int32_t* expert_count, int32_t* expert_offset,
+                           int32_t* active_experts, int32_t* n_active,
+                           int32_t* route_src, int32_t* route_pos,
+                           void* workspace, size_t workspace_bytes, uint16_t* y,
+                           const uint16_t* se_gate, const uint16_t* se_up,
+                           const uint16_t* se_down, int Is,
+                           void* se_workspace, size_t se_workspace_bytes,
+                           uint16_t* y_shared, void* stream);
+
 /* Static English description of a status code (never NULL). */
 const char* moe_status_string(moe_status s);
 

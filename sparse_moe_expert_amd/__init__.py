@@ -22,6 +22,7 @@ from ._lib import (
     moe_router_logits,
     moe_route_topk,
     moe_shared_expert,
+    moe_step_shared,
     moe_status_string,
     moe_packed_weights_size,
     moe_step,
@@ -46,6 +47,7 @@ __all__ = [
     "moe_router_logits",
     "moe_route_topk",
     "moe_shared_expert",
+    "moe_step_shared",
     "moe_status_string",
     "moe_packed_weights_size",
     "moe_step",

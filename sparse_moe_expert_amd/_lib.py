@@ -45,6 +45,8 @@ SIGNATURES = {
     "moe_step_packed": (_I, [_P, _P, _P] + [_P] * 7 + [_P] + [_I] * 5 + [_P] * 8 + [_P, ctypes.c_size_t, _P, _P]),
     "moe_shared_expert_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
     "moe_shared_expert": (_I, [_P] * 4 + [_I] * 3 + [_P, ctypes.c_size_t, _P, _P]),
+    "moe_step_shared": (_I, [_P, _P, _P] + [_P] * 7 + [_P] + [_I] * 5 + [_P] * 8 + [_P, ctypes.c_size_t, _P]
+                        + [_P] * 3 + [_I, _P, ctypes.c_size_t, _P, _P]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -350,6 +352,51 @@ def moe_step(x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor]
                                         ctypes.c_size_t(workspace.numel()), _ptr(y), _stream(dev))
     _check("moe_step_packed", st)
     return y
+
+
+def moe_step_shared(x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor], weights: ExpertWeights,
+                    k: int, topk_idx: torch.Tensor, topk_w: torch.Tensor, buckets: Buckets,
+                    workspace: torch.Tensor, y: torch.Tensor, shared: tuple, y_shared: torch.Tensor,
+                    se_workspace: torch.Tensor, packed: Optional[torch.Tensor] = None) -> tuple:
+    """moe_step (moe_step_packed with `packed`) and the dense shared expert
+    `shared` = (w_gate [Is,H], w_up [Is,H], w_down [H,Is], bf16) of the same
+    tokens in one call: y = the routed output, y_shared = the shared expert's."""
+    x = _check_x(x)
+    T, H = x.shape
+    E, H_w, I = weights.shape
+    dev = x.device
+    if H_w != H:
+        raise ValueError(f"weights are for H={H_w}, x has H={H}")
+    _need(logits, "logits", torch.float32, (T, E), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,), dev)
+    shapes = [(E, I, H // 2), (E, I, H // 16), (E, I, H // 2), (E, I, H // 16),
+              (E, H, I // 2), (E, H, I // 16)]
+    for name, t, shp in zip(ExpertWeights._fields, weights, shapes):
+        _need(t, name, torch.uint8, shp, dev)
+    _need(weights.g_scale, "g_scale", torch.float32, (E, 3), dev)
+    _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    for name, t, n in zip(Buckets._fields, buckets, (E, E + 1, E, 1, T * k, T * k)):
+        _need(t, name, torch.int32, (n,), dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    _need(y, "y", torch.bfloat16, (T, H), dev)
+    w_g, w_u, w_d = shared
+    Is = w_g.shape[0]
+    for t, name, shape in ((w_g, "w_gate", (Is, H)), (w_u, "w_up", (Is, H)), (w_d, "w_down", (H, Is))):
+        _need(t, name, torch.bfloat16, shape, dev)
+    _need(y_shared, "y_shared", torch.bfloat16, (T, H), dev)
+    _need(se_workspace, "se_workspace", torch.uint8, None, dev)
+    if packed is not None:
+        _need(packed, "packed", torch.uint8, (moe_packed_weights_size(E, H, I),), dev)
+    st = load_library().moe_step_shared(_ptr(x), _ptr(logits), _ptr(bias), *(_ptr(t) for t in weights),
+                                        _ptr(packed), T, H, I, E, k, _ptr(topk_idx), _ptr(topk_w),
+                                        *(_ptr(t) for t in buckets), _ptr(workspace),
+                                        ctypes.c_size_t(workspace.numel()), _ptr(y), _ptr(w_g), _ptr(w_u),
+                                        _ptr(w_d), Is, _ptr(se_workspace), ctypes.c_size_t(se_workspace.numel()),
+                                        _ptr(y_shared), _stream(dev))
+    _check("moe_step_shared", st)
+    return y, y_shared
 
 
 def moe_status_string(status: int) -> str:

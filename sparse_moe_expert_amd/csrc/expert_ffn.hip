@@ -50,6 +50,7 @@
 #include <type_traits>
 
 #include "row_dot.h"
+#include "shared_rows.h"
 #include "work_list.h"
 
 namespace moe {
@@ -83,6 +84,7 @@ struct FfnParams {
   int plan_max;            // capacity of the item list
   int32_t* rd_list;        // workspace: row-dot experts, most routes first (plan_kernel)
   int rd_plan;             // the row-dot kernels take their experts from rd_list
+  SharedRows sr;           // shared-expert down rows riding along in gate_up_kernel (dn_nc 0: none)
 };
 
 constexpr int kGuUnits = 4;          // gate rows (and as many up rows) per wave per tile
@@ -290,7 +292,12 @@ __global__ __launch_bounds__(kThreads, 4) void gate_up_kernel(FfnParams p, int n
   // one task per workgroup (the host launches exactly n_tasks): no loop
   // around the tile, so the compiler's load waits stay per use
   const int task = blockIdx.x;
-  if (task >= n_tasks) return;
+  if (task >= n_tasks) {
+    // workgroups after the tasks: down rows of a shared expert (moe_step_shared)
+    se_down_side(p.sr, (task - n_tasks) * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
+                 threadIdx.x & (kWave - 1));
+    return;
+  }
   const int a = task / g.tiles, tile = task - a * g.tiles;
   const int e = row_dot_expert(p, a);
   if (e < 0) return;
@@ -925,7 +932,9 @@ constexpr int kMfmaMinRoutesPacked = 1; // with the packed copy: every expert of
 
 template <int LG>
 void launch_gate_up(const FfnParams& p, long long tasks, hipStream_t s) {
-  const unsigned grid = (unsigned)std::max<long long>(1, tasks);
+  const int side_waves = p.sr.dn_nc > 0 ? (p.sr.H + kSeSideDownRows - 1) / kSeSideDownRows : 0;
+  const unsigned grid = (unsigned)(std::max<long long>(1, tasks) + (side_waves + kThreads / kWave - 1) /
+                                                                       (kThreads / kWave));
   const int row_bytes = p.H * 2;
   const size_t x_lds = (size_t)std::max(1, std::min(kXStageBytes / row_bytes, 64)) * row_bytes;
   gate_up_kernel<LG><<<grid, kThreads, x_lds, s>>>(p, (int)tasks);
@@ -1003,7 +1012,8 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
                       const int32_t* expert_offset, const int32_t* active_experts, const int32_t* n_active,
                       const int32_t* route_src, const int32_t* route_pos, const uint8_t* packed, int T, int H,
                       int I, int E, int k, void* workspace, size_t workspace_bytes, uint16_t* y, hipStream_t s,
-                      bool lists_ready) {
+                      bool lists_ready, const SharedRows* sr, bool* sr_done) {
+  if (sr_done) *sr_done = false;
   if (stage < 1 || stage > 3) return MOE_ERR_INVALID_SHAPE;
   if (T < 0 || k < 1 || E < 1 || k > E || H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
     return MOE_ERR_INVALID_SHAPE;
@@ -1035,6 +1045,7 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   p.plan_max = L.plan_max;
   p.rd_list = reinterpret_cast<int32_t*>(ws + L.rd_off);
   p.y = y;
+  p.sr = SharedRows{};
   p.lr_gu = lr_gu;
   p.lr_d = lr_d;
   p.packed = packed;
@@ -1060,6 +1071,8 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   }
   if (stage & 1) {
     if (row_dots) {
+      p.sr = sr && sr->dn_nc > 0 ? *sr : SharedRows{};
+      if (sr_done) *sr_done = p.sr.dn_nc > 0;
       if (lr_gu == 64) launch_gate_up<64>(p, tasks_gu, s);
       else launch_gate_up<0>(p, tasks_gu, s);
       if (launch_status() != MOE_OK) return MOE_ERR_HIP;

@@ -97,6 +97,31 @@ struct WorkLists {
   int rd_plan;        // the row-dot kernels read rd_list
 };
 
+// A dense bf16 shared expert computed within a routed step (moe_step_shared):
+// x [T,H], wg / wu [Is,H], wd [H,Is], h [T,Is] (workspace), y [T,H].  Its
+// gate/up rows may ride along in the one-workgroup routing kernel and its
+// down rows in the gate/up row-dot kernel, as extra workgroups of those
+// launches.  gu_nc / dn_nc: 16-byte chunks per lane of a gate/up row
+// (H / 512) and of a down row (Is / 512), 0 where that half cannot ride
+// along (the ride-along code is compiled for gu_nc 1, 2, 4 and dn_nc 1, 2).
+struct SharedRows {
+  const uint16_t* x;
+  const uint16_t* wg;
+  const uint16_t* wu;
+  const uint16_t* wd;
+  uint16_t* h;
+  uint16_t* y;
+  int T, H, Is;
+  int gu_nc, dn_nc;
+};
+
+// Argument checks of moe_shared_expert (no launch)
+moe_status shared_check(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                        int T, int H, int Is, const void* workspace, size_t workspace_bytes, const uint16_t* y);
+// The shared expert's own kernels: gate/up, then down
+moe_status shared_gate_up(const SharedRows& s, hipStream_t st);
+moe_status shared_down(const SharedRows& s, hipStream_t st);
+
 // Whether moe_expert_ffn for these sizes reads work lists, and where they go
 // in its workspace (*wl); *scratch_bytes = the workspace bytes in front of
 // them, free until the expert kernels run.
@@ -105,24 +130,29 @@ bool ffn_work_lists(int T, int H, int I, int E, int k, bool packed, void* worksp
 
 // The expert FFN as in moe_expert_ffn_stage, with the packed weights (NULL:
 // none; the MFMA tiles then read the standard layout).  lists_ready: the
-// work lists were built by the bucketing (moe_step) for these buckets.
+// work lists were built by the bucketing (moe_step) for these buckets.  With
+// `sr` (may be NULL; its gate/up rows already enqueued) the gate/up row-dot
+// kernel also computes the shared expert's down rows; *sr_done says whether it
+// did.
 moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const uint8_t* s_gate,
                       const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
                       const float* g_scale, const float* topk_w, const int32_t* expert_count,
                       const int32_t* expert_offset, const int32_t* active_experts, const int32_t* n_active,
                       const int32_t* route_src, const int32_t* route_pos, const uint8_t* packed, int T, int H,
                       int I, int E, int k, void* workspace, size_t workspace_bytes, uint16_t* y, hipStream_t s,
-                      bool lists_ready = false);
+                      bool lists_ready = false, const SharedRows* sr = nullptr, bool* sr_done = nullptr);
 
 // Routing and bucketing as in moe_route_bucket; `scratch` (may be NULL) is
 // device memory the call may use until it returns (large batches bucket in
 // parallel with it; moe_step lends the FFN workspace, unused at that point).
 // With `wl` (may be NULL) the one-workgroup bucketing kernels also build the
-// expert kernels' work lists; *lists_built says whether they did.
+// expert kernels' work lists; *lists_built says whether they did.  With `sr`
+// (may be NULL) the one-workgroup routing kernel also computes the shared
+// expert's gate/up rows; *sr_done says whether it did.
 moe_status route_bucket(const float* logits, const float* bias, int T, int E, int k, int32_t* topk_idx,
                         float* topk_w, int32_t* expert_count, int32_t* expert_offset, int32_t* active_experts,
                         int32_t* n_active, int32_t* route_src, int32_t* route_pos, int32_t* scratch,
                         size_t scratch_bytes, hipStream_t s, const WorkLists* wl = nullptr,
-                        bool* lists_built = nullptr);
+                        bool* lists_built = nullptr, const SharedRows* sr = nullptr, bool* sr_done = nullptr);
 
 }  // namespace moe

@@ -29,7 +29,8 @@ static moe_status step(const uint16_t* x, const float* logits, const float* bias
                        const uint8_t* s_down, const float* g_scale, const uint8_t* packed, int T, int H, int I,
                        int E, int k, int32_t* topk_idx, float* topk_w, int32_t* expert_count,
                        int32_t* expert_offset, int32_t* active_experts, int32_t* n_active, int32_t* route_src,
-                       int32_t* route_pos, void* workspace, size_t workspace_bytes, uint16_t* y, void* stream) {
+                       int32_t* route_pos, void* workspace, size_t workspace_bytes, uint16_t* y, void* stream,
+                       const moe::SharedRows* side = nullptr) {
   // argument checks of the FFN call first, so that an invalid call launches nothing
   if (T < 0 || k < 1 || E < 1 || k > E || H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
     return MOE_ERR_INVALID_SHAPE;
@@ -58,15 +59,21 @@ static moe_status step(const uint16_t* x, const float* logits, const float* bias
   moe::WorkLists wl;
   size_t scratch_bytes = workspace_bytes;
   const bool want_lists = moe::ffn_work_lists(T, H, I, E, k, packed != nullptr, workspace, &wl, &scratch_bytes);
-  bool lists_built = false;
-  const moe_status st = moe::route_bucket(logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset,
-                                          active_experts, n_active, route_src, route_pos,
-                                          static_cast<int32_t*>(workspace), scratch_bytes, s,
-                                          want_lists ? &wl : nullptr, &lists_built);
+  bool lists_built = false, gu_done = false, dn_done = false;
+  moe_status st = moe::route_bucket(logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset,
+                                    active_experts, n_active, route_src, route_pos, static_cast<int32_t*>(workspace),
+                                    scratch_bytes, s, want_lists ? &wl : nullptr, &lists_built, side, &gu_done);
   if (st != MOE_OK) return st;
-  return moe::expert_ffn(3, x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
-                         expert_offset, active_experts, n_active, route_src, route_pos, packed, T, H, I, E, k,
-                         workspace, workspace_bytes, y, s, lists_built);
+  // a shared expert's gate/up rows that did not ride along in the routing
+  // kernel run on their own before the expert kernels (whose row-dot kernel
+  // may carry its down rows)
+  if (side && !gu_done && moe::shared_gate_up(*side, s) != MOE_OK) return MOE_ERR_HIP;
+  st = moe::expert_ffn(3, x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
+                       expert_offset, active_experts, n_active, route_src, route_pos, packed, T, H, I, E, k,
+                       workspace, workspace_bytes, y, s, lists_built, side, &dn_done);
+  if (st != MOE_OK) return st;
+  if (side && !dn_done) return moe::shared_down(*side, s);
+  return MOE_OK;
 }
 
 extern "C" moe_status moe_step(const uint16_t* x, const float* logits, const float* bias,
@@ -94,4 +101,30 @@ extern "C" moe_status moe_step_packed(const uint16_t* x, const float* logits, co
   return step(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, packed, T, H, I, E, k, topk_idx,
               topk_w, expert_count, expert_offset, active_experts, n_active, route_src, route_pos, workspace,
               workspace_bytes, y, stream);
+}
+
+// The step and a dense bf16 shared expert of the same tokens: y as
+// moe_step(_packed) computes it, y_shared as moe_shared_expert does, bit for
+// bit.  At decode sizes the shared expert's rows ride along in the step's own
+// launches (gate/up in the routing kernel, down in the gate/up row-dot
+// kernel) instead of two kernels of their own.
+extern "C" moe_status moe_step_shared(const uint16_t* x, const float* logits, const float* bias,
+                                      const uint8_t* w_gate, const uint8_t* s_gate, const uint8_t* w_up,
+                                      const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                                      const float* g_scale, const uint8_t* packed, int T, int H, int I, int E,
+                                      int k, int32_t* topk_idx, float* topk_w, int32_t* expert_count,
+                                      int32_t* expert_offset, int32_t* active_experts, int32_t* n_active,
+                                      int32_t* route_src, int32_t* route_pos, void* workspace,
+                                      size_t workspace_bytes, uint16_t* y, const uint16_t* se_gate,
+                                      const uint16_t* se_up, const uint16_t* se_down, int Is, void* se_workspace,
+                                      size_t se_workspace_bytes, uint16_t* y_shared, void* stream) {
+  const moe_status st = moe::shared_check(x, se_gate, se_up, se_down, T, H, Is, se_workspace, se_workspace_bytes,
+                                          y_shared);
+  if (st != MOE_OK) return st;
+  const int gu = H / 512, dn = Is / 512;
+  const moe::SharedRows side{x, se_gate, se_up, se_down, static_cast<uint16_t*>(se_workspace), y_shared, T, H, Is,
+                             (gu == 1 || gu == 2 || gu == 4) ? gu : 0, (dn == 1 || dn == 2) ? dn : 0};
+  return step(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, packed, T, H, I, E, k, topk_idx,
+              topk_w, expert_count, expert_offset, active_experts, n_active, route_src, route_pos, workspace,
+              workspace_bytes, y, stream, &side);
 }

@@ -30,6 +30,7 @@
 // wavefronts in the chunk + the expert's running base gives the position.
 // Positions never depend on timing, so the result is exact and reproducible.
 #include "select.h"
+#include "shared_rows.h"
 #include "work_list.h"
 
 namespace moe {
@@ -280,7 +281,14 @@ __global__ __launch_bounds__(NT) void route_bucket_small_kernel(
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
-    int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos) {
+    int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos, SharedRows sr) {
+  // workgroups after the first compute rows of a shared expert's gate/up
+  // (moe_step_shared), one per wave, while the first one routes
+  if (blockIdx.x > 0) {
+    se_gate_up_side(sr, (int)(blockIdx.x - 1) * (NT / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
+                    threadIdx.x & (kWave - 1));
+    return;
+  }
   __shared__ int s_cnt[NT];
   __shared__ int s_ids[kSmallMaxRoutes];
   constexpr int NW = NT / kWave;
@@ -434,8 +442,10 @@ namespace moe {
 moe_status route_bucket(const float* logits, const float* bias, int T, int E, int k, int32_t* topk_idx,
                         float* topk_w, int32_t* expert_count, int32_t* expert_offset, int32_t* active_experts,
                         int32_t* n_active, int32_t* route_src, int32_t* route_pos, int32_t* scratch,
-                        size_t scratch_bytes, hipStream_t s, const WorkLists* wl, bool* lists_built) {
+                        size_t scratch_bytes, hipStream_t s, const WorkLists* wl, bool* lists_built,
+                        const SharedRows* sr, bool* sr_done) {
   if (lists_built) *lists_built = false;
+  if (sr_done) *sr_done = false;
   const WorkLists lists = wl ? *wl : WorkLists{};
   moe_status st = check_route_args(logits, bias, T, E, k, topk_idx, topk_w);
   if (st != MOE_OK) return st;
@@ -444,13 +454,16 @@ moe_status route_bucket(const float* logits, const float* bias, int T, int E, in
   const int bits = id_bits_for(E);
   const int V = (E + kWave - 1) / kWave;
   if (T <= kSmallMaxTokens && T * k <= kSmallMaxRoutes) {
+    const SharedRows side = sr && sr->gu_nc > 0 ? *sr : SharedRows{};
+    const int side_rows = side.gu_nc > 0 ? side.Is : 0;
+    if (sr_done) *sr_done = side_rows > 0;
 #define MOE_RBS1(VV, KK)                                                                                       \
-  if (E <= 512 && T <= 8) route_bucket_small_kernel<VV, KK, 512><<<1, 512, 0, s>>>(logits, bias, T, E, k, topk_idx, topk_w, \
-                                                                 expert_count, expert_offset, active_experts,     \
-                                                                 n_active, route_src, route_pos); else \
-  route_bucket_small_kernel<VV, KK, 1024><<<1, 1024, 0, s>>>(logits, bias, T, E, k, topk_idx, topk_w,       \
-                                                                 expert_count, expert_offset, active_experts,     \
-                                                                 n_active, route_src, route_pos)
+  if (E <= 512 && T <= 8) route_bucket_small_kernel<VV, KK, 512><<<1 + (side_rows + 7) / 8, 512, 0, s>>>(     \
+      logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset, active_experts, n_active, route_src, \
+      route_pos, side); else                                                                                   \
+  route_bucket_small_kernel<VV, KK, 1024><<<1 + (side_rows + 15) / 16, 1024, 0, s>>>(                         \
+      logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset, active_experts, n_active, route_src, \
+      route_pos, side)
 #define MOE_RBS(VV) \
   if (k == kUnrolledK) MOE_RBS1(VV, kUnrolledK); else MOE_RBS1(VV, 0)
     if (V <= 1) { MOE_RBS(1); }

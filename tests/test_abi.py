@@ -193,4 +193,24 @@ def test_shared_expert_host_checks(lib):
     mis = ctypes.c_void_p(al.value + 4)
     assert f(mis, al, al, al, 4, 512, 512, al, 1 << 20, al, None) == 4        # misaligned x
     assert lib.moe_shared_expert_workspace_size(4, 2048, 512) == 4096
+
+
+def test_step_shared_host_checks(lib):
+    """moe_step_shared checks the shared expert's arguments, then the step's,
+    before any launch (every case fails on the host)."""
+    import ctypes
+    buf = (ctypes.c_uint8 * 64)()
+    al = ctypes.c_void_p((ctypes.addressof(buf) + 15) & ~15)
+    f = lib.moe_step_shared
+
+    def call(T=4, H=512, I=256, E=64, k=4, Is=512, se=al, se_bytes=1 << 20, x=al):
+        return f(x, al, None, *([al] * 7), None, T, H, I, E, k, *([al] * 8), al, 1 << 30, al,
+                 se, al, al, Is, al, se_bytes, al, None)
+    assert call(Is=100) == 2                      # Is not a multiple of 32
+    assert call(Is=8192) == 3                     # Is above the envelope
+    assert call(se=None) == 1                     # null shared-expert weight
+    assert call(se_bytes=16) == 5                 # shared workspace too small
+    assert call(E=0) == 2                         # the step's own shape check
+    assert call(k=65, E=128) == 3                 # the step's envelope (k > 32)
+    assert call(T=0, x=None) == 0                 # T = 0: nothing to do
     assert lib.moe_shared_expert_workspace_size(0, 2048, 512) == 0

@@ -64,3 +64,57 @@ def test_beside_routed_step():
     idx, w = oracle.route_topk(wl.logits, None, wl.k)
     ref = oracle.moe_output(wl.x, wl.bank, idx, w) + oracle.shared_expert_output(wl.x, wg, wu, wd)
     assert_output(y, ref, "routed + shared, two streams")
+
+
+def _custom(T, H, I, E, k):
+    from dataclasses import replace
+    from moe_inputs.configs import get_config
+    return make_workload(replace(get_config("tiny"), name="step_shared", T=T, H=H, I=I, E=E, k=k), x_seed=T + E)
+
+
+# (workload, Is, packed): which of the shared expert's halves ride along in
+# the step's launches - decode_t4: both (512-thread routing workgroup);
+# T=12: both (1024-thread routing workgroup, two chunks per down row);
+# verify_t32: gate/up on its own (routing takes several kernels), down in
+# the row-dot kernel; decode_t256_zipf packed: down on its own (no row-dot
+# kernel), standard layout: down beside the sorted row-dot experts; H=512,
+# Is=2048: gate/up with one chunk per row, down on its own (four chunks).
+STEP_SHARED_CASES = [
+    ("decode_t4", 512, True), ((12, 2048, 512, 512, 10), 1024, True), ("verify_t32", 512, True),
+    ("decode_t256_zipf", 512, True), ("decode_t256_zipf", 512, False), ((5, 512, 256, 64, 4), 2048, False),
+]
+
+
+@pytest.mark.parametrize("case", STEP_SHARED_CASES,
+                         ids=lambda c: "%s_Is%d_%s" % (c[0] if isinstance(c[0], str) else "T%d_H%d_I%d_E%d_k%d" % c[0],
+                                                       c[1], "packed" if c[2] else "std"))
+def test_step_shared(case):
+    """moe_step_shared: y bit for bit moe_step(_packed)'s, y_shared bit for
+    bit moe_shared_expert's and within tolerance of the oracle's."""
+    name, Is, packed = case
+    wl = make_workload(name) if isinstance(name, str) else _custom(*name)
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    wg, wu, wd = _weights(H, Is, seed=T + Is)
+    gw, uw, dw = _dev_bf16(wg), _dev_bf16(wu), _dev_bf16(wd)
+    x = x_bits(wl.x)
+    logits = to_dev(wl.logits)
+    bias = None if wl.bias is None else to_dev(wl.bias)
+    W = device_weights(wl.bank)
+    pk = device_packed(wl.bank) if packed else None
+    path = "packed" if packed else "step"
+    ref_step = sme.MoeStep(T, H, I, E, k, DEV, path=path)
+    ref_step.run(x, logits, bias, W, packed=pk)
+    ref_shared = sme.moe_shared_expert(x, gw, uw, dw)
+    st = sme.MoeStep(T, H, I, E, k, DEV, path=path)
+    ys = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(max(16, sme.load_library().moe_shared_expert_workspace_size(T, H, Is)), dtype=torch.uint8,
+                     device=DEV)
+    for _ in range(2):   # a second call over the same buffers gives the same bits
+        sme.moe_step_shared(x, logits, bias, W, k, st.topk_idx, st.topk_w, st.buckets, st.workspace, st.y,
+                            (gw, uw, dw), ys, ws, packed=pk)
+        torch.cuda.synchronize()
+        assert torch.equal(st.topk_idx, ref_step.topk_idx)
+        assert torch.equal(st.y.view(torch.int16), ref_step.y.view(torch.int16))
+        assert torch.equal(ys.view(torch.int16), ref_shared.view(torch.int16))
+    ref = oracle.shared_expert_output(wl.x, wg, wu, wd)
+    assert_output(ys.float().cpu().numpy().astype(np.float64), ref, f"moe_step_shared {case}")
