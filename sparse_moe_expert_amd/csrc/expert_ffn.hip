@@ -289,15 +289,20 @@ __global__ __launch_bounds__(kThreads, 4) void gate_up_kernel(FfnParams p, int n
   __shared__ __align__(16) uint8_t s_sc[2 * kScaleTileBytes];
   extern __shared__ __align__(16) uint8_t s_x[];                // activation rows of a group of routes
   const Geo<LG, kGuUnits> g(p.lr_gu, p.I);
-  // one task per workgroup (the host launches exactly n_tasks): no loop
-  // around the tile, so the compiler's load waits stay per use
-  const int task = blockIdx.x;
-  if (task >= n_tasks) {
-    // workgroups after the tasks: down rows of a shared expert (moe_step_shared)
-    se_down_side(p.sr, (task - n_tasks) * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
+  // one task per workgroup (the host launches n_tasks of them after the
+  // shared rows' ones): no loop around the tile, so the compiler's load waits
+  // stay per use
+  // the first workgroups take the down rows of a shared expert
+  // (moe_step_shared), if any: dispatched first, they run beside the tasks
+  // instead of after them
+  const int side = se_down_side_blocks(p.sr, kThreads / kWave);
+  if ((int)blockIdx.x < side) {
+    se_down_side(p.sr, (int)blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
                  threadIdx.x & (kWave - 1));
     return;
   }
+  const int task = blockIdx.x - side;
+  if (task >= n_tasks) return;
   const int a = task / g.tiles, tile = task - a * g.tiles;
   const int e = row_dot_expert(p, a);
   if (e < 0) return;
@@ -932,9 +937,7 @@ constexpr int kMfmaMinRoutesPacked = 1; // with the packed copy: every expert of
 
 template <int LG>
 void launch_gate_up(const FfnParams& p, long long tasks, hipStream_t s) {
-  const int side_waves = p.sr.dn_nc > 0 ? (p.sr.H + kSeSideDownRows - 1) / kSeSideDownRows : 0;
-  const unsigned grid = (unsigned)(std::max<long long>(1, tasks) + (side_waves + kThreads / kWave - 1) /
-                                                                       (kThreads / kWave));
+  const unsigned grid = (unsigned)(std::max<long long>(1, tasks) + se_down_side_blocks(p.sr, kThreads / kWave));
   const int row_bytes = p.H * 2;
   const size_t x_lds = (size_t)std::max(1, std::min(kXStageBytes / row_bytes, 64)) * row_bytes;
   gate_up_kernel<LG><<<grid, kThreads, x_lds, s>>>(p, (int)tasks);

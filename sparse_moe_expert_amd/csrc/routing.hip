@@ -275,6 +275,12 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_scatter_kernel(
 constexpr int kSmallMaxTokens = 16;
 constexpr int kSmallMaxRoutes = 256;
 
+// shared-expert gate/up rows per extra workgroup of the small routing kernel
+// (two per 512-thread workgroup, two of which fit a compute unit; four per
+// 1024-thread one, one of which fits): every such workgroup resident at once
+template <int NT>
+constexpr int kSmallSideWaves = NT >= 1024 ? 4 : 2;
+
 template <int V, int KC, int NT>
 __global__ __launch_bounds__(NT) void route_bucket_small_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
@@ -283,10 +289,13 @@ __global__ __launch_bounds__(NT) void route_bucket_small_kernel(
     int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
     int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos, SharedRows sr) {
   // workgroups after the first compute rows of a shared expert's gate/up
-  // (moe_step_shared), one per wave, while the first one routes
+  // (moe_step_shared), one per wave, while the first one routes; only the
+  // first kSmallSideWaves<NT> waves of such a workgroup take rows, which
+  // spreads the weight and activation reads over more compute units
   if (blockIdx.x > 0) {
-    se_gate_up_side(sr, (int)(blockIdx.x - 1) * (NT / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
-                    threadIdx.x & (kWave - 1));
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w < kSmallSideWaves<NT>)
+      se_gate_up_side(sr, (int)(blockIdx.x - 1) * kSmallSideWaves<NT> + w, threadIdx.x & (kWave - 1));
     return;
   }
   __shared__ int s_cnt[NT];
@@ -458,10 +467,10 @@ moe_status route_bucket(const float* logits, const float* bias, int T, int E, in
     const int side_rows = side.gu_nc > 0 ? side.Is : 0;
     if (sr_done) *sr_done = side_rows > 0;
 #define MOE_RBS1(VV, KK)                                                                                       \
-  if (E <= 512 && T <= 8) route_bucket_small_kernel<VV, KK, 512><<<1 + (side_rows + 7) / 8, 512, 0, s>>>(     \
+  if (E <= 512 && T <= 8) route_bucket_small_kernel<VV, KK, 512><<<1 + (side_rows + kSmallSideWaves<512> - 1) / kSmallSideWaves<512>, 512, 0, s>>>(     \
       logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset, active_experts, n_active, route_src, \
       route_pos, side); else                                                                                   \
-  route_bucket_small_kernel<VV, KK, 1024><<<1 + (side_rows + 15) / 16, 1024, 0, s>>>(                         \
+  route_bucket_small_kernel<VV, KK, 1024><<<1 + (side_rows + kSmallSideWaves<1024> - 1) / kSmallSideWaves<1024>, 1024, 0, s>>>(                         \
       logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset, active_experts, n_active, route_src, \
       route_pos, side)
 #define MOE_RBS(VV) \

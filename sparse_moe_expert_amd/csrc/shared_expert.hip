@@ -16,13 +16,17 @@
 namespace moe {
 namespace {
 
-constexpr int kSeThreads = 256;       // four waves, one weight row each
+constexpr int kSeThreads = 256;       // down: four waves, one weight row each
 constexpr int kSeWaves = kSeThreads / kWave;
+// gate/up: two waves (two rows of W_gate and W_up each) per workgroup, so
+// that the rows' weight and activation reads spread over more compute units
+constexpr int kSeGuThreads = 128;
+constexpr int kSeGuWaves = kSeGuThreads / kWave;
 
 template <int NC>
-__global__ __launch_bounds__(kSeThreads) void shared_gate_up_kernel(SharedRows s) {
+__global__ __launch_bounds__(kSeGuThreads) void shared_gate_up_kernel(SharedRows s) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int r = blockIdx.x * kSeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = blockIdx.x * kSeGuWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (r >= s.Is) return;
   se_gate_up_row<NC>(s, r, lane);
 }
@@ -40,16 +44,16 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 
 moe_status shared_gate_up(const SharedRows& sr, hipStream_t s) {
-  const unsigned g = (unsigned)((sr.Is + kSeWaves - 1) / kSeWaves);
+  const unsigned g = (unsigned)((sr.Is + kSeGuWaves - 1) / kSeGuWaves);
   switch (sr.H / 512) {
-    case 1: shared_gate_up_kernel<1><<<g, kSeThreads, 0, s>>>(sr); break;
-    case 2: shared_gate_up_kernel<2><<<g, kSeThreads, 0, s>>>(sr); break;
-    case 3: shared_gate_up_kernel<3><<<g, kSeThreads, 0, s>>>(sr); break;
-    case 4: shared_gate_up_kernel<4><<<g, kSeThreads, 0, s>>>(sr); break;
-    case 5: shared_gate_up_kernel<5><<<g, kSeThreads, 0, s>>>(sr); break;
-    case 6: shared_gate_up_kernel<6><<<g, kSeThreads, 0, s>>>(sr); break;
-    case 7: shared_gate_up_kernel<7><<<g, kSeThreads, 0, s>>>(sr); break;
-    default: shared_gate_up_kernel<8><<<g, kSeThreads, 0, s>>>(sr); break;
+    case 1: shared_gate_up_kernel<1><<<g, kSeGuThreads, 0, s>>>(sr); break;
+    case 2: shared_gate_up_kernel<2><<<g, kSeGuThreads, 0, s>>>(sr); break;
+    case 3: shared_gate_up_kernel<3><<<g, kSeGuThreads, 0, s>>>(sr); break;
+    case 4: shared_gate_up_kernel<4><<<g, kSeGuThreads, 0, s>>>(sr); break;
+    case 5: shared_gate_up_kernel<5><<<g, kSeGuThreads, 0, s>>>(sr); break;
+    case 6: shared_gate_up_kernel<6><<<g, kSeGuThreads, 0, s>>>(sr); break;
+    case 7: shared_gate_up_kernel<7><<<g, kSeGuThreads, 0, s>>>(sr); break;
+    default: shared_gate_up_kernel<8><<<g, kSeGuThreads, 0, s>>>(sr); break;
   }
   return launch_status();
 }

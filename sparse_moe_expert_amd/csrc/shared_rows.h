@@ -93,6 +93,11 @@ __device__ __forceinline__ void se_down_rows(const SharedRows& s, int c0, int la
 // extra workgroups) takes gate/up row v, or down rows kSeSideDownRows * v ..
 constexpr int kSeSideDownRows = 4;
 
+// workgroups of `waves` waves that the down rows take (0 when they do not ride along)
+__host__ __device__ inline int se_down_side_blocks(const SharedRows& s, int waves) {
+  return s.dn_nc > 0 ? ((s.H + kSeSideDownRows - 1) / kSeSideDownRows + waves - 1) / waves : 0;
+}
+
 __device__ __forceinline__ void se_gate_up_side(const SharedRows& s, int v, int lane) {
   if (v >= s.Is) return;
   switch (s.gu_nc) {
