@@ -90,7 +90,8 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_kernel_decode_t4_traffic.json")
 KERNEL_SOURCES = ["sparse_moe_expert_amd/csrc/expert_ffn.hip", "sparse_moe_expert_amd/csrc/row_dot.h",
-                  "sparse_moe_expert_amd/csrc/moe_common.h"]
+                  "sparse_moe_expert_amd/csrc/moe_common.h", "sparse_moe_expert_amd/csrc/shared_rows.h",
+                  "sparse_moe_expert_amd/csrc/work_list.h"]
 
 
 def kernel_sources_digest() -> str:

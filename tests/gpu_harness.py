@@ -65,10 +65,11 @@ def run_gpu(x_u16, logits, bias, bank, k, step: sme.MoeStep = None, path: str = 
     return collect(st)
 
 
-def collect(st: sme.MoeStep) -> dict:
-    """Copy every output to the host."""
+def collect(st: sme.MoeStep, with_y: bool = True) -> dict:
+    """Copy every output to the host (with_y False: routing outputs only,
+    for calls that never wrote y)."""
     b = st.buckets
-    return {
+    out = {
         "idx": st.topk_idx.cpu().numpy(),
         "w": st.topk_w.cpu().numpy(),
         "expert_count": b.expert_count.cpu().numpy(),
@@ -77,9 +78,11 @@ def collect(st: sme.MoeStep) -> dict:
         "n_active": b.n_active.cpu().numpy(),
         "route_src": b.route_src.cpu().numpy(),
         "route_pos": b.route_pos.cpu().numpy(),
-        "y": st.y.float().cpu().numpy().astype(np.float64),
-        "y_bits": st.y.view(torch.int16).cpu().numpy(),
     }
+    if with_y:
+        out["y"] = st.y.float().cpu().numpy().astype(np.float64)
+        out["y_bits"] = st.y.view(torch.int16).cpu().numpy()
+    return out
 
 
 def assert_route(g: dict, idx_ref, w_ref):
