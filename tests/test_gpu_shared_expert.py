@@ -118,3 +118,46 @@ def test_step_shared(case):
         assert torch.equal(ys.view(torch.int16), ref_shared.view(torch.int16))
     ref = oracle.shared_expert_output(wl.x, wg, wu, wd)
     assert_output(ys.float().cpu().numpy().astype(np.float64), ref, f"moe_step_shared {case}")
+
+
+def test_step_shared_graph_replays():
+    """moe_step_shared captured in a graph (decode_t4, both halves riding
+    along): three replays with inputs A, B, A and eager work between them,
+    each against the eager result for its input, bit for bit."""
+    wl = make_workload("decode_t4")
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    wg, wu, wd = _weights(H, I, seed=3)
+    sh = (_dev_bf16(wg), _dev_bf16(wu), _dev_bf16(wd))
+    W = device_weights(wl.bank)
+    pk = device_packed(wl.bank)
+    xa, xb = x_bits(wl.x), x_bits(make_workload("decode_t4", x_seed=77).x)
+    la, lb = to_dev(wl.logits), to_dev(np.roll(wl.logits, 5, axis=1).copy())
+    x_in, l_in = xa.clone(), la.clone()
+    st = sme.MoeStep(T, H, I, E, k, DEV, path="packed")
+    ys = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(max(16, sme.load_library().moe_shared_expert_workspace_size(T, H, I)), dtype=torch.uint8,
+                     device=DEV)
+
+    def call():
+        sme.moe_step_shared(x_in, l_in, None, W, k, st.topk_idx, st.topk_w, st.buckets, st.workspace, st.y, sh, ys,
+                            ws, packed=pk)
+
+    eager = {}
+    for name, xv, lv in (("A", xa, la), ("B", xb, lb)):
+        x_in.copy_(xv)
+        l_in.copy_(lv)
+        call()
+        torch.cuda.synchronize()
+        eager[name] = (st.y.clone(), ys.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for name, xv, lv in (("A", xa, la), ("B", xb, lb), ("A", xa, la)):
+        x_in.copy_(xv)
+        l_in.copy_(lv)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.y.view(torch.int16), eager[name][0].view(torch.int16)), name
+        assert torch.equal(ys.view(torch.int16), eager[name][1].view(torch.int16)), name
+        torch.add(ys, 1.0)   # eager work between replays
+        torch.cuda.synchronize()
