@@ -382,6 +382,8 @@ def cpu_baseline(cfg, budget_s: float, expert_bytes: int):
         "unit": "TB/s",
         "us_per_step": round(s_per_step * 1e6, 1),
         "cores": int(cores),
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
         "kind": "oracle",
         "sample": f"{steps} whole steps of {cfg.name} (x seeds {seed}..{seed + steps - 1}), "
                   f"route + buckets + FFN in fp64, {total:.1f} s",

@@ -551,7 +551,11 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
   t.lane = lane;
   const uint32_t code_row = (uint32_t)K / 2, scale_row = (uint32_t)K / 16;
   const uint32_t mat_codes = (uint32_t)N * code_row, mat_scales = (uint32_t)N * scale_row;
-  t.rb = GU ? make_rsrc(p.x, (uint32_t)p.T * (uint32_t)p.H * 2u) : make_rsrc(p.h, (uint32_t)R * (uint32_t)p.I * 2u);
+  // operand rows: gate/up gathers x rows by token (the host keeps T*H*2 below
+  // 2^31); down reads the item's own h rows, from a resource based at its
+  // first route, so offsets stay below 128 rows whatever the batch size
+  t.rb = GU ? make_rsrc(p.x, (uint32_t)p.T * (uint32_t)p.H * 2u)
+            : make_rsrc(p.h + (size_t)off * p.I, (uint32_t)cnt * (uint32_t)p.I * 2u);
   const int steps = K / kMmK;
   if constexpr (PACKED) {
     // packed matrices: gate and up of every expert, then down (tile order)
@@ -587,8 +591,8 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
     const int mtiles = (mc + 31) >> 5;
     __syncthreads();                                         // previous chunk done with LDS
     if (tid < kMmRoutes) {
-      const int pos = off + m0 + min(tid, mc - 1);           // rows past the chunk repeat its last route
-      s_row[tid] = GU ? min(max(p.route_src[pos] / p.k, 0), p.T - 1) : pos;
+      const int loc = m0 + min(tid, mc - 1);                 // rows past the chunk repeat its last route
+      s_row[tid] = GU ? min(max(p.route_src[off + loc] / p.k, 0), p.T - 1) : loc;
     }
     __syncthreads();
     // operand chunk q = (4i + wave)*64 + lane sits at row q/8, position q%8,
@@ -1021,6 +1025,8 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   if (T < 0 || k < 1 || E < 1 || k > E || H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
     return MOE_ERR_INVALID_SHAPE;
   if (E > 1024 || k > 32 || H > 4096 || I > 4096) return MOE_ERR_UNSUPPORTED;
+  // the activations are read through one buffer resource (32-bit offsets)
+  if ((long long)T * H * 2 >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   const int chunks_h = H / 32, chunks_i = I / 32;
   const int lr_gu = lanes_per_row(chunks_h), lr_d = lanes_per_row(chunks_i);
   // one 16-byte chunk per lane: H/32 and I/32 must be powers of two <= 64

@@ -35,6 +35,7 @@ static moe_status step(const uint16_t* x, const float* logits, const float* bias
   if (T < 0 || k < 1 || E < 1 || k > E || H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
     return MOE_ERR_INVALID_SHAPE;
   if (E > 1024 || k > 32 || H > 4096 || I > 4096) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * H * 2 >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   const int chunks_h = H / 32, chunks_i = I / 32;
   if (chunks_h != moe::lanes_per_row(chunks_h) || chunks_i != moe::lanes_per_row(chunks_i))
     return MOE_ERR_UNSUPPORTED;

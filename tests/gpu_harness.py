@@ -1,13 +1,17 @@
 """Helpers for the GPU parity tests: run the HIP path, run the oracle, compare.
 
-Acceptance (fixed before any kernel ran): expert ids and every bucket array
-bit-exact; gate weights within 1e-6 absolute; the bf16 output within
-max|y - y_ref| <= 2e-2 * rms(y_ref), rms over the compared outputs (exactly 0
-when the reference is exactly 0).  That bound is the one for the five
-workloads.  Small edge-case shapes outside them (a few dozen outputs per token)
-can have max|y_ref| well above 5 * rms, where the bf16 rounding of the output
-itself (relative 2^-8) already reaches the bound; their tests use
-assert_output_rounded, which adds half a bf16 ulp of each reference value.
+Acceptance: expert ids and every bucket array bit-exact; gate weights within
+1e-6 absolute; the bf16 output within
+
+    |y - y_ref| <= 2e-2 * rms(y_ref) + half a bf16 ulp of y_ref   (elementwise),
+
+rms over the compared outputs (and exactly 0 where the reference is exactly
+0 everywhere).  The 2e-2 * rms term bounds the computation's error; the half
+ulp is the output format's own rounding, which no bf16 output can avoid: at
+the 256-token Zipf workload max|y_ref| is ~9 rms, and the correctly rounded
+bf16 of the oracle's exact output is already 0.0211 rms away from it at two
+elements (pinned on the CPU in tests/test_rounding_model.py).  Each
+comparison also reports the plain ratio max|y - y_ref| / rms.
 """
 
 from __future__ import annotations
@@ -97,16 +101,6 @@ def assert_buckets(g: dict, b_ref: dict):
     assert int(g["n_active"][0]) == int(b_ref["n_active"])
 
 
-def assert_output(y_gpu: np.ndarray, y_ref: np.ndarray, tag: str = ""):
-    rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
-    err = float(np.max(np.abs(y_gpu - y_ref))) if y_ref.size else 0.0
-    if rms == 0.0:
-        assert err == 0.0, f"{tag}: reference is exactly 0, max|y| = {err}"
-    else:
-        assert err <= Y_REL_TOL * rms, f"{tag}: max err {err:.3e} > {Y_REL_TOL} * rms {rms:.3e}"
-    return err, rms
-
-
 def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
     """Half the bf16 spacing at |v| (8 significant bits): the largest error of
     rounding an exact value to bf16."""
@@ -115,12 +109,13 @@ def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, (e - 8).astype(np.int64))
 
 
-def assert_output_rounded(y_gpu: np.ndarray, y_ref: np.ndarray, tag: str = ""):
-    """|y - y_ref| <= 2e-2 * rms(y_ref) + half a bf16 ulp of y_ref, elementwise."""
+def assert_output(y_gpu: np.ndarray, y_ref: np.ndarray, tag: str = ""):
+    """|y - y_ref| <= 2e-2 * rms(y_ref) + half a bf16 ulp of y_ref, elementwise;
+    returns (max|y - y_ref|, rms)."""
     rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
     d = np.abs(y_gpu - y_ref)
     if rms == 0.0:
-        assert float(d.max(initial=0.0)) == 0.0, f"{tag}: reference is exactly 0"
+        assert float(d.max(initial=0.0)) == 0.0, f"{tag}: reference is exactly 0, max|y| = {d.max(initial=0.0)}"
         return 0.0, 0.0
     bound = Y_REL_TOL * rms + bf16_half_ulp(y_ref)
     worst = int(np.argmax(d - bound))
@@ -129,9 +124,42 @@ def assert_output_rounded(y_gpu: np.ndarray, y_ref: np.ndarray, tag: str = ""):
     return float(d.max()), rms
 
 
+_DECODERS = {}
+
+
+def shared_decoder(bank) -> oracle.ExpertDecoder:
+    """One oracle decoder per expert bank for the whole session, keeping every
+    expert it has decoded (the oracle's dequantisation, ~0.15 s per expert at
+    H = 2048, I = 512, costs far more than a route's products, and the
+    workloads at the Flash-Next shape share one bank: each expert is decoded
+    once per session; 512 experts hold ~12.6 GB of fp64 matrices)."""
+    key = id(bank)
+    if key not in _DECODERS:
+        _DECODERS[key] = (bank, oracle.ExpertDecoder(bank, cache=int(bank.w_gate.shape[0])))
+    return _DECODERS[key][1]
+
+
 def oracle_all(x_u16, logits, bias, bank, k, tokens=None):
     E = logits.shape[1]
     idx, w = oracle.route_topk(logits, bias, k)
     b = oracle.bucket_routes(idx, E)
-    y = oracle.moe_output(x_u16, bank, idx, w, tokens=tokens)
+    y = oracle.moe_output(x_u16, bank, idx, w, tokens=tokens, decoder=shared_decoder(bank))
     return idx, w, b, y
+
+
+def chunk_columns(idx: np.ndarray, b: dict, tokens, chunk: int = 128):
+    """Compared (expert, column-in-chunk) pairs for the routes of `tokens`.
+
+    The matrix-core kernels take an expert's routes (in bucket order) in
+    chunks of `chunk`; a route at bucket position p of expert e sits in column
+    (p - offset[e]) % chunk of its chunk, i.e. route tile col // 32 and lane
+    col % 32 of the tile.  Returns the set of (e, col) pairs and the set of
+    cols covered over all experts."""
+    k = idx.shape[1]
+    pairs = set()
+    for t in tokens:
+        for j in range(k):
+            e = int(idx[t, j])
+            p = int(b["route_pos"][t * k + j])
+            pairs.add((e, (p - int(b["expert_offset"][e])) % chunk))
+    return pairs, {c for _, c in pairs}

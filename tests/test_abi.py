@@ -108,6 +108,17 @@ def test_expert_ffn_host_checks(lib):
     assert lib.moe_expert_ffn_workspace_size(8, 256, 128, 8, 2) > need
 
 
+def test_activation_bytes_limit(lib):
+    """The activations are read through 32-bit buffer offsets: T*H*2 must stay
+    below 2^31 (else MOE_ERR_UNSUPPORTED, nothing launched); one token fewer
+    passes the envelope and fails later on the small workspace."""
+    T = (1 << 31) // (2 * 2048)
+    assert _ffn(lib, T=T, H=2048, I=512, E=512, k=10, ws=16) == 3
+    assert _ffn(lib, T=T - 1, H=2048, I=512, E=512, k=10, ws=16) == 5
+    assert _step(lib, T=T, H=2048, I=512, E=512, k=10, ws=16) == 3
+    assert _step(lib, T=T - 1, H=2048, I=512, E=512, k=10, ws=16) == 5
+
+
 def test_route_bucket_host_checks(lib):
     f = lib.moe_route_bucket
     assert f(A, None, 4, 8, 9, A, A, A, A, A, A, A, A, None) == 2

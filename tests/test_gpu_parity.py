@@ -3,8 +3,8 @@
 Expert ids and route buckets must match bit for bit; gate weights within 1e-6;
 the bf16 output within max|err| <= 2e-2 * rms(ref).  The five workloads run at
 their full sizes in the same launch configuration the benchmark times; the
-oracle computes every token for the small ones and a fixed sample of tokens
-(including ones routed to the hottest experts) for the large ones.  Edge
+oracle computes every output of every workload (every route column of the
+128-route MFMA chunks that occurs is covered).  Edge
 cases: ragged token counts, k = E, all tokens on the same experts, all
 routes on distinct experts, zero input, guard regions around the output and
 workspace, bitwise run-to-run determinism, and graph replays with changed
@@ -21,13 +21,14 @@ from gpu_harness import (
     DEV,
     assert_buckets,
     assert_output,
-    assert_output_rounded,
     assert_route,
+    chunk_columns,
     collect,
     device_packed,
     device_weights,
     oracle_all,
     run_gpu,
+    shared_decoder,
     to_dev,
     x_bits,
 )
@@ -37,33 +38,53 @@ from moe_inputs.configs import CONFIG_ORDER
 pytestmark = pytest.mark.gpu
 
 
-def _sample_tokens(wl, idx):
-    T = wl.T
-    if T <= 8:
-        return list(range(T))
-    counts = np.bincount(idx.reshape(-1), minlength=wl.E)
-    hot = int(np.argmax(counts))
-    hot_tokens = sorted(set(int(t) for t in np.argwhere(idx == hot)[:, 0]))
-    picks = {0, 1, T // 2, T - 1} | set(hot_tokens[:2]) | set(hot_tokens[-2:])
-    return sorted(picks)
+# Every workload is compared on every output (the whole [T, H] output, rms
+# over all of it).  The oracle decodes each expert of the shared bank once
+# per session.
+def _parity_tokens(wl, idx):
+    return list(range(wl.T))
+
+
+_REFS = {}
+
+
+def _workload_reference(name):
+    """Routing, buckets, compared tokens and the oracle's output on them, once
+    per workload (shared by the three paths)."""
+    if name not in _REFS:
+        wl = make_workload(name)
+        idx, w = oracle.route_topk(wl.logits, wl.bias, wl.k)
+        b = oracle.bucket_routes(idx, wl.E)
+        tokens = _parity_tokens(wl, idx)
+        y = oracle.moe_output(wl.x, wl.bank, idx, w, tokens=tokens, decoder=shared_decoder(wl.bank))
+        _REFS[name] = (wl, idx, w, b, tokens, y)
+    return _REFS[name]
 
 
 PATHS = ["step", "packed", "calls"]
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("name", CONFIG_ORDER)
 def test_workload_parity(name, path):
-    wl = make_workload(name)
-    print(f"[parity] {name} T={wl.T} E={wl.E} k={wl.k} path={path}", flush=True)
+    print(f"[parity] {name} path={path}", flush=True)
+    wl, idx, w, b, tokens, y_ref = _workload_reference(name)
     g = run_gpu(wl.x, wl.logits, wl.bias, wl.bank, wl.k, path=path)
-    idx, w = oracle.route_topk(wl.logits, wl.bias, wl.k)
     assert_route(g, idx, w)
-    assert_buckets(g, oracle.bucket_routes(idx, wl.E))
-    tokens = _sample_tokens(wl, idx)
-    y_ref = oracle.moe_output(wl.x, wl.bank, idx, w, tokens=tokens)
+    assert_buckets(g, b)
+    pairs, cols = chunk_columns(idx, b, tokens)
+    if wl.T >= 64:
+        # every route column that occurs in the 128-route chunks of the
+        # matrix-core kernels (route tile col // 32, lane col % 32) is compared
+        # somewhere
+        _, all_cols = chunk_columns(idx, b, range(wl.T))
+        assert cols == all_cols, sorted(all_cols - cols)[:8]
     err, rms = assert_output(g["y"][tokens], y_ref, name)
-    print(f"[parity] {name}: tokens={len(tokens)} max_err={err:.3e} rms={rms:.3e}", flush=True)
+    over = int(np.sum(np.abs(g["y"][tokens] - y_ref) > 2e-2 * rms))
+    print(f"[parity] {name} path={path}: tokens={len(tokens)}/{wl.T} routes={len(tokens) * wl.k} "
+          f"expert_column_pairs={len(pairs)} chunk_columns={len(cols)} max_err={err:.3e} rms={rms:.3e} "
+          f"ratio={err / rms if rms else 0.0:.4f} elements_over_plain_2e-2_rms={over}", flush=True)
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -73,11 +94,10 @@ def test_ragged_token_counts(shape, T, path):
     wl = make_workload(shape, T=T, x_seed=100 + T)
     print(f"[ragged] {shape} T={T} path={path}", flush=True)
     g = run_gpu(wl.x, wl.logits, wl.bias, wl.bank, wl.k, path=path)
-    idx, w, b, y = oracle_all(wl.x, wl.logits, wl.bias, wl.bank, wl.k,
-                              tokens=range(T) if shape == "tiny" else range(min(T, 5)))
+    idx, w, b, y = oracle_all(wl.x, wl.logits, wl.bias, wl.bank, wl.k)
     assert_route(g, idx, w)
     assert_buckets(g, b)
-    assert_output(g["y"][: y.shape[0]], y, f"{shape} T={T}")
+    assert_output(g["y"], y, f"{shape} T={T}")
 
 
 # Shapes whose row tiles run past the matrix: with H = 256 a gate/up tile
@@ -114,9 +134,9 @@ def test_ragged_row_tiles(shape, path):
     idx, w, b, y = oracle_all(wl.x, wl.logits, wl.bias, wl.bank, wl.k)
     assert_route(g, idx, w)
     assert_buckets(g, b)
-    # shapes this small have max|y| up to ~5 * rms: the output's own bf16
-    # rounding is part of the bound here
-    assert_output_rounded(g["y"], y, f"ragged tiles {shape}")
+    # shapes this small have max|y| up to ~6 * rms: the output's own bf16
+    # rounding alone can exceed 2e-2 * rms here
+    assert_output(g["y"], y, f"ragged tiles {shape}")
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -143,12 +163,12 @@ def test_all_tokens_on_same_experts(T, path):
     bias = np.zeros(wl.E, np.float32)
     bias[chosen] = 50.0
     g = run_gpu(wl.x, wl.logits, bias, wl.bank, wl.k, path=path)
-    toks = [0, T // 2, T - 1]
-    idx, w, b, y = oracle_all(wl.x, wl.logits, bias, wl.bank, wl.k, tokens=toks)
+    idx, w, b, y = oracle_all(wl.x, wl.logits, bias, wl.bank, wl.k)
     assert int(b["n_active"]) == 10 and sorted(np.unique(idx)) == chosen
     assert_route(g, idx, w)
     assert_buckets(g, b)
-    assert_output(g["y"][toks], y, "all-equal experts")
+    err, rms = assert_output(g["y"], y, "all-equal experts")
+    print(f"[same experts] T={T} path={path}: every token, max_err={err:.3e} rms={rms:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("path", ["step", "packed"])
@@ -162,11 +182,11 @@ def test_all_routes_on_distinct_experts(T, path):
     for t in range(T):
         logits[t, perm[t]] = 10.0 - np.arange(k, dtype=np.float32) * 0.5
     g = run_gpu(wl.x, logits, None, wl.bank, k, path=path)
-    idx, w, b, y = oracle_all(wl.x, logits, None, wl.bank, k, tokens=[0, T - 1])
+    idx, w, b, y = oracle_all(wl.x, logits, None, wl.bank, k)
     assert np.all(b["expert_count"][b["expert_count"] > 0] == 1) and int(b["n_active"]) == T * k
     assert_route(g, idx, w)
     assert_buckets(g, b)
-    assert_output(g["y"][[0, T - 1]], y, "all-disjoint experts")
+    assert_output(g["y"], y, "all-disjoint experts")
 
 
 def test_zero_input_gives_exact_zero():

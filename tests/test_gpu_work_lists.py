@@ -72,12 +72,12 @@ def test_chunk_boundary(T, path):
     wl, bias = _forced(T, 256, 128, 40, 4, chosen, seed=T)
     st = _run(wl, wl.logits, bias, path)
     g = collect(st)
-    toks = [0, 64, T - 1]
-    idx, w, b, y = oracle_all(wl.x, wl.logits, bias, wl.bank, wl.k, tokens=toks)
+    idx, w, b, y = oracle_all(wl.x, wl.logits, bias, wl.bank, wl.k)
     assert sorted(np.unique(idx)) == chosen and np.all(b["expert_count"][chosen] == T)
     assert_route(g, idx, w)
     assert_buckets(g, b)
-    assert_output(g["y"][toks], y, f"chunk boundary T={T}")
+    err, rms = assert_output(g["y"], y, f"chunk boundary T={T}")
+    print(f"[chunk boundary] T={T} path={path}: every token, max_err={err:.3e} rms={rms:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("path", ["step", "packed", "calls"])
@@ -95,11 +95,10 @@ def test_wide_expert_count(T, path):
     bias[[1, 500, 999]] = [3.0, 2.5, 2.0]
     st = _run(wl, wl.logits, bias, path)
     g = collect(st)
-    toks = [0, T // 2, T - 1]
-    idx, w, b, y = oracle_all(wl.x, wl.logits, bias, wl.bank, wl.k, tokens=toks)
+    idx, w, b, y = oracle_all(wl.x, wl.logits, bias, wl.bank, wl.k)
     assert_route(g, idx, w)
     assert_buckets(g, b)
-    assert_output(g["y"][toks], y, f"E=1000 T={T}")
+    assert_output(g["y"], y, f"E=1000 T={T}")
 
 
 @pytest.mark.parametrize("path", ["step", "packed", "calls"])
@@ -115,9 +114,8 @@ def test_every_token_on_every_expert(T, E, k, path):
     wl = make_workload(cfg, x_seed=9)
     st = _run(wl, wl.logits, None, path)
     g = collect(st)
-    toks = [0, T // 2, T - 1]
-    idx, w, b, y = oracle_all(wl.x, wl.logits, None, wl.bank, wl.k, tokens=toks)
+    idx, w, b, y = oracle_all(wl.x, wl.logits, None, wl.bank, wl.k)
     assert np.all(b["expert_count"] == T)
     assert_route(g, idx, w)
     assert_buckets(g, b)
-    assert_output(g["y"][toks], y, f"k=E={E} T={T}")
+    assert_output(g["y"], y, f"k=E={E} T={T}")
