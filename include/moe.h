@@ -50,7 +50,8 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = 3,         /* outside the supported envelope (see each call) */
   MOE_ERR_MISALIGNED = 4,          /* a tensor pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < moe_expert_ffn_workspace_size() */
-  MOE_ERR_HIP = 6                  /* a HIP runtime call failed (launch or device query) */
+  MOE_ERR_HIP = 6,                 /* a HIP runtime call failed (launch or device query) */
+  MOE_ERR_SCRATCH_TOO_SMALL = 7    /* moe_step_noalloc: the sizes need more than its static scratch */
 } moe_status;
 
 /*
@@ -397,6 +398,42 @@ moe_status moe_step_shared(const uint16_t* x, const float* logits, const float* 
                            const uint16_t* se_down, int Is,
                            void* se_workspace, size_t se_workspace_bytes,
                            uint16_t* y_shared, void* stream);
+
+/*
+ * moe_step_noalloc — moe_step (moe_step_packed when `packed` is not NULL)
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  It takes
+ * no workspace argument: its workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (8 MiB) inside the library, one copy per GPU the
+ * library runs on, held until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ *   Arguments and outputs: as moe_step / moe_step_packed, without workspace
+ *   and workspace_bytes; outputs bit for bit those of moe_step with a
+ *   workspace of its own.
+ *   Limit: moe_step_workspace_size(T,H,I,E,k) <= MOE_NOALLOC_SCRATCH_BYTES
+ *   (at H = 2048, I = 512, E = 512, k = 10: up to 90 tokens), else
+ *   MOE_ERR_SCRATCH_TOO_SMALL and nothing is launched; every other check as
+ *   for moe_step, before any launch.
+ *   The scratch needs no clearing: like moe_step's workspace, nothing in it
+ *   is read before the same call wrote it.  Every call on one GPU shares that
+ *   GPU's array, so calls that overlap on one GPU (on different streams, or
+ *   from different host threads) race; serialise them.  `stream` must belong
+ *   to the current device.  The first call on each device looks up the
+ *   array's device address (a host-side query, not a launch); make that
+ *   first call outside graph capture.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+moe_status moe_step_noalloc(const uint16_t* x, const float* logits, const float* bias,
+                            const uint8_t* w_gate, const uint8_t* s_gate,
+                            const uint8_t* w_up, const uint8_t* s_up,
+                            const uint8_t* w_down, const uint8_t* s_down,
+                            const float* g_scale, const uint8_t* packed,
+                            int T, int H, int I, int E, int k,
+                            int32_t* topk_idx, float* topk_w,
+                            int32_t* expert_count, int32_t* expert_offset,
+                            int32_t* active_experts, int32_t* n_active,
+                            int32_t* route_src, int32_t* route_pos,
+                            uint16_t* y, void* stream);
 
 /* Static English description of a status code (never NULL). */
 const char* moe_status_string(moe_status s);

@@ -26,7 +26,9 @@ from ._lib import (
     moe_status_string,
     moe_packed_weights_size,
     moe_step,
+    moe_step_noalloc,
     moe_step_workspace_size,
+    NOALLOC_SCRATCH_BYTES,
     pack_weights,
 )
 from .step import MoeStep, expert_weights_from_numpy
@@ -51,7 +53,9 @@ __all__ = [
     "moe_status_string",
     "moe_packed_weights_size",
     "moe_step",
+    "moe_step_noalloc",
     "moe_step_workspace_size",
+    "NOALLOC_SCRATCH_BYTES",
     "pack_weights",
     "MoeStep",
     "expert_weights_from_numpy",

@@ -25,6 +25,7 @@ MOE_STATUS = {
     4: "MOE_ERR_MISALIGNED",
     5: "MOE_ERR_WORKSPACE_TOO_SMALL",
     6: "MOE_ERR_HIP",
+    7: "MOE_ERR_SCRATCH_TOO_SMALL",
 }
 
 # Exported C symbols and their ctypes signatures.
@@ -47,6 +48,7 @@ SIGNATURES = {
     "moe_shared_expert": (_I, [_P] * 4 + [_I] * 3 + [_P, ctypes.c_size_t, _P, _P]),
     "moe_step_shared": (_I, [_P, _P, _P] + [_P] * 7 + [_P] + [_I] * 5 + [_P] * 8 + [_P, ctypes.c_size_t, _P]
                         + [_P] * 3 + [_I, _P, ctypes.c_size_t, _P, _P]),
+    "moe_step_noalloc": (_I, [_P, _P, _P] + [_P] * 7 + [_P] + [_I] * 5 + [_P] * 8 + [_P, _P]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -351,6 +353,42 @@ def moe_step(x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor]
                                         *(_ptr(t) for t in buckets), _ptr(workspace),
                                         ctypes.c_size_t(workspace.numel()), _ptr(y), _stream(dev))
     _check("moe_step_packed", st)
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20    # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_step_noalloc(x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor], weights: ExpertWeights,
+                     k: int, topk_idx: torch.Tensor, topk_w: torch.Tensor, buckets: Buckets, y: torch.Tensor,
+                     packed: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_step (moe_step_packed with `packed`) with the library's static
+    scratch as its workspace: no workspace argument, nothing allocated."""
+    x = _check_x(x)
+    T, H = x.shape
+    E, H_w, I = weights.shape
+    dev = x.device
+    if H_w != H:
+        raise ValueError(f"weights are for H={H_w}, x has H={H}")
+    _need(logits, "logits", torch.float32, (T, E), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,), dev)
+    shapes = [(E, I, H // 2), (E, I, H // 16), (E, I, H // 2), (E, I, H // 16),
+              (E, H, I // 2), (E, H, I // 16)]
+    for name, t, shp in zip(ExpertWeights._fields, weights, shapes):
+        _need(t, name, torch.uint8, shp, dev)
+    _need(weights.g_scale, "g_scale", torch.float32, (E, 3), dev)
+    _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    for name, t, n in zip(Buckets._fields, buckets, (E, E + 1, E, 1, T * k, T * k)):
+        _need(t, name, torch.int32, (n,), dev)
+    _need(y, "y", torch.bfloat16, (T, H), dev)
+    if packed is not None:
+        _need(packed, "packed", torch.uint8, (moe_packed_weights_size(E, H, I),), dev)
+    st = load_library().moe_step_noalloc(_ptr(x), _ptr(logits), _ptr(bias), *(_ptr(t) for t in weights),
+                                         _ptr(packed), T, H, I, E, k, _ptr(topk_idx), _ptr(topk_w),
+                                         *(_ptr(t) for t in buckets), _ptr(y), _stream(dev))
+    _check("moe_step_noalloc", st)
     return y
 
 

@@ -26,6 +26,8 @@ extern "C" const char* moe_status_string(moe_status s) {
     case MOE_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than moe_expert_ffn_workspace_size()";
     case MOE_ERR_HIP: return "HIP runtime error (launch or device query)";
+    case MOE_ERR_SCRATCH_TOO_SMALL:
+      return "sizes need more workspace than moe_step_noalloc's static scratch (MOE_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

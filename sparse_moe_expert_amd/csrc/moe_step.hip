@@ -17,20 +17,23 @@
 // mechanisms", paragraphs "MonoMoE" and "Hazy Research Megakernels", the
 // latter noting that publication and readiness checks are a cost of their
 // own).
+#include <mutex>
+
 #include "moe_common.h"
 
 extern "C" size_t moe_step_workspace_size(int T, int H, int I, int E, int k) {
   return moe_expert_ffn_workspace_size(T, H, I, E, k);
 }
 
-// The step with optional packed weights (NULL: none).
-static moe_status step(const uint16_t* x, const float* logits, const float* bias, const uint8_t* w_gate,
-                       const uint8_t* s_gate, const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,
-                       const uint8_t* s_down, const float* g_scale, const uint8_t* packed, int T, int H, int I,
-                       int E, int k, int32_t* topk_idx, float* topk_w, int32_t* expert_count,
-                       int32_t* expert_offset, int32_t* active_experts, int32_t* n_active, int32_t* route_src,
-                       int32_t* route_pos, void* workspace, size_t workspace_bytes, uint16_t* y, void* stream,
-                       const moe::SharedRows* side = nullptr) {
+// Host checks of the step with optional packed weights (NULL: none): every
+// argument, before anything is launched.
+static moe_status step_check(const uint16_t* x, const float* logits, const float* bias, const uint8_t* w_gate,
+                             const uint8_t* s_gate, const uint8_t* w_up, const uint8_t* s_up,
+                             const uint8_t* w_down, const uint8_t* s_down, const float* g_scale,
+                             const uint8_t* packed, int T, int H, int I, int E, int k, int32_t* topk_idx,
+                             float* topk_w, int32_t* expert_count, int32_t* expert_offset,
+                             int32_t* active_experts, int32_t* n_active, int32_t* route_src, int32_t* route_pos,
+                             const void* workspace, size_t workspace_bytes, uint16_t* y) {
   // argument checks of the FFN call first, so that an invalid call launches nothing
   if (T < 0 || k < 1 || E < 1 || k > E || H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0)
     return MOE_ERR_INVALID_SHAPE;
@@ -51,6 +54,21 @@ static moe_status step(const uint16_t* x, const float* logits, const float* bias
     if (!moe::aligned16(q)) return MOE_ERR_MISALIGNED;
   if ((bias && !moe::aligned16(bias)) || (packed && !moe::aligned16(packed))) return MOE_ERR_MISALIGNED;
   if (workspace_bytes < moe_step_workspace_size(T, H, I, E, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return MOE_OK;
+}
+
+// The step with optional packed weights (NULL: none).
+static moe_status step(const uint16_t* x, const float* logits, const float* bias, const uint8_t* w_gate,
+                       const uint8_t* s_gate, const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,
+                       const uint8_t* s_down, const float* g_scale, const uint8_t* packed, int T, int H, int I,
+                       int E, int k, int32_t* topk_idx, float* topk_w, int32_t* expert_count,
+                       int32_t* expert_offset, int32_t* active_experts, int32_t* n_active, int32_t* route_src,
+                       int32_t* route_pos, void* workspace, size_t workspace_bytes, uint16_t* y, void* stream,
+                       const moe::SharedRows* side = nullptr) {
+  const moe_status chk = step_check(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, packed, T,
+                                    H, I, E, k, topk_idx, topk_w, expert_count, expert_offset, active_experts,
+                                    n_active, route_src, route_pos, workspace, workspace_bytes, y);
+  if (chk != MOE_OK || T == 0) return chk;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   // The expert kernels' work lists, when they read any, are built by the
   // one-workgroup bucketing kernel, which holds the counts already (one
@@ -128,4 +146,59 @@ extern "C" moe_status moe_step_shared(const uint16_t* x, const float* logits, co
   return step(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, packed, T, H, I, E, k, topk_idx,
               topk_w, expert_count, expert_offset, active_experts, n_active, route_src, route_pos, workspace,
               workspace_bytes, y, stream, &side);
+}
+
+// ------------------------------------------------------------------ no allocation
+
+// The workspace of moe_step_noalloc: a static device array, one copy per GPU
+// the library runs on, held until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: kernels receive the address
+// that hipGetSymbolAddress returns for the current device (scratch_on_device).
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's copy of `scratch`, looked up on the first
+// call on each device (with that device current) and kept.
+moe_status scratch_on_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_step_noalloc(const uint16_t* x, const float* logits, const float* bias,
+                                       const uint8_t* w_gate, const uint8_t* s_gate, const uint8_t* w_up,
+                                       const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                                       const float* g_scale, const uint8_t* packed, int T, int H, int I, int E,
+                                       int k, int32_t* topk_idx, float* topk_w, int32_t* expert_count,
+                                       int32_t* expert_offset, int32_t* active_experts, int32_t* n_active,
+                                       int32_t* route_src, int32_t* route_pos, uint16_t* y, void* stream) {
+  // every host check first, against the scratch size (a stand-in aligned
+  // address: nothing is dereferenced on the host)
+  const void* stand_in = reinterpret_cast<const void*>(uintptr_t(256));
+  const moe_status chk = step_check(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, packed, T,
+                                    H, I, E, k, topk_idx, topk_w, expert_count, expert_offset, active_experts,
+                                    n_active, route_src, route_pos, stand_in, kNoAllocScratchBytes, y);
+  if (chk == MOE_ERR_WORKSPACE_TOO_SMALL) return MOE_ERR_SCRATCH_TOO_SMALL;
+  if (chk != MOE_OK || T == 0) return chk;
+  void* ws = nullptr;
+  const moe_status st = scratch_on_device(&ws);
+  if (st != MOE_OK) return st;
+  return step(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, packed, T, H, I, E, k, topk_idx,
+              topk_w, expert_count, expert_offset, active_experts, n_active, route_src, route_pos, ws,
+              kNoAllocScratchBytes, y, stream);
 }

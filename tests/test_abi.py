@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert sme.moe_status_string(s)
     assert sme.moe_status_string(99) == "unknown status"
 
@@ -225,3 +225,30 @@ def test_step_shared_host_checks(lib):
     assert call(k=65, E=128) == 3                 # the step's envelope (k > 32)
     assert call(T=0, x=None) == 0                 # T = 0: nothing to do
     assert lib.moe_shared_expert_workspace_size(0, 2048, 512) == 0
+
+
+def _noalloc(lib, T=4, H=256, I=128, E=8, k=2, null_at=None, packed=None):
+    ins = [A] * 10          # x, logits, bias, 6 weight arrays, g_scale
+    ins[2] = None
+    outs = [A] * 8          # topk_idx, topk_w, 6 bucket arrays
+    if null_at is not None:
+        (ins if null_at < 10 else outs)[null_at if null_at < 10 else null_at - 10] = None
+    return lib.moe_step_noalloc(*ins, packed, T, H, I, E, k, *outs, A, None)
+
+
+def test_step_noalloc_host_checks(lib):
+    """moe_step_noalloc checks every argument and the static scratch's size
+    (MOE_NOALLOC_SCRATCH_BYTES, 8 MiB) before any HIP call."""
+    assert sme.NOALLOC_SCRATCH_BYTES == 8 << 20
+    assert _noalloc(lib, k=9) == 2
+    assert _noalloc(lib, H=48) == 2
+    assert _noalloc(lib, E=2048) == 3
+    assert _noalloc(lib, T=0) == 0
+    assert _noalloc(lib, null_at=1) == 1
+    assert _noalloc(lib, null_at=17) == 1
+    assert _noalloc(lib, H=96, I=64, packed=A) == 3      # outside the envelope
+    # the workspace of 90 tokens at the Flash-Next shape fits the scratch, 91 do not
+    assert lib.moe_step_workspace_size(90, 2048, 512, 512, 10) <= sme.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_step_workspace_size(91, 2048, 512, 512, 10) > sme.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(lib, T=91, H=2048, I=512, E=512, k=10) == 7
+    assert _noalloc(lib, T=4096, H=2048, I=512, E=512, k=10) == 7
