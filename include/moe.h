@@ -194,9 +194,10 @@ size_t moe_expert_ffn_workspace_size(int T, int H, int I, int E, int k);
  *               call are unspecified and never need a reset.
  *   y           [T, H] bf16 bits        out
  * Shapes: T >= 0 (T = 0 launches nothing), 1 <= k <= E, H and I multiples of
- * 32.  Envelope: E <= 1024, k <= 32, H and I powers of two from 32 to 4096
- * (the Flash-Next shape H = 2048, I = 512 qualifies); else
- * MOE_ERR_UNSUPPORTED.
+ * 32.  Envelope: E <= 1024, k <= 32, H and I from 32 to 4096 (H/32 and I/32
+ * need not be powers of two: the Flash-Next expert, H = 2560 and I = 640,
+ * qualifies), T*H*2 < 2^31 (the activations are addressed with 32-bit
+ * offsets); else MOE_ERR_UNSUPPORTED.
  */
 moe_status moe_expert_ffn(const uint16_t* x,
                           const uint8_t* w_gate, const uint8_t* s_gate,

@@ -62,12 +62,30 @@ CONFIGS = {
         description="Prefill chunk T=4096, uniform routing"),
 }
 
+# The Flash-Next expert as the pages size it, beside the five workloads:
+# hidden 2560 and expert intermediate 640, i.e. 3 * (2560*640/2 + 2560*640/16)
+# = 2.637 MiB of NVFP4 per expert (page "Qwen3.8 Flash Next on LiL/vLLM: why
+# the MTP decode step is host-bound, and what LMCache does and does not do to
+# it", section "11.13 Where the decode step's time actually goes"), K = 2560
+# with 512 experts and N = 160 per rank of four (page "Persistent execution
+# for Flash-Next GGUF on SM70", section "Primary sources and transferable
+# mechanisms", paragraph "MonoMoE").  Their rows hold 80 and 20 16-byte
+# chunks, which are not powers of two.
+EXTRA_CONFIGS = {
+    "flashnext_t4": WorkloadConfig(
+        "flashnext_t4", T=4, H=2560, I=640, E=512, k=10, bias="none",
+        description="Decode verify step at the Flash-Next expert shape H=2560 I=640, T=4 E=512 top-10"),
+    "flashnext_t256": WorkloadConfig(
+        "flashnext_t256", T=256, H=2560, I=640, E=512, k=10, bias="none",
+        description="256-token batch at the Flash-Next expert shape H=2560 I=640, E=512 top-10"),
+}
+
 # Stable order used by tests and reports.
 CONFIG_ORDER = ["tiny", "decode_t4", "verify_t32", "decode_t256_zipf", "prefill_t4096"]
 
 
 def get_config(name: str) -> WorkloadConfig:
     try:
-        return CONFIGS[name]
+        return CONFIGS[name] if name in CONFIGS else EXTRA_CONFIGS[name]
     except KeyError:
         raise KeyError(f"unknown workload {name!r}; known: {CONFIG_ORDER}") from None

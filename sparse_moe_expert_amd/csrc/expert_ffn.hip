@@ -908,6 +908,280 @@ void launch_down_combine(const FfnParams& p, unsigned grid, size_t dyn, int slot
   else down_combine_kernel<LD, kDcMaxRoutes / kDcWaves><<<grid, kDcThreads, dyn, s>>>(p);
 }
 
+// ------------------------------------------------------------------ rows of several chunks per lane
+
+// Row-dot kernels for row lengths whose 16-byte chunk count C = cols/32 is
+// not a power of two up to 64 (H = 2560 and I = 640 of the Flash-Next expert
+// give C = 80 and 20; H = 4096 gives 128).  kNcLanes lanes share a row and
+// lane sl reads chunks sl, sl + 16, ..., sl + 16*(NC-1), NC = ceil(C / 16);
+// a chunk index past the row (the tail) is given an offset past the buffer
+// resource, which reads zero codes and zero scales, so it adds exactly zero
+// to the dot product (its operand chunk is read clamped to the last chunk of
+// the row: finite, and never past the buffer).  Scales are read per chunk
+// (two bytes) next to its codes; each unit's products follow the same
+// dot_chunk and fixed-order lane sums as the one-chunk kernels.
+constexpr int kNcLanes = 16;                 // lanes per row
+constexpr int kNcRowsPerWave = kWave / kNcLanes;
+constexpr uint32_t kNcOutOfRange = 0x80000000u;
+
+// Offsets of chunk i of this lane in a row of C chunks starting at byte
+// `row_code` (codes) / `row_scale` (scales); kNcOutOfRange past the row.
+__device__ __forceinline__ void nc_chunk_offsets(int sl, int i, int C, uint32_t row_code, uint32_t row_scale,
+                                                 bool row_ok, uint32_t& oc, uint32_t& os) {
+  const int c = sl + i * kNcLanes;
+  const bool ok = row_ok && c < C;
+  oc = ok ? row_code + (uint32_t)c * 16u : kNcOutOfRange;
+  os = ok ? row_scale + (uint32_t)c * 2u : kNcOutOfRange;
+}
+
+// Gate and up rows of one tile (kWavesPerBlock * kNcRowsPerWave = 16 rows of
+// I) for all routes of expert e, one row per 16-lane group.
+template <int NC>
+__global__ __launch_bounds__(kThreads, 2) void gate_up_nc_kernel(FfnParams p, int n_tasks) {
+  constexpr int kRpt = kWavesPerBlock * kNcRowsPerWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub = lane / kNcLanes, sl = lane & (kNcLanes - 1);
+  const int tiles = (p.I + kRpt - 1) / kRpt;
+  const int task = blockIdx.x;
+  if (task >= n_tasks) return;
+  const int a = task / tiles, tile = task - a * tiles;
+  const int e = row_dot_expert(p, a);
+  if (e < 0) return;
+  const int C = p.H / 32;
+  const uint32_t code_row = (uint32_t)p.H / 2, scale_row = (uint32_t)p.H / 16;
+  const uint32_t mat_codes = (uint32_t)p.I * code_row, mat_scales = (uint32_t)p.I * scale_row;
+  const auto rg = make_rsrc(p.wg + (size_t)e * mat_codes, mat_codes);
+  const auto ru = make_rsrc(p.wu + (size_t)e * mat_codes, mat_codes);
+  const auto rsg = make_rsrc(p.sg + (size_t)e * mat_scales, mat_scales);
+  const auto rsu = make_rsrc(p.su + (size_t)e * mat_scales, mat_scales);
+  const int row = tile * kRpt + wave * kNcRowsPerWave + sub;
+  const bool row_ok = row < p.I;
+  uint4 cg[NC], cu[NC];
+  uint32_t vg[NC], vu[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    uint32_t oc, os;
+    nc_chunk_offsets(sl, i, C, (uint32_t)row * code_row, (uint32_t)row * scale_row, row_ok, oc, os);
+    cg[i] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rg, oc, 0, kStreamAux));
+    cu[i] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(ru, oc, 0, kStreamAux));
+    vg[i] = __builtin_amdgcn_raw_buffer_load_b16(rsg, os, 0, kStreamAux);
+    vu[i] = __builtin_amdgcn_raw_buffer_load_b16(rsu, os, 0, kStreamAux);
+  }
+  compiler_fence();
+  int off, cnt;
+  expert_routes(p, e, off, cnt);
+  const float Gg = sload(p.gsc, e * 3 + 0), Gu = sload(p.gsc, e * 3 + 1);
+  for (int r = 0; r < cnt; ++r) {
+    const int pos = off + r;
+    const int tok = min(max(sload(p.route_src, pos) / p.k, 0), p.T - 1);
+    const uint16_t* xrow = p.x + (size_t)tok * p.H;
+    const float one = opaque_one();
+    float ag = 0.0f, au = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      uint32_t xr[16];
+      load_operand_chunk(xrow, min(sl + i * kNcLanes, C - 1), xr);
+      ag = dot_chunk(cg[i], vg[i], xr, ag, one);
+      au = dot_chunk(cu[i], vu[i], xr, au, one);
+    }
+    const float gs = row16_sum(ag) * Gg, us = row16_sum(au) * Gu;
+    if (sl == 0 && row_ok) p.h[(size_t)pos * p.I + row] = (uint16_t)f32_to_bf16_rne(silu(gs) * us);
+  }
+}
+
+// Down rows of one tile (16 rows of H) for all routes of expert e -> o (fp32).
+template <int NC>
+__global__ __launch_bounds__(kThreads, 2) void down_nc_kernel(FfnParams p, int n_tasks) {
+  constexpr int kRpt = kWavesPerBlock * kNcRowsPerWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub = lane / kNcLanes, sl = lane & (kNcLanes - 1);
+  const int tiles = (p.H + kRpt - 1) / kRpt;
+  const int task = blockIdx.x;
+  if (task >= n_tasks) return;
+  const int a = task / tiles, tile = task - a * tiles;
+  const int e = row_dot_expert(p, a);
+  if (e < 0) return;
+  const int C = p.I / 32;
+  const uint32_t code_row = (uint32_t)p.I / 2, scale_row = (uint32_t)p.I / 16;
+  const uint32_t mat_codes = (uint32_t)p.H * code_row, mat_scales = (uint32_t)p.H * scale_row;
+  const auto rd = make_rsrc(p.wd + (size_t)e * mat_codes, mat_codes);
+  const auto rds = make_rsrc(p.sd + (size_t)e * mat_scales, mat_scales);
+  const int row = tile * kRpt + wave * kNcRowsPerWave + sub;
+  const bool row_ok = row < p.H;
+  uint4 cd[NC];
+  uint32_t vd[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    uint32_t oc, os;
+    nc_chunk_offsets(sl, i, C, (uint32_t)row * code_row, (uint32_t)row * scale_row, row_ok, oc, os);
+    cd[i] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, oc, 0, kStreamAux));
+    vd[i] = __builtin_amdgcn_raw_buffer_load_b16(rds, os, 0, kStreamAux);
+  }
+  compiler_fence();
+  int off, cnt;
+  expert_routes(p, e, off, cnt);
+  const float Gd = sload(p.gsc, e * 3 + 2);
+  for (int r = 0; r < cnt; ++r) {
+    const int pos = off + r;
+    const uint16_t* hrow = p.h + (size_t)pos * p.I;
+    const float one = opaque_one();
+    float ad = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      uint32_t hr[16];
+      load_operand_chunk(hrow, min(sl + i * kNcLanes, C - 1), hr);
+      ad = dot_chunk(cd[i], vd[i], hr, ad, one);
+    }
+    const float v = row16_sum(ad) * Gd;
+    if (sl == 0 && row_ok) p.o[(size_t)pos * p.H + row] = v;
+  }
+}
+
+// Down projection and weighted unroute of a small batch (the design of
+// down_combine_kernel, rows of NC chunks per lane): workgroup b owns rows
+// [4b, 4b + 4) of y for every token; its sixteen waves take the active slots
+// a = wave + 16u, u < SLOTS; all routes' h and the o of its rows stay in LDS;
+// each token's routes are summed in slot order.
+template <int NC, int SLOTS>
+__global__ __launch_bounds__(kDcThreads, 1) void down_combine_nc_kernel(FfnParams p) {
+  extern __shared__ __align__(16) uint8_t s_dyn8[];   // [R, I] bf16 h, then [R, 4] fp32 o
+  __shared__ int s_src[kDcMaxRoutes];
+  __shared__ float s_w[kDcMaxRoutes];
+  constexpr int rpw = kNcRowsPerWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sub = lane / kNcLanes, sl = lane & (kNcLanes - 1);
+  const int row0 = blockIdx.x * rpw;
+  const int R = p.T * p.k;
+  const int S = min(p.E, R);
+  const int C = p.I / 32;
+  uint16_t* s_h = reinterpret_cast<uint16_t*>(s_dyn8);
+  float* s_o = reinterpret_cast<float*>(s_dyn8 + (size_t)R * p.I * 2);
+
+  int e_u[SLOTS];
+#pragma unroll
+  for (int u = 0; u < SLOTS; ++u) {
+    const int a = wave + u * kDcWaves;
+    e_u[u] = a < S ? slot_expert(p, a) : -1;
+  }
+  const uint32_t code_row = (uint32_t)p.I / 2, scale_row = (uint32_t)p.I / 16;
+  // one resource spans all of W_down (and one its scales); the host checks
+  // that their byte counts fit 31 bits
+  const auto rd = make_rsrc(p.wd, (uint32_t)p.E * p.H * code_row);
+  const auto rds = make_rsrc(p.sd, (uint32_t)p.E * p.H * scale_row);
+  const int row = row0 + sub;
+  const bool row_ok = row < p.H;
+  uint4 cd[SLOTS][NC];
+  uint32_t vd[SLOTS][NC];
+#pragma unroll
+  for (int u = 0; u < SLOTS; ++u) {
+    const uint32_t r = (uint32_t)max(e_u[u], 0) * (uint32_t)p.H + (uint32_t)row;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      uint32_t oc, os;
+      nc_chunk_offsets(sl, i, C, r * code_row, r * scale_row, row_ok && e_u[u] >= 0, oc, os);
+      cd[u][i] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rd, oc, 0, kStreamAux));
+      vd[u][i] = __builtin_amdgcn_raw_buffer_load_b16(rds, os, 0, kStreamAux);
+    }
+  }
+  // every route's h row into LDS (16-byte pieces; h rows are whole pieces),
+  // the route positions and gate weights, while the weights are in flight
+  const int h_pieces = R * p.I / 8;
+  for (int q = tid; q < h_pieces; q += kDcThreads)
+    reinterpret_cast<uint4*>(s_dyn8)[q] = reinterpret_cast<const uint4*>(p.h)[q];
+  if (tid < R) {
+    s_src[tid] = min(max(p.route_src[tid], 0), R - 1);
+    s_w[tid] = p.topk_w[tid];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < SLOTS; ++u) {
+    if (e_u[u] < 0) continue;
+    int off, cnt;
+    expert_routes(p, e_u[u], off, cnt);
+    const float gd = sload(p.gsc, e_u[u] * 3 + 2);
+    for (int t = 0; t < cnt; ++t) {
+      const int pos = off + t;
+      const float one = opaque_one();
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        uint32_t hr[16];
+        load_operand_chunk(s_h + (size_t)pos * p.I, min(sl + i * kNcLanes, C - 1), hr);
+        acc = dot_chunk(cd[u][i], vd[u][i], hr, acc, one);
+      }
+      const float v = row16_sum(acc) * gd;
+      if (sl == 0 && row_ok) s_o[s_src[pos] * rpw + sub] = v;
+    }
+  }
+  __syncthreads();
+  // y[t, row0 + r] = sum over slots j in order of w[t,j] * o[route (t,j), r]
+  for (int i = tid; i < p.T * rpw; i += kDcThreads) {
+    const int t = i / rpw, r = i - t * rpw;
+    if (row0 + r >= p.H) continue;
+    float acc = 0.0f;
+    for (int j = 0; j < p.k; ++j) acc = fmaf(s_w[t * p.k + j], s_o[(t * p.k + j) * rpw + r], acc);
+    p.y[(size_t)t * p.H + row0 + r] = (uint16_t)f32_to_bf16_rne(acc);
+  }
+}
+
+// Chunks per lane of the multi-chunk kernels for rows of C chunks, or 0 when
+// the one-chunk kernels take the row (C a power of two up to 64).
+inline int nc_chunks(int C) {
+  if (C <= 64 && (C & (C - 1)) == 0) return 0;
+  const int nc = (C + kNcLanes - 1) / kNcLanes;
+  return nc == 7 ? 8 : nc;                   // compiled for 1..6 and 8 (C <= 128)
+}
+
+void launch_gate_up_nc(int nc, const FfnParams& p, long long tasks, hipStream_t s) {
+  const unsigned grid = (unsigned)std::max<long long>(1, tasks);
+  switch (nc) {
+    case 1: gate_up_nc_kernel<1><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+    case 2: gate_up_nc_kernel<2><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+    case 3: gate_up_nc_kernel<3><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+    case 4: gate_up_nc_kernel<4><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+    case 5: gate_up_nc_kernel<5><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+    case 6: gate_up_nc_kernel<6><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+    default: gate_up_nc_kernel<8><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+  }
+}
+
+void launch_down_nc(int nc, const FfnParams& p, long long tasks, hipStream_t s) {
+  const unsigned grid = (unsigned)std::max<long long>(1, tasks);
+  switch (nc) {
+    case 1: down_nc_kernel<1><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+    case 2: down_nc_kernel<2><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+    case 3: down_nc_kernel<3><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+    case 4: down_nc_kernel<4><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+    case 5: down_nc_kernel<5><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+    case 6: down_nc_kernel<6><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+    default: down_nc_kernel<8><<<grid, kThreads, 0, s>>>(p, (int)tasks); break;
+  }
+}
+
+template <int NC>
+void launch_down_combine_nc_slots(const FfnParams& p, unsigned grid, size_t dyn, int slots, hipStream_t s) {
+  const int per_wave = (slots + kDcWaves - 1) / kDcWaves;
+  if (per_wave <= 1) down_combine_nc_kernel<NC, 1><<<grid, kDcThreads, dyn, s>>>(p);
+  else if (per_wave == 2) down_combine_nc_kernel<NC, 2><<<grid, kDcThreads, dyn, s>>>(p);
+  else if (per_wave <= 4) down_combine_nc_kernel<NC, 4><<<grid, kDcThreads, dyn, s>>>(p);
+  else down_combine_nc_kernel<NC, kDcMaxRoutes / kDcWaves><<<grid, kDcThreads, dyn, s>>>(p);
+}
+
+void launch_down_combine_nc(int nc, const FfnParams& p, unsigned grid, size_t dyn, int slots, hipStream_t s) {
+  switch (nc) {
+    case 1: launch_down_combine_nc_slots<1>(p, grid, dyn, slots, s); break;
+    case 2: launch_down_combine_nc_slots<2>(p, grid, dyn, slots, s); break;
+    case 3: launch_down_combine_nc_slots<3>(p, grid, dyn, slots, s); break;
+    case 4: launch_down_combine_nc_slots<4>(p, grid, dyn, slots, s); break;
+    case 5: launch_down_combine_nc_slots<5>(p, grid, dyn, slots, s); break;
+    case 6: launch_down_combine_nc_slots<6>(p, grid, dyn, slots, s); break;
+    default: launch_down_combine_nc_slots<8>(p, grid, dyn, slots, s); break;
+  }
+}
+
 // ------------------------------------------------------------------ host
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -976,12 +1250,18 @@ struct FfnPolicy {
 FfnPolicy ffn_policy(int T, int H, int I, int E, int k, bool packed) {
   FfnPolicy f;
   const long long R = (long long)T * k;
-  const int lr_d = lanes_per_row(I / 32);
+  const int lr_d = nc_chunks(I / 32) ? kNcLanes : lanes_per_row(I / 32);
   const size_t h_bytes = (size_t)R * I * 2;
   // one buffer resource spans all of W_down: its byte count must fit 31 bits
   const bool dc_fits = (size_t)E * H * (I / 2) < (size_t)0x7FFFFFFF;
   const size_t dc_lds = h_bytes + (size_t)R * (kWave / lr_d) * 4;   // h and o of the fused down/unroute kernel
-  f.down_combine = R <= kDcMaxRoutes && dc_lds <= (size_t)kDcMaxLds && dc_fits;
+  // multi-chunk rows: the fused kernel holds nc chunks of each of its waves'
+  // slots (1, 2, 4 or 8 slots per wave) in registers; beyond 8 it would spill
+  const int nc_d = nc_chunks(I / 32);
+  const long long dc_slots = std::min<long long>(E, R), per_wave = (dc_slots + kDcWaves - 1) / kDcWaves;
+  const int slots_var = per_wave <= 1 ? 1 : per_wave == 2 ? 2 : per_wave <= 4 ? 4 : 8;
+  const bool dc_regs = nc_d == 0 || nc_d * slots_var <= 8;
+  f.down_combine = R <= kDcMaxRoutes && dc_lds <= (size_t)kDcMaxLds && dc_fits && dc_regs;
   // Experts with many routes go to the MFMA kernels; only batches large
   // enough to have such experts (and not small enough for the fused
   // down/unroute kernel) launch them.  K (H for gate/up, I for down) must be a
@@ -1027,10 +1307,10 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   if (E > 1024 || k > 32 || H > 4096 || I > 4096) return MOE_ERR_UNSUPPORTED;
   // the activations are read through one buffer resource (32-bit offsets)
   if ((long long)T * H * 2 >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
-  const int chunks_h = H / 32, chunks_i = I / 32;
-  const int lr_gu = lanes_per_row(chunks_h), lr_d = lanes_per_row(chunks_i);
-  // one 16-byte chunk per lane: H/32 and I/32 must be powers of two <= 64
-  if (chunks_h != lr_gu || chunks_i != lr_d) return MOE_ERR_UNSUPPORTED;
+  // rows of C = cols/32 chunks: one chunk per lane when C is a power of two
+  // up to 64, else nc 16-lane passes (the multi-chunk kernels)
+  const int nc_gu = nc_chunks(H / 32), nc_d = nc_chunks(I / 32);
+  const int lr_gu = nc_gu ? kNcLanes : lanes_per_row(H / 32), lr_d = nc_d ? kNcLanes : lanes_per_row(I / 32);
   if (T == 0) return MOE_OK;
   const void* ptrs[] = {x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
                         expert_offset, active_experts, n_active, route_src, route_pos, workspace, y};
@@ -1066,8 +1346,8 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   p.rd_plan = pol.rd_plan ? 1 : 0;
 
   const long long slots = std::min<long long>(E, (long long)T * k);
-  const int rpt_gu = kWavesPerBlock * (kWave / lr_gu) * kGuUnits;
-  const int rpt_d = kWavesPerBlock * (kWave / lr_d) * kDUnits;
+  const int rpt_gu = nc_gu ? kWavesPerBlock * kNcRowsPerWave : kWavesPerBlock * (kWave / lr_gu) * kGuUnits;
+  const int rpt_d = nc_d ? kWavesPerBlock * kNcRowsPerWave : kWavesPerBlock * (kWave / lr_d) * kDUnits;
   const long long tasks_gu = slots * ((I + rpt_gu - 1) / rpt_gu);
   const long long tasks_d = slots * ((H + rpt_d - 1) / rpt_d);
   if (tasks_gu > kMaxGrid || tasks_d > kMaxGrid) return MOE_ERR_UNSUPPORTED;
@@ -1080,10 +1360,14 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   }
   if (stage & 1) {
     if (row_dots) {
-      p.sr = sr && sr->dn_nc > 0 ? *sr : SharedRows{};
-      if (sr_done) *sr_done = p.sr.dn_nc > 0;
-      if (lr_gu == 64) launch_gate_up<64>(p, tasks_gu, s);
-      else launch_gate_up<0>(p, tasks_gu, s);
+      if (nc_gu) {
+        launch_gate_up_nc(nc_gu, p, tasks_gu, s);      // carries no shared-expert rows
+      } else {
+        p.sr = sr && sr->dn_nc > 0 ? *sr : SharedRows{};
+        if (sr_done) *sr_done = p.sr.dn_nc > 0;
+        if (lr_gu == 64) launch_gate_up<64>(p, tasks_gu, s);
+        else launch_gate_up<0>(p, tasks_gu, s);
+      }
       if (launch_status() != MOE_OK) return MOE_ERR_HIP;
     }
     if (mfma) {
@@ -1098,12 +1382,14 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
     const int rpw = kWave / lr_d;
     const size_t dyn = h_bytes + (size_t)R * rpw * 4;
     const unsigned grid = (unsigned)((H + rpw - 1) / rpw);
-    if (lr_d == 16) launch_down_combine<16>(p, grid, dyn, (int)slots, s);
+    if (nc_d) launch_down_combine_nc(nc_d, p, grid, dyn, (int)slots, s);
+    else if (lr_d == 16) launch_down_combine<16>(p, grid, dyn, (int)slots, s);
     else launch_down_combine<0>(p, grid, dyn, (int)slots, s);
     return launch_status();
   }
   if (row_dots) {
-    if (lr_d == 16) launch_down<16>(p, tasks_d, s);
+    if (nc_d) launch_down_nc(nc_d, p, tasks_d, s);
+    else if (lr_d == 16) launch_down<16>(p, tasks_d, s);
     else launch_down<0>(p, tasks_d, s);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }

@@ -39,9 +39,6 @@ static moe_status step_check(const uint16_t* x, const float* logits, const float
     return MOE_ERR_INVALID_SHAPE;
   if (E > 1024 || k > 32 || H > 4096 || I > 4096) return MOE_ERR_UNSUPPORTED;
   if ((long long)T * H * 2 >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
-  const int chunks_h = H / 32, chunks_i = I / 32;
-  if (chunks_h != moe::lanes_per_row(chunks_h) || chunks_i != moe::lanes_per_row(chunks_i))
-    return MOE_ERR_UNSUPPORTED;
   // packed weights exist only for H and I multiples of the MFMA step
   if (packed && (H % moe::kPackK != 0 || I % moe::kPackK != 0)) return MOE_ERR_INVALID_SHAPE;
   if (T == 0) return MOE_OK;

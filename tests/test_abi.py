@@ -95,7 +95,10 @@ def test_expert_ffn_host_checks(lib):
     assert _ffn(lib, H=48) == 2          # H not a multiple of 32
     assert _ffn(lib, I=100) == 2
     assert _ffn(lib, k=9) == 2
-    assert _ffn(lib, H=96) == 3          # not a power of two
+    # H/32 = 3 and I/32 = 20 (not powers of two) pass the envelope and fail
+    # on the small workspace (nothing launched); H = 8192 is outside it
+    assert _ffn(lib, H=96, ws=16) == 5
+    assert _ffn(lib, H=2560, I=640, E=512, k=10, ws=16) == 5
     assert _ffn(lib, H=8192) == 3
     assert _ffn(lib, T=0) == 0
     assert _ffn(lib, null_at=3) == 1
@@ -149,7 +152,9 @@ def _step(lib, T=4, H=256, I=128, E=8, k=2, ws=1 << 24, null_at=None, bad_at=Non
 def test_step_host_checks(lib):
     assert _step(lib, k=9) == 2
     assert _step(lib, H=48) == 2
-    assert _step(lib, H=96) == 3
+    assert _step(lib, H=96, ws=16) == 5
+    assert _step(lib, H=2560, I=640, E=512, k=10, ws=16) == 5
+    assert _step(lib, H=8192) == 3
     assert _step(lib, E=2048) == 3
     assert _step(lib, T=0) == 0
     assert _step(lib, null_at=1) == 1           # logits
@@ -246,7 +251,8 @@ def test_step_noalloc_host_checks(lib):
     assert _noalloc(lib, T=0) == 0
     assert _noalloc(lib, null_at=1) == 1
     assert _noalloc(lib, null_at=17) == 1
-    assert _noalloc(lib, H=96, I=64, packed=A) == 3      # outside the envelope
+    assert _noalloc(lib, H=96, I=64, packed=A) == 2      # packed weights need multiples of 64
+    assert _noalloc(lib, H=8192) == 3                    # outside the envelope
     # the workspace of 90 tokens at the Flash-Next shape fits the scratch, 91 do not
     assert lib.moe_step_workspace_size(90, 2048, 512, 512, 10) <= sme.NOALLOC_SCRATCH_BYTES
     assert lib.moe_step_workspace_size(91, 2048, 512, 512, 10) > sme.NOALLOC_SCRATCH_BYTES
