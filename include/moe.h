@@ -153,7 +153,7 @@ moe_status moe_route_bucket(const float* logits, const float* bias,
 
 /*
  * Bytes of device workspace moe_expert_ffn needs for these sizes (0 when
- * T == 0 or a size is not positive): the per-route intermediates, 2*I + 4*H
+ * T == 0 or a size is not positive): the per-route intermediates, 2*I + 2*H
  * bytes per route; the dense kernels' work list, 16 bytes for each of at
  * most min(E, T*k) + T*k/128 items (rounded up to a multiple of 8) plus 16;
  * and the row-dot kernels' expert list, 4 bytes for each of min(E, T*k)
@@ -172,7 +172,10 @@ size_t moe_expert_ffn_workspace_size(int T, int H, int I, int E, int k);
  *         (a fixed order, never arrival order), rounded once to bf16 (RNE).
  * Each active expert's weights are streamed from HBM once per call for all
  * of its routes (unique-expert reuse).  Accumulation is fp32; h is kept as
- * bf16 between the two projections.
+ * bf16 between the two projections; where a route's down output o_p goes
+ * through memory (batches too large for the fused small-batch kernel) it is
+ * rounded once to fp16 before the fp32 weighting (the per-route FP16 down
+ * rounding of the SM70 design note, step 4).
  *
  * NVFP4 weights: element = e2m1 * e4m3 * global.  e2m1 codes are packed two
  * per byte, element 2i in the low nibble of byte i; one e4m3 (OCP E4M3FN)
@@ -189,7 +192,7 @@ size_t moe_expert_ffn_workspace_size(int T, int H, int I, int E, int k);
  *   route_pos                           in   (from moe_bucket_routes)
  *   workspace   device buffer of workspace_bytes >= moe_expert_ffn_workspace_size(T,H,I,E,k),
  *               owned by the caller; holds the per-route intermediates h
- *               (bf16 [T*k, I]) and o (fp32 [T*k, H]) and the work lists
+ *               (bf16 [T*k, I]) and o (fp16 [T*k, H]) and the work lists
  *               of the expert kernels.  Its contents before and after a
  *               call are unspecified and never need a reset.
  *   y           [T, H] bf16 bits        out
@@ -412,7 +415,7 @@ moe_status moe_step_shared(const uint16_t* x, const float* logits, const float* 
  *   and workspace_bytes; outputs bit for bit those of moe_step with a
  *   workspace of its own.
  *   Limit: moe_step_workspace_size(T,H,I,E,k) <= MOE_NOALLOC_SCRATCH_BYTES
- *   (at H = 2048, I = 512, E = 512, k = 10: up to 90 tokens), else
+ *   (at H = 2048, I = 512, E = 512, k = 10: up to 163 tokens), else
  *   MOE_ERR_SCRATCH_TOO_SMALL and nothing is launched; every other check as
  *   for moe_step, before any launch.
  *   The scratch needs no clearing: like moe_step's workspace, nothing in it

@@ -74,7 +74,7 @@ struct FfnParams {
   const int32_t* route_pos;
   int T, H, I, E, k;
   uint16_t* h;   // workspace: [R, I] bf16, row = bucket position
-  float* o;      // workspace: [R, H] fp32, row = bucket position
+  uint16_t* o;   // workspace: [R, H] fp16 bits, row = bucket position
   uint16_t* y;
   int lr_gu;     // lanes per gate/up row (power of two, <= 64)
   int lr_d;      // lanes per down row
@@ -358,7 +358,7 @@ __device__ __forceinline__ void down_tile(const FfnParams& p, const Geo<LD, kDUn
       const int row = g.row0(tile, u) + g.sub;
       const float v = (LD == 16 ? row16_sum(ad[u]) : group_sum(ad[u], g.lr)) * Gd;
       // with 16 lanes per row, lane u of the row stores unit u
-      if (g.sl == (LD == 16 ? u : 0) && row < p.H) p.o[(size_t)pos * p.H + row] = v;
+      if (g.sl == (LD == 16 ? u : 0) && row < p.H) p.o[(size_t)pos * p.H + row] = f32_to_f16_bits(v);
     }
   }
 }
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 4) void down_kernel(FfnParams p, int n_ta
 // then read from that XCD's L2 after the first tile.
 //
 // Epilogue: gate/up writes h = bf16(SiLU(g Gg) * (u Gu)); down writes
-// o = Gd * acc (fp32) for the combine kernel.
+// o = fp16(Gd * acc) for the combine kernel.
 constexpr int kMmThreads = 256;
 constexpr int kMmRows = 128;                 // weight rows per workgroup (32 per wave)
 constexpr int kMmRoutes = 128;               // routes per chunk
@@ -682,9 +682,9 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
           for (int m = 0; m < NMAT; ++m) {
             const int nm = n + m * kMmRows;
             if (nm < N)
-              *reinterpret_cast<float4*>(p.o + (size_t)pos * p.H + nm) =
-                  make_float4(acc[m][jt][4 * q] * Gd, acc[m][jt][4 * q + 1] * Gd, acc[m][jt][4 * q + 2] * Gd,
-                              acc[m][jt][4 * q + 3] * Gd);
+              *reinterpret_cast<uint2*>(p.o + (size_t)pos * p.H + nm) =
+                  make_uint2(f32_to_f16_bits(acc[m][jt][4 * q] * Gd) | (f32_to_f16_bits(acc[m][jt][4 * q + 1] * Gd) << 16),
+                             f32_to_f16_bits(acc[m][jt][4 * q + 2] * Gd) | (f32_to_f16_bits(acc[m][jt][4 * q + 3] * Gd) << 16));
           }
         }
       }
@@ -720,42 +720,50 @@ __global__ __launch_bounds__(kWlThreads) void plan_kernel(FfnParams p) {
 
 // ------------------------------------------------------------------ combine
 
-constexpr int kCombineCols = 4 * kThreads;   // output columns per workgroup
+constexpr int kCombineCols = 8 * kThreads;   // output columns per workgroup
 constexpr int kMaxK = 32;
 
-// y[t, c..c+3] = sum over slots j in order of w[t,j] * o[route_pos[t*k+j], c..c+3].
-// One workgroup per (token, 1024 columns): the token's weights and route
-// positions are staged once, then every o load (16 bytes per thread) is
-// issued before the sum.
+// y[t, c..c+7] = sum over slots j in order of w[t,j] * o[route_pos[t*k+j], c..c+7],
+// in fp32 from the routes' fp16 down outputs (each route's result is rounded
+// once to fp16 before the fp32 weighting, as the SM70 design note's
+// contract keeps it: page "Persistent execution for Flash-Next GGUF on
+// SM70", section "First implementation boundary", step 4).  One workgroup
+// per (token, 2048 columns): the token's weights and route positions are
+// staged once, then every o load (16 bytes per thread) is issued before the
+// sum.
 __global__ __launch_bounds__(kThreads) void combine_kernel(FfnParams p) {
   __shared__ float s_w[kMaxK];
   __shared__ int s_pos[kMaxK];
   const int col_blocks = (p.H + kCombineCols - 1) / kCombineCols;
   const int t = blockIdx.x / col_blocks;
-  const int c = (blockIdx.x - t * col_blocks) * kCombineCols + 4 * threadIdx.x;
+  const int c = (blockIdx.x - t * col_blocks) * kCombineCols + 8 * threadIdx.x;
   const int R = p.T * p.k;
   if (threadIdx.x < p.k) {
     s_w[threadIdx.x] = p.topk_w[(size_t)t * p.k + threadIdx.x];
     s_pos[threadIdx.x] = min(max(p.route_pos[(size_t)t * p.k + threadIdx.x], 0), R - 1);
   }
   __syncthreads();
-  if (c >= p.H) return;
-  float4 ov[kMaxK];
+  if (c >= p.H) return;                        // H is a multiple of 32: c + 8 <= H
+  uint4 ov[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j)
-    if (j < p.k) ov[j] = *reinterpret_cast<const float4*>(p.o + (size_t)s_pos[j] * p.H + c);
-  float y0 = 0.0f, y1 = 0.0f, y2 = 0.0f, y3 = 0.0f;
+    if (j < p.k) ov[j] = *reinterpret_cast<const uint4*>(p.o + (size_t)s_pos[j] * p.H + c);
+  float yv[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j < p.k) {
-      y0 = fmaf(s_w[j], ov[j].x, y0);
-      y1 = fmaf(s_w[j], ov[j].y, y1);
-      y2 = fmaf(s_w[j], ov[j].z, y2);
-      y3 = fmaf(s_w[j], ov[j].w, y3);
+      const uint32_t d[4] = {ov[j].x, ov[j].y, ov[j].z, ov[j].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        yv[2 * q] = fmaf(s_w[j], f16_bits_to_f32(d[q] & 0xFFFFu), yv[2 * q]);
+        yv[2 * q + 1] = fmaf(s_w[j], f16_bits_to_f32(d[q] >> 16), yv[2 * q + 1]);
+      }
     }
   }
-  reinterpret_cast<uint2*>(p.y)[((size_t)t * p.H + c) >> 2] =
-      make_uint2(f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16), f32_to_bf16_rne(y2) | (f32_to_bf16_rne(y3) << 16));
+  uint32_t yb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) yb[q] = f32_to_bf16_rne(yv[2 * q]) | (f32_to_bf16_rne(yv[2 * q + 1]) << 16);
+  *reinterpret_cast<uint4*>(p.y + (size_t)t * p.H + c) = make_uint4(yb[0], yb[1], yb[2], yb[3]);
 }
 
 // ------------------------------------------------------------------ down + combine (small batches)
@@ -1035,7 +1043,7 @@ __global__ __launch_bounds__(kThreads, 2) void down_nc_kernel(FfnParams p, int n
       ad = dot_chunk(cd[i], vd[i], hr, ad, one);
     }
     const float v = row16_sum(ad) * Gd;
-    if (sl == 0 && row_ok) p.o[(size_t)pos * p.H + row] = v;
+    if (sl == 0 && row_ok) p.o[(size_t)pos * p.H + row] = f32_to_f16_bits(v);
   }
 }
 
@@ -1187,7 +1195,7 @@ void launch_down_combine_nc(int nc, const FfnParams& p, unsigned grid, size_t dy
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WorkspaceLayout {
-  size_t h_off, o_off, plan_off, rd_off, total;   // h [R, I] bf16, o [R, H] fp32, MFMA work plan, row-dot list
+  size_t h_off, o_off, plan_off, rd_off, total;   // h [R, I] bf16, o [R, H] fp16, MFMA work plan, row-dot list
   int plan_max;
 };
 
@@ -1196,7 +1204,7 @@ WorkspaceLayout workspace_layout(int T, int H, int I, int E, int k) {
   const size_t R = (size_t)T * (size_t)k;
   L.h_off = 0;
   L.o_off = align256(R * (size_t)I * 2);
-  L.plan_off = L.o_off + align256(R * (size_t)H * 4);
+  L.plan_off = L.o_off + align256(R * (size_t)H * 2);
   // at most one partial chunk per expert slot plus R / kMmRoutes full ones;
   // the list has room for a multiple of 8 items (the MFMA grids' bound)
   L.plan_max = (int)(std::min<size_t>((size_t)E, R) + R / kMmRoutes);
@@ -1329,7 +1337,7 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   p.T = T; p.H = H; p.I = I; p.E = E; p.k = k;
   char* ws = static_cast<char*>(workspace);
   p.h = reinterpret_cast<uint16_t*>(ws + L.h_off);
-  p.o = reinterpret_cast<float*>(ws + L.o_off);
+  p.o = reinterpret_cast<uint16_t*>(ws + L.o_off);
   p.plan = reinterpret_cast<int32_t*>(ws + L.plan_off);
   p.plan_max = L.plan_max;
   p.rd_list = reinterpret_cast<int32_t*>(ws + L.rd_off);

@@ -24,6 +24,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// fp32 -> fp16 bits, round to nearest even (v_cvt_f16_f32), and back (exact).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) {
   return __builtin_bit_cast(bf16x2, u);
 }

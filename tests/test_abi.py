@@ -107,7 +107,7 @@ def test_expert_ffn_host_checks(lib):
     assert need > 0 and need % 256 == 0
     assert _ffn(lib, ws=need - 1) == 5
     assert lib.moe_expert_ffn_workspace_size(0, 256, 128, 8, 2) == 0
-    # grows with T*k: h (bf16 [R,I]) and o (fp32 [R,H])
+    # grows with T*k: h (bf16 [R,I]) and o (fp16 [R,H])
     assert lib.moe_expert_ffn_workspace_size(8, 256, 128, 8, 2) > need
 
 
@@ -167,7 +167,7 @@ def test_step_host_checks(lib):
 
 def _workspace_formula(T, H, I, E, k):
     """moe_expert_ffn_workspace_size as the header states it: h (2*I bytes
-    per route), o (4*H bytes per route), a work list of 16 bytes per item
+    per route), o (2*H bytes per route), a work list of 16 bytes per item
     for min(E, T*k) + T*k // 128 items rounded up to 8, plus 16, and an expert
     list of 4 bytes per slot, min(E, T*k) of them, plus 4; each region
     rounded up to 256 bytes."""
@@ -175,7 +175,7 @@ def _workspace_formula(T, H, I, E, k):
     R = T * k
     items = min(E, R) + R // 128
     items = (items + 7) // 8 * 8
-    return up(R * I * 2) + up(R * H * 4) + up(16 + 16 * items) + up(4 + 4 * min(E, R))
+    return up(R * I * 2) + up(R * H * 2) + up(16 + 16 * items) + up(4 + 4 * min(E, R))
 
 
 def test_workspace_size_formula(lib):
@@ -253,8 +253,8 @@ def test_step_noalloc_host_checks(lib):
     assert _noalloc(lib, null_at=17) == 1
     assert _noalloc(lib, H=96, I=64, packed=A) == 2      # packed weights need multiples of 64
     assert _noalloc(lib, H=8192) == 3                    # outside the envelope
-    # the workspace of 90 tokens at the Flash-Next shape fits the scratch, 91 do not
-    assert lib.moe_step_workspace_size(90, 2048, 512, 512, 10) <= sme.NOALLOC_SCRATCH_BYTES
-    assert lib.moe_step_workspace_size(91, 2048, 512, 512, 10) > sme.NOALLOC_SCRATCH_BYTES
-    assert _noalloc(lib, T=91, H=2048, I=512, E=512, k=10) == 7
+    # the workspace of 163 tokens at H = 2048, I = 512 fits the scratch, 164 do not
+    assert lib.moe_step_workspace_size(163, 2048, 512, 512, 10) <= sme.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_step_workspace_size(164, 2048, 512, 512, 10) > sme.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(lib, T=164, H=2048, I=512, E=512, k=10) == 7
     assert _noalloc(lib, T=4096, H=2048, I=512, E=512, k=10) == 7
