@@ -404,6 +404,36 @@ moe_status moe_step_shared(const uint16_t* x, const float* logits, const float* 
                            uint16_t* y_shared, void* stream);
 
 /*
+ * moe_expert_ffn_per_route — the routed experts without unique-expert reuse:
+ * the baseline of the reuse measurement on page "Persistent execution for
+ * Flash-Next GGUF on SM70" (section "Measurements that can accept or reject
+ * the design": variants on the same storage and decoder; section
+ * "Opportunity sized from the actual routes": bytes issued per route against
+ * the distinct experts' bytes).  Every route (t, j) streams the weights of
+ * its expert topk_idx[t, j] itself (an expert picked by n tokens is read n
+ * times); no bucket arrays are used.  Same result definition as
+ * moe_expert_ffn (h in bf16, each route's down output rounded once to fp16,
+ * y summed in slot order in fp32 and rounded once to bf16).
+ *   x, w_*, s_*, g_scale, y   as for moe_expert_ffn
+ *   topk_idx, topk_w          [T, k] as from moe_route_topk
+ *   workspace                 >= moe_expert_ffn_workspace_size(T,H,I,E,k)
+ *                             bytes, owned by the caller (h [T*k, I] bf16 and
+ *                             o [T*k, H] fp16), contents unspecified
+ * Shapes and envelope: those of moe_expert_ffn, plus T*k*ceil(H/16) below
+ * 2^31 workgroups.  For measurement beside the reuse path; moe_step is the
+ * product path.
+ */
+moe_status moe_expert_ffn_per_route(const uint16_t* x,
+                                    const uint8_t* w_gate, const uint8_t* s_gate,
+                                    const uint8_t* w_up, const uint8_t* s_up,
+                                    const uint8_t* w_down, const uint8_t* s_down,
+                                    const float* g_scale,
+                                    const int32_t* topk_idx, const float* topk_w,
+                                    int T, int H, int I, int E, int k,
+                                    void* workspace, size_t workspace_bytes,
+                                    uint16_t* y, void* stream);
+
+/*
  * moe_step_noalloc — moe_step (moe_step_packed when `packed` is not NULL)
  * for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  It takes

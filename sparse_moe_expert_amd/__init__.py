@@ -17,6 +17,7 @@ from ._lib import (
     make_workspace,
     moe_bucket_routes,
     moe_expert_ffn,
+    moe_expert_ffn_per_route,
     moe_expert_ffn_workspace_size,
     moe_route_bucket,
     moe_router_logits,
@@ -44,6 +45,7 @@ __all__ = [
     "make_workspace",
     "moe_bucket_routes",
     "moe_expert_ffn",
+    "moe_expert_ffn_per_route",
     "moe_expert_ffn_workspace_size",
     "moe_route_bucket",
     "moe_router_logits",

@@ -48,6 +48,7 @@ SIGNATURES = {
     "moe_shared_expert": (_I, [_P] * 4 + [_I] * 3 + [_P, ctypes.c_size_t, _P, _P]),
     "moe_step_shared": (_I, [_P, _P, _P] + [_P] * 7 + [_P] + [_I] * 5 + [_P] * 8 + [_P, ctypes.c_size_t, _P]
                         + [_P] * 3 + [_I, _P, ctypes.c_size_t, _P, _P]),
+    "moe_expert_ffn_per_route": (_I, [_P] * 10 + [_I] * 5 + [_P, ctypes.c_size_t, _P, _P]),
     "moe_step_noalloc": (_I, [_P, _P, _P] + [_P] * 7 + [_P] + [_I] * 5 + [_P] * 8 + [_P, _P]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
 }
@@ -353,6 +354,28 @@ def moe_step(x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor]
                                         *(_ptr(t) for t in buckets), _ptr(workspace),
                                         ctypes.c_size_t(workspace.numel()), _ptr(y), _stream(dev))
     _check("moe_step_packed", st)
+    return y
+
+
+def moe_expert_ffn_per_route(x: torch.Tensor, weights: ExpertWeights, topk_idx: torch.Tensor,
+                             topk_w: torch.Tensor, workspace: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+    """The expert FFN without unique-expert reuse (every route streams its own
+    expert's weights): the baseline beside moe_expert_ffn."""
+    x = _check_x(x)
+    T, H = x.shape
+    E, H_w, I = weights.shape
+    dev = x.device
+    if H_w != H:
+        raise ValueError(f"weights are for H={H_w}, x has H={H}")
+    k = topk_idx.shape[1]
+    _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    _need(y, "y", torch.bfloat16, (T, H), dev)
+    st = load_library().moe_expert_ffn_per_route(_ptr(x), *(_ptr(t) for t in weights), _ptr(topk_idx), _ptr(topk_w),
+                                                 T, H, I, E, k, _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                                 _ptr(y), _stream(dev))
+    _check("moe_expert_ffn_per_route", st)
     return y
 
 

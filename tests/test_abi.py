@@ -258,3 +258,22 @@ def test_step_noalloc_host_checks(lib):
     assert lib.moe_step_workspace_size(164, 2048, 512, 512, 10) > sme.NOALLOC_SCRATCH_BYTES
     assert _noalloc(lib, T=164, H=2048, I=512, E=512, k=10) == 7
     assert _noalloc(lib, T=4096, H=2048, I=512, E=512, k=10) == 7
+
+
+def test_per_route_host_checks(lib):
+    """moe_expert_ffn_per_route: shape, envelope, pointer and workspace checks
+    before any launch."""
+    f = lib.moe_expert_ffn_per_route
+
+    def call(T=4, H=256, I=128, E=8, k=2, ws=1 << 20, null_at=None):
+        ptrs = [A] * 10
+        if null_at is not None:
+            ptrs[null_at] = None
+        return f(*ptrs, T, H, I, E, k, A, ctypes.c_size_t(ws), A, None)
+    assert call(k=9) == 2
+    assert call(H=48) == 2
+    assert call(H=8192) == 3
+    assert call(T=0) == 0
+    assert call(null_at=8) == 1                      # topk_idx
+    need = lib.moe_expert_ffn_workspace_size(4, 256, 128, 8, 2)
+    assert call(ws=need - 1) == 5
