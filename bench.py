@@ -32,7 +32,11 @@ plus the previous output (a residual stream).  `protocol` adds seven timed
 rounds (median, min, max), the same step on one bank (cache-resident), the
 expert FFN alone, a device-to-device copy as the practical bandwidth ceiling
 and the bytes a per-route kernel would stream; `cpu_baseline.one_core` is the
-oracle with its BLAS on one thread.
+oracle with its BLAS on one thread.  `configs` times every workload (the five
+configurations and the Flash-Next expert shape H=2560, I=640 at decode) the
+same way, with the no-reuse per-route variant beside the step at decode_t4
+and verify_t32, the bf16 MFMA rate on the method's own flops at the prefill
+chunk, and the oracle's host time per step on a labelled token sample.
 """
 
 from __future__ import annotations
@@ -82,6 +86,11 @@ def parse():
     ap.add_argument("--protocol", type=int, default=1,
                     help="1: add the protocol figures (timed rounds, cache-resident step, FFN alone, copy ceiling); "
                          "0: skip them (counter runs)")
+    ap.add_argument("--configs", type=int, default=1,
+                    help="1: time every workload (the five configs and the Flash-Next expert shape) after the "
+                         "headline and report them under `configs`; 0: skip")
+    ap.add_argument("--config-steps", type=int, default=96,
+                    help="steps timed per workload in the configs leg")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the bench, run a plain device-to-device copy of this many MiB three times "
                          "(the known-size kernel that calibrates FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -476,6 +485,139 @@ def protocol_leg(step, full, gu_steps, xs, ls, bias, banks, pks, stream, dev, NB
 
     return protocol
 
+MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense bf16, published
+
+
+def oracle_step_seconds(wl, budget_s: float):
+    """The oracle (as it stands) on one step of `wl`: routing and buckets on
+    the whole batch, the FFN on the first n tokens (n grows until the budget
+    is spent or every token is done), scaled by T / n.  Returns (seconds per
+    step, sample description)."""
+    import oracle
+    t0 = time.perf_counter()
+    idx, w = oracle.route_topk(wl.logits, wl.bias, wl.k)
+    oracle.bucket_routes(idx, wl.E)
+    t_route = time.perf_counter() - t0
+    n, t_ffn = 0, 0.0
+    while n < wl.T and (n == 0 or t_ffn < budget_s):
+        m = min(wl.T - n, max(1, n))                  # double the sample each round
+        t0 = time.perf_counter()
+        oracle.moe_output(wl.x, wl.bank, idx, w, tokens=range(n, n + m))
+        t_ffn += time.perf_counter() - t0
+        n += m
+    return t_route + t_ffn * wl.T / n, (f"routing and buckets on all {wl.T} tokens, FFN on tokens 0..{n - 1} "
+                                        f"({t_ffn:.1f} s) scaled by {wl.T}/{n}")
+
+
+def configs_leg(args, dev, NB: int):
+    """Every workload at its full size, one after another on the same box:
+    the step (path `packed`) graph-replayed over NB weight banks (8 banks of
+    ~0.9 GB at the Flash-Next shape, distinct addresses, so no expert is
+    re-read from the 256 MB Infinity Cache within NB steps): us/step,
+    tokens/s, unique expert bytes per step, effective TB/s on them and the
+    fraction of 8 TB/s; at the prefill chunk also the bf16 MFMA rate on the
+    method's own 6*H*I flops per route against 2.5 PFLOP/s; at decode_t4 and
+    verify_t32 the no-reuse variant (moe_route_topk + moe_expert_ffn_per_route,
+    every route streaming its own expert) beside the step; and the oracle's
+    host time per step.  The Flash-Next expert shape (H = 2560, I = 640) is
+    reported beside the five workloads."""
+    import numpy as np
+    import torch
+    import sparse_moe_expert_amd as sme
+    from moe_inputs import get_config, make_workload
+    from moe_inputs.configs import CONFIG_ORDER
+    names = CONFIG_ORDER + ["flashnext_t4"]
+    dev_banks = {}
+    out = {}
+    stream = torch.cuda.current_stream(dev)
+    for name in names:
+        cfg = get_config(name)
+        T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+        log(f"[bench] configs: {name}")
+        wls = [make_workload(name, x_seed=b) for b in range(NB)]
+        key = (E, H, I)
+        if key not in dev_banks:
+            dev_banks.clear()                                    # one shape's banks resident at a time
+            torch.cuda.empty_cache()
+            W0 = sme.expert_weights_from_numpy(wls[0].bank, dev)
+            banks = [W0] + [sme.ExpertWeights(*(torch.roll(t, shifts=67 * b, dims=0).contiguous() for t in W0))
+                            for b in range(1, NB)]
+            pks = [sme.pack_weights(W) for W in banks] if H % 64 == 0 and I % 64 == 0 else [None] * NB
+            dev_banks[key] = (banks, pks)
+        banks, pks = dev_banks[key]
+        path = "packed" if pks[0] is not None else "step"
+        xs = [torch.from_numpy(w.x.view(np.int16)).to(dev) for w in wls]
+        ls = [torch.from_numpy(w.logits).to(dev) for w in wls]
+        bias = None if wls[0].bias is None else torch.from_numpy(wls[0].bias).to(dev)
+        step = sme.MoeStep(T, H, I, E, k, dev, path=path)
+        n_unique = []
+        for b in range(NB):
+            step.run(xs[b], ls[b], bias, banks[b], packed=pks[b])
+            torch.cuda.synchronize()
+            n_unique.append(int(step.buckets.n_active.item()))
+        ebytes = cfg.expert_bytes() + EXPERT_BYTES_EXTRA
+        ubytes = float(np.mean(n_unique)) * ebytes
+
+        def timed(fn_graph, nsteps_per_replay):
+            fn_graph.replay()
+            torch.cuda.synchronize()
+            reps = max(2, args.config_steps // nsteps_per_replay)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn_graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e-3 / (reps * nsteps_per_replay), reps * nsteps_per_replay
+
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for b in range(NB):
+                step.run(xs[b], ls[b], bias, banks[b], packed=pks[b])
+        s_step, n_timed = timed(g, NB)
+        rec = {"T": T, "H": H, "I": I, "E": E, "k": k, "path": path, "steps_timed": n_timed,
+               "us_per_step": round(s_step * 1e6, 3), "tokens_per_s": round(T / s_step, 1),
+               "unique_experts_per_step": round(float(np.mean(n_unique)), 2),
+               "unique_expert_bytes_per_step": int(ubytes),
+               "eff_TBps": round(ubytes / s_step / 1e12, 4),
+               "frac_of_8TBps": round(ubytes / s_step / 1e12 / (HBM_PEAK_GBPS / 1e3), 4)}
+        if T >= 1024:
+            flops = 6.0 * H * I * T * k
+            rec["mfma_TFLOPs_algorithmic"] = round(flops / s_step / 1e12, 1)
+            rec["mfma_frac_of_2.5PFLOPs"] = round(flops / s_step / 1e12 / MFMA_PEAK_TFLOPS, 4)
+        if name in ("decode_t4", "verify_t32"):
+            idxs = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in range(NB)]
+            wts = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in range(NB)]
+            ws = sme.make_workspace(T, H, I, E, k, dev)
+            y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            for b in range(NB):
+                sme.moe_route_topk(ls[b], bias, k, idxs[b], wts[b])
+            gpr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gpr):
+                for b in range(NB):
+                    sme.moe_route_topk(ls[b], bias, k, idxs[b], wts[b])
+                    sme.moe_expert_ffn_per_route(xs[b], banks[b], idxs[b], wts[b], ws, y)
+            s_pr, _ = timed(gpr, NB)
+            issued = T * k * ebytes
+            rec["per_route_variant"] = {
+                "us_per_step": round(s_pr * 1e6, 3),
+                "route_issued_bytes_per_step": int(issued),
+                "issued_TBps": round(issued / s_pr / 1e12, 4),
+                "step_speedup_from_reuse": round(s_pr / s_step, 3),
+                "note": "moe_route_topk + moe_expert_ffn_per_route (every route streams its own expert), graph "
+                        "over the same banks and routing sets"}
+        if args.cpu_seconds > 0:
+            s_or, sample = oracle_step_seconds(wls[0], min(5.0, args.cpu_seconds / 2))
+            rec["oracle"] = {"s_per_step": round(s_or, 4), "gpu_speedup": round(s_or / s_step, 1),
+                             "sample": sample}
+        log(f"[bench] {name}: {rec['us_per_step']} us/step, {rec['eff_TBps']} TB/s"
+            + (f", per-route {rec['per_route_variant']['us_per_step']} us" if "per_route_variant" in rec else ""))
+        out[name] = rec
+        del g, step
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -639,6 +781,10 @@ def main():
     if args.cpu_seconds > 0:
         log(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s budget)")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, expert_bytes)
+    if args.configs:
+        del banks, pks, full, tail, g_dom, gu_steps, step
+        torch.cuda.empty_cache()
+        out["configs"] = configs_leg(args, dev, NB)
     print(json.dumps(out), flush=True)
 
 
