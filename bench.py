@@ -236,11 +236,48 @@ def layers_leg(args, cfg, x0, banks, pks, bias, dev, expert_bytes: int):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
     nbytes = float(np.sum(n_unique)) * expert_bytes + L * E * H * 4
-    return {"layers": L, "us_per_pass": round(us, 2), "us_per_layer": round(us / L, 3),
-            "effective_TBps": round(nbytes / us / 1e6, 4), "unique_experts_per_layer": n_unique,
-            "bytes_per_pass": int(nbytes), "passes": reps,
-            "per_layer": "router projection + route/bucket + expert FFN (library) + residual add (torch, bf16); "
-                         "the input of layer l+1 is the input of layer l plus its output"}
+    out = {"layers": L, "us_per_pass": round(us, 2), "us_per_layer": round(us / L, 3),
+           "effective_TBps": round(nbytes / us / 1e6, 4), "unique_experts_per_layer": n_unique,
+           "bytes_per_pass": int(nbytes), "passes": reps,
+           "per_layer": "router projection + route/bucket + expert FFN (library) + residual add (torch, bf16); "
+                        "the input of layer l+1 is the input of layer l plus its output"}
+
+    # the same chain with the router projection, selection and buckets in one
+    # call (moe_router_route_bucket: one launch up to 16 tokens) followed by
+    # the expert FFN (moe_expert_ffn on the standard layout: below 64 tokens
+    # the packed copy is not read)
+    if T <= 16:
+        counters = [torch.zeros(1, dtype=torch.int32, device=dev) for _ in range(L)]
+
+        def one_pass_fused():
+            for l in range(L):
+                st = steps[l]
+                sme.moe_router_route_bucket(xs_l[l], w_rs[l], bias, k, logits[l], st.topk_idx, st.topk_w,
+                                            st.buckets, counters[l])
+                st.ffn(xs_l[l], banks[l])
+                if l + 1 < L:
+                    torch.add(xs_l[l], st.y, out=xs_l[l + 1])
+
+        one_pass_fused()
+        torch.cuda.synchronize()
+        gf = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gf):
+            one_pass_fused()
+        for _ in range(3):
+            gf.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            gf.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        usf = e0.elapsed_time(e1) * 1e3 / reps
+        out["fused_router"] = {
+            "us_per_pass": round(usf, 2), "us_per_layer": round(usf / L, 3),
+            "effective_TBps": round(nbytes / usf / 1e6, 4),
+            "per_layer": "moe_router_route_bucket (projection, top-k and buckets in one launch) + moe_expert_ffn "
+                         "+ residual add (torch)"}
+    return out
 
 
 def shared_expert_weights(L, H, Is, dev, seed=500):

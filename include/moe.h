@@ -152,6 +152,41 @@ moe_status moe_route_bucket(const float* logits, const float* bias,
                             void* stream);
 
 /*
+ * moe_router_route_bucket — moe_router_logits, moe_route_topk and
+ * moe_bucket_routes in one call: tokens -> logits -> top-k ids and gate
+ * weights -> route buckets, outputs identical bit for bit to the three calls
+ * in sequence.  Small batches (T <= 16 and T*k <= 256) run all of it in one
+ * launch: the router's projection spans many workgroups, so the fused kernel
+ * hands its results to the selection explicitly (page "Persistent execution
+ * for Flash-Next GGUF on SM70", section "Router: selection and expert-task
+ * production"): each workgroup makes its logits visible at device scope and
+ * counts itself in `counter`; the last one to arrive routes and buckets the
+ * batch and sets `counter` back to 0.  No workgroup waits for another.
+ * Larger batches run the projection and moe_route_bucket back to back.
+ * Measured on one MI355X at T = 4, H = 2048, E = 512, k = 10: the one-launch
+ * form takes ~11.7 us against 4.7 + 4.3 us for the projection and routing
+ * kernels it replaces (the device-scope hand-off - an L2 write-back and
+ * invalidate around one atomic per workgroup - costs more than the kernel
+ * boundary); for latency prefer moe_router_logits then moe_step.
+ *   x, w_router, logits        as for moe_router_logits (logits is an output)
+ *   bias, k, topk_idx, topk_w  as for moe_route_topk
+ *   expert_count ... route_pos as for moe_bucket_routes
+ *   counter   [1] int32, device memory owned by the caller: 0 before the
+ *             first call (e.g. allocated zeroed); every call leaves it 0, so
+ *             the call can be captured in a graph and replayed.  Concurrent
+ *             calls need distinct counters.
+ * Shapes and envelope: those of the three calls (H a multiple of 8 up to
+ * 4096, E <= 1024, k <= 32, R <= 2^24); every check runs before any launch.
+ */
+moe_status moe_router_route_bucket(const uint16_t* x, const float* w_router, const float* bias,
+                                   int T, int H, int E, int k, float* logits,
+                                   int32_t* topk_idx, float* topk_w,
+                                   int32_t* expert_count, int32_t* expert_offset,
+                                   int32_t* active_experts, int32_t* n_active,
+                                   int32_t* route_src, int32_t* route_pos,
+                                   int32_t* counter, void* stream);
+
+/*
  * Bytes of device workspace moe_expert_ffn needs for these sizes (0 when
  * T == 0 or a size is not positive): the per-route intermediates, 2*I + 2*H
  * bytes per route; the dense kernels' work list, 16 bytes for each of at

@@ -21,6 +21,7 @@ from ._lib import (
     moe_expert_ffn_workspace_size,
     moe_route_bucket,
     moe_router_logits,
+    moe_router_route_bucket,
     moe_route_topk,
     moe_shared_expert,
     moe_step_shared,
@@ -49,6 +50,7 @@ __all__ = [
     "moe_expert_ffn_workspace_size",
     "moe_route_bucket",
     "moe_router_logits",
+    "moe_router_route_bucket",
     "moe_route_topk",
     "moe_shared_expert",
     "moe_step_shared",

@@ -36,6 +36,7 @@ SIGNATURES = {
     "moe_route_topk": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
     "moe_bucket_routes": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "moe_route_bucket": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_router_route_bucket": (_I, [_P, _P, _P] + [_I] * 4 + [_P] * 11),
     "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "moe_expert_ffn": (_I, [_P] * 15 + [_I] * 5 + [_P, ctypes.c_size_t, _P, _P]),
     "moe_expert_ffn_stage": (_I, [_I] + [_P] * 15 + [_I] * 5 + [_P, ctypes.c_size_t, _P, _P]),
@@ -222,6 +223,31 @@ def moe_route_bucket(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int,
                                          *(_ptr(t) for t in b), _stream(dev))
     _check("moe_route_bucket", st)
     return topk_idx, topk_w, b
+
+
+def moe_router_route_bucket(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor], k: int,
+                            logits: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                            buckets: "Buckets", counter: torch.Tensor) -> None:
+    """Router projection, top-k and buckets in one call (one launch for small
+    batches); `counter` is an int32 [1] device tensor, zero before the first
+    call and left zero by every call."""
+    x = _check_x(x)
+    T, H = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    _need(w_router, "w_router", torch.float32, (E, H), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,), dev)
+    _need(logits, "logits", torch.float32, (T, E), dev)
+    _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    for name, t, n in zip(Buckets._fields, buckets, (E, E + 1, E, 1, T * k, T * k)):
+        _need(t, name, torch.int32, (n,), dev)
+    _need(counter, "counter", torch.int32, (1,), dev)
+    st = load_library().moe_router_route_bucket(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k, _ptr(logits),
+                                                _ptr(topk_idx), _ptr(topk_w), *(_ptr(t) for t in buckets),
+                                                _ptr(counter), _stream(dev))
+    _check("moe_router_route_bucket", st)
 
 
 class ExpertWeights(NamedTuple):

@@ -29,6 +29,7 @@
 // are found with one ballot per id bit; rank among them + counts of earlier
 // wavefronts in the chunk + the expert's running base gives the position.
 // Positions never depend on timing, so the result is exact and reproducible.
+#include "router_rows.h"
 #include "select.h"
 #include "shared_rows.h"
 #include "work_list.h"
@@ -281,23 +282,15 @@ constexpr int kSmallMaxRoutes = 256;
 template <int NT>
 constexpr int kSmallSideWaves = NT >= 1024 ? 4 : 2;
 
+// The routing and bucketing of the whole batch by the NT threads of one
+// workgroup (every thread calls it).
 template <int V, int KC, int NT>
-__global__ __launch_bounds__(NT) void route_bucket_small_kernel(
+__device__ __forceinline__ void route_bucket_block(
     const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
-    int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos, SharedRows sr) {
-  // workgroups after the first compute rows of a shared expert's gate/up
-  // (moe_step_shared), one per wave, while the first one routes; only the
-  // first kSmallSideWaves<NT> waves of such a workgroup take rows, which
-  // spreads the weight and activation reads over more compute units
-  if (blockIdx.x > 0) {
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (w < kSmallSideWaves<NT>)
-      se_gate_up_side(sr, (int)(blockIdx.x - 1) * kSmallSideWaves<NT> + w, threadIdx.x & (kWave - 1));
-    return;
-  }
+    int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos) {
   __shared__ int s_cnt[NT];
   __shared__ int s_ids[kSmallMaxRoutes];
   constexpr int NW = NT / kWave;
@@ -372,6 +365,73 @@ __global__ __launch_bounds__(NT) void route_bucket_small_kernel(
     route_src[pos] = tid;
     route_pos[tid] = pos;
   }
+}
+
+template <int V, int KC, int NT>
+__global__ __launch_bounds__(NT) void route_bucket_small_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
+    int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos, SharedRows sr) {
+  // workgroups after the first compute rows of a shared expert's gate/up
+  // (moe_step_shared), one per wave, while the first one routes; only the
+  // first kSmallSideWaves<NT> waves of such a workgroup take rows, which
+  // spreads the weight and activation reads over more compute units
+  if (blockIdx.x > 0) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w < kSmallSideWaves<NT>)
+      se_gate_up_side(sr, (int)(blockIdx.x - 1) * kSmallSideWaves<NT> + w, threadIdx.x & (kWave - 1));
+    return;
+  }
+  route_bucket_block<V, KC, NT>(logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset,
+                                active_experts, n_active, route_src, route_pos);
+}
+
+// The router projection, selection and bucketing of a small batch in one
+// launch (page "Persistent execution for Flash-Next GGUF on SM70", section
+// "Router: selection and expert-task production": the projection's results
+// span many workgroups, so a fused kernel needs an explicit hand-off from
+// the last producer to the selection).  Workgroup b computes the logits of
+// expert rows NT/256 * b .. (one row per 256 threads, router_rows.h), makes
+// them visible at device scope, and counts itself in `counter`; the
+// workgroup that arrives last (the counter read G - 1) makes the others'
+// logits visible to itself, routes and buckets the whole batch exactly as
+// route_bucket_small_kernel does, and sets the counter back to 0 for the
+// next call.  No workgroup waits for another, so there is no forward-progress
+// question: whichever workgroup is last finds every logit written.
+template <int NCH, int V, int KC, int NT>
+__global__ __launch_bounds__(NT) void router_route_bucket_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ w_router, const float* __restrict__ bias, int T,
+    int H, int E, int k, float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
+    int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos, int32_t* __restrict__ counter) {
+  constexpr int kRows = NT / kRtThreads;                     // expert rows per workgroup
+  __shared__ double s_part[kRows][kRtWaves][kRsGroup];
+  __shared__ int s_last;
+  const int grp = threadIdx.x / kRtThreads;
+  router_row<NCH>(x, w_router, T, H, E, logits, (int)blockIdx.x * kRows + grp, (int)threadIdx.x % kRtThreads,
+                  s_part[grp]);
+  // Hand-off.  Every wave waits until its logit stores have reached the
+  // L2; after the barrier one thread counts the workgroup in with an
+  // agent-scope acquire-release atomic: its release writes this XCD's L2 back
+  // (every store of the workgroup is in it by then), its acquire invalidates
+  // this CU's L1 and this XCD's L2, so the workgroup that arrives last reads
+  // every other's logits from memory.  One fence pair per workgroup: a
+  // device-scope fence in every wave costs an L2 write-back and invalidate
+  // per wave.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (int)gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  route_bucket_block<V, KC, NT>(logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset,
+                                active_experts, n_active, route_src, route_pos);
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 int id_bits_for(int E) {
@@ -516,4 +576,53 @@ extern "C" moe_status moe_route_bucket(const float* logits, const float* bias, i
                                        int32_t* route_src, int32_t* route_pos, void* stream) {
   return moe::route_bucket(logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset, active_experts,
                            n_active, route_src, route_pos, nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+extern "C" moe_status moe_router_route_bucket(const uint16_t* x, const float* w_router, const float* bias, int T,
+                                              int H, int E, int k, float* logits, int32_t* topk_idx, float* topk_w,
+                                              int32_t* expert_count, int32_t* expert_offset,
+                                              int32_t* active_experts, int32_t* n_active, int32_t* route_src,
+                                              int32_t* route_pos, int32_t* counter, void* stream) {
+  using namespace moe;
+  if (T < 0 || E < 1 || H < 8 || H % 8 != 0) return MOE_ERR_INVALID_SHAPE;
+  moe_status st = check_route_args(logits, bias, T, E, k, topk_idx, topk_w);
+  if (st != MOE_OK) return st;
+  st = check_bucket_args(T, E, k, expert_count, expert_offset, active_experts, n_active, route_src, route_pos);
+  if (st != MOE_OK) return st;
+  if (H > kRtMaxH || ((long long)T + 63) / 64 > 65535) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !counter) return MOE_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(counter)) return MOE_ERR_MISALIGNED;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T > kSmallMaxTokens || T * k > kSmallMaxRoutes) {
+    // larger batches: the projection, then the routing, as two calls
+    st = moe_router_logits(x, w_router, T, H, E, logits, stream);
+    if (st != MOE_OK) return st;
+    return route_bucket(logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset, active_experts,
+                        n_active, route_src, route_pos, nullptr, 0, s);
+  }
+  const int V = (E + kWave - 1) / kWave;
+  const int nch = (H / 8 + kRtThreads - 1) / kRtThreads;     // 16-byte pieces per thread: 1 or 2
+  // 1024 threads: four expert rows per workgroup (E / 4 workgroups count in;
+  // measured faster than two rows per 512-thread workgroup, whose 2x more
+  // hand-offs cost more than the smaller workgroup saves in the selection,
+  // and than eight or more rows per workgroup, which slows the projection)
+  constexpr int kNt = 1024;
+  const unsigned grid = (unsigned)((E + kNt / kRtThreads - 1) / (kNt / kRtThreads));
+#define MOE_RRB1(VV, KK)                                                                                      \
+  if (nch <= 1) router_route_bucket_kernel<1, VV, KK, kNt><<<grid, kNt, 0, s>>>(x, w_router, bias, T, H, E, k, \
+      logits, topk_idx, topk_w, expert_count, expert_offset, active_experts, n_active, route_src, route_pos,    \
+      counter); else                                                                                          \
+  router_route_bucket_kernel<2, VV, KK, kNt><<<grid, kNt, 0, s>>>(x, w_router, bias, T, H, E, k, logits,       \
+      topk_idx, topk_w, expert_count, expert_offset, active_experts, n_active, route_src, route_pos, counter)
+#define MOE_RRB(VV) \
+  if (k == kUnrolledK) MOE_RRB1(VV, kUnrolledK); else MOE_RRB1(VV, 0)
+  if (V <= 1) { MOE_RRB(1); }
+  else if (V <= 2) { MOE_RRB(2); }
+  else if (V <= 4) { MOE_RRB(4); }
+  else if (V <= 8) { MOE_RRB(8); }
+  else { MOE_RRB(16); }
+#undef MOE_RRB
+#undef MOE_RRB1
+  return launch_status();
 }

@@ -277,3 +277,20 @@ def test_per_route_host_checks(lib):
     assert call(null_at=8) == 1                      # topk_idx
     need = lib.moe_expert_ffn_workspace_size(4, 256, 128, 8, 2)
     assert call(ws=need - 1) == 5
+
+
+def test_router_route_bucket_host_checks(lib):
+    """moe_router_route_bucket: every check before any launch."""
+    f = lib.moe_router_route_bucket
+
+    def call(T=4, H=64, E=8, k=2, counter=A, bias=None, x=A):
+        return f(x, A, bias, T, H, E, k, A, A, A, *([A] * 6), counter, None)
+    assert call(H=60) == 2              # H not a multiple of 8
+    assert call(k=9) == 2               # k > E
+    assert call(E=2048) == 3            # E beyond the envelope
+    assert call(H=8192) == 3            # H beyond the envelope
+    assert call(T=0, x=None) == 0       # T = 0: nothing launched
+    assert call(counter=None) == 1
+    assert call(x=None) == 1
+    assert call(counter=P(260)) == 4
+    assert call(bias=P(8)) == 4
