@@ -49,7 +49,9 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "bucket_block.h"
 #include "row_dot.h"
+#include "select.h"
 #include "shared_rows.h"
 #include "work_list.h"
 
@@ -66,6 +68,7 @@ struct FfnParams {
   const uint8_t* sd;
   const float* gsc;
   const float* topk_w;
+  const int32_t* topk_idx;   // route-slot mode of the small-batch down/unroute (else unused)
   const int32_t* count;
   const int32_t* offset;
   const int32_t* active;
@@ -307,6 +310,100 @@ __global__ __launch_bounds__(kThreads, 4) void gate_up_kernel(FfnParams p, int n
   const int e = row_dot_expert(p, a);
   if (e < 0) return;
   gate_up_tile<LG>(p, g, s_sc, s_x, e, tile);
+}
+
+// ------------------------------------------------------------------ selection + gate/up (small batches)
+
+// A small batch's selection and gate/up in one launch, with no hand-off
+// between workgroups: workgroup (r, tile), r = t*k + j, selects token t's k
+// experts itself (its first wave; select.h, the rule of moe_route_topk, so
+// the result is that call's bit for bit) and computes the gate/up rows of
+// tile `tile` of the j-th of them for that one route: h[r, rows] in the
+// workspace, indexed by flat route id.  Every token's selection is repeated
+// by k * tiles workgroups (one wave each), and an expert picked by several
+// tokens is streamed once per route: at four tokens the distinct experts
+// carry ~96% of the route-issued bytes, and the weights start streaming
+// without waiting for a routing kernel, its boundary and a dependent read of
+// the active list.  Rows of H = 2048 (one 16-byte chunk per lane, 64 lanes
+// per row), as gate_up_kernel<64>.  The workgroups of route (t, 0), tile 0,
+// write token t's topk_idx and topk_w.
+constexpr int kSgXBytes = 4096;           // one activation row of H = 2048
+
+template <int V, int KC>
+__global__ __launch_bounds__(kThreads, 4) void select_gate_up_kernel(FfnParams p, const float* __restrict__ logits,
+                                                                     const float* __restrict__ bias,
+                                                                     int32_t* __restrict__ topk_idx,
+                                                                     float* __restrict__ topk_w, int n_tasks) {
+  __shared__ __align__(16) uint8_t s_sc[2 * kScaleTileBytes];
+  __shared__ __align__(16) uint8_t s_x[kSgXBytes];
+  __shared__ int s_e;
+  const Geo<64, kGuUnits> g(64, p.I);
+  const int task = blockIdx.x;
+  if (task >= n_tasks) return;
+  const int r = task / g.tiles, tile = task - r * g.tiles;
+  const int t = r / p.k, j = r - t * p.k;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  // token t's activation row, one 16-byte piece per thread: it does not
+  // depend on the routing, so it is issued first
+  const u32x4 xv =
+      __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(p.x + (size_t)t * p.H, kSgXBytes), (uint32_t)tid * 16, 0, 0);
+  compiler_fence();
+  if (g.wave == 0) {
+    int e_l;
+    float w_l;
+    select_token<V, KC>(logits + (size_t)t * p.E, bias, p.E, p.k, lane, e_l, w_l);
+    if (lane == j) s_e = e_l;
+    if (j == 0 && tile == 0 && lane < p.k) {
+      topk_idx[(size_t)t * p.k + lane] = e_l;
+      topk_w[(size_t)t * p.k + lane] = w_l;
+    }
+  }
+  *reinterpret_cast<u32x4*>(s_x + tid * 16) = xv;
+  __syncthreads();
+  const int e = min(max(__builtin_amdgcn_readfirstlane(s_e), 0), p.E - 1);
+
+  // the tile of expert e, as gate_up_tile: scale bytes, then the weight rows
+  const uint32_t code_row = (uint32_t)p.H / 2, scale_row = (uint32_t)p.H / 16;
+  const uint32_t mat_codes = (uint32_t)p.I * code_row, mat_scales = (uint32_t)p.I * scale_row;
+  const uint32_t blk = (uint32_t)g.rpt * scale_row;
+  const int half = (int)(g.wave >= kWavesPerBlock / 2);
+  const uint32_t sbyte = (uint32_t)(tid & (kThreads / 2 - 1)) * 16;
+  const auto rs = make_rsrc((half ? p.su : p.sg) + (size_t)e * mat_scales, mat_scales);
+  const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rs, sbyte + (uint32_t)tile * blk, 0, kStreamAux);
+  compiler_fence();
+  const auto rg = make_rsrc(p.wg + (size_t)e * mat_codes, mat_codes);
+  const auto ru = make_rsrc(p.wu + (size_t)e * mat_codes, mat_codes);
+  const uint32_t lane_c = (uint32_t)g.sub * code_row + (uint32_t)g.sl * 16;
+  uint4 cg[kGuUnits], cu[kGuUnits];
+#pragma unroll
+  for (int u = 0; u < kGuUnits; ++u) {
+    const uint32_t r0 = (uint32_t)g.row0(tile, u);
+    cg[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rg, lane_c + r0 * code_row, 0, kStreamAux));
+    cu[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(ru, lane_c + r0 * code_row, 0, kStreamAux));
+  }
+  compiler_fence();
+  const float Gg = sload(p.gsc, e * 3 + 0), Gu = sload(p.gsc, e * 3 + 1);
+  *reinterpret_cast<u32x4*>(s_sc + half * blk + sbyte) = sv;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+  const float one = opaque_one();
+  uint32_t xr[16];
+  load_operand_chunk(reinterpret_cast<const uint16_t*>(s_x), g.sl, xr);
+  float ag[kGuUnits], au[kGuUnits];
+#pragma unroll
+  for (int u = 0; u < kGuUnits; ++u) {
+    const int rin = (u * kWavesPerBlock + g.wave) * g.rpw + g.sub;
+    const uint32_t sg = *reinterpret_cast<const uint16_t*>(s_sc + rin * scale_row + g.sl * 2);
+    const uint32_t su = *reinterpret_cast<const uint16_t*>(s_sc + blk + rin * scale_row + g.sl * 2);
+    ag[u] = dot_chunk(cg[u], sg, xr, 0.0f, one);
+    au[u] = dot_chunk(cu[u], su, xr, 0.0f, one);
+  }
+  static_assert(kGuUnits == 4, "the row scatter maps 4 units to 4 lane rows");
+  const int row = g.row0(tile, lane >> 4);
+  const float gs = rows_scatter4(row16_sum(ag[0]), row16_sum(ag[1]), row16_sum(ag[2]), row16_sum(ag[3])) * Gg;
+  const float us = rows_scatter4(row16_sum(au[0]), row16_sum(au[1]), row16_sum(au[2]), row16_sum(au[3])) * Gu;
+  if ((lane & 15) == 0 && row < p.I) p.h[(size_t)r * p.I + row] = (uint16_t)f32_to_bf16_rne(silu(gs) * us);
 }
 
 // ------------------------------------------------------------------ down
@@ -797,17 +894,32 @@ constexpr int kDcHLoads = kDcMaxLds / 16 / kDcThreads;   // 16-byte h pieces per
 // ordinary buffer loads and none sits in a loop, which keeps the compiler's
 // wait counts exact (with LDS-direct loads in flight as well it waits for
 // everything).
-template <int LD, int SLOTS>
+//
+// Route slots (RS, after select_gate_up_kernel): slot a is route a itself
+// (expert topk_idx[a], h row a, one route), so the buckets are not needed;
+// the launch's last workgroup buckets the routes instead (bucket_block.h) and
+// writes the six bucket arrays, beside the down workgroups.
+template <int LD, int SLOTS, bool RS = false>
 __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_kernel(FfnParams p) {
   extern __shared__ __align__(16) uint8_t s_dyn8[];   // [R, I] bf16 h, then [R, rpw] fp32 o
   __shared__ int s_src[kDcMaxRoutes];
   __shared__ float s_w[kDcMaxRoutes];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int R = p.T * p.k;
+  if constexpr (RS) {
+    if ((int)blockIdx.x == (int)gridDim.x - 1) {
+      // the bucketing workgroup: its dynamic LDS holds the bucketing state
+      bucket_block(p.topk_idx, R, p.E, *reinterpret_cast<BucketShared*>(s_dyn8), const_cast<int32_t*>(p.count),
+                   const_cast<int32_t*>(p.offset), const_cast<int32_t*>(p.active),
+                   const_cast<int32_t*>(p.n_active_ptr), const_cast<int32_t*>(p.route_src),
+                   const_cast<int32_t*>(p.route_pos), WorkLists{});
+      return;
+    }
+  }
   const int ld = LD ? LD : p.lr_d, rpw = kWave / ld, sub = lane / ld, sl = lane & (ld - 1);
   const int row0 = blockIdx.x * rpw;
-  const int R = p.T * p.k;
-  const int S = min(p.E, R);
+  const int S = RS ? R : min(p.E, R);
   uint16_t* s_h = reinterpret_cast<uint16_t*>(s_dyn8);
   float* s_o = reinterpret_cast<float*>(s_dyn8 + (size_t)R * p.I * 2);
 
@@ -825,7 +937,7 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
   }
   // route positions and gate weights (an index past R re-reads the last)
   const int rt = min(tid, R - 1);
-  const int src_r = p.route_src[rt];
+  const int src_r = RS ? rt : p.route_src[rt];
   const float w_r = p.topk_w[rt];
   compiler_fence();
 
@@ -833,7 +945,8 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
 #pragma unroll
   for (int u = 0; u < SLOTS; ++u) {
     const int a = wave + u * kDcWaves;
-    e_u[u] = a < S ? slot_expert(p, a) : -1;
+    if constexpr (RS) e_u[u] = a < S ? min(max(sload(p.topk_idx, a), 0), p.E - 1) : -1;
+    else e_u[u] = a < S ? slot_expert(p, a) : -1;
   }
   const uint32_t code_row = (uint32_t)p.I / 2, scale_row = (uint32_t)p.I / 16;
   // one resource spans all of W_down (and one its scales); the host checks
@@ -862,7 +975,12 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
     cnt_u[u] = 0;
     gd_u[u] = 0.0f;
     if (e_u[u] >= 0) {
-      expert_routes(p, e_u[u], off_u[u], cnt_u[u]);
+      if constexpr (RS) {
+        off_u[u] = wave + u * kDcWaves;     // the route itself: h row a, one route
+        cnt_u[u] = 1;
+      } else {
+        expert_routes(p, e_u[u], off_u[u], cnt_u[u]);
+      }
       gd_u[u] = sload(p.gsc, e_u[u] * 3 + 2);
     }
   }
@@ -906,14 +1024,14 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
   }
 }
 
-template <int LD>
+template <int LD, bool RS = false>
 void launch_down_combine(const FfnParams& p, unsigned grid, size_t dyn, int slots, hipStream_t s) {
   const int per_wave = (slots + kDcWaves - 1) / kDcWaves;
-  if (per_wave <= 1) down_combine_kernel<LD, 1><<<grid, kDcThreads, dyn, s>>>(p);
-  else if (per_wave == 2) down_combine_kernel<LD, 2><<<grid, kDcThreads, dyn, s>>>(p);
-  else if (per_wave == 3) down_combine_kernel<LD, 3><<<grid, kDcThreads, dyn, s>>>(p);
-  else if (per_wave == 4) down_combine_kernel<LD, 4><<<grid, kDcThreads, dyn, s>>>(p);
-  else down_combine_kernel<LD, kDcMaxRoutes / kDcWaves><<<grid, kDcThreads, dyn, s>>>(p);
+  if (per_wave <= 1) down_combine_kernel<LD, 1, RS><<<grid, kDcThreads, dyn, s>>>(p);
+  else if (per_wave == 2) down_combine_kernel<LD, 2, RS><<<grid, kDcThreads, dyn, s>>>(p);
+  else if (per_wave == 3) down_combine_kernel<LD, 3, RS><<<grid, kDcThreads, dyn, s>>>(p);
+  else if (per_wave == 4) down_combine_kernel<LD, 4, RS><<<grid, kDcThreads, dyn, s>>>(p);
+  else down_combine_kernel<LD, kDcMaxRoutes / kDcWaves, RS><<<grid, kDcThreads, dyn, s>>>(p);
 }
 
 // ------------------------------------------------------------------ rows of several chunks per lane
@@ -1445,3 +1563,73 @@ extern "C" moe_status moe_expert_ffn(const uint16_t* x, const uint8_t* w_gate, c
                               expert_offset, active_experts, n_active, route_src, route_pos, T, H, I, E, k,
                               workspace, workspace_bytes, y, stream);
 }
+
+namespace moe {
+
+// Batches up to this many routes take the small step (selection inside the
+// gate/up launch, route-slot down/unroute with the bucketing beside it);
+// measured at the decode shape against routing + the expert kernels.
+constexpr int kSmallStepMaxRoutes = 40;
+
+bool small_step_ok(int T, int H, int I, int E, int k) {
+  if (T < 1 || (long long)T * k > kSmallStepMaxRoutes) return false;
+  if (H != 64 * 32 || E > 1024 || k > 32) return false;          // gate/up rows of one chunk per lane: H = 2048
+  const int C = I / 32;
+  if (C > 64 || (C & (C - 1)) != 0) return false;                 // down rows of one chunk per lane
+  return ffn_policy(T, H, I, E, k, false).down_combine;
+}
+
+template <int V, int KC>
+void launch_select_gate_up(const FfnParams& p, const float* logits, const float* bias, int32_t* topk_idx,
+                           float* topk_w, int tasks, hipStream_t s) {
+  select_gate_up_kernel<V, KC><<<(unsigned)tasks, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks);
+}
+
+template <int V>
+void launch_select_gate_up_k(int k, const FfnParams& p, const float* logits, const float* bias, int32_t* topk_idx,
+                             float* topk_w, int tasks, hipStream_t s) {
+  if (k == 10) launch_select_gate_up<V, 10>(p, logits, bias, topk_idx, topk_w, tasks, s);
+  else launch_select_gate_up<V, 0>(p, logits, bias, topk_idx, topk_w, tasks, s);
+}
+
+moe_status small_step(const uint16_t* x, const float* logits, const float* bias, const uint8_t* w_gate,
+                      const uint8_t* s_gate, const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,
+                      const uint8_t* s_down, const float* g_scale, int T, int H, int I, int E, int k,
+                      int32_t* topk_idx, float* topk_w, int32_t* expert_count, int32_t* expert_offset,
+                      int32_t* active_experts, int32_t* n_active, int32_t* route_src, int32_t* route_pos,
+                      void* workspace, uint16_t* y, hipStream_t s) {
+  const WorkspaceLayout L = workspace_layout(T, H, I, E, k);
+  FfnParams p{};
+  p.x = x; p.wg = w_gate; p.sg = s_gate; p.wu = w_up; p.su = s_up; p.wd = w_down; p.sd = s_down;
+  p.gsc = g_scale; p.topk_w = topk_w; p.topk_idx = topk_idx;
+  p.count = expert_count; p.offset = expert_offset; p.active = active_experts; p.n_active_ptr = n_active;
+  p.route_src = route_src; p.route_pos = route_pos;
+  p.T = T; p.H = H; p.I = I; p.E = E; p.k = k;
+  char* ws = static_cast<char*>(workspace);
+  p.h = reinterpret_cast<uint16_t*>(ws + L.h_off);
+  p.o = reinterpret_cast<uint16_t*>(ws + L.o_off);
+  p.y = y;
+  p.sr = SharedRows{};
+  p.lr_gu = 64;
+  p.lr_d = lanes_per_row(I / 32);
+  const int R = T * k;
+  // selection + gate/up: one workgroup per (route, 16 rows of I)
+  const int tiles = (I + kWavesPerBlock * kGuUnits - 1) / (kWavesPerBlock * kGuUnits);
+  const int tasks = R * tiles;
+  const int V = (E + kWave - 1) / kWave;
+  if (V <= 1) launch_select_gate_up_k<1>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
+  else if (V <= 2) launch_select_gate_up_k<2>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
+  else if (V <= 4) launch_select_gate_up_k<4>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
+  else if (V <= 8) launch_select_gate_up_k<8>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
+  else launch_select_gate_up_k<16>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
+  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  // route-slot down/unroute over rows of y, and one bucketing workgroup
+  const int rpw = kWave / p.lr_d;
+  const size_t dyn = std::max((size_t)R * I * 2 + (size_t)R * rpw * 4, sizeof(BucketShared));
+  const unsigned grid = (unsigned)((H + rpw - 1) / rpw) + 1;
+  if (p.lr_d == 16) launch_down_combine<16, true>(p, grid, dyn, R, s);
+  else launch_down_combine<0, true>(p, grid, dyn, R, s);
+  return launch_status();
+}
+
+}  // namespace moe

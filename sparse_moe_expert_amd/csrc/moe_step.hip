@@ -1,9 +1,12 @@
 // moe_step: one routed-MoE step (routing, bucketing, expert FFN with the
 // weighted unroute) in one call.
 //
-// It enqueues moe_route_bucket and then moe_expert_ffn on the caller's
-// stream: three kernels at decode sizes (route + bucket in one workgroup,
-// gate/up, down + unroute).  A one-kernel form of the step - every workgroup
+// Small batches (at most 40 routes at H = 2048) take two kernels: the
+// selection inside the gate/up launch (every workgroup, one per route and
+// row tile, selects its token's experts itself; no routing kernel, no
+// hand-off), then the down/unroute with one slot per route and the
+// bucketing in one more workgroup of that launch.  Larger batches enqueue
+// moe_route_bucket and then moe_expert_ffn on the caller's stream.  A one-kernel form of the step - every workgroup
 // routing the batch itself, gate/up publishing each expert's intermediate
 // through device-coherent stores and per-expert counters, down waiting on
 // them, the last route of a token combining it - was built and measured on
@@ -67,6 +70,12 @@ static moe_status step(const uint16_t* x, const float* logits, const float* bias
                                     n_active, route_src, route_pos, workspace, workspace_bytes, y);
   if (chk != MOE_OK || T == 0) return chk;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  // small batches: the selection inside the gate/up launch (no routing
+  // kernel), the bucketing beside the down/unroute
+  if (!side && moe::small_step_ok(T, H, I, E, k))
+    return moe::small_step(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, T, H, I, E, k,
+                           topk_idx, topk_w, expert_count, expert_offset, active_experts, n_active, route_src,
+                           route_pos, workspace, y, s);
   // The expert kernels' work lists, when they read any, are built by the
   // one-workgroup bucketing kernel, which holds the counts already (one
   // launch less than building them in the FFN call).  The FFN workspace in
