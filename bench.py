@@ -97,10 +97,13 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_kernel_decode_t4_traffic.json")
+def traffic_file(kernel: str, workload: str) -> str:
+    """The committed counter record of this kernel at this workload."""
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
 KERNEL_SOURCES = ["sparse_moe_expert_amd/csrc/expert_ffn.hip", "sparse_moe_expert_amd/csrc/row_dot.h",
                   "sparse_moe_expert_amd/csrc/moe_common.h", "sparse_moe_expert_amd/csrc/shared_rows.h",
-                  "sparse_moe_expert_amd/csrc/work_list.h"]
+                  "sparse_moe_expert_amd/csrc/work_list.h", "sparse_moe_expert_amd/csrc/select.h",
+                  "sparse_moe_expert_amd/csrc/bucket_block.h"]
 
 
 def kernel_sources_digest() -> str:
@@ -112,16 +115,18 @@ def kernel_sources_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per gate/up launch from the committed counter runs (FETCH_SIZE
-    + WRITE_SIZE, calibrated against a copy of known size), or None when
-    there are none for this workload or the kernel sources changed since."""
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    runs (FETCH_SIZE + WRITE_SIZE, calibrated against a copy of known size),
+    or None when there are none for this workload and kernel or the kernel
+    sources changed since."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kernel, workload)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("sources_sha256") != kernel_sources_digest():
+    if (rec.get("workload") != workload or rec.get("kernel", "gate_up_kernel") != kernel
+            or rec.get("sources_sha256") != kernel_sources_digest()):
         return None
     return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
@@ -741,18 +746,34 @@ def main():
     # Each pair keeps its own step object, so the routing stays that pair's.
     stream = torch.cuda.current_stream(dev)
     reps = max(1, args.ffn_launches // NB)
-    kname = "gate_up_kernel"
-    dom_bytes = float(np.mean(n_unique)) * GATE_UP_BYTES_PER_EXPERT + T * H * 2 + n_routes * I * 2
+    # Small batches (at most 40 routes at H = 2048, the rows of one 16-byte
+    # chunk per lane) run the small step, whose first launch selects and
+    # computes gate/up per route: that launch is the dominant kernel and
+    # streams each route's expert tile (route-issued bytes).  Otherwise the
+    # gate/up row-dot kernel of moe_expert_ffn on the bucketed routes.
+    C_i = I // 32
+    small = (T * k <= 40 and H == 2048 and C_i <= 64 and C_i & (C_i - 1) == 0 and args.path in ("packed", "step"))
     gu_steps = []
     for b in range(NB):
         sb = sme.MoeStep(T, H, I, E, k, dev, path=args.path)
         sb.routing(ls[b], bias)
         gu_steps.append(sb)
+    if small:
+        kname = "select_gate_up_kernel"
+        dom_bytes = n_routes * GATE_UP_BYTES_PER_EXPERT + T * H * 2 + n_routes * I * 2 + T * E * 4
+        dom_bytes_unique = float(np.mean(n_unique)) * GATE_UP_BYTES_PER_EXPERT + T * H * 2 + n_routes * I * 2
+    else:
+        kname = "gate_up_kernel"
+        dom_bytes = float(np.mean(n_unique)) * GATE_UP_BYTES_PER_EXPERT + T * H * 2 + n_routes * I * 2
+        dom_bytes_unique = dom_bytes
     g_dom = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_dom):
         for _ in range(reps):
             for b in range(NB):
-                gu_steps[b].ffn(xs[b], banks[b], stage=1)
+                if small:
+                    gu_steps[b].run(xs[b], ls[b], bias, banks[b], packed=pks[b], stage=1)
+                else:
+                    gu_steps[b].ffn(xs[b], banks[b], stage=1)
     g_dom.replay()                      # warm-up
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -791,9 +812,12 @@ def main():
                    "unique_expert_bytes_per_step": int(bytes_per_step)},
         "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg.name),
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg.name, kname),
                      "avg_launch_us": round(avg * 1e6, 3),
-                     "bytes_per_launch": int(dom_bytes), "launches": n_dom},
+                     "bytes_per_launch": int(dom_bytes), "launches": n_dom,
+                     "bytes_basis": ("route-issued: each route's expert gate/up tile, x, logits, h"
+                                     if small else "unique experts' gate/up weights, x, h"),
+                     "achieved_on_unique_expert_bytes": round(dom_bytes_unique / avg / 1e9, 1)},
     }
     if protocol is not None:
         out["protocol"] = protocol

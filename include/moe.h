@@ -6,7 +6,7 @@
  *   moe_route_topk     router logits -> top-k expert ids and gate weights
  *   moe_bucket_routes  top-k ids -> routes grouped by expert (stable order)
  *   moe_expert_ffn     bf16 tokens + NVFP4 experts + buckets -> bf16 output
- * or the same step in one call, moe_step (one kernel for small batches).
+ * or the same step in one call, moe_step (two kernels for small batches).
  * The router projection that produces the logits is a prerequisite outside
  * these calls (the MonoMoE host wrapper takes precomputed router logits and
  * the SM70 design note keeps the router GEMV as an explicit prerequisite:
@@ -309,6 +309,33 @@ moe_status moe_step(const uint16_t* x, const float* logits, const float* bias,
                     void* workspace, size_t workspace_bytes,
                     uint16_t* y,
                     void* stream);
+
+/*
+ * moe_step_stage — one part of moe_step / moe_step_packed (`packed` may be
+ * NULL), same arguments, so that a caller can time the step's phases:
+ *   stage 1: everything up to and including the gate/up projection (for
+ *            small batches the launch that selects and computes gate/up; for
+ *            larger ones the routing and bucketing kernels and the gate/up
+ *            kernels);
+ *   stage 2: the rest (down projection and weighted unroute; for small
+ *            batches also the bucketing); reads what stage 1 left in the
+ *            outputs and the workspace for the same inputs;
+ *   stage 3: the whole step (exactly moe_step / moe_step_packed).
+ * Stages 1 then 2 give moe_step's outputs bit for bit.  Any other stage
+ * returns MOE_ERR_INVALID_SHAPE; every other check as for moe_step.
+ */
+moe_status moe_step_stage(int stage, const uint16_t* x, const float* logits, const float* bias,
+                          const uint8_t* w_gate, const uint8_t* s_gate,
+                          const uint8_t* w_up, const uint8_t* s_up,
+                          const uint8_t* w_down, const uint8_t* s_down,
+                          const float* g_scale, const uint8_t* packed,
+                          int T, int H, int I, int E, int k,
+                          int32_t* topk_idx, float* topk_w,
+                          int32_t* expert_count, int32_t* expert_offset,
+                          int32_t* active_experts, int32_t* n_active,
+                          int32_t* route_src, int32_t* route_pos,
+                          void* workspace, size_t workspace_bytes,
+                          uint16_t* y, void* stream);
 
 /*
  * Bytes of the packed copy of all expert weights that moe_pack_weights

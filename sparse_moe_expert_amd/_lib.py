@@ -42,6 +42,7 @@ SIGNATURES = {
     "moe_expert_ffn_stage": (_I, [_I] + [_P] * 15 + [_I] * 5 + [_P, ctypes.c_size_t, _P, _P]),
     "moe_step_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "moe_step": (_I, [_P, _P, _P] + [_P] * 7 + [_I] * 5 + [_P] * 8 + [_P, ctypes.c_size_t, _P, _P]),
+    "moe_step_stage": (_I, [_I, _P, _P, _P] + [_P] * 7 + [_P] + [_I] * 5 + [_P] * 8 + [_P, ctypes.c_size_t, _P, _P]),
     "moe_packed_weights_size": (ctypes.c_size_t, [_I, _I, _I]),
     "moe_pack_weights": (_I, [_P] * 6 + [_I] * 3 + [_P, _P]),
     "moe_step_packed": (_I, [_P, _P, _P] + [_P] * 7 + [_P] + [_I] * 5 + [_P] * 8 + [_P, ctypes.c_size_t, _P, _P]),
@@ -344,9 +345,11 @@ def pack_weights(weights: ExpertWeights) -> torch.Tensor:
 
 def moe_step(x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor], weights: ExpertWeights,
              k: int, topk_idx: torch.Tensor, topk_w: torch.Tensor, buckets: Buckets,
-             workspace: torch.Tensor, y: torch.Tensor, packed: Optional[torch.Tensor] = None) -> torch.Tensor:
+             workspace: torch.Tensor, y: torch.Tensor, packed: Optional[torch.Tensor] = None,
+             stage: int = 3) -> torch.Tensor:
     """One whole step (route, bucket, expert FFN) in one call; fills every output.  With `packed`
-    (from pack_weights of the same weights) it runs moe_step_packed."""
+    (from pack_weights of the same weights) it runs moe_step_packed.  stage 1 or 2 runs one part
+    of it (moe_step_stage)."""
     x = _check_x(x)
     T, H = x.shape
     E, H_w, I = weights.shape
@@ -368,6 +371,15 @@ def moe_step(x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor]
     _need(workspace, "workspace", torch.uint8, None, dev)
     if y.dtype != torch.bfloat16 or tuple(y.shape) != (T, H) or not y.is_contiguous() or y.device != dev:
         raise ValueError("y must be a contiguous bfloat16 [T, H] tensor on x's device")
+    if stage != 3:
+        if packed is not None:
+            _need(packed, "packed", torch.uint8, (moe_packed_weights_size(E, H, I),), dev)
+        st = load_library().moe_step_stage(stage, _ptr(x), _ptr(logits), _ptr(bias), *(_ptr(t) for t in weights),
+                                           _ptr(packed), T, H, I, E, k, _ptr(topk_idx), _ptr(topk_w),
+                                           *(_ptr(t) for t in buckets), _ptr(workspace),
+                                           ctypes.c_size_t(workspace.numel()), _ptr(y), _stream(dev))
+        _check("moe_step_stage", st)
+        return y
     if packed is None:
         st = load_library().moe_step(_ptr(x), _ptr(logits), _ptr(bias), *(_ptr(t) for t in weights),
                                      T, H, I, E, k, _ptr(topk_idx), _ptr(topk_w), *(_ptr(t) for t in buckets),

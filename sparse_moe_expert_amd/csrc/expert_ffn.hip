@@ -1597,7 +1597,7 @@ moe_status small_step(const uint16_t* x, const float* logits, const float* bias,
                       const uint8_t* s_down, const float* g_scale, int T, int H, int I, int E, int k,
                       int32_t* topk_idx, float* topk_w, int32_t* expert_count, int32_t* expert_offset,
                       int32_t* active_experts, int32_t* n_active, int32_t* route_src, int32_t* route_pos,
-                      void* workspace, uint16_t* y, hipStream_t s) {
+                      void* workspace, uint16_t* y, hipStream_t s, int stage) {
   const WorkspaceLayout L = workspace_layout(T, H, I, E, k);
   FfnParams p{};
   p.x = x; p.wg = w_gate; p.sg = s_gate; p.wu = w_up; p.su = s_up; p.wd = w_down; p.sd = s_down;
@@ -1617,12 +1617,15 @@ moe_status small_step(const uint16_t* x, const float* logits, const float* bias,
   const int tiles = (I + kWavesPerBlock * kGuUnits - 1) / (kWavesPerBlock * kGuUnits);
   const int tasks = R * tiles;
   const int V = (E + kWave - 1) / kWave;
-  if (V <= 1) launch_select_gate_up_k<1>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
-  else if (V <= 2) launch_select_gate_up_k<2>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
-  else if (V <= 4) launch_select_gate_up_k<4>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
-  else if (V <= 8) launch_select_gate_up_k<8>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
-  else launch_select_gate_up_k<16>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
-  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  if (stage & 1) {
+    if (V <= 1) launch_select_gate_up_k<1>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
+    else if (V <= 2) launch_select_gate_up_k<2>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
+    else if (V <= 4) launch_select_gate_up_k<4>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
+    else if (V <= 8) launch_select_gate_up_k<8>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
+    else launch_select_gate_up_k<16>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
+    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  }
+  if (!(stage & 2)) return MOE_OK;
   // route-slot down/unroute over rows of y, and one bucketing workgroup
   const int rpw = kWave / p.lr_d;
   const size_t dyn = std::max((size_t)R * I * 2 + (size_t)R * rpw * 4, sizeof(BucketShared));

@@ -167,12 +167,14 @@ moe_status route_bucket(const float* logits, const float* bias, int T, int E, in
 // 2048): the selection inside the gate/up launch (one workgroup per route and
 // row tile), then the route-slot down/unroute with the bucketing beside it.
 // Outputs identical to route_bucket + expert_ffn.  Arguments already checked.
+// stage 1: the selection and gate/up launch only; 2: the down/unroute and
+// bucketing launch only (after stage 1 on the same workspace); 3: both.
 bool small_step_ok(int T, int H, int I, int E, int k);
 moe_status small_step(const uint16_t* x, const float* logits, const float* bias, const uint8_t* w_gate,
                       const uint8_t* s_gate, const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,
                       const uint8_t* s_down, const float* g_scale, int T, int H, int I, int E, int k,
                       int32_t* topk_idx, float* topk_w, int32_t* expert_count, int32_t* expert_offset,
                       int32_t* active_experts, int32_t* n_active, int32_t* route_src, int32_t* route_pos,
-                      void* workspace, uint16_t* y, hipStream_t s);
+                      void* workspace, uint16_t* y, hipStream_t s, int stage = 3);
 
 }  // namespace moe

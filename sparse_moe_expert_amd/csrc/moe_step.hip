@@ -64,7 +64,7 @@ static moe_status step(const uint16_t* x, const float* logits, const float* bias
                        int E, int k, int32_t* topk_idx, float* topk_w, int32_t* expert_count,
                        int32_t* expert_offset, int32_t* active_experts, int32_t* n_active, int32_t* route_src,
                        int32_t* route_pos, void* workspace, size_t workspace_bytes, uint16_t* y, void* stream,
-                       const moe::SharedRows* side = nullptr) {
+                       const moe::SharedRows* side = nullptr, int stage = 3) {
   const moe_status chk = step_check(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, packed, T,
                                     H, I, E, k, topk_idx, topk_w, expert_count, expert_offset, active_experts,
                                     n_active, route_src, route_pos, workspace, workspace_bytes, y);
@@ -75,7 +75,11 @@ static moe_status step(const uint16_t* x, const float* logits, const float* bias
   if (!side && moe::small_step_ok(T, H, I, E, k))
     return moe::small_step(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, T, H, I, E, k,
                            topk_idx, topk_w, expert_count, expert_offset, active_experts, n_active, route_src,
-                           route_pos, workspace, y, s);
+                           route_pos, workspace, y, s, stage);
+  if (stage == 2)                                  // the expert FFN's second stage (it rebuilds its work lists)
+    return moe::expert_ffn(2, x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
+                           expert_offset, active_experts, n_active, route_src, route_pos, packed, T, H, I, E, k,
+                           workspace, workspace_bytes, y, s);
   // The expert kernels' work lists, when they read any, are built by the
   // one-workgroup bucketing kernel, which holds the counts already (one
   // launch less than building them in the FFN call).  The FFN workspace in
@@ -93,7 +97,7 @@ static moe_status step(const uint16_t* x, const float* logits, const float* bias
   // kernel run on their own before the expert kernels (whose row-dot kernel
   // may carry its down rows)
   if (side && !gu_done && moe::shared_gate_up(*side, s) != MOE_OK) return MOE_ERR_HIP;
-  st = moe::expert_ffn(3, x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
+  st = moe::expert_ffn(stage, x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
                        expert_offset, active_experts, n_active, route_src, route_pos, packed, T, H, I, E, k,
                        workspace, workspace_bytes, y, s, lists_built, side, &dn_done);
   if (st != MOE_OK) return st;
@@ -207,4 +211,18 @@ extern "C" moe_status moe_step_noalloc(const uint16_t* x, const float* logits, c
   return step(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, packed, T, H, I, E, k, topk_idx,
               topk_w, expert_count, expert_offset, active_experts, n_active, route_src, route_pos, ws,
               kNoAllocScratchBytes, y, stream);
+}
+
+extern "C" moe_status moe_step_stage(int stage, const uint16_t* x, const float* logits, const float* bias,
+                                     const uint8_t* w_gate, const uint8_t* s_gate, const uint8_t* w_up,
+                                     const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                                     const float* g_scale, const uint8_t* packed, int T, int H, int I, int E, int k,
+                                     int32_t* topk_idx, float* topk_w, int32_t* expert_count,
+                                     int32_t* expert_offset, int32_t* active_experts, int32_t* n_active,
+                                     int32_t* route_src, int32_t* route_pos, void* workspace,
+                                     size_t workspace_bytes, uint16_t* y, void* stream) {
+  if (stage < 1 || stage > 3) return MOE_ERR_INVALID_SHAPE;
+  return step(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, packed, T, H, I, E, k, topk_idx,
+              topk_w, expert_count, expert_offset, active_experts, n_active, route_src, route_pos, workspace,
+              workspace_bytes, y, stream, nullptr, stage);
 }

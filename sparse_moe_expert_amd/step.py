@@ -78,13 +78,16 @@ class MoeStep:
         moe_expert_ffn(x, weights, self.topk_w, self.buckets, self.workspace, self.y, stage=stage)
 
     def run(self, x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor],
-            weights: ExpertWeights, packed: Optional[torch.Tensor] = None) -> torch.Tensor:
+            weights: ExpertWeights, packed: Optional[torch.Tensor] = None, stage: int = 3) -> torch.Tensor:
+        """The step; stage 1 or 2 (paths "step" and "packed") runs one part of it."""
         if self.path in ("step", "packed"):
             if self.path == "packed" and packed is None:
                 raise ValueError('path "packed" needs the packed weights (pack_weights)')
             moe_step(x, logits, bias, weights, self.k, self.topk_idx, self.topk_w, self.buckets,
-                     self.workspace, self.y, packed=packed if self.path == "packed" else None)
+                     self.workspace, self.y, packed=packed if self.path == "packed" else None, stage=stage)
         else:
+            if stage != 3:
+                raise ValueError('stages are run on paths "step" and "packed"')
             self.routing(logits, bias)
             self.ffn(x, weights)
         return self.y

@@ -81,3 +81,26 @@ def test_small_step_guard_regions():
     assert torch.all(big_y[0] == 3.0) and torch.all(big_y[T + 1] == 3.0)
     idx, w, b, y = oracle_all(wl.x, wl.logits, None, wl.bank, k)
     assert_output(big_y[1: T + 1].float().cpu().numpy().astype(np.float64), y, "guarded small step")
+
+
+@pytest.mark.parametrize("name,path", [("decode_t4", "step"), ("decode_t4", "packed"), ("verify_t32", "step"),
+                                       ("decode_t256_zipf", "packed")])
+def test_step_stages_compose(name, path):
+    """moe_step_stage 1 then 2 gives moe_step's outputs bit for bit (the small
+    step's two launches at decode_t4; routing, buckets and gate/up, then down
+    and the unroute, at the larger batches)."""
+    wl = make_workload(name, x_seed=77)
+    W = device_weights(wl.bank)
+    pk = device_packed(wl.bank) if path == "packed" else None
+    bias = None if wl.bias is None else to_dev(wl.bias)
+    full = sme.MoeStep(wl.T, wl.H, wl.I, wl.E, wl.k, DEV, path=path)
+    full.run(x_bits(wl.x), to_dev(wl.logits), bias, W, packed=pk)
+    st = sme.MoeStep(wl.T, wl.H, wl.I, wl.E, wl.k, DEV, path=path)
+    st.run(x_bits(wl.x), to_dev(wl.logits), bias, W, packed=pk, stage=1)
+    st.run(x_bits(wl.x), to_dev(wl.logits), bias, W, packed=pk, stage=2)
+    torch.cuda.synchronize()
+    assert torch.equal(full.topk_idx, st.topk_idx)
+    assert torch.equal(full.topk_w.view(torch.int32), st.topk_w.view(torch.int32))
+    for ta, tb in zip(full.buckets, st.buckets):
+        assert torch.equal(ta, tb)
+    assert torch.equal(full.y.view(torch.int16), st.y.view(torch.int16))
