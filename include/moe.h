@@ -317,9 +317,9 @@ moe_status moe_step(const uint16_t* x, const float* logits, const float* bias,
  *            small batches the launch that selects and computes gate/up; for
  *            larger ones the routing and bucketing kernels and the gate/up
  *            kernels);
- *   stage 2: the rest (down projection and weighted unroute; for small
- *            batches also the bucketing); reads what stage 1 left in the
- *            outputs and the workspace for the same inputs;
+ *   stage 2: the rest (down projection and weighted unroute); reads what
+ *            stage 1 left in the outputs and the workspace for the same
+ *            inputs;
  *   stage 3: the whole step (exactly moe_step / moe_step_packed).
  * Stages 1 then 2 give moe_step's outputs bit for bit.  Any other stage
  * returns MOE_ERR_INVALID_SHAPE; every other check as for moe_step.

@@ -49,7 +49,6 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "bucket_block.h"
 #include "row_dot.h"
 #include "select.h"
 #include "shared_rows.h"
@@ -325,9 +324,105 @@ __global__ __launch_bounds__(kThreads, 4) void gate_up_kernel(FfnParams p, int n
 // carry ~96% of the route-issued bytes, and the weights start streaming
 // without waiting for a routing kernel, its boundary and a dependent read of
 // the active list.  Rows of H = 2048 (one 16-byte chunk per lane, 64 lanes
-// per row), as gate_up_kernel<64>.  The workgroups of route (t, 0), tile 0,
-// write token t's topk_idx and topk_w.
+// per row), as gate_up_kernel<64>.  One more workgroup, the launch's last,
+// writes every routing output (small_route_bucket): at 59 registers eight
+// of these workgroups fit a CU, so it runs beside the others.
 constexpr int kSgXBytes = 4096;           // one activation row of H = 2048
+constexpr int kSgMaxRoutes = 40;          // routes of a small batch (the small step's limit)
+
+// The routing outputs of a small batch (at most kSgMaxRoutes routes), by one
+// workgroup of kThreads threads of the selection launch, beside the gate/up
+// workgroups (which select for themselves and need none of it): wave w
+// selects tokens w, w + 4, ... and writes topk_idx and topk_w; then the
+// buckets - an LDS histogram of the route ids, one workgroup-wide scan of
+// (routes, active experts) over four experts per thread for the offsets and
+// active positions, and the stable scatter: route r goes to offset(e) plus
+// the number of earlier routes to e (ballots per id bit; all routes lie in
+// one wavefront), the route order of moe_bucket_routes.
+template <int V, int KC>
+__device__ __forceinline__ void small_route_bucket(const FfnParams& p, const float* __restrict__ logits,
+                                                   const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
+                                                   float* __restrict__ topk_w) {
+  static_assert(kSgMaxRoutes <= kWave, "the scatter ranks one wavefront of routes");
+  __shared__ int s_ids[kSgMaxRoutes];
+  __shared__ int s_cnt[1024];                          // counts, then offsets
+  __shared__ int s_wt[kWavesPerBlock];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int R = p.T * p.k;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_cnt[4 * tid + i] = 0;
+  for (int t = wave; t < p.T; t += kWavesPerBlock) {
+    int e;
+    float w;
+    select_token<V, KC>(logits + (size_t)t * p.E, bias, p.E, p.k, lane, e, w);
+    if (lane < p.k) {
+      topk_idx[(size_t)t * p.k + lane] = e;
+      topk_w[(size_t)t * p.k + lane] = w;
+      s_ids[t * p.k + lane] = e;
+    }
+  }
+  __syncthreads();
+  if (tid < R) atomicAdd(&s_cnt[s_ids[tid]], 1);      // integer counts: order-free
+  __syncthreads();
+  int c[4], cs = 0, as = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[i] = s_cnt[4 * tid + i];
+    cs += c[i];
+    as += c[i] > 0;
+  }
+  // exclusive scan over the workgroup of routes + (active experts << 16)
+  const int v = cs + (as << 16);
+  const int inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) s_wt[wave] = inc;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) {
+    base += w < wave ? s_wt[w] : 0;
+    total += s_wt[w];
+  }
+  int scan = base + inc - v;
+  const int total_active = total >> 16;
+  int32_t* count = const_cast<int32_t*>(p.count);
+  int32_t* offset = const_cast<int32_t*>(p.offset);
+  int32_t* active = const_cast<int32_t*>(p.active);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * tid + i;
+    const int off = scan & 0xFFFF, apos = scan >> 16;
+    if (e < p.E) {
+      count[e] = c[i];
+      offset[e] = off;
+      if (c[i] > 0) active[apos] = e;
+      if (e >= total_active) active[e] = -1;
+    }
+    s_cnt[e] = off;                                    // this thread's own entries: no barrier needed before
+    scan += c[i] + ((c[i] > 0) << 16);
+  }
+  if (tid == 0) {
+    offset[p.E] = total & 0xFFFF;
+    *const_cast<int32_t*>(p.n_active_ptr) = total_active;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const bool valid = lane < R;
+    const int e = valid ? s_ids[lane] : 0;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 10; ++b) {                     // ids are below 1024
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(same & ((1ull << lane) - 1ull));
+    if (valid) {
+      const int pos = s_cnt[e] + rank;
+      const_cast<int32_t*>(p.route_src)[pos] = lane;
+      const_cast<int32_t*>(p.route_pos)[lane] = pos;
+    }
+  }
+}
 
 template <int V, int KC>
 __global__ __launch_bounds__(kThreads, 4) void select_gate_up_kernel(FfnParams p, const float* __restrict__ logits,
@@ -339,7 +434,11 @@ __global__ __launch_bounds__(kThreads, 4) void select_gate_up_kernel(FfnParams p
   __shared__ int s_e;
   const Geo<64, kGuUnits> g(64, p.I);
   const int task = blockIdx.x;
-  if (task >= n_tasks) return;
+  if (task >= n_tasks) {
+    // the launch's last workgroup: every routing output
+    small_route_bucket<V, KC>(p, logits, bias, topk_idx, topk_w);
+    return;
+  }
   const int r = task / g.tiles, tile = task - r * g.tiles;
   const int t = r / p.k, j = r - t * p.k;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -353,10 +452,6 @@ __global__ __launch_bounds__(kThreads, 4) void select_gate_up_kernel(FfnParams p
     float w_l;
     select_token<V, KC>(logits + (size_t)t * p.E, bias, p.E, p.k, lane, e_l, w_l);
     if (lane == j) s_e = e_l;
-    if (j == 0 && tile == 0 && lane < p.k) {
-      topk_idx[(size_t)t * p.k + lane] = e_l;
-      topk_w[(size_t)t * p.k + lane] = w_l;
-    }
   }
   *reinterpret_cast<u32x4*>(s_x + tid * 16) = xv;
   __syncthreads();
@@ -896,9 +991,7 @@ constexpr int kDcHLoads = kDcMaxLds / 16 / kDcThreads;   // 16-byte h pieces per
 // everything).
 //
 // Route slots (RS, after select_gate_up_kernel): slot a is route a itself
-// (expert topk_idx[a], h row a, one route), so the buckets are not needed;
-// the launch's last workgroup buckets the routes instead (bucket_block.h) and
-// writes the six bucket arrays, beside the down workgroups.
+// (expert topk_idx[a], h row a, one route), so the buckets are not needed.
 template <int LD, int SLOTS, bool RS = false>
 __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_kernel(FfnParams p) {
   extern __shared__ __align__(16) uint8_t s_dyn8[];   // [R, I] bf16 h, then [R, rpw] fp32 o
@@ -907,16 +1000,6 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int R = p.T * p.k;
-  if constexpr (RS) {
-    if ((int)blockIdx.x == (int)gridDim.x - 1) {
-      // the bucketing workgroup: its dynamic LDS holds the bucketing state
-      bucket_block(p.topk_idx, R, p.E, *reinterpret_cast<BucketShared*>(s_dyn8), const_cast<int32_t*>(p.count),
-                   const_cast<int32_t*>(p.offset), const_cast<int32_t*>(p.active),
-                   const_cast<int32_t*>(p.n_active_ptr), const_cast<int32_t*>(p.route_src),
-                   const_cast<int32_t*>(p.route_pos), WorkLists{});
-      return;
-    }
-  }
   const int ld = LD ? LD : p.lr_d, rpw = kWave / ld, sub = lane / ld, sl = lane & (ld - 1);
   const int row0 = blockIdx.x * rpw;
   const int S = RS ? R : min(p.E, R);
@@ -1566,10 +1649,11 @@ extern "C" moe_status moe_expert_ffn(const uint16_t* x, const uint8_t* w_gate, c
 
 namespace moe {
 
-// Batches up to this many routes take the small step (selection inside the
-// gate/up launch, route-slot down/unroute with the bucketing beside it);
+// Batches up to this many routes take the small step (the selection and the
+// routing outputs inside the gate/up launch, then the route-slot
+// down/unroute);
 // measured at the decode shape against routing + the expert kernels.
-constexpr int kSmallStepMaxRoutes = 40;
+constexpr int kSmallStepMaxRoutes = kSgMaxRoutes;
 
 bool small_step_ok(int T, int H, int I, int E, int k) {
   if (T < 1 || (long long)T * k > kSmallStepMaxRoutes) return false;
@@ -1582,7 +1666,7 @@ bool small_step_ok(int T, int H, int I, int E, int k) {
 template <int V, int KC>
 void launch_select_gate_up(const FfnParams& p, const float* logits, const float* bias, int32_t* topk_idx,
                            float* topk_w, int tasks, hipStream_t s) {
-  select_gate_up_kernel<V, KC><<<(unsigned)tasks, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks);
+  select_gate_up_kernel<V, KC><<<(unsigned)tasks + 1, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks);
 }
 
 template <int V>
@@ -1615,7 +1699,7 @@ moe_status small_step(const uint16_t* x, const float* logits, const float* bias,
   const int R = T * k;
   // selection + gate/up: one workgroup per (route, 16 rows of I)
   const int tiles = (I + kWavesPerBlock * kGuUnits - 1) / (kWavesPerBlock * kGuUnits);
-  const int tasks = R * tiles;
+  const int tasks = R * tiles;                       // and one routing workgroup after them
   const int V = (E + kWave - 1) / kWave;
   if (stage & 1) {
     if (V <= 1) launch_select_gate_up_k<1>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
@@ -1626,10 +1710,10 @@ moe_status small_step(const uint16_t* x, const float* logits, const float* bias,
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
   if (!(stage & 2)) return MOE_OK;
-  // route-slot down/unroute over rows of y, and one bucketing workgroup
+  // route-slot down/unroute over rows of y
   const int rpw = kWave / p.lr_d;
-  const size_t dyn = std::max((size_t)R * I * 2 + (size_t)R * rpw * 4, sizeof(BucketShared));
-  const unsigned grid = (unsigned)((H + rpw - 1) / rpw) + 1;
+  const size_t dyn = (size_t)R * I * 2 + (size_t)R * rpw * 4;
+  const unsigned grid = (unsigned)((H + rpw - 1) / rpw);
   if (p.lr_d == 16) launch_down_combine<16, true>(p, grid, dyn, R, s);
   else launch_down_combine<0, true>(p, grid, dyn, R, s);
   return launch_status();

@@ -163,12 +163,12 @@ moe_status route_bucket(const float* logits, const float* bias, int T, int E, in
                         size_t scratch_bytes, hipStream_t s, const WorkLists* wl = nullptr,
                         bool* lists_built = nullptr, const SharedRows* sr = nullptr, bool* sr_done = nullptr);
 
-// The small-batch step (moe_step below kSmallStepMaxRoutes routes at H =
-// 2048): the selection inside the gate/up launch (one workgroup per route and
-// row tile), then the route-slot down/unroute with the bucketing beside it.
+// The small-batch step (moe_step up to 40 routes at H = 2048): the selection
+// inside the gate/up launch (one workgroup per route and row tile, one more
+// for the routing outputs), then the route-slot down/unroute.
 // Outputs identical to route_bucket + expert_ffn.  Arguments already checked.
-// stage 1: the selection and gate/up launch only; 2: the down/unroute and
-// bucketing launch only (after stage 1 on the same workspace); 3: both.
+// stage 1: the selection and gate/up launch only; 2: the down/unroute launch
+// only (after stage 1 on the same workspace); 3: both.
 bool small_step_ok(int T, int H, int I, int E, int k);
 moe_status small_step(const uint16_t* x, const float* logits, const float* bias, const uint8_t* w_gate,
                       const uint8_t* s_gate, const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,

@@ -3,9 +3,9 @@
 //
 // Small batches (at most 40 routes at H = 2048) take two kernels: the
 // selection inside the gate/up launch (every workgroup, one per route and
-// row tile, selects its token's experts itself; no routing kernel, no
-// hand-off), then the down/unroute with one slot per route and the
-// bucketing in one more workgroup of that launch.  Larger batches enqueue
+// row tile, selects its token's experts itself; one more workgroup writes
+// the routing outputs; no routing kernel, no hand-off), then the
+// down/unroute with one slot per route.  Larger batches enqueue
 // moe_route_bucket and then moe_expert_ffn on the caller's stream.  A one-kernel form of the step - every workgroup
 // routing the batch itself, gate/up publishing each expert's intermediate
 // through device-coherent stores and per-expert counters, down waiting on
@@ -70,8 +70,8 @@ static moe_status step(const uint16_t* x, const float* logits, const float* bias
                                     n_active, route_src, route_pos, workspace, workspace_bytes, y);
   if (chk != MOE_OK || T == 0) return chk;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  // small batches: the selection inside the gate/up launch (no routing
-  // kernel), the bucketing beside the down/unroute
+  // small batches: the selection and the routing outputs inside the gate/up
+  // launch (no routing kernel), then the route-slot down/unroute
   if (!side && moe::small_step_ok(T, H, I, E, k))
     return moe::small_step(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, T, H, I, E, k,
                            topk_idx, topk_w, expert_count, expert_offset, active_experts, n_active, route_src,
