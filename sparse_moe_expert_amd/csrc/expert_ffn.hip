@@ -652,10 +652,21 @@ __device__ __forceinline__ void wait_vm() {
 // workgroup-scope fence, which waits for every outstanding vector load -
 // including the prefetched steps.  Inside the step loop the only data other
 // waves read is operand rows written to LDS by buffer_load ... lds, whose
-// completion each wave establishes with wait_vm before the barrier, and LDS
-// reads that the MFMAs have already consumed.
+// completion each wave establishes with wait_vm before the barrier.
 __device__ __forceinline__ void step_barrier() {
   compiler_fence();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// The barrier after which a stage is refilled: each wave first waits for its
+// own LDS reads of that stage to return.  The MFMAs that consume them may be
+// scheduled after the barrier, and a read still queued in the LDS unit could
+// otherwise see rows that another wave's next buffer_load ... lds has
+// already written.
+__device__ __forceinline__ void stage_release_barrier() {
+  compiler_fence();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   compiler_fence();
 }
@@ -674,7 +685,10 @@ struct MmTile {
   uint32_t x_goff[4];                                  // operand chunk sources, per step add ks*128
   int wave, lane;
   uint4 wc[kMmStages][NA];
-  uint32_t wsv[kMmStages][NA];
+  // the scale pairs stay 16-bit until their step uses them: widened in the
+  // ring, the compiler zero-extends the ones still in flight at the loop's
+  // back edge and waits for their loads there, draining the prefetch
+  uint16_t wsv[kMmStages][NA];
 
   template <int T>
   __device__ __forceinline__ void issue(int ks) {
@@ -801,13 +815,21 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) acc[m][jt] = f32x16{};
 
+    // the prologue's steps in order: the waits the compiler puts before
+    // each step's first use of its weight registers count the loads issued
+    // after them, and take the smallest count over the loop's entry and back
+    // edge - a scale load scheduled behind the next steps' loads here would
+    // shorten the prefetch of every iteration
     t.template issue<0>(0);
+    compiler_fence();
     t.template issue<1>(min(1, steps - 1));
+    compiler_fence();
     t.template issue<2>(min(2, steps - 1));
+    compiler_fence();
 
     auto body = [&](auto stage_c, int ks) {
       constexpr int S = decltype(stage_c)::value;
-      step_barrier();                                        // every wave is done with step ks-1's stage
+      stage_release_barrier();                               // every wave is done with step ks-1's stage
       // Always three steps ahead, so that every path has the same loads in
       // flight (the last three re-read the final step into a free stage).
       t.template issue<(S + 3) % kMmStages>(min(ks + 3, steps - 1));
@@ -846,40 +868,62 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
     if (s0 + 1 < steps) body(std::integral_constant<int, 1>{}, s0 + 1);
     if (s0 + 2 < steps) body(std::integral_constant<int, 2>{}, s0 + 2);
     wait_vm<0>();                                            // the surplus loads have landed
+    __syncthreads();                                         // every wave is done with the operand stages
 
-    // epilogue: per 32 x 32 block, a lane holds 4 runs of 4 consecutive weight
-    // rows 8*q + 4*(lane/32) + 0..3 for one route column
+    // Epilogue, through LDS: per 32 x 32 block a lane holds 4 runs of 4
+    // consecutive weight rows 8*q + 4*(lane/32) + 0..3 for one route column,
+    // i.e. 8-byte pieces of 32 different output rows per store.  They are
+    // written to LDS first, one stage per route tile jt (32 routes x the
+    // workgroup's rows), the 16-byte chunk c of route r at position
+    // c ^ (r % chunks), so that 16 consecutive routes hit 16 different bank
+    // groups; then every wave stores whole contiguous runs of one route's
+    // output row (16 bytes per lane).
+    constexpr int kChunks = kWgRows / 8;                     // 16-byte chunks of one route's rows in the tile
+    constexpr int kRouteBytes = kWgRows * 2;
+    static_assert(32 * kRouteBytes <= kMmStageBytes, "a route tile's outputs fit one operand stage");
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
-      const int m_loc = jt * 32 + l32;
-      if (m_loc >= mc) continue;
-      const int pos = off + m0 + m_loc;
+      if (jt < mtiles) {
+        uint8_t* st = jt == 0 ? s_x0 : (jt == 1 ? s_x1 : (jt == 2 ? s_x2 : s_x3));
+        uint8_t* rowp = st + l32 * kRouteBytes + half * 8;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wave * 32 + q * 8 + half * 4;
-        if (n >= N) continue;
-        if constexpr (GU) {
-          const float Gg = sload(p.gsc, e * 3 + 0), Gu = sload(p.gsc, e * 3 + 1);
-          uint32_t hv[2];
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (GU) {
+            const float Gg = sload(p.gsc, e * 3 + 0), Gu = sload(p.gsc, e * 3 + 1);
+            uint32_t hv[2];
 #pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2) {
-            const float g0 = acc[0][jt][4 * q + 2 * t2] * Gg, g1 = acc[0][jt][4 * q + 2 * t2 + 1] * Gg;
-            const float u0 = acc[1][jt][4 * q + 2 * t2] * Gu, u1 = acc[1][jt][4 * q + 2 * t2 + 1] * Gu;
-            hv[t2] = f32_to_bf16_rne(silu(g0) * u0) | (f32_to_bf16_rne(silu(g1) * u1) << 16);
-          }
-          *reinterpret_cast<uint2*>(p.h + (size_t)pos * p.I + n) = make_uint2(hv[0], hv[1]);
-        } else {
-          const float Gd = sload(p.gsc, e * 3 + 2);
+            for (int t2 = 0; t2 < 2; ++t2) {
+              const float g0 = acc[0][jt][4 * q + 2 * t2] * Gg, g1 = acc[0][jt][4 * q + 2 * t2 + 1] * Gg;
+              const float u0 = acc[1][jt][4 * q + 2 * t2] * Gu, u1 = acc[1][jt][4 * q + 2 * t2 + 1] * Gu;
+              hv[t2] = f32_to_bf16_rne(silu(g0) * u0) | (f32_to_bf16_rne(silu(g1) * u1) << 16);
+            }
+            const int c = wave * 4 + q;
+            *reinterpret_cast<uint2*>(rowp + ((c ^ (l32 % kChunks)) * 16)) = make_uint2(hv[0], hv[1]);
+          } else {
+            const float Gd = sload(p.gsc, e * 3 + 2);
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m) {
-            const int nm = n + m * kMmRows;
-            if (nm < N)
-              *reinterpret_cast<uint2*>(p.o + (size_t)pos * p.H + nm) =
+            for (int m = 0; m < NMAT; ++m) {
+              const int c = m * (kMmRows / 8) + wave * 4 + q;
+              *reinterpret_cast<uint2*>(rowp + ((c ^ (l32 % kChunks)) * 16)) =
                   make_uint2(f32_to_f16_bits(acc[m][jt][4 * q] * Gd) | (f32_to_f16_bits(acc[m][jt][4 * q + 1] * Gd) << 16),
                              f32_to_f16_bits(acc[m][jt][4 * q + 2] * Gd) | (f32_to_f16_bits(acc[m][jt][4 * q + 3] * Gd) << 16));
+            }
           }
         }
       }
+    }
+    __syncthreads();
+    uint16_t* const out = GU ? p.h : p.o;
+    const int total = mc * kChunks;
+    for (int idx = tid; idx < total; idx += kMmThreads) {
+      const int r = idx / kChunks, j = idx % kChunks;        // route of the chunk, its position in LDS
+      const int c = j ^ (r % 32 % kChunks);                  // the output chunk stored there
+      const int n = n0 + c * 8;
+      if (n >= N) continue;                                  // N is a multiple of 32: whole chunks
+      const int jt = r >> 5;
+      const uint8_t* st = jt == 0 ? s_x0 : (jt == 1 ? s_x1 : (jt == 2 ? s_x2 : s_x3));
+      const uint4 v = *reinterpret_cast<const uint4*>(st + (r & 31) * kRouteBytes + j * 16);
+      *reinterpret_cast<uint4*>(out + (size_t)(off + m0 + r) * N + n) = v;
     }
   }
 }
