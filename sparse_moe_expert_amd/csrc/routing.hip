@@ -29,6 +29,9 @@
 // are found with one ballot per id bit; rank among them + counts of earlier
 // wavefronts in the chunk + the expert's running base gives the position.
 // Positions never depend on timing, so the result is exact and reproducible.
+// Batches of 1025 to 65536 routes bucket in one launch of one such
+// workgroup per 1024-route chunk (bucket_chunked_kernel), larger ones in
+// three launches over a scratch array of per-chunk counts.
 #include "router_rows.h"
 #include "bucket_block.h"
 #include "select.h"
@@ -69,8 +72,9 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_routes_kernel(
                route_pos, wl);
 }
 
-// Bucketing of large batches in parallel (three kernels over chunks of
-// kBucketThreads routes), with a caller-provided scratch array counts[C][E]:
+// Bucketing of batches beyond kChunkedMaxRoutes routes in parallel (three
+// kernels over chunks of kBucketThreads routes), with a caller-provided
+// scratch array counts[C][E]:
 //   bucket_count_kernel    chunk c: per-expert route counts of the chunk
 //   bucket_scan_kernel     one workgroup: for every expert the exclusive
 //                          prefix of its counts over the chunks (in place),
@@ -155,6 +159,125 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_scatter_kernel(
   if (valid) {
     for (int w = 0; w < wave; ++w) rank += s_wcnt[w][e];
     const int pos = s_base[e] + rank;
+    route_src[pos] = r;
+    route_pos[r] = pos;
+  }
+}
+
+// Bucketing of batches of 1025 to kChunkedMaxRoutes routes in one launch of
+// one workgroup per chunk of kBucketThreads routes, without scratch memory.
+// Workgroup c counts the expert ids of the whole batch (160 KB at 40960
+// routes, read from L2) into two LDS histograms - every route, and the routes
+// before its chunk - so that it knows each expert's total, offset and the
+// number of its routes in earlier chunks without waiting for another
+// workgroup; integer atomics make both histograms independent of order.  It
+// then ranks its own chunk's routes like the one-workgroup bucketing
+// (ballots per id bit inside a wavefront, counts of earlier wavefronts) and
+// scatters them.  Workgroup 0 also writes the per-expert arrays and the work
+// lists.  The positions equal the one-workgroup bucketing's.
+constexpr int kChunkedMaxRoutes = 1 << 16;
+constexpr int kChunkedGroups = kChunkedMaxRoutes / 4 / kBucketThreads;   // 16-byte id groups per thread
+static_assert(kChunkedGroups * 4 * kBucketThreads >= kChunkedMaxRoutes, "one load pass covers every id");
+
+struct ChunkedShared {
+  int tot[1024];
+  int pre[1024];
+  uint8_t wcnt[kBucketWaves][1024];
+  int wave_tot[kBucketWaves + 1];
+  WorkListShared wl;
+};
+
+__global__ __launch_bounds__(kBucketThreads) void bucket_chunked_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int id_bits, int32_t* __restrict__ expert_count,
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ active_experts, int32_t* __restrict__ n_active,
+    int32_t* __restrict__ route_src, int32_t* __restrict__ route_pos, WorkLists wl) {
+  __shared__ ChunkedShared sh;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6, c = blockIdx.x;
+  sh.tot[tid] = 0;
+  for (int i = tid; i < kBucketWaves * 1024 / 4; i += kBucketThreads) reinterpret_cast<int*>(&sh.wcnt[0][0])[i] = 0;
+  __syncthreads();
+  // ids outside [0, E) violate the precondition; clamping keeps every access
+  // in bounds.  Thread t takes the whole 16-byte groups t + 1024 u, all of
+  // them loaded before the first atomic (one round trip instead of one per
+  // pass; the resource ends at the last whole group, past which loads read
+  // zeros and are not counted), and threads 0..2 the last R % 4 routes.  The
+  // routes before c * 1024 (the earlier chunks, whole groups) are counted
+  // first; the histogram at that point is the prefix, copied before the rest
+  // is counted.
+  const int groups = R / 4;
+  const auto rid = make_rsrc(ids, (uint32_t)groups * 16u);
+  const int own_group = c * (kBucketThreads / 4);
+  u32x4 v[kChunkedGroups];
+#pragma unroll
+  for (int u = 0; u < kChunkedGroups; ++u)
+    v[u] = __builtin_amdgcn_raw_buffer_load_b128(rid, (uint32_t)(u * kBucketThreads + tid) * 16u, 0, 0);
+  const int rt = groups * 4 + tid;
+  const int e_tail = rt < R ? min(max(ids[rt], 0), E - 1) : -1;
+#pragma unroll
+  for (int u = 0; u < kChunkedGroups; ++u) {
+    const int g = u * kBucketThreads + tid;
+    if (g < min(groups, own_group)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) atomicAdd(&sh.tot[min(max((int)v[u][i], 0), E - 1)], 1);
+    }
+  }
+  __syncthreads();
+  sh.pre[tid] = sh.tot[tid];
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kChunkedGroups; ++u) {
+    const int g = u * kBucketThreads + tid;
+    if (g >= own_group && g < groups) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) atomicAdd(&sh.tot[min(max((int)v[u][i], 0), E - 1)], 1);
+    }
+  }
+  if (e_tail >= 0) atomicAdd(&sh.tot[e_tail], 1);   // the tail lies in the last chunk, never before c
+  __syncthreads();
+  const int cnt = tid < E ? sh.tot[tid] : 0;
+  int off, apos, total_routes, total_active;
+  if (R < (1 << 16)) {
+    int total;
+    const int scan = block_exclusive_scan(cnt + ((cnt > 0) << 16), sh.wave_tot, &total);
+    off = scan & 0xFFFF;
+    apos = scan >> 16;
+    total_routes = total & 0xFFFF;
+    total_active = total >> 16;
+  } else {
+    off = block_exclusive_scan(cnt, sh.wave_tot, &total_routes);
+    apos = block_exclusive_scan(cnt > 0 ? 1 : 0, sh.wave_tot, &total_active);
+  }
+  if (c == 0) {                                   // uniform in the workgroup
+    if (tid < E) {
+      expert_count[tid] = cnt;
+      expert_offset[tid] = off;
+      if (cnt > 0) active_experts[apos] = tid;
+      if (tid >= total_active) active_experts[tid] = -1;
+    }
+    if (tid == 0) {
+      expert_offset[E] = total_routes;
+      *n_active = total_active;
+    }
+    if (wl.plan) build_work_lists(wl, sh.wl, tid < E ? tid : -1, cnt, off);   // uniform: a kernel argument
+  }
+  if (tid < E) sh.pre[tid] += off;               // first position of the expert's routes in this chunk
+  // this chunk's routes: rank = earlier routes of the same expert in the chunk
+  const int r = c * kBucketThreads + tid;
+  const bool valid = r < R;
+  const int e = valid ? min(max(ids[r], 0), E - 1) : 0;
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < id_bits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    same &= bit ? bal : ~bal;
+  }
+  int rank = __popcll(same & ((1ull << lane) - 1ull));
+  __syncthreads();                                // sh.pre holds the bases
+  if (valid && rank == 0) sh.wcnt[wave][e] = (uint8_t)__popcll(same);
+  __syncthreads();
+  if (valid) {
+    for (int w = 0; w < wave; ++w) rank += sh.wcnt[w][e];
+    const int pos = sh.pre[e] + rank;
     route_src[pos] = r;
     route_pos[r] = pos;
   }
@@ -442,6 +565,14 @@ moe_status route_bucket(const float* logits, const float* bias, int T, int E, in
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   const long long R = (long long)T * k;
   const long long C = (R + kBucketThreads - 1) / kBucketThreads;
+  if (C > 1 && R <= kChunkedMaxRoutes) {
+    bucket_chunked_kernel<<<(unsigned)C, kBucketThreads, 0, s>>>(topk_idx, (int)R, E, bits, expert_count,
+                                                                  expert_offset, active_experts, n_active, route_src,
+                                                                  route_pos, lists);
+    st = launch_status();
+    if (lists_built) *lists_built = st == MOE_OK && wl != nullptr;
+    return st;
+  }
   if (scratch && C > kChunkMinChunks && (size_t)C * E * sizeof(int32_t) <= scratch_bytes) {
     bucket_count_kernel<<<(unsigned)C, kBucketThreads, 0, s>>>(topk_idx, (int)R, E, scratch);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;

@@ -308,13 +308,20 @@ def test_fused_routing_matches_two_calls(name):
 
 # (T, E, k, ties, bias): batches on both sides of the one-workgroup routing
 # limit (16 tokens), expert counts that are not a multiple of 64, k = E,
-# k = 32, k = 1, the unrolled k = 10 and other k, and heavy ties.
+# k = 32, k = 1, the unrolled k = 10 and other k, and heavy ties; then the
+# chunked bucketing (one workgroup per 1024 routes): 1023, 1024 and 1025
+# routes, 1030 routes over 100 experts, k = E = 8 (every expert in every
+# chunk, 64 routes of one expert in a wavefront), 65536 routes (its limit)
+# and 65568 (past it: the one-workgroup bucketing).
 ROUTING_EDGE_CASES = [
     (1, 512, 10, False, False), (4, 512, 10, False, True), (6, 512, 10, True, False),
     (16, 512, 4, False, False), (7, 100, 9, True, True), (13, 100, 5, False, False),
     (16, 1000, 4, True, False), (3, 64, 10, False, False), (5, 8, 8, False, False),
     (2, 1024, 32, True, False), (16, 1024, 1, False, False), (8, 200, 8, True, False),
     (17, 512, 10, False, True), (40, 100, 3, True, False), (64, 512, 10, False, False),
+    (1023, 512, 1, False, False), (1024, 512, 1, True, False), (205, 512, 5, False, True),
+    (103, 100, 10, True, False), (400, 8, 8, False, False), (2048, 512, 32, False, True),
+    (2049, 512, 32, True, False),
 ]
 
 
