@@ -314,12 +314,14 @@ __global__ __launch_bounds__(kThreads, 4) void gate_up_kernel(FfnParams p, int n
 // ------------------------------------------------------------------ selection + gate/up (small batches)
 
 // A small batch's selection and gate/up in one launch, with no hand-off
-// between workgroups: workgroup (r, tile), r = t*k + j, selects token t's k
-// experts itself (its first wave; select.h, the rule of moe_route_topk, so
-// the result is that call's bit for bit) and computes the gate/up rows of
-// tile `tile` of the j-th of them for that one route: h[r, rows] in the
-// workspace, indexed by flat route id.  Every token's selection is repeated
-// by k * tiles workgroups (one wave each), and an expert picked by several
+// between workgroups: workgroup (r, tile), r = t*k + j, selects token t's
+// j-th expert itself (its first wave runs the rounds of the selection up to
+// round j; select.h, the rule of moe_route_topk, so the result is that
+// call's bit for bit) and computes the gate/up rows of tile `tile` of that
+// expert for that one route: h[r, rows] in the workspace, indexed by flat
+// route id.  Every token's selection is repeated by k * tiles workgroups
+// (one wave each; slot 0's start streaming after one round, slot k-1's after
+// all k), and an expert picked by several
 // tokens is streamed once per route: at four tokens the distinct experts
 // carry ~96% of the route-issued bytes, and the weights start streaming
 // without waiting for a routing kernel, its boundary and a dependent read of
@@ -448,10 +450,10 @@ __global__ __launch_bounds__(kThreads, 4) void select_gate_up_kernel(FfnParams p
       __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(p.x + (size_t)t * p.H, kSgXBytes), (uint32_t)tid * 16, 0, 0);
   compiler_fence();
   if (g.wave == 0) {
-    int e_l;
-    float w_l;
-    select_token<V, KC>(logits + (size_t)t * p.E, bias, p.E, p.k, lane, e_l, w_l);
-    if (lane == j) s_e = e_l;
+    // only slot j's expert: the rounds of the selection up to round j (the
+    // routing workgroup writes the full top-k and its weights)
+    const int e_j = select_slot<V, KC>(logits + (size_t)t * p.E, bias, p.E, j, lane);
+    if (lane == 0) s_e = e_j;
   }
   *reinterpret_cast<u32x4*>(s_x + tid * 16) = xv;
   __syncthreads();

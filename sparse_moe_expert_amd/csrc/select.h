@@ -77,9 +77,11 @@ constexpr uint32_t kIdMask = 1023;             // expert ids < 1024
 // KC > 0 fixes k = KC at compile time: the rounds are then unrolled into one
 // straight-line block, so the shift of one round's winning list can fill the
 // wait states of the next round's reduction (k is then ignored).
-template <int V, int KC = 0>
-__device__ __forceinline__ void select_token(const float* __restrict__ row, const float* __restrict__ bias, int E,
-                                             int k, int lane, int& my_e, float& my_w) {
+// Lane l's V (score, id) keys of one token's row, sorted descending - see
+// select_token.
+template <int V>
+__device__ __forceinline__ void sorted_keys(const float* __restrict__ row, const float* __restrict__ bias, int E,
+                                            int lane, uint64_t (&K)[V]) {
   const int e0 = lane * V;
   float zv[V];
   const bool full = (V % 4 == 0) && (E % 4 == 0) && (e0 + V <= E);
@@ -101,7 +103,6 @@ __device__ __forceinline__ void select_token(const float* __restrict__ row, cons
       if (e < E) zv[i] = bias ? row[e] + bias[e] : row[e];
     }
   }
-  uint64_t K[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const bool ok = e0 + i < E;
@@ -129,26 +130,54 @@ __device__ __forceinline__ void select_token(const float* __restrict__ row, cons
       }
     }
   }
+}
+
+// One round: the wave maximum of the lanes' leading keys (*best, wave
+// uniform) and its expert id (returned); the winning lane drops its leading
+// key.  The all-ones/zero mask is made opaque so the compiler keeps V
+// bitwise selects (v_bfi) instead of rewriting the shift as a lane-dependent
+// index into K, which it lowers to V*V selects.
+template <int V>
+__device__ __forceinline__ int select_round(uint64_t (&K)[V], int lane, uint32_t* best) {
+  const uint32_t lead = (uint32_t)(K[0] >> 32);
+  const uint32_t wbest = wave_max_u32(lead);
+  const int wl = __builtin_ctzll(__ballot(lead == wbest));
+  const uint32_t low = __builtin_amdgcn_readlane((uint32_t)K[0], wl);
+  *best = wbest;
+  uint32_t m = lane == wl ? 0xFFFFFFFFu : 0u;
+  asm volatile("" : "+v"(m));
+  const uint64_t m64 = ((uint64_t)m << 32) | m;
+#pragma unroll
+  for (int i = 0; i + 1 < V; ++i) K[i] = (K[i + 1] & m64) | (K[i] & ~m64);
+  K[V - 1] &= ~m64;
+  return (int)(kIdMask - (low & kIdMask));
+}
+
+// Top-k of one token's row: idx/weights of slot j end up in lane j.
+//
+// Each lane first sorts its V (score, id) pairs as 64-bit keys - ordered(z)
+// in the high word, 1023 - id in the low word, so one unsigned comparison
+// orders by score descending and id ascending - with a bitonic network.  A
+// round then only needs the wave maximum of the lanes' leading scores, the
+// lowest lane holding it (lanes own ascending id ranges, so that is the
+// lowest id among equal scores) and a one-step shift of that lane's list:
+// no per-round rescan and no divergent branch.
+//
+// KC > 0 fixes k = KC at compile time: the rounds are then unrolled into one
+// straight-line block, so the shift of one round's winning list can fill the
+// wait states of the next round's reduction (k is then ignored).
+template <int V, int KC = 0>
+__device__ __forceinline__ void select_token(const float* __restrict__ row, const float* __restrict__ bias, int E,
+                                             int k, int lane, int& my_e, float& my_w) {
+  uint64_t K[V];
+  sorted_keys<V>(row, bias, E, lane, K);
   uint32_t my_key = 0, key0 = 0;
   my_e = 0;
   auto round = [&](int j) {
-    const uint32_t lead = (uint32_t)(K[0] >> 32);
-    const uint32_t wbest = wave_max_u32(lead);
-    const int wl = __builtin_ctzll(__ballot(lead == wbest));
-    const uint32_t low = __builtin_amdgcn_readlane((uint32_t)K[0], wl);
-    const int e_sel = (int)(kIdMask - (low & kIdMask));
+    uint32_t wbest;
+    const int e_sel = select_round<V>(K, lane, &wbest);
     if (j == 0) key0 = wbest;
     if (lane == j) { my_key = wbest; my_e = e_sel; }
-    // The winning lane drops its leading key.  The all-ones/zero mask is
-    // made opaque so the compiler keeps V bitwise selects (v_bfi) instead of
-    // rewriting the shift as a lane-dependent index into K, which it lowers
-    // to V*V selects.
-    uint32_t m = lane == wl ? 0xFFFFFFFFu : 0u;
-    asm volatile("" : "+v"(m));
-    const uint64_t m64 = ((uint64_t)m << 32) | m;
-#pragma unroll
-    for (int i = 0; i + 1 < V; ++i) K[i] = (K[i + 1] & m64) | (K[i] & ~m64);
-    K[V - 1] &= ~m64;
   };
   if constexpr (KC > 0) {
 #pragma unroll
@@ -161,6 +190,28 @@ __device__ __forceinline__ void select_token(const float* __restrict__ row, cons
   const int kk = KC > 0 ? KC : k;
   const float pj = (lane < kk) ? __builtin_expf(from_ordered(my_key) - z0) : 0.0f;
   my_w = pj / wave_sum_f32(pj);
+}
+
+// The expert of slot j alone (wave uniform): the rounds of select_token up
+// to round j, so slot 0 costs one round and slot k - 1 all k of them.  With
+// KC > 0 the rounds are unrolled up to KC and left early.
+template <int V, int KC = 0>
+__device__ __forceinline__ int select_slot(const float* __restrict__ row, const float* __restrict__ bias, int E,
+                                           int j, int lane) {
+  uint64_t K[V];
+  sorted_keys<V>(row, bias, E, lane, K);
+  uint32_t wbest;
+  int e = 0;
+  if constexpr (KC > 0) {
+#pragma unroll
+    for (int r = 0; r < KC; ++r) {
+      e = select_round<V>(K, lane, &wbest);
+      if (r == j) break;
+    }
+  } else {
+    for (int r = 0; r <= j; ++r) e = select_round<V>(K, lane, &wbest);
+  }
+  return e;
 }
 
 // Inclusive scan across a 64-lane wavefront with DPP: shifts of 1, 2, 4, 8
