@@ -1299,9 +1299,22 @@ __global__ __launch_bounds__(kThreads, 2) void down_nc_kernel(FfnParams p, int n
 // [4b, 4b + 4) of y for every token; its sixteen waves take the active slots
 // a = wave + 16u, u < SLOTS; all routes' h and the o of its rows stay in LDS;
 // each token's routes are summed in slot order.
+// Eight waves per workgroup and exactly ceil(slots / 8) slots per wave (at
+// most kDcNcMaxChunks chunks of weights per lane in flight): under 80
+// registers three workgroups fit a CU, so a batch's row blocks (H / 4 of
+// them) run in one round on 256 compute units up to H = 3072.
+constexpr int kDcNcThreads = 512;
+constexpr int kDcNcWaves = kDcNcThreads / kWave;
+constexpr int kDcNcMaxChunks = 10;          // NC * SLOTS
+constexpr int kDcNcHLoads = kDcMaxLds / 16 / kDcNcThreads;   // h pieces per thread at most
+
+// LDS bytes of the h rows in down_combine_nc_kernel: whole kilobytes (one
+// wave's piece of the buffer_load ... lds staging).
+constexpr uint32_t dc_nc_h_lds(uint32_t h_bytes) { return (h_bytes + 1023u) & ~1023u; }
+
 template <int NC, int SLOTS>
-__global__ __launch_bounds__(kDcThreads, 1) void down_combine_nc_kernel(FfnParams p) {
-  extern __shared__ __align__(16) uint8_t s_dyn8[];   // [R, I] bf16 h, then [R, 4] fp32 o
+__global__ __launch_bounds__(kDcNcThreads, 3) void down_combine_nc_kernel(FfnParams p) {
+  extern __shared__ __align__(16) uint8_t s_dyn8[];   // [R, I] bf16 h (to a whole KB), then [R, 4] fp32 o
   __shared__ int s_src[kDcMaxRoutes];
   __shared__ float s_w[kDcMaxRoutes];
   constexpr int rpw = kNcRowsPerWave;
@@ -1313,12 +1326,31 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_nc_kernel(FfnParam
   const int S = min(p.E, R);
   const int C = p.I / 32;
   uint16_t* s_h = reinterpret_cast<uint16_t*>(s_dyn8);
-  float* s_o = reinterpret_cast<float*>(s_dyn8 + (size_t)R * p.I * 2);
+  const uint32_t h_bytes = (uint32_t)R * p.I * 2;
+  float* s_o = reinterpret_cast<float*>(s_dyn8 + dc_nc_h_lds(h_bytes));
+
+  // every route's h row straight into LDS first (buffer_load ... lds, one
+  // kilobyte per wave and piece; a wave whose piece lies past h issues none,
+  // and lanes past the end of h read zeros into the padding up to the next
+  // kilobyte), then the route positions and gate weights: all of it lands
+  // before the weight rows issued next, whose loads stay in flight at the
+  // barrier
+  const auto rh = make_rsrc(p.h, h_bytes);
+#pragma unroll
+  for (int i = 0; i < kDcNcHLoads; ++i) {
+    const uint32_t blk = (uint32_t)(i * kDcNcWaves + wave) * (kWave * 16);
+    if (blk < h_bytes)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, s_dyn8 + blk, 16, blk + (uint32_t)lane * 16, 0, 0, 0);
+  }
+  const int rt = min(tid, R - 1);
+  const int src_r = p.route_src[rt];
+  const float w_r = p.topk_w[rt];
+  compiler_fence();
 
   int e_u[SLOTS];
 #pragma unroll
   for (int u = 0; u < SLOTS; ++u) {
-    const int a = wave + u * kDcWaves;
+    const int a = wave + u * kDcNcWaves;
     e_u[u] = a < S ? slot_expert(p, a) : -1;
   }
   const uint32_t code_row = (uint32_t)p.I / 2, scale_row = (uint32_t)p.I / 16;
@@ -1341,16 +1373,15 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_nc_kernel(FfnParam
       vd[u][i] = __builtin_amdgcn_raw_buffer_load_b16(rds, os, 0, kStreamAux);
     }
   }
-  // every route's h row into LDS (16-byte pieces; h rows are whole pieces),
-  // the route positions and gate weights, while the weights are in flight
-  const int h_pieces = R * p.I / 8;
-  for (int q = tid; q < h_pieces; q += kDcThreads)
-    reinterpret_cast<uint4*>(s_dyn8)[q] = reinterpret_cast<const uint4*>(p.h)[q];
+  compiler_fence();
+  wait_vm<2 * SLOTS * NC>();                   // h, positions and weights have landed; the rows need not
   if (tid < R) {
-    s_src[tid] = min(max(p.route_src[tid], 0), R - 1);
-    s_w[tid] = p.topk_w[tid];
+    s_src[tid] = min(max(src_r, 0), R - 1);
+    s_w[tid] = w_r;
   }
-  __syncthreads();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
 #pragma unroll
   for (int u = 0; u < SLOTS; ++u) {
     if (e_u[u] < 0) continue;
@@ -1373,7 +1404,7 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_nc_kernel(FfnParam
   }
   __syncthreads();
   // y[t, row0 + r] = sum over slots j in order of w[t,j] * o[route (t,j), r]
-  for (int i = tid; i < p.T * rpw; i += kDcThreads) {
+  for (int i = tid; i < p.T * rpw; i += kDcNcThreads) {
     const int t = i / rpw, r = i - t * rpw;
     if (row0 + r >= p.H) continue;
     float acc = 0.0f;
@@ -1416,24 +1447,36 @@ void launch_down_nc(int nc, const FfnParams& p, long long tasks, hipStream_t s) 
   }
 }
 
-template <int NC>
-void launch_down_combine_nc_slots(const FfnParams& p, unsigned grid, size_t dyn, int slots, hipStream_t s) {
-  const int per_wave = (slots + kDcWaves - 1) / kDcWaves;
-  if (per_wave <= 1) down_combine_nc_kernel<NC, 1><<<grid, kDcThreads, dyn, s>>>(p);
-  else if (per_wave == 2) down_combine_nc_kernel<NC, 2><<<grid, kDcThreads, dyn, s>>>(p);
-  else if (per_wave <= 4) down_combine_nc_kernel<NC, 4><<<grid, kDcThreads, dyn, s>>>(p);
-  else down_combine_nc_kernel<NC, kDcMaxRoutes / kDcWaves><<<grid, kDcThreads, dyn, s>>>(p);
+// Slots per wave of down_combine_nc_kernel for a batch's expert slots.
+int dc_nc_slots_per_wave(long long slots) { return (int)((slots + kDcNcWaves - 1) / kDcNcWaves); }
+
+// down_combine_nc_kernel<NC, S> with S = the slots per wave; only the
+// instances with NC * S <= kDcNcMaxChunks exist (the policy sends no other
+// batch here): false for any other.
+template <int NC, int S = 1>
+bool launch_down_combine_nc_slots(const FfnParams& p, unsigned grid, size_t dyn, int per_wave, hipStream_t s) {
+  if constexpr (NC * S > kDcNcMaxChunks) {
+    return false;
+  } else {
+    if (per_wave == S) {
+      down_combine_nc_kernel<NC, S><<<grid, kDcNcThreads, dyn, s>>>(p);
+      return true;
+    }
+    return launch_down_combine_nc_slots<NC, S + 1>(p, grid, dyn, per_wave, s);
+  }
 }
 
-void launch_down_combine_nc(int nc, const FfnParams& p, unsigned grid, size_t dyn, int slots, hipStream_t s) {
+bool launch_down_combine_nc(int nc, const FfnParams& p, unsigned grid, size_t dyn, int slots, hipStream_t s) {
+  const int per_wave = dc_nc_slots_per_wave(slots);
   switch (nc) {
-    case 1: launch_down_combine_nc_slots<1>(p, grid, dyn, slots, s); break;
-    case 2: launch_down_combine_nc_slots<2>(p, grid, dyn, slots, s); break;
-    case 3: launch_down_combine_nc_slots<3>(p, grid, dyn, slots, s); break;
-    case 4: launch_down_combine_nc_slots<4>(p, grid, dyn, slots, s); break;
-    case 5: launch_down_combine_nc_slots<5>(p, grid, dyn, slots, s); break;
-    case 6: launch_down_combine_nc_slots<6>(p, grid, dyn, slots, s); break;
-    default: launch_down_combine_nc_slots<8>(p, grid, dyn, slots, s); break;
+    case 1: return launch_down_combine_nc_slots<1>(p, grid, dyn, per_wave, s);
+    case 2: return launch_down_combine_nc_slots<2>(p, grid, dyn, per_wave, s);
+    case 3: return launch_down_combine_nc_slots<3>(p, grid, dyn, per_wave, s);
+    case 4: return launch_down_combine_nc_slots<4>(p, grid, dyn, per_wave, s);
+    case 5: return launch_down_combine_nc_slots<5>(p, grid, dyn, per_wave, s);
+    case 6: return launch_down_combine_nc_slots<6>(p, grid, dyn, per_wave, s);
+    case 8: return launch_down_combine_nc_slots<8>(p, grid, dyn, per_wave, s);
+    default: return false;
   }
 }
 
@@ -1509,13 +1552,13 @@ FfnPolicy ffn_policy(int T, int H, int I, int E, int k, bool packed) {
   const size_t h_bytes = (size_t)R * I * 2;
   // one buffer resource spans all of W_down: its byte count must fit 31 bits
   const bool dc_fits = (size_t)E * H * (I / 2) < (size_t)0x7FFFFFFF;
-  const size_t dc_lds = h_bytes + (size_t)R * (kWave / lr_d) * 4;   // h and o of the fused down/unroute kernel
+  // h and o of the fused down/unroute kernel
+  const size_t dc_lds = (nc_chunks(I / 32) ? dc_nc_h_lds((uint32_t)h_bytes) : h_bytes) + (size_t)R * (kWave / lr_d) * 4;
   // multi-chunk rows: the fused kernel holds nc chunks of each of its waves'
-  // slots (1, 2, 4 or 8 slots per wave) in registers; beyond 8 it would spill
+  // slots in registers, at most kDcNcMaxChunks of them
   const int nc_d = nc_chunks(I / 32);
-  const long long dc_slots = std::min<long long>(E, R), per_wave = (dc_slots + kDcWaves - 1) / kDcWaves;
-  const int slots_var = per_wave <= 1 ? 1 : per_wave == 2 ? 2 : per_wave <= 4 ? 4 : 8;
-  const bool dc_regs = nc_d == 0 || nc_d * slots_var <= 8;
+  const long long dc_slots = std::min<long long>(E, R);
+  const bool dc_regs = nc_d == 0 || nc_d * dc_nc_slots_per_wave(dc_slots) <= kDcNcMaxChunks;
   f.down_combine = R <= kDcMaxRoutes && dc_lds <= (size_t)kDcMaxLds && dc_fits && dc_regs;
   // Experts with many routes go to the MFMA kernels; only batches large
   // enough to have such experts (and not small enough for the fused
@@ -1635,9 +1678,11 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   if (!(stage & 2)) return MOE_OK;
   if (down_combine) {
     const int rpw = kWave / lr_d;
-    const size_t dyn = h_bytes + (size_t)R * rpw * 4;
+    const size_t dyn = (nc_d ? dc_nc_h_lds((uint32_t)h_bytes) : h_bytes) + (size_t)R * rpw * 4;
     const unsigned grid = (unsigned)((H + rpw - 1) / rpw);
-    if (nc_d) launch_down_combine_nc(nc_d, p, grid, dyn, (int)slots, s);
+    if (nc_d) {
+      if (!launch_down_combine_nc(nc_d, p, grid, dyn, (int)slots, s)) return MOE_ERR_UNSUPPORTED;
+    }
     else if (lr_d == 16) launch_down_combine<16>(p, grid, dyn, (int)slots, s);
     else launch_down_combine<0>(p, grid, dyn, (int)slots, s);
     return launch_status();
