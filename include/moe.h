@@ -137,11 +137,13 @@ moe_status moe_bucket_routes(const int32_t* topk_idx, int T, int E, int k,
  * moe_route_bucket — moe_route_topk followed by moe_bucket_routes, fused.
  *
  * Same arguments, outputs, envelope and errors as the two calls in sequence
- * (outputs are identical bit for bit).  For T <= 64 both steps run in one
- * workgroup of one kernel, the fused routing kernel's design for small
- * batches (page "How I forked vLLM and made Qwen3.8-Flash-Next decode 1.6x
- * faster on one GPU", section "5. Hand-written kernels", paragraph "Fused MoE
- * routing"); larger batches run the two kernels back to back.
+ * (outputs are identical bit for bit).  For T <= 16 with T*k <= 256 and
+ * E <= 512 both steps run in one workgroup of one kernel, the fused routing
+ * kernel's design for small batches (page "How I forked vLLM and made
+ * Qwen3.8-Flash-Next decode 1.6x faster on one GPU", section "5. Hand-written
+ * kernels", paragraph "Fused MoE routing"); larger batches run the selection
+ * over the chip, then the bucketing: one workgroup up to 1024 routes, one
+ * launch of one workgroup per 1024-route chunk up to 65536.
  */
 moe_status moe_route_bucket(const float* logits, const float* bias,
                             int T, int E, int k,
@@ -155,7 +157,7 @@ moe_status moe_route_bucket(const float* logits, const float* bias,
  * moe_router_route_bucket — moe_router_logits, moe_route_topk and
  * moe_bucket_routes in one call: tokens -> logits -> top-k ids and gate
  * weights -> route buckets, outputs identical bit for bit to the three calls
- * in sequence.  Small batches (T <= 16 and T*k <= 256) run all of it in one
+ * in sequence.  Small batches (T <= 16, T*k <= 256, E <= 512) run all of it in one
  * launch: the router's projection spans many workgroups, so the fused kernel
  * hands its results to the selection explicitly (page "Persistent execution
  * for Flash-Next GGUF on SM70", section "Router: selection and expert-task
@@ -443,8 +445,8 @@ moe_status moe_shared_expert(const uint16_t* x, const uint16_t* w_gate, const ui
  *              The caller adds y and y_shared.  No output may overlap
  *              another output or an input.
  * The shared expert's argument checks come first, then the step's; a
- * failing check launches nothing.  At decode sizes (at most 8 tokens with at
- * most 512 experts, or 16 tokens with at most 1024; H of 512, 1024 or 2048
+ * failing check launches nothing.  At decode sizes (at most 16 tokens and
+ * 256 routes with at most 512 experts; H of 512, 1024 or 2048
  * for the gate/up rows, Is of 512 or 1024 for the down rows) the shared
  * expert's rows run as extra workgroups of the step's routing and gate/up
  * launches; otherwise its own two kernels run on the same stream.

@@ -1748,7 +1748,10 @@ constexpr int kSmallStepMaxRoutes = kSgMaxRoutes;
 
 bool small_step_ok(int T, int H, int I, int E, int k) {
   if (T < 1 || (long long)T * k > kSmallStepMaxRoutes) return false;
-  if (H != 64 * 32 || E > 1024 || k > 32) return false;          // gate/up rows of one chunk per lane: H = 2048
+  if (H != 64 * 32 || k > 32) return false;                       // gate/up rows of one chunk per lane: H = 2048
+  // up to eight selection keys per lane: sixteen would take ~146 registers,
+  // more than the gate/up workgroups (four per CU at least) may hold
+  if (E > 8 * kWave) return false;
   const int C = I / 32;
   if (C > 64 || (C & (C - 1)) != 0) return false;                 // down rows of one chunk per lane
   return ffn_policy(T, H, I, E, k, false).down_combine;
@@ -1796,8 +1799,7 @@ moe_status small_step(const uint16_t* x, const float* logits, const float* bias,
     if (V <= 1) launch_select_gate_up_k<1>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
     else if (V <= 2) launch_select_gate_up_k<2>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
     else if (V <= 4) launch_select_gate_up_k<4>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
-    else if (V <= 8) launch_select_gate_up_k<8>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
-    else launch_select_gate_up_k<16>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
+    else launch_select_gate_up_k<8>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
   if (!(stage & 2)) return MOE_OK;

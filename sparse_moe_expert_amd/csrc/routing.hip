@@ -292,6 +292,10 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_chunked_kernel(
 // inside a 64-route group, per-expert counts of earlier groups).
 constexpr int kSmallMaxTokens = 16;
 constexpr int kSmallMaxRoutes = 256;
+// Up to 512 experts (eight keys per lane): sorting sixteen 64-bit keys per
+// lane takes ~146 registers, more than a 1024-thread workgroup may hold, so
+// larger E select in route_topk_kernel (no register cap) and bucket apart.
+constexpr int kSmallMaxExperts = 8 * kWave;
 
 // shared-expert gate/up rows per extra workgroup of the small routing kernel
 // (two per 512-thread workgroup, two of which fit a compute unit; four per
@@ -539,7 +543,7 @@ moe_status route_bucket(const float* logits, const float* bias, int T, int E, in
   if (st != MOE_OK || T == 0) return st;
   const int bits = id_bits_for(E);
   const int V = (E + kWave - 1) / kWave;
-  if (T <= kSmallMaxTokens && T * k <= kSmallMaxRoutes) {
+  if (T <= kSmallMaxTokens && T * k <= kSmallMaxRoutes && E <= kSmallMaxExperts) {
     const SharedRows side = sr && sr->gu_nc > 0 ? *sr : SharedRows{};
     const int side_rows = side.gu_nc > 0 ? side.Is : 0;
     if (sr_done) *sr_done = side_rows > 0;
@@ -555,8 +559,7 @@ moe_status route_bucket(const float* logits, const float* bias, int T, int E, in
     if (V <= 1) { MOE_RBS(1); }
     else if (V <= 2) { MOE_RBS(2); }
     else if (V <= 4) { MOE_RBS(4); }
-    else if (V <= 8) { MOE_RBS(8); }
-    else { MOE_RBS(16); }
+    else { MOE_RBS(8); }
 #undef MOE_RBS
 #undef MOE_RBS1
     return launch_status();
@@ -619,8 +622,9 @@ extern "C" moe_status moe_router_route_bucket(const uint16_t* x, const float* w_
   if (!x || !w_router || !counter) return MOE_ERR_NULL_POINTER;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(counter)) return MOE_ERR_MISALIGNED;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (T > kSmallMaxTokens || T * k > kSmallMaxRoutes) {
-    // larger batches: the projection, then the routing, as two calls
+  if (T > kSmallMaxTokens || T * k > kSmallMaxRoutes || E > kSmallMaxExperts) {
+    // larger batches and more than 512 experts: the projection, then the
+    // routing, as two calls
     st = moe_router_logits(x, w_router, T, H, E, logits, stream);
     if (st != MOE_OK) return st;
     return route_bucket(logits, bias, T, E, k, topk_idx, topk_w, expert_count, expert_offset, active_experts,
@@ -645,8 +649,7 @@ extern "C" moe_status moe_router_route_bucket(const uint16_t* x, const float* w_
   if (V <= 1) { MOE_RRB(1); }
   else if (V <= 2) { MOE_RRB(2); }
   else if (V <= 4) { MOE_RRB(4); }
-  else if (V <= 8) { MOE_RRB(8); }
-  else { MOE_RRB(16); }
+  else { MOE_RRB(8); }
 #undef MOE_RRB
 #undef MOE_RRB1
   return launch_status();

@@ -5,7 +5,8 @@ its route-slot down/unroute.
 Every output (ids, weights, the six bucket arrays, y) must equal bit for bit
 what moe_route_bucket + moe_expert_ffn produce on the same inputs, and match
 the oracle; shapes cover one to four tokens, k = 1, k = 32, E = 64 and
-E = 1000, a bias, ties, both weight paths, guard regions around y and the
+E = 1000 (past the small step's 512 experts: the general path, which must
+give the same outputs), a bias, ties, both weight paths, guard regions around y and the
 workspace, and graph replays with changed inputs.
 """
 
