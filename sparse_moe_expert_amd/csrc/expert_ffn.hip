@@ -47,6 +47,7 @@
 // the scalar path (routing metadata: s_load, its own counter), and a WG's
 // dependent round trips all happen while its weights are in flight.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "row_dot.h"
@@ -86,6 +87,7 @@ struct FfnParams {
   int plan_max;            // capacity of the item list
   int32_t* rd_list;        // workspace: row-dot experts, most routes first (plan_kernel)
   int rd_plan;             // the row-dot kernels take their experts from rd_list
+  int32_t* queues;         // workspace: unit counters of the streaming down kernel
   SharedRows sr;           // shared-expert down rows riding along in gate_up_kernel (dn_nc 0: none)
 };
 
@@ -930,6 +932,217 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
   }
 }
 
+// Streaming form of the packed down tiles, for large batches (their items
+// outnumber the CU slots several times): one workgroup per CU slot takes
+// units - one row tile of one item - from a counter per XCD class until the
+// list is done.  Workgroup b counts in class b % 8 (the XCD it is dealt to),
+// and unit u of class c is row tile u % tiles_n of item (u / tiles_n) * 8 + c,
+// so an item's tiles stay on one XCD and each class walks the list longest
+// first, as the one-unit-per-workgroup grid does.  The next unit is claimed
+// at the current unit's first step and set up at its fifth; its first three
+// steps are issued during the current unit's last three (the one-unit grid
+// re-reads the final step there), so the next unit's head - the list entry,
+// the first operand bytes - overlaps the current unit's last steps and
+// epilogue, and no workgroup is dispatched per unit.  The epilogue runs one
+// route tile at a time through the stage that holds no prefetched rows.  K
+// must run a multiple of four steps, at least eight.  The workgroup that
+// finishes last clears the counters for the next launch.
+constexpr int kQueueStride = kWlQueueStride;             // ints per counter (one 128-byte line each)
+static_assert(kWlQueueInts == (kXcds + 1) * kQueueStride, "8 class counters, then the finished count");
+
+// One lane's claim: an offset the compiler cannot see is zero keeps its
+// atomic optimizer from turning the add into a wave-wide one whose result it
+// reads at once (a wait for every load in flight).
+__device__ __forceinline__ int atomic_claim(int32_t* c) {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return __hip_atomic_fetch_add(c + z, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Ties a ring entry to the program point: its conversion cannot be scheduled
+// before this (after the step's wait, and so after the next step's loads).
+__device__ __forceinline__ void pin(uint4& w, uint16_t& s) {
+  asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w), "+v"(s));
+}
+
+template <int NSUB>
+__global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_down_stream_kernel(FfnParams p, int32_t* queue) {
+  using Tile = MmTile<false, true, NSUB>;
+  constexpr int kWgRows = kMmRows * NSUB;
+  constexpr int LPS = Tile::kLoadsPerStep;
+  __shared__ __align__(16) uint8_t s_x0[kMmStageBytes];
+  __shared__ __align__(16) uint8_t s_x1[kMmStageBytes];
+  __shared__ __align__(16) uint8_t s_x2[kMmStageBytes];
+  __shared__ __align__(16) uint8_t s_x3[kMmStageBytes];
+  __shared__ int s_unit;                                     // the claimed unit
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, half = lane >> 5;
+  const int N = p.H, K = p.I;
+  const int tiles_n = (N + kWgRows - 1) / kWgRows;
+  const int steps = K / kMmK;
+  const int cls = blockIdx.x % kXcds;
+  int32_t* const ctr = queue + cls * kQueueStride;
+  const int n_items = min(sload(p.plan, 0), p.plan_max);
+  const int R = p.T * p.k;
+  const size_t mat = packed_matrix_bytes(N, K), codes = packed_code_bytes(N, K);
+  const uint8_t* const mbase = p.packed + 2 * (size_t)p.E * packed_matrix_bytes(p.I, p.H);
+
+  // unit u of this class: expert, first bucket position, routes, first row;
+  // cnt = 0 past the list
+  struct Unit {
+    int e, off, cnt, n0;
+  };
+  auto unit_of = [&](int u) {
+    Unit w = {0, 0, 0, 0};
+    const int it = (u / tiles_n) * kXcds + cls;
+    if (u >= 0 && it < n_items) {
+      w.e = min(max(sload(p.plan, 4 + 4 * it), 0), p.E - 1);
+      w.off = min(max(sload(p.plan, 5 + 4 * it), 0), R);
+      w.cnt = min(max(sload(p.plan, 6 + 4 * it), 0), min(kMmRoutes, R - w.off));
+      w.n0 = (u % tiles_n) * kWgRows;
+    }
+    return w;
+  };
+  Tile t;
+  t.s_x[0] = s_x0;
+  t.s_x[1] = s_x1;
+  t.s_x[2] = s_x2;
+  t.s_x[3] = s_x3;
+  t.wave = wave;
+  t.lane = lane;
+  // the unit's weight tiles and h rows (rows past its routes repeat its last)
+  auto point_at = [&](const Unit& w) {
+#pragma unroll
+    for (int m = 0; m < NSUB; ++m) {
+      const uint8_t* me = mbase + (size_t)w.e * mat;
+      t.rc[m] = make_rsrc(me, (uint32_t)codes);
+      t.rs[m] = make_rsrc(me + codes, (uint32_t)(mat - codes));
+      const uint32_t tile_step0 = (uint32_t)(w.n0 / kMmRows + m) * (uint32_t)steps;
+      t.w_voff[m] = (uint32_t)(wave * 64 + lane) * 16 + tile_step0 * 4096u;
+      t.s_voff[m] = (uint32_t)(wave * 64 + lane) * 2 + tile_step0 * 512u;
+    }
+    t.rb = make_rsrc(p.h + (size_t)w.off * p.I, (uint32_t)w.cnt * (uint32_t)p.I * 2u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = (i * 4 + wave) * 64 + lane;
+      const int row = q >> 3, c = (q & 7) ^ ((row >> 1) & 7);
+      t.x_goff[i] = (uint32_t)min(row, w.cnt - 1) * (uint32_t)K * 2u + (uint32_t)c * 16;
+    }
+  };
+
+  if (tid == 0) s_unit = atomic_claim(ctr);
+  __syncthreads();
+  Unit cur = unit_of(__builtin_amdgcn_readfirstlane(s_unit));
+  if (cur.cnt > 0) {
+    point_at(cur);
+    t.template issue<0>(0);
+    compiler_fence();
+    t.template issue<1>(1);
+    compiler_fence();
+    t.template issue<2>(2);
+    compiler_fence();
+    for (;;) {
+      const int mtiles = (cur.cnt + 31) >> 5;
+      Unit nxt = {0, 0, 0, 0};
+      int claimed = 0;
+      f32x16 acc[NSUB][4];
+#pragma unroll
+      for (int m = 0; m < NSUB; ++m)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) acc[m][jt] = f32x16{};
+
+      auto body = [&](auto stage_c, int ks) {
+        constexpr int S = decltype(stage_c)::value;
+        stage_release_barrier();                             // every wave is done with step ks-1's stage
+        if (ks == 4) nxt = unit_of(__builtin_amdgcn_readfirstlane(s_unit));   // claimed at step 0
+        if (ks == steps - 3 && nxt.cnt > 0) point_at(nxt);
+        // three steps ahead: the current unit's, then the next unit's first
+        // three, or (no next unit) the final step again into a free stage
+        const int is = ks + 3 < steps ? ks + 3 : (nxt.cnt > 0 ? ks + 3 - steps : steps - 1);
+        t.template issue<(S + 3) % kMmStages>(is);
+        if (ks == 0 && tid == 0) claimed = atomic_claim(ctr);
+        wait_vm<3 * LPS>();
+        step_barrier();                                      // step ks's operand rows are in LDS
+        if (ks == 3 && tid == 0) s_unit = claimed;
+        const uint8_t* stage = S == 0 ? s_x0 : (S == 1 ? s_x1 : (S == 2 ? s_x2 : s_x3));
+        bf16x8 af[NSUB][4];
+#pragma unroll
+        for (int m = 0; m < NSUB; ++m) {
+          pin(t.wc[S][m], t.wsv[S][m]);
+          dequant_frags(t.wc[S][m], t.wsv[S][m], af[m]);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          if (jt < mtiles) {
+            const int row = jt * 32 + l32;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+              const int c = (half * 4 + kk) ^ ((row >> 1) & 7);
+              const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(stage + row * (kMmK * 2) + c * 16);
+#pragma unroll
+              for (int m = 0; m < NSUB; ++m)
+                acc[m][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[m][kk], bfr, acc[m][jt], 0, 0, 0);
+            }
+          }
+        }
+      };
+      for (int s0 = 0; s0 < steps; s0 += kMmStages) {
+        body(std::integral_constant<int, 0>{}, s0);
+        body(std::integral_constant<int, 1>{}, s0 + 1);
+        body(std::integral_constant<int, 2>{}, s0 + 2);
+        body(std::integral_constant<int, 3>{}, s0 + 3);
+      }
+
+      // Epilogue through stage 3 (the final step's, the only one without
+      // prefetched rows), one route tile per pass: o = fp16(Gd * acc) to LDS
+      // as in the one-unit kernel, then every wave stores whole runs of one
+      // route's output row.
+      constexpr int kChunks = kWgRows / 8;
+      constexpr int kRouteBytes = kWgRows * 2;
+      static_assert(32 * kRouteBytes <= kMmStageBytes, "a route tile's outputs fit one operand stage");
+      const float Gd = sload(p.gsc, cur.e * 3 + 2);
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        if (jt < mtiles) {
+          stage_release_barrier();                           // stage 3 is free (step reads or the previous pass)
+          uint8_t* rowp = s_x3 + l32 * kRouteBytes + half * 8;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int m = 0; m < NSUB; ++m) {
+              const int c = m * (kMmRows / 8) + wave * 4 + q;
+              *reinterpret_cast<uint2*>(rowp + ((c ^ (l32 % kChunks)) * 16)) =
+                  make_uint2(f32_to_f16_bits(acc[m][jt][4 * q] * Gd) | (f32_to_f16_bits(acc[m][jt][4 * q + 1] * Gd) << 16),
+                             f32_to_f16_bits(acc[m][jt][4 * q + 2] * Gd) | (f32_to_f16_bits(acc[m][jt][4 * q + 3] * Gd) << 16));
+            }
+          }
+          // the tile's outputs are in LDS: each wave's writes have landed
+          // before the barrier (it does not wait for them by itself)
+          stage_release_barrier();
+          const int rc = min(32, cur.cnt - jt * 32);
+          for (int idx = tid; idx < rc * kChunks; idx += kMmThreads) {
+            const int r = idx / kChunks, j = idx % kChunks;
+            const int c = j ^ (r % kChunks);
+            const int n = cur.n0 + c * 8;
+            if (n >= N) continue;                            // N is a multiple of 32: whole chunks
+            const uint4 v = *reinterpret_cast<const uint4*>(s_x3 + r * kRouteBytes + j * 16);
+            *reinterpret_cast<uint4*>(p.o + (size_t)(cur.off + jt * 32 + r) * N + n) = v;
+          }
+        }
+      }
+      if (nxt.cnt <= 0) break;
+      cur = nxt;
+    }
+    wait_vm<0>();                                            // the final re-reads have landed in LDS
+  }
+  // the last workgroup to finish clears the counters
+  if (tid == 0 && atomic_claim(queue + kXcds * kQueueStride) == (int)gridDim.x - 1) {
+    for (int c = 0; c <= kXcds; ++c)
+      __hip_atomic_store(queue + c * kQueueStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // ------------------------------------------------------------------ work lists
 
 static_assert(kMmRoutes == kWlRoutes, "an MFMA item is one route chunk of the MFMA kernels");
@@ -953,6 +1166,7 @@ __global__ __launch_bounds__(kWlThreads) void plan_kernel(FfnParams p) {
   wl.plan_max = p.plan_max;
   wl.mfma_min = p.mfma_min;
   wl.rd_plan = p.rd_plan;
+  wl.queues = p.queues;
   build_work_lists(wl, sh, e, cnt, off);
 }
 
@@ -1485,7 +1699,7 @@ bool launch_down_combine_nc(int nc, const FfnParams& p, unsigned grid, size_t dy
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WorkspaceLayout {
-  size_t h_off, o_off, plan_off, rd_off, total;   // h [R, I] bf16, o [R, H] fp16, MFMA work plan, row-dot list
+  size_t h_off, o_off, plan_off, rd_off, q_off, total;   // h [R, I] bf16, o [R, H] fp16, MFMA work plan, row-dot list, unit counters
   int plan_max;
 };
 
@@ -1501,7 +1715,8 @@ WorkspaceLayout workspace_layout(int T, int H, int I, int E, int k) {
   const size_t cap = ((size_t)L.plan_max + kXcds - 1) / kXcds * kXcds;
   L.rd_off = L.plan_off + align256((4 + 4 * cap) * 4);
   // the row-dot list: its length and one expert per slot
-  L.total = L.rd_off + align256((1 + std::min<size_t>((size_t)E, R)) * 4);
+  L.q_off = L.rd_off + align256((1 + std::min<size_t>((size_t)E, R)) * 4);
+  L.total = L.q_off + align256((size_t)kWlQueueInts * 4);
   return L;
 }
 
@@ -1510,6 +1725,41 @@ constexpr int kMfmaMinTokens = 64;      // batches from this size launch the MFM
 constexpr int kRowPlanMinTokens = 16;   // batches above this size order the row-dot experts by count
 constexpr int kMfmaMinRoutes = 16;      // experts with this many routes use them (standard weight layout)
 constexpr int kMfmaMinRoutesPacked = 1; // with the packed copy: every expert of such a batch
+
+// The streaming down kernel: K (= I) must run a multiple of four steps, at
+// least eight, and the batch must hold enough routes for the items to
+// outnumber the CU slots several times (with fewer, each workgroup takes one
+// or two units and the claims and the pass-wise epilogue cost more than the
+// streaming saves: measured at 2560 routes).
+constexpr long long kStreamMinRoutes = 16384;
+bool down_stream_fits(int I, long long R) {
+  const int steps = I / kMmK;
+  return I % kMmK == 0 && steps % kMmStages == 0 && steps >= 8 && R >= kStreamMinRoutes;
+}
+
+// Grid of the streaming down kernel: one workgroup per CU slot of the
+// current device (compute units times the workgroups one holds, looked up
+// once per device), at most one per unit, a multiple of the 8 classes; 0 when
+// the device cannot be queried.
+constexpr int kStreamMaxDevices = 64;
+unsigned down_stream_grid(long long units) {
+  static std::atomic<int> slots[kStreamMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kStreamMaxDevices) return 0;
+  int n = slots[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ffn_mfma_down_stream_kernel<2>, kMmThreads, 0) !=
+            hipSuccess ||
+        cus <= 0)
+      return 0;
+    n = cus * std::max(per_cu, 1);
+    slots[dev].store(n, std::memory_order_relaxed);
+  }
+  const long long g = std::max<long long>(1, std::min<long long>(units, n));
+  return (unsigned)((g + kXcds - 1) / kXcds * kXcds);
+}
 
 template <int LG>
 void launch_gate_up(const FfnParams& p, long long tasks, hipStream_t s) {
@@ -1587,6 +1837,7 @@ bool ffn_work_lists(int T, int H, int I, int E, int k, bool packed, void* worksp
   wl->plan_max = L.plan_max;
   wl->mfma_min = f.mfma_min;
   wl->rd_plan = f.rd_plan ? 1 : 0;
+  wl->queues = reinterpret_cast<int32_t*>(ws + L.q_off);
   *scratch_bytes = L.plan_off;
   return f.mfma || f.rd_plan;
 }
@@ -1631,6 +1882,7 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   p.plan = reinterpret_cast<int32_t*>(ws + L.plan_off);
   p.plan_max = L.plan_max;
   p.rd_list = reinterpret_cast<int32_t*>(ws + L.rd_off);
+  p.queues = reinterpret_cast<int32_t*>(ws + L.q_off);
   p.y = y;
   p.sr = SharedRows{};
   p.lr_gu = lr_gu;
@@ -1697,8 +1949,14 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
     if (p.packed) {
       // two row tiles per wave: each item's h rows are staged half as often
       // and every B fragment feeds two MFMAs
-      const unsigned grid = (unsigned)(items8 * ((H + 2 * kMmRows - 1) / (2 * kMmRows)));
-      ffn_mfma_kernel<false, true, 2><<<grid, kMmThreads, 0, s>>>(p);
+      const long long units = items8 * ((H + 2 * kMmRows - 1) / (2 * kMmRows));
+      if (down_stream_fits(I, R)) {
+        const unsigned grid = down_stream_grid(units);
+        if (grid == 0) return MOE_ERR_HIP;
+        ffn_mfma_down_stream_kernel<2><<<grid, kMmThreads, 0, s>>>(p, p.queues);
+      } else {
+        ffn_mfma_kernel<false, true, 2><<<(unsigned)units, kMmThreads, 0, s>>>(p);
+      }
     } else {
       const unsigned grid = (unsigned)(items8 * ((H + kMmRows - 1) / kMmRows));
       ffn_mfma_kernel<false, false, 1><<<grid, kMmThreads, 0, s>>>(p);

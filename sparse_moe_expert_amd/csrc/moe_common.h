@@ -103,6 +103,7 @@ struct WorkLists {
   int plan_max;       // capacity of the MFMA item list
   int mfma_min;       // experts with at least this many routes take the MFMA kernels (0: none do)
   int rd_plan;        // the row-dot kernels read rd_list
+  int32_t* queues;    // unit counters of the streaming down kernel (zeroed with the lists), or null
 };
 
 // A dense bf16 shared expert computed within a routed step (moe_step_shared):

@@ -24,6 +24,10 @@
 namespace moe {
 
 constexpr int kWlThreads = 1024;
+// Unit counters of the streaming down kernel: 8 class counters and a
+// finished count, one 128-byte line each; zeroed here, before its first launch.
+constexpr int kWlQueueStride = 32;
+constexpr int kWlQueueInts = 9 * kWlQueueStride;
 constexpr int kWlRoutes = 128;     // routes per MFMA item (the MFMA kernels' route chunk)
 constexpr int kRdBins = 64;
 
@@ -37,6 +41,7 @@ struct WorkListShared {
 __device__ __forceinline__ void build_work_lists(const WorkLists& wl, WorkListShared& sh, int e, int cnt, int off) {
   const int tid = threadIdx.x;
   if (tid < 4) sh.cnt[tid] = 0;
+  if (wl.queues && tid < kWlQueueInts / kWlQueueStride) wl.queues[tid * kWlQueueStride] = 0;
   if (tid < kRdBins) sh.rh[tid] = 0;
   __syncthreads();
   int mcnt = 0, rcnt = 0;
