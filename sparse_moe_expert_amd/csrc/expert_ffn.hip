@@ -596,11 +596,15 @@ __global__ __launch_bounds__(kThreads, 4) void down_kernel(FfnParams p, int n_ta
 // the accumulator).  Each weight is loaded and dequantised once.
 //
 // The operand rows (x gathered by token for gate/up, the expert's contiguous
-// h rows for down) go straight into a three-stage LDS ring with
+// h rows for down) go straight into a four-stage LDS ring with
 // global_load_lds, 16-byte chunks placed at chunk ^ ((row >> 1) & 7) so that
 // the B-fragment reads of 16 lanes hit 16 different bank groups.  Weight
-// codes and scales run three steps ahead in a four-entry register ring (the
-// loop is latency-bound on these loads otherwise).
+// codes and scales go into a four-entry register ring.  The one-unit kernel
+// issues a step's loads two steps ahead (measured: one and three steps ahead
+// are no faster at prefill, and three is ~2 µs slower at 256 Zipf-routed
+// tokens, whose loads then crowd the memory system for little cover); the
+// streaming kernel keeps three, the span over which it issues the next
+// unit's first steps.
 // Workgroups are numbered so that the n-tiles of one expert share an XCD
 // (workgroups are dealt round robin to the 8 XCDs): its gathered rows are
 // then read from that XCD's L2 after the first tile.
@@ -611,7 +615,8 @@ constexpr int kMmThreads = 256;
 constexpr int kMmRows = 128;                 // weight rows per workgroup (32 per wave)
 constexpr int kMmRoutes = 128;               // routes per chunk
 constexpr int kMmK = 64;                     // reduction per step
-constexpr int kMmStages = 4;                 // operand-ring stages: three steps in flight
+constexpr int kMmStages = 4;                 // operand-ring stages
+constexpr int kMmLead = 2;                   // one-unit kernel: steps issued ahead of the one in use
 constexpr int kMmStageBytes = kMmRoutes * kMmK * 2;   // 16 KB of operand rows per step
 constexpr int kXcds = 8;
 static_assert(kMmRows == kPackRows && kMmK == kPackK, "packed weights follow the MFMA tile");
@@ -824,20 +829,19 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
     // after them, and take the smallest count over the loop's entry and back
     // edge - a scale load scheduled behind the next steps' loads here would
     // shorten the prefetch of every iteration
+    static_assert(kMmLead == 2, "the prologue issues kMmLead steps");
     t.template issue<0>(0);
     compiler_fence();
     t.template issue<1>(min(1, steps - 1));
-    compiler_fence();
-    t.template issue<2>(min(2, steps - 1));
     compiler_fence();
 
     auto body = [&](auto stage_c, int ks) {
       constexpr int S = decltype(stage_c)::value;
       stage_release_barrier();                               // every wave is done with step ks-1's stage
-      // Always three steps ahead, so that every path has the same loads in
-      // flight (the last three re-read the final step into a free stage).
-      t.template issue<(S + 3) % kMmStages>(min(ks + 3, steps - 1));
-      wait_vm<3 * LPS>();
+      // Always kMmLead steps ahead, so that every path has the same loads in
+      // flight (the last ones re-read the final step into a free stage).
+      t.template issue<(S + kMmLead) % kMmStages>(min(ks + kMmLead, steps - 1));
+      wait_vm<kMmLead * LPS>();
       step_barrier();                                        // step ks's operand rows are in LDS
       const uint8_t* stage = S == 0 ? s_x0 : (S == 1 ? s_x1 : (S == 2 ? s_x2 : s_x3));
       bf16x8 af[NMAT][4];
