@@ -599,12 +599,10 @@ __global__ __launch_bounds__(kThreads, 4) void down_kernel(FfnParams p, int n_ta
 // h rows for down) go straight into a four-stage LDS ring with
 // global_load_lds, 16-byte chunks placed at chunk ^ ((row >> 1) & 7) so that
 // the B-fragment reads of 16 lanes hit 16 different bank groups.  Weight
-// codes and scales go into a four-entry register ring.  The one-unit kernel
-// issues a step's loads two steps ahead (measured: one and three steps ahead
-// are no faster at prefill, and three is ~2 µs slower at 256 Zipf-routed
-// tokens, whose loads then crowd the memory system for little cover); the
-// streaming kernel keeps three, the span over which it issues the next
-// unit's first steps.
+// codes and scales go into a four-entry register ring.  A step's loads are
+// issued two steps ahead (measured: one and three steps ahead are no faster
+// at prefill, and three is ~2 µs slower at 256 Zipf-routed tokens, whose
+// loads then crowd the memory system for little cover).
 // Workgroups are numbered so that the n-tiles of one expert share an XCD
 // (workgroups are dealt round robin to the 8 XCDs): its gathered rows are
 // then read from that XCD's L2 after the first tile.
@@ -943,13 +941,13 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
 // and unit u of class c is row tile u % tiles_n of item (u / tiles_n) * 8 + c,
 // so an item's tiles stay on one XCD and each class walks the list longest
 // first, as the one-unit-per-workgroup grid does.  The next unit is claimed
-// at the current unit's first step and set up at its fifth; its first three
-// steps are issued during the current unit's last three (the one-unit grid
-// re-reads the final step there), so the next unit's head - the list entry,
-// the first operand bytes - overlaps the current unit's last steps and
-// epilogue, and no workgroup is dispatched per unit.  The epilogue runs one
-// route tile at a time through the stage that holds no prefetched rows.  K
-// must run a multiple of four steps, at least eight.  The workgroup that
+// at the current unit's first step and set up at its fifth; its first
+// kMmLead steps are issued during the current unit's last ones (the one-unit
+// grid re-reads the final step there), so the next unit's head - the list
+// entry, the first operand bytes - overlaps the current unit's last steps
+// and epilogue, and no workgroup is dispatched per unit.  The epilogue runs
+// one route tile at a time through stage 3, which holds no prefetched rows.
+// K must run a multiple of four steps, at least eight.  The workgroup that
 // finishes last clears the counters for the next launch.
 constexpr int kQueueStride = kWlQueueStride;             // ints per counter (one 128-byte line each)
 static_assert(kWlQueueInts == (kXcds + 1) * kQueueStride, "8 class counters, then the finished count");
@@ -1040,11 +1038,10 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_down_stream_kernel(Ffn
   Unit cur = unit_of(__builtin_amdgcn_readfirstlane(s_unit));
   if (cur.cnt > 0) {
     point_at(cur);
+    static_assert(kMmLead == 2, "the prologue issues kMmLead steps");
     t.template issue<0>(0);
     compiler_fence();
     t.template issue<1>(1);
-    compiler_fence();
-    t.template issue<2>(2);
     compiler_fence();
     for (;;) {
       const int mtiles = (cur.cnt + 31) >> 5;
@@ -1060,13 +1057,13 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_down_stream_kernel(Ffn
         constexpr int S = decltype(stage_c)::value;
         stage_release_barrier();                             // every wave is done with step ks-1's stage
         if (ks == 4) nxt = unit_of(__builtin_amdgcn_readfirstlane(s_unit));   // claimed at step 0
-        if (ks == steps - 3 && nxt.cnt > 0) point_at(nxt);
-        // three steps ahead: the current unit's, then the next unit's first
-        // three, or (no next unit) the final step again into a free stage
-        const int is = ks + 3 < steps ? ks + 3 : (nxt.cnt > 0 ? ks + 3 - steps : steps - 1);
-        t.template issue<(S + 3) % kMmStages>(is);
+        if (ks == steps - kMmLead && nxt.cnt > 0) point_at(nxt);
+        // kMmLead steps ahead: the current unit's, then the next unit's
+        // first ones, or (no next unit) the final step again into a free stage
+        const int is = ks + kMmLead < steps ? ks + kMmLead : (nxt.cnt > 0 ? ks + kMmLead - steps : steps - 1);
+        t.template issue<(S + kMmLead) % kMmStages>(is);
         if (ks == 0 && tid == 0) claimed = atomic_claim(ctr);
-        wait_vm<3 * LPS>();
+        wait_vm<kMmLead * LPS>();
         step_barrier();                                      // step ks's operand rows are in LDS
         if (ks == 3 && tid == 0) s_unit = claimed;
         const uint8_t* stage = S == 0 ? s_x0 : (S == 1 ? s_x1 : (S == 2 ? s_x2 : s_x3));
