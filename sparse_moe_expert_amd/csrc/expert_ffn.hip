@@ -1460,6 +1460,95 @@ __global__ __launch_bounds__(kThreads, 2) void gate_up_nc_kernel(FfnParams p, in
   }
 }
 
+// The small step for gate/up rows of several chunks per lane (H = 2560: 80
+// chunks, the Flash-Next expert): as select_gate_up_kernel - workgroup
+// (route r, 16 rows of I), r = t*k + j, selects token t's j-th expert itself
+// (wave 0 runs the selection rounds up to round j) and computes that tile
+// for that one route, h[r, rows] by flat route id; the launch's last
+// workgroup writes every routing output - with gate_up_nc_kernel's rows
+// (kNcLanes lanes per row, NC chunks per lane).  Token t's activation row
+// goes to LDS while wave 0 selects: it does not depend on the routing.
+constexpr int kSgNcXBytes = 8192;            // one activation row, H <= 4096
+
+template <int V, int KC, int NC>
+__global__ __launch_bounds__(kThreads, 2) void select_gate_up_nc_kernel(FfnParams p, const float* __restrict__ logits,
+                                                                        const float* __restrict__ bias,
+                                                                        int32_t* __restrict__ topk_idx,
+                                                                        float* __restrict__ topk_w, int n_tasks) {
+  constexpr int kRpt = kWavesPerBlock * kNcRowsPerWave;
+  constexpr int kXLoads = kSgNcXBytes / 16 / kThreads;
+  __shared__ __align__(16) uint8_t s_x[kSgNcXBytes];
+  __shared__ int s_e;
+  const int task = blockIdx.x;
+  if (task >= n_tasks) {
+    // the launch's last workgroup: every routing output
+    small_route_bucket<V, KC>(p, logits, bias, topk_idx, topk_w);
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sub = lane / kNcLanes, sl = lane & (kNcLanes - 1);
+  const int tiles = (p.I + kRpt - 1) / kRpt;
+  const int r = task / tiles, tile = task - r * tiles;
+  const int t = r / p.k, j = r - t * p.k;
+  const int C = p.H / 32;
+  // the activation row, 16 bytes per thread and pass (pieces past the row
+  // read zeros and are not stored)
+  const uint32_t x_bytes = (uint32_t)p.H * 2;
+  const auto rx = make_rsrc(p.x + (size_t)t * p.H, x_bytes);
+  u32x4 xv[kXLoads];
+#pragma unroll
+  for (int q = 0; q < kXLoads; ++q)
+    xv[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(tid + q * kThreads) * 16, 0, 0);
+  compiler_fence();
+  if (wave == 0) {
+    // only slot j's expert: the rounds of the selection up to round j
+    const int e_j = select_slot<V, KC>(logits + (size_t)t * p.E, bias, p.E, j, lane);
+    if (lane == 0) s_e = e_j;
+  }
+#pragma unroll
+  for (int q = 0; q < kXLoads; ++q) {
+    const uint32_t o = (uint32_t)(tid + q * kThreads) * 16;
+    if (o < x_bytes) *reinterpret_cast<u32x4*>(s_x + o) = xv[q];
+  }
+  __syncthreads();
+  const int e = min(max(__builtin_amdgcn_readfirstlane(s_e), 0), p.E - 1);
+
+  // the tile's rows of expert e, as gate_up_nc_kernel
+  const uint32_t code_row = (uint32_t)p.H / 2, scale_row = (uint32_t)p.H / 16;
+  const uint32_t mat_codes = (uint32_t)p.I * code_row, mat_scales = (uint32_t)p.I * scale_row;
+  const auto rg = make_rsrc(p.wg + (size_t)e * mat_codes, mat_codes);
+  const auto ru = make_rsrc(p.wu + (size_t)e * mat_codes, mat_codes);
+  const auto rsg = make_rsrc(p.sg + (size_t)e * mat_scales, mat_scales);
+  const auto rsu = make_rsrc(p.su + (size_t)e * mat_scales, mat_scales);
+  const int row = tile * kRpt + wave * kNcRowsPerWave + sub;
+  const bool row_ok = row < p.I;
+  uint4 cg[NC], cu[NC];
+  uint32_t vg[NC], vu[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    uint32_t oc, os;
+    nc_chunk_offsets(sl, i, C, (uint32_t)row * code_row, (uint32_t)row * scale_row, row_ok, oc, os);
+    cg[i] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rg, oc, 0, kStreamAux));
+    cu[i] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(ru, oc, 0, kStreamAux));
+    vg[i] = __builtin_amdgcn_raw_buffer_load_b16(rsg, os, 0, kStreamAux);
+    vu[i] = __builtin_amdgcn_raw_buffer_load_b16(rsu, os, 0, kStreamAux);
+  }
+  compiler_fence();
+  const float Gg = sload(p.gsc, e * 3 + 0), Gu = sload(p.gsc, e * 3 + 1);
+  const float one = opaque_one();
+  float ag = 0.0f, au = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    uint32_t xr[16];
+    load_operand_chunk(reinterpret_cast<const uint16_t*>(s_x), min(sl + i * kNcLanes, C - 1), xr);
+    ag = dot_chunk(cg[i], vg[i], xr, ag, one);
+    au = dot_chunk(cu[i], vu[i], xr, au, one);
+  }
+  const float gs = row16_sum(ag) * Gg, us = row16_sum(au) * Gu;
+  if (sl == 0 && row_ok) p.h[(size_t)r * p.I + row] = (uint16_t)f32_to_bf16_rne(silu(gs) * us);
+}
+
 // Down rows of one tile (16 rows of H) for all routes of expert e -> o (fp32).
 template <int NC>
 __global__ __launch_bounds__(kThreads, 2) void down_nc_kernel(FfnParams p, int n_tasks) {
@@ -1527,7 +1616,9 @@ constexpr int kDcNcHLoads = kDcMaxLds / 16 / kDcNcThreads;   // h pieces per thr
 // wave's piece of the buffer_load ... lds staging).
 constexpr uint32_t dc_nc_h_lds(uint32_t h_bytes) { return (h_bytes + 1023u) & ~1023u; }
 
-template <int NC, int SLOTS>
+// Route slots (RS, after select_gate_up_nc_kernel): slot a is route a itself
+// (expert topk_idx[a], h row a, one route), as in down_combine_kernel.
+template <int NC, int SLOTS, bool RS = false>
 __global__ __launch_bounds__(kDcNcThreads, 3) void down_combine_nc_kernel(FfnParams p) {
   extern __shared__ __align__(16) uint8_t s_dyn8[];   // [R, I] bf16 h (to a whole KB), then [R, 4] fp32 o
   __shared__ int s_src[kDcMaxRoutes];
@@ -1538,7 +1629,7 @@ __global__ __launch_bounds__(kDcNcThreads, 3) void down_combine_nc_kernel(FfnPar
   const int sub = lane / kNcLanes, sl = lane & (kNcLanes - 1);
   const int row0 = blockIdx.x * rpw;
   const int R = p.T * p.k;
-  const int S = min(p.E, R);
+  const int S = RS ? R : min(p.E, R);
   const int C = p.I / 32;
   uint16_t* s_h = reinterpret_cast<uint16_t*>(s_dyn8);
   const uint32_t h_bytes = (uint32_t)R * p.I * 2;
@@ -1558,7 +1649,7 @@ __global__ __launch_bounds__(kDcNcThreads, 3) void down_combine_nc_kernel(FfnPar
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, s_dyn8 + blk, 16, blk + (uint32_t)lane * 16, 0, 0, 0);
   }
   const int rt = min(tid, R - 1);
-  const int src_r = p.route_src[rt];
+  const int src_r = RS ? rt : p.route_src[rt];
   const float w_r = p.topk_w[rt];
   compiler_fence();
 
@@ -1566,7 +1657,8 @@ __global__ __launch_bounds__(kDcNcThreads, 3) void down_combine_nc_kernel(FfnPar
 #pragma unroll
   for (int u = 0; u < SLOTS; ++u) {
     const int a = wave + u * kDcNcWaves;
-    e_u[u] = a < S ? slot_expert(p, a) : -1;
+    if constexpr (RS) e_u[u] = a < S ? min(max(sload(p.topk_idx, a), 0), p.E - 1) : -1;
+    else e_u[u] = a < S ? slot_expert(p, a) : -1;
   }
   const uint32_t code_row = (uint32_t)p.I / 2, scale_row = (uint32_t)p.I / 16;
   // one resource spans all of W_down (and one its scales); the host checks
@@ -1600,8 +1692,8 @@ __global__ __launch_bounds__(kDcNcThreads, 3) void down_combine_nc_kernel(FfnPar
 #pragma unroll
   for (int u = 0; u < SLOTS; ++u) {
     if (e_u[u] < 0) continue;
-    int off, cnt;
-    expert_routes(p, e_u[u], off, cnt);
+    int off = wave + u * kDcNcWaves, cnt = 1;   // route slots: the route itself
+    if constexpr (!RS) expert_routes(p, e_u[u], off, cnt);
     const float gd = sload(p.gsc, e_u[u] * 3 + 2);
     for (int t = 0; t < cnt; ++t) {
       const int pos = off + t;
@@ -1668,29 +1760,31 @@ int dc_nc_slots_per_wave(long long slots) { return (int)((slots + kDcNcWaves - 1
 // down_combine_nc_kernel<NC, S> with S = the slots per wave; only the
 // instances with NC * S <= kDcNcMaxChunks exist (the policy sends no other
 // batch here): false for any other.
-template <int NC, int S = 1>
+template <int NC, bool RS, int S = 1>
 bool launch_down_combine_nc_slots(const FfnParams& p, unsigned grid, size_t dyn, int per_wave, hipStream_t s) {
   if constexpr (NC * S > kDcNcMaxChunks) {
     return false;
   } else {
     if (per_wave == S) {
-      down_combine_nc_kernel<NC, S><<<grid, kDcNcThreads, dyn, s>>>(p);
+      down_combine_nc_kernel<NC, S, RS><<<grid, kDcNcThreads, dyn, s>>>(p);
       return true;
     }
-    return launch_down_combine_nc_slots<NC, S + 1>(p, grid, dyn, per_wave, s);
+    return launch_down_combine_nc_slots<NC, RS, S + 1>(p, grid, dyn, per_wave, s);
   }
 }
 
+// slots: expert slots (bucketed), or routes (RS: the small step's route slots)
+template <bool RS = false>
 bool launch_down_combine_nc(int nc, const FfnParams& p, unsigned grid, size_t dyn, int slots, hipStream_t s) {
   const int per_wave = dc_nc_slots_per_wave(slots);
   switch (nc) {
-    case 1: return launch_down_combine_nc_slots<1>(p, grid, dyn, per_wave, s);
-    case 2: return launch_down_combine_nc_slots<2>(p, grid, dyn, per_wave, s);
-    case 3: return launch_down_combine_nc_slots<3>(p, grid, dyn, per_wave, s);
-    case 4: return launch_down_combine_nc_slots<4>(p, grid, dyn, per_wave, s);
-    case 5: return launch_down_combine_nc_slots<5>(p, grid, dyn, per_wave, s);
-    case 6: return launch_down_combine_nc_slots<6>(p, grid, dyn, per_wave, s);
-    case 8: return launch_down_combine_nc_slots<8>(p, grid, dyn, per_wave, s);
+    case 1: return launch_down_combine_nc_slots<1, RS>(p, grid, dyn, per_wave, s);
+    case 2: return launch_down_combine_nc_slots<2, RS>(p, grid, dyn, per_wave, s);
+    case 3: return launch_down_combine_nc_slots<3, RS>(p, grid, dyn, per_wave, s);
+    case 4: return launch_down_combine_nc_slots<4, RS>(p, grid, dyn, per_wave, s);
+    case 5: return launch_down_combine_nc_slots<5, RS>(p, grid, dyn, per_wave, s);
+    case 6: return launch_down_combine_nc_slots<6, RS>(p, grid, dyn, per_wave, s);
+    case 8: return launch_down_combine_nc_slots<8, RS>(p, grid, dyn, per_wave, s);
     default: return false;
   }
 }
@@ -2007,26 +2101,45 @@ constexpr int kSmallStepMaxRoutes = kSgMaxRoutes;
 
 bool small_step_ok(int T, int H, int I, int E, int k) {
   if (T < 1 || (long long)T * k > kSmallStepMaxRoutes) return false;
-  if (H != 64 * 32 || k > 32) return false;                       // gate/up rows of one chunk per lane: H = 2048
+  if (k > 32) return false;
   // up to eight selection keys per lane: sixteen would take ~146 registers,
   // more than the gate/up workgroups (four per CU at least) may hold
   if (E > 8 * kWave) return false;
-  const int C = I / 32;
-  if (C > 64 || (C & (C - 1)) != 0) return false;                 // down rows of one chunk per lane
+  // gate/up rows of one chunk per lane at H = 2048, or of several chunks per
+  // lane (the row-dot kernels' one-chunk rows at other powers of two stay on
+  // the three-kernel path)
+  if (H != 64 * 32 && (nc_chunks(H / 32) == 0 || H * 2 > kSgNcXBytes)) return false;
+  const int C = I / 32, nc_d = nc_chunks(C);
+  if (nc_d == 0 && C > 64) return false;                          // down rows of one chunk per lane
+  // the route-slot down/unroute holds nc_d chunks of every route slot of a
+  // wave in registers
+  if (nc_d > 0 && nc_d * dc_nc_slots_per_wave((long long)T * k) > kDcNcMaxChunks) return false;
   return ffn_policy(T, H, I, E, k, false).down_combine;
 }
 
+// nc = 0: rows of one chunk per lane (select_gate_up_kernel); else
+// select_gate_up_nc_kernel<.., nc> (compiled for nc = 1..6 and 8)
 template <int V, int KC>
-void launch_select_gate_up(const FfnParams& p, const float* logits, const float* bias, int32_t* topk_idx,
+void launch_select_gate_up(int nc, const FfnParams& p, const float* logits, const float* bias, int32_t* topk_idx,
                            float* topk_w, int tasks, hipStream_t s) {
-  select_gate_up_kernel<V, KC><<<(unsigned)tasks + 1, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks);
+  const unsigned grid = (unsigned)tasks + 1;
+  switch (nc) {
+    case 0: select_gate_up_kernel<V, KC><<<grid, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks); break;
+    case 1: select_gate_up_nc_kernel<V, KC, 1><<<grid, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks); break;
+    case 2: select_gate_up_nc_kernel<V, KC, 2><<<grid, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks); break;
+    case 3: select_gate_up_nc_kernel<V, KC, 3><<<grid, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks); break;
+    case 4: select_gate_up_nc_kernel<V, KC, 4><<<grid, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks); break;
+    case 5: select_gate_up_nc_kernel<V, KC, 5><<<grid, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks); break;
+    case 6: select_gate_up_nc_kernel<V, KC, 6><<<grid, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks); break;
+    default: select_gate_up_nc_kernel<V, KC, 8><<<grid, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks); break;
+  }
 }
 
 template <int V>
-void launch_select_gate_up_k(int k, const FfnParams& p, const float* logits, const float* bias, int32_t* topk_idx,
-                             float* topk_w, int tasks, hipStream_t s) {
-  if (k == 10) launch_select_gate_up<V, 10>(p, logits, bias, topk_idx, topk_w, tasks, s);
-  else launch_select_gate_up<V, 0>(p, logits, bias, topk_idx, topk_w, tasks, s);
+void launch_select_gate_up_k(int k, int nc, const FfnParams& p, const float* logits, const float* bias,
+                             int32_t* topk_idx, float* topk_w, int tasks, hipStream_t s) {
+  if (k == 10) launch_select_gate_up<V, 10>(nc, p, logits, bias, topk_idx, topk_w, tasks, s);
+  else launch_select_gate_up<V, 0>(nc, p, logits, bias, topk_idx, topk_w, tasks, s);
 }
 
 moe_status small_step(const uint16_t* x, const float* logits, const float* bias, const uint8_t* w_gate,
@@ -2047,26 +2160,32 @@ moe_status small_step(const uint16_t* x, const float* logits, const float* bias,
   p.o = reinterpret_cast<uint16_t*>(ws + L.o_off);
   p.y = y;
   p.sr = SharedRows{};
-  p.lr_gu = 64;
-  p.lr_d = lanes_per_row(I / 32);
+  const int nc_gu = H == 64 * 32 ? 0 : nc_chunks(H / 32), nc_d = nc_chunks(I / 32);
+  p.lr_gu = nc_gu ? kNcLanes : 64;
+  p.lr_d = nc_d ? kNcLanes : lanes_per_row(I / 32);
   const int R = T * k;
   // selection + gate/up: one workgroup per (route, 16 rows of I)
+  static_assert(kWavesPerBlock * kGuUnits == kWavesPerBlock * kNcRowsPerWave, "16 rows of I per workgroup");
   const int tiles = (I + kWavesPerBlock * kGuUnits - 1) / (kWavesPerBlock * kGuUnits);
   const int tasks = R * tiles;                       // and one routing workgroup after them
   const int V = (E + kWave - 1) / kWave;
   if (stage & 1) {
-    if (V <= 1) launch_select_gate_up_k<1>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
-    else if (V <= 2) launch_select_gate_up_k<2>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
-    else if (V <= 4) launch_select_gate_up_k<4>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
-    else launch_select_gate_up_k<8>(k, p, logits, bias, topk_idx, topk_w, tasks, s);
+    if (V <= 1) launch_select_gate_up_k<1>(k, nc_gu, p, logits, bias, topk_idx, topk_w, tasks, s);
+    else if (V <= 2) launch_select_gate_up_k<2>(k, nc_gu, p, logits, bias, topk_idx, topk_w, tasks, s);
+    else if (V <= 4) launch_select_gate_up_k<4>(k, nc_gu, p, logits, bias, topk_idx, topk_w, tasks, s);
+    else launch_select_gate_up_k<8>(k, nc_gu, p, logits, bias, topk_idx, topk_w, tasks, s);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
   if (!(stage & 2)) return MOE_OK;
   // route-slot down/unroute over rows of y
   const int rpw = kWave / p.lr_d;
-  const size_t dyn = (size_t)R * I * 2 + (size_t)R * rpw * 4;
+  const size_t h_bytes = (size_t)R * I * 2;
+  const size_t dyn = (nc_d ? dc_nc_h_lds((uint32_t)h_bytes) : h_bytes) + (size_t)R * rpw * 4;
   const unsigned grid = (unsigned)((H + rpw - 1) / rpw);
-  if (p.lr_d == 16) launch_down_combine<16, true>(p, grid, dyn, R, s);
+  if (nc_d) {
+    if (!launch_down_combine_nc<true>(nc_d, p, grid, dyn, R, s)) return MOE_ERR_UNSUPPORTED;
+  }
+  else if (p.lr_d == 16) launch_down_combine<16, true>(p, grid, dyn, R, s);
   else launch_down_combine<0, true>(p, grid, dyn, R, s);
   return launch_status();
 }
