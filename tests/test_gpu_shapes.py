@@ -1,8 +1,9 @@
 """Row lengths whose 16-byte chunk count is not a power of two, on the GPU.
 
 The Flash-Next expert as the pages size it (H = 2560, I = 640: 80 and 20
-chunks per row) at the decode step (T = 4: the multi-chunk gate/up and fused
-down/unroute kernels) and at 256 tokens (the MFMA tiles with the packed copy;
+chunks per row) at the decode step (T = 4: the small step with multi-chunk
+rows on the step paths, the multi-chunk gate/up and fused down/unroute
+kernels on the separate calls) and at 256 tokens (the MFMA tiles with the packed copy;
 on the standard layout the experts with fewer than 16 routes take the
 multi-chunk gate/up, per-expert down and combine kernels), plus smaller
 shapes that reach every chunk count the kernels are compiled for and rows
@@ -42,7 +43,9 @@ def test_flash_next_expert_shape(name, path):
 # with a tail), 5, 6, 12, 20, 24, 40, 80, 96 and 128.  Small batches take the
 # fused down/unroute kernel when every route's h fits its LDS (64 KB) and the
 # per-expert down tiles plus the combine otherwise (I = 2560 at T = 20, I =
-# 4096 at T = 4); T = 70 takes the MFMA path as well.
+# 4096 at T = 4); on the step paths those of at most 40 routes whose down
+# fits take the small step (selection inside the gate/up launch, route-slot
+# down/unroute); T = 70 takes the MFMA path as well.
 ODD_ROW_SHAPES = [
     (96, 160, 8, 2, 4),
     (192, 384, 8, 3, 10),

@@ -1,6 +1,8 @@
-"""The small-batch step: moe_step up to 40 routes at H = 2048 selects inside
-its gate/up launch (one workgroup per route and row tile) and buckets beside
-its route-slot down/unroute.
+"""The small-batch step: moe_step up to 40 routes selects inside its gate/up
+launch (one workgroup per route and row tile) and buckets beside it, then
+runs its route-slot down/unroute; rows of one 16-byte chunk per lane at H =
+2048, of several chunks per lane at other sizes (H = 2560 of the Flash-Next
+expert), and likewise for the down rows.
 
 Every output (ids, weights, the six bucket arrays, y) must equal bit for bit
 what moe_route_bucket + moe_expert_ffn produce on the same inputs, and match
@@ -25,8 +27,8 @@ from moe_inputs.configs import get_config
 pytestmark = pytest.mark.gpu
 
 
-def _wl(T, E, k, seed, I=512):
-    cfg = replace(get_config("decode_t4"), name="small_step", T=T, E=E, k=k, I=I)
+def _wl(T, E, k, seed, I=512, H=2048):
+    cfg = replace(get_config("decode_t4"), name="small_step", T=T, E=E, k=k, I=I, H=H)
     return make_workload(cfg, x_seed=seed)
 
 
@@ -40,8 +42,28 @@ CASES = [(4, 512, 10, 512, False, False), (1, 512, 10, 512, True, False), (2, 51
 @pytest.mark.parametrize("path", ["step", "packed"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "T%d_E%d_k%d_I%d_bias%d_ties%d" % c)
 def test_small_step_equals_calls_and_oracle(case, path):
-    T, E, k, I, with_bias, ties = case
-    wl = _wl(T, E, k, 60 + T + k, I=I)
+    _check_small_step(*case, path=path)
+
+
+# (T, E, k, H, I, bias, ties): rows of several chunks per lane - the
+# Flash-Next expert (H = 2560, I = 640: 80 and 20 chunks), H = 1280 and 3072
+# (40 and 96 chunks), and H = 2048 with I = 4096 (one-chunk gate/up rows,
+# 128-chunk down rows); each within the route-slot down's register bound
+NC_CASES = [(4, 512, 10, 2560, 640, False, False), (2, 512, 10, 2560, 640, True, True),
+            (4, 64, 10, 1280, 768, False, False), (4, 16, 4, 3072, 640, True, False),
+            (1, 16, 4, 2048, 4096, False, False)]
+
+
+@pytest.mark.parametrize("path", ["step", "packed"])
+@pytest.mark.parametrize("case", NC_CASES, ids=lambda c: "T%d_E%d_k%d_H%d_I%d_bias%d_ties%d" % c)
+def test_small_step_several_chunks_equals_calls_and_oracle(case, path):
+    T, E, k, H, I, with_bias, ties = case
+    _check_small_step(T, E, k, I, with_bias, ties, path=path, H=H)
+
+
+def _check_small_step(T, E, k, I, with_bias, ties, path, H=2048):
+    print(f"[small step] T={T} E={E} k={k} H={H} I={I} bias={with_bias} ties={ties} path={path}", flush=True)
+    wl = _wl(T, E, k, 60 + T + k, I=I, H=H)
     logits = wl.logits
     if ties:
         logits = (np.round(logits * 4.0) / 4.0).astype(np.float32)
@@ -62,7 +84,7 @@ def test_small_step_equals_calls_and_oracle(case, path):
     idx, w, bk, y = oracle_all(wl.x, logits, bias, wl.bank, k)
     assert_route(g, idx, w)
     assert_buckets(g, bk)
-    assert_output(g["y"], y, f"small step {case}")
+    assert_output(g["y"], y, f"small step T={T} E={E} k={k} H={H} I={I}")
 
 
 def test_small_step_guard_regions():
