@@ -106,11 +106,12 @@ def test_small_step_guard_regions():
     assert_output(big_y[1: T + 1].float().cpu().numpy().astype(np.float64), y, "guarded small step")
 
 
-@pytest.mark.parametrize("name,path", [("decode_t4", "step"), ("decode_t4", "packed"), ("verify_t32", "step"),
-                                       ("decode_t256_zipf", "packed")])
+@pytest.mark.parametrize("name,path", [("decode_t4", "step"), ("decode_t4", "packed"), ("flashnext_t4", "step"),
+                                       ("verify_t32", "step"), ("decode_t256_zipf", "packed")])
 def test_step_stages_compose(name, path):
     """moe_step_stage 1 then 2 gives moe_step's outputs bit for bit (the small
-    step's two launches at decode_t4; routing, buckets and gate/up, then down
+    step's two launches at decode_t4 and, with rows of several chunks per
+    lane, at the Flash-Next shape; routing, buckets and gate/up, then down
     and the unroute, at the larger batches)."""
     wl = make_workload(name, x_seed=77)
     W = device_weights(wl.bank)
