@@ -457,8 +457,8 @@ def protocol_leg(step, full, gu_steps, xs, ls, bias, banks, pks, stream, dev, NB
     seven timed rounds of about 100 steps each (median, min, max), the same
     step replayed on one bank and routing set (cache-resident: the MALL holds
     its experts), the expert FFN alone (moe_expert_ffn over the NB pairs, HIP
-    events), a plain device-to-device copy as the box's practical bandwidth
-    ceiling, and the bytes a per-route kernel would stream."""
+    events), a plain device-to-device copy as the device's practical
+    bandwidth ceiling, and the bytes a per-route kernel would stream."""
     import numpy as np
     import torch
     log("[bench] protocol figures")

@@ -6,9 +6,9 @@ router logits; it implements none of the routed-MoE step itself (no top-k, no
 bucketing, no dequantisation, no expert FFN, no combine).
 
 Workload shapes and distributions follow the five configurations the routed
-MoE is judged on: a tiny case (T=4, H=256, I=128, E=8, top-2) and four cases
-at the Flash-Next expert shape (H=2048, I=512, E=512, top-10) with T = 4, 32,
-256 and 4096 tokens.
+MoE step is measured on: a tiny case (T=4, H=256, I=128, E=8, top-2) and four
+cases at H=2048, I=512, E=512, top-10 with T = 4, 32, 256 and 4096 tokens;
+the Flash-Next expert shape (H=2560, I=640) is an extra configuration.
 """
 
 from .configs import CONFIGS, WorkloadConfig, get_config
