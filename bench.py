@@ -32,7 +32,9 @@ plus the previous output (a residual stream).  `protocol` adds seven timed
 rounds (median, min, max), the same step on one bank (cache-resident), the
 expert FFN alone, a device-to-device copy as the practical bandwidth ceiling
 and the bytes a per-route kernel would stream; `cpu_baseline.one_core` is the
-oracle with its BLAS on one thread.  `configs` times every workload (the five
+oracle with its BLAS on one thread.  `clocks` samples the GPU's clocks and
+socket power (amdsmi) while the headline steps replay back to back for a few
+seconds after the timed region.  `configs` times every workload (the five
 configurations and the Flash-Next expert shape H=2560, I=640 at decode) the
 same way, with the no-reuse per-route variant beside the step at decode_t4
 and verify_t32, the bf16 MFMA rate on the method's own flops at the prefill
@@ -91,6 +93,9 @@ def parse():
                          "headline and report them under `configs`; 0: skip")
     ap.add_argument("--config-steps", type=int, default=96,
                     help="steps timed per workload in the configs leg")
+    ap.add_argument("--clock-seconds", type=float, default=3.0,
+                    help="seconds of back-to-back headline steps during which amdsmi samples the GPU's "
+                         "clocks and power (0 skips the `clocks` record)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the bench, run a plain device-to-device copy of this many MiB three times "
                          "(the known-size kernel that calibrates FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -400,6 +405,116 @@ def shared_leg(args, cfg, x0, banks, pks, bias, dev, expert_bytes: int):
                              "moe_shared_expert",
             "per_layer": "router projection + routed step + shared expert (library) + residual add (torch); "
                          "fused: moe_step_shared in place of the step and the shared-expert call"}
+
+
+def _smi_handle(dev):
+    """amdsmi handle of the GPU torch uses (matched by PCI bus), or an error string."""
+    import amdsmi
+    import torch
+    amdsmi.amdsmi_init()
+    handles = amdsmi.amdsmi_get_processor_handles()
+    if not handles:
+        return None, "amdsmi lists no GPU"
+    props = torch.cuda.get_device_properties(dev)
+    bus = getattr(props, "pci_bus_id", None)
+    if bus is not None:
+        for h in handles:
+            try:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                if int(bdf.split(":")[1], 16) == int(bus):
+                    return h, None
+            except Exception:
+                continue
+    if len(handles) == 1:
+        return handles[0], None
+    return None, f"{len(handles)} GPUs listed and none matched PCI bus {bus}"
+
+
+def _smi_sample(amdsmi, h):
+    """One reading: gfx and memory clocks (MHz), socket power (W), busy (%), hotspot temperature (C)."""
+    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+
+    def num(key):
+        v = m.get(key)
+        if isinstance(v, (list, tuple)):
+            v = [x for x in v if isinstance(x, (int, float)) and x not in (0xFFFF, 0xFFFFFFFF)]
+            return float(sum(v) / len(v)) if v else None
+        return float(v) if isinstance(v, (int, float)) and v not in (0xFFFF, 0xFFFFFFFF) else None
+
+    return {"gfx_MHz": num("current_gfxclk") or num("current_gfxclks"),
+            "mem_MHz": num("current_uclk"),
+            "power_W": num("current_socket_power") or num("average_socket_power"),
+            "busy_pct": num("average_gfx_activity"),
+            "hotspot_C": num("temperature_hotspot")}
+
+
+def clocks_leg(full, NB: int, dev, seconds: float):
+    """Clocks and power while the headline graph replays back to back.
+
+    A thread samples amdsmi's GPU metrics every ~10 ms while the main thread
+    keeps the graph queued (a synchronisation every 32 replays) for `seconds`;
+    one idle reading is taken before.  Reported: median, min and max of each
+    quantity over the samples.  Any amdsmi failure is reported instead of the
+    figures (no effect on the timed results, which were taken before)."""
+    import threading
+
+    import torch
+    try:
+        import amdsmi
+        h, err = _smi_handle(dev)
+        if h is None:
+            return {"error": err}
+        torch.cuda.synchronize()
+        idle = _smi_sample(amdsmi, h)
+    except Exception as e:           # no driver access for this user, older metrics table, ...
+        return {"error": f"{type(e).__name__}: {e}"}
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                samples.append(_smi_sample(amdsmi, h))
+            except Exception:
+                pass
+            stop.wait(0.01)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    full.replay()
+    torch.cuda.synchronize()
+    th.start()
+    t_end = time.perf_counter() + seconds
+    n = 0
+    while time.perf_counter() < t_end:
+        full.replay()
+        n += 1
+        if n % 32 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+
+    # the firmware refreshes the metrics table far less often than we read
+    # it: keep the readings taken under load (busy >= 50%); the first ones
+    # still show the idle state that preceded the replays
+    loaded = [x for x in samples if (x.get("busy_pct") or 0) >= 50]
+    use = loaded if loaded else samples
+
+    def stats(key):
+        v = sorted(x[key] for x in use if x.get(key) is not None)
+        if not v:
+            return None
+        return {"median": round(v[len(v) // 2], 1), "min": round(v[0], 1), "max": round(v[-1], 1)}
+
+    return {"samples": len(samples), "samples_under_load": len(loaded), "steps": n * NB, "seconds": seconds,
+            "gfx_clock_MHz": stats("gfx_MHz"), "mem_clock_MHz": stats("mem_MHz"),
+            "socket_power_W": stats("power_W"), "gfx_busy_pct": stats("busy_pct"),
+            "hotspot_C": stats("hotspot_C"), "idle": idle,
+            "note": "amdsmi GPU metrics read every ~10 ms while the headline graph replays back to back "
+                    "(after the timed region); figures over the readings that show the GPU busy"}
 
 
 def cpu_baseline(cfg, budget_s: float, expert_bytes: int):
@@ -821,6 +936,9 @@ def main():
     }
     if protocol is not None:
         out["protocol"] = protocol
+    if args.clock_seconds > 0:
+        log(f"[bench] clocks and power ({args.clock_seconds:.1f} s of steps)")
+        out["clocks"] = clocks_leg(full, NB, dev, args.clock_seconds)
     if args.router_copies > 0:
         log(f"[bench] router projection leg ({args.router_copies} weight copies)")
         out["router"] = router_leg(args, cfg, wls[0], dev)
