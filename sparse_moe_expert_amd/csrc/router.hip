@@ -145,6 +145,15 @@ __global__ __launch_bounds__(kRtThreads) void router_gemm_kernel(const uint16_t*
   }
 }
 
+// tokens per pass: the smallest of 1, 2, 4, 8 that holds the batch (at most 8)
+template <int NCH>
+void launch_router_rows(int T, const uint16_t* x, const float* w, int H, int E, float* logits, hipStream_t s) {
+  if (T <= 1) router_rows_kernel<NCH, 1><<<E, kRtThreads, 0, s>>>(x, w, T, H, E, logits);
+  else if (T <= 2) router_rows_kernel<NCH, 2><<<E, kRtThreads, 0, s>>>(x, w, T, H, E, logits);
+  else if (T <= 4) router_rows_kernel<NCH, 4><<<E, kRtThreads, 0, s>>>(x, w, T, H, E, logits);
+  else router_rows_kernel<NCH, kRsGroup><<<E, kRtThreads, 0, s>>>(x, w, T, H, E, logits);
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -160,8 +169,8 @@ extern "C" moe_status moe_router_logits(const uint16_t* x, const float* w_router
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T <= kRsMaxTokens) {
     const int nc = (H / 8 + kRtThreads - 1) / kRtThreads;   // 16-byte pieces per thread
-    if (nc <= 1) router_rows_kernel<1><<<E, kRtThreads, 0, s>>>(x, w_router, T, H, E, logits);
-    else router_rows_kernel<2><<<E, kRtThreads, 0, s>>>(x, w_router, T, H, E, logits);
+    if (nc <= 1) launch_router_rows<1>(T, x, w_router, H, E, logits, s);
+    else launch_router_rows<2>(T, x, w_router, H, E, logits, s);
     return launch_status();
   }
   if (T >= kRgMinTokens) {

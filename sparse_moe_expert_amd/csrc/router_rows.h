@@ -57,13 +57,15 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 // loads and products spread over 256 lanes.  Thread i of the group holds the
 // row's values h = 8(i + 256c) .. +8 as fp64 and reads the same 16 bytes of
 // each token's activation row directly (cached: every group reads the same
-// x), eight tokens at a time; wavefront sums go to LDS (s_part, the group's
+// x), G (up to eight) tokens at a time - a batch of T <= 4 tokens takes the
+// smallest G >= T, so no wavefront sum is formed for an absent token; the
+// sums do not depend on G; wavefront sums go to LDS (s_part, the group's
 // own) and are added in wave order.  Every thread of the workgroup calls it
 // (it has workgroup barriers); a group whose row e lies past E computes
 // nothing and stores nothing.
 constexpr int kRsGroup = 8;
 
-template <int NCH>
+template <int NCH, int G = kRsGroup>
 __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x, const float* __restrict__ w, int T, int H,
                                            int E, float* __restrict__ logits, int e, int gtid,
                                            double (&s_part)[kRtWaves][kRsGroup]) {
@@ -82,20 +84,21 @@ __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x, const
     wd[c][0] = a.x; wd[c][1] = a.y; wd[c][2] = a.z; wd[c][3] = a.w;
     wd[c][4] = b.x; wd[c][5] = b.y; wd[c][6] = b.z; wd[c][7] = b.w;
   }
-  for (int t0 = 0; t0 < T; t0 += kRsGroup) {
-    const int nt = min(kRsGroup, T - t0);
-    uint4 xv[kRsGroup][NCH];
+  static_assert(G >= 1 && G <= kRsGroup, "at most kRsGroup tokens per pass");
+  for (int t0 = 0; t0 < T; t0 += G) {
+    const int nt = min(G, T - t0);
+    uint4 xv[G][NCH];
 #pragma unroll
-    for (int g = 0; g < kRsGroup; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int h0 = 8 * (gtid + kRtThreads * c);
         xv[g][c] = make_uint4(0u, 0u, 0u, 0u);
         if (row_ok && g < nt && h0 < H) xv[g][c] = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + g) * H + h0);
       }
-    double acc[kRsGroup];
+    double acc[G];
 #pragma unroll
-    for (int g = 0; g < kRsGroup; ++g) {
+    for (int g = 0; g < G; ++g) {
       double a = 0.0;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
@@ -110,7 +113,7 @@ __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x, const
     }
     if (lane == 0) {
 #pragma unroll
-      for (int g = 0; g < kRsGroup; ++g) s_part[wave][g] = acc[g];
+      for (int g = 0; g < G; ++g) s_part[wave][g] = acc[g];
     }
     __syncthreads();
     if (row_ok && gtid < nt) {
@@ -122,12 +125,12 @@ __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x, const
   }
 }
 
-template <int NCH>
+template <int NCH, int G>
 __global__ __launch_bounds__(kRtThreads) void router_rows_kernel(const uint16_t* __restrict__ x,
                                                                  const float* __restrict__ w, int T, int H, int E,
                                                                  float* __restrict__ logits) {
   __shared__ double s_part[kRtWaves][kRsGroup];
-  router_row<NCH>(x, w, T, H, E, logits, (int)blockIdx.x, (int)threadIdx.x, s_part);
+  router_row<NCH, G>(x, w, T, H, E, logits, (int)blockIdx.x, (int)threadIdx.x, s_part);
 }
 
 }  // namespace
