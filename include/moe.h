@@ -446,11 +446,16 @@ moe_status moe_shared_expert(const uint16_t* x, const uint16_t* w_gate, const ui
  *              The caller adds y and y_shared.  No output may overlap
  *              another output or an input.
  * The shared expert's argument checks come first, then the step's; a
- * failing check launches nothing.  At decode sizes (at most 16 tokens and
- * 256 routes with at most 512 experts; H of 512, 1024 or 2048
- * for the gate/up rows, Is of 512 or 1024 for the down rows) the shared
- * expert's rows run as extra workgroups of the step's routing and gate/up
- * launches; otherwise its own two kernels run on the same stream.
+ * failing check launches nothing.  Where the step takes its two-launch form
+ * (at most 40 routes at H = 2048, rows of I of one 16-byte chunk per lane),
+ * Is is 512 or 1024 and T * Is * 2 bytes fit the down launch's LDS, the
+ * shared gate/up rows run as extra workgroups of the selection launch and
+ * its down rows in the last waves of the down/unroute workgroups.  Other
+ * decode sizes (at most 16 tokens and 256 routes with at most 512 experts;
+ * H of 512, 1024 or 2048 for the gate/up rows, Is of 512 or 1024 for the
+ * down rows) run the shared rows as extra workgroups of the step's routing
+ * and gate/up launches; otherwise its own two kernels run on the same
+ * stream.
  */
 moe_status moe_step_shared(const uint16_t* x, const float* logits, const float* bias,
                            const uint8_t* w_gate, const uint8_t* s_gate,

@@ -437,9 +437,16 @@ __global__ __launch_bounds__(kThreads, 4) void select_gate_up_kernel(FfnParams p
   __shared__ __align__(16) uint8_t s_x[kSgXBytes];
   __shared__ int s_e;
   const Geo<64, kGuUnits> g(64, p.I);
-  const int task = blockIdx.x;
+  // a shared expert's gate/up rows (one per wave) come first, so that their
+  // loads are issued ahead of the tiles' weight stream
+  const int se_blocks = p.sr.gu_nc > 0 ? (p.sr.Is + kWavesPerBlock - 1) / kWavesPerBlock : 0;
+  if ((int)blockIdx.x < se_blocks) {
+    se_gate_up_side_small(p.sr, (int)blockIdx.x * kWavesPerBlock + g.wave, threadIdx.x & (kWave - 1));
+    return;
+  }
+  const int task = (int)blockIdx.x - se_blocks;
   if (task >= n_tasks) {
-    // the launch's last workgroup: every routing output
+    // the workgroup after the gate/up tiles: every routing output
     small_route_bucket<V, KC>(p, logits, bias, topk_idx, topk_w);
     return;
   }
@@ -1227,6 +1234,55 @@ constexpr int kDcThreads = 1024;           // sixteen waves share one row block
 constexpr int kDcWaves = kDcThreads / kWave;
 constexpr int kDcLoadsPerSlot = 2;         // one b128 code load and one b16 scale load
 constexpr int kDcHLoads = kDcMaxLds / 16 / kDcThreads;   // 16-byte h pieces per thread
+// Shared-expert down row `row` (weights w: NC chunks of this lane) for every
+// token, its h read from LDS (s_hs: [T, Is] bf16): the products and the
+// fixed-order lane sum of se_down_rows, kSeTokens tokens' sums in flight
+// together.
+template <int NC>
+__device__ __forceinline__ void se_down_row_lds(const SharedRows& sr, const u32x4 (&wv)[2], const uint8_t* s_hs,
+                                                int row, int lane) {
+  // the row's registers pass through an empty asm statement before the token
+  // loop, so that the wait for its loads is placed here, in straight-line
+  // code, with an exact count (for a use inside the loop the compiler waits
+  // for every load in flight, the slots' weight rows included)
+  u32x4 w[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    w[c] = wv[c];
+    asm volatile("" : "+v"(w[c]));
+  }
+  const size_t rb = (size_t)sr.Is * 2;
+  auto pass = [&](int t0) {
+    float acc[kSeTokens];
+#pragma unroll
+    for (int j = 0; j < kSeTokens; ++j) {
+      const uint8_t* hr = s_hs + (size_t)min(t0 + j, sr.T - 1) * rb + (size_t)lane * 16;
+      u32x4 hv[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) hv[c] = *reinterpret_cast<const u32x4*>(hr + c * 64 * 16);
+      acc[j] = se_dot<NC>(w, hv);
+    }
+#pragma unroll
+    for (int j = 0; j < kSeTokens; ++j) {
+      const float ys = wave_sum_xor(acc[j]);
+      if (lane == 0 && t0 + j < sr.T && row < sr.H) sr.y[(size_t)(t0 + j) * sr.H + row] = (uint16_t)f32_to_bf16_rne(ys);
+    }
+  };
+  // up to kSeTokens tokens (the decode batches) in straight-line code: in a
+  // loop the compiler would wait for every load in flight before its first
+  // iteration, the slots' weight rows included
+  if (sr.T <= kSeTokens) {
+    pass(0);
+  } else {
+    for (int t0 = 0; t0 < sr.T; t0 += kSeTokens) pass(t0);
+  }
+}
+
+// Byte offset of a shared expert's h in the route-slot down/unroute's LDS:
+// after the routes' h ([R, I] bf16) and o ([R, rpw] fp32), 16-byte aligned.
+__host__ __device__ inline size_t dc_se_h_offset(int R, int I, int rpw) {
+  return ((size_t)R * I * 2 + (size_t)R * rpw * 4 + 15) & ~(size_t)15;
+}
 
 // Down projection and weighted unroute of a small batch in one kernel, with
 // the work split by output rows instead of by expert: workgroup b owns rows
@@ -1253,8 +1309,14 @@ constexpr int kDcHLoads = kDcMaxLds / 16 / kDcThreads;   // 16-byte h pieces per
 //
 // Route slots (RS, after select_gate_up_kernel): slot a is route a itself
 // (expert topk_idx[a], h row a, one route), so the buckets are not needed.
-template <int LD, int SLOTS, bool RS = false>
+// A shared expert's down rows can ride along there (SE): the last rpw waves
+// each take output row row0 + i of it, loading that weight row ahead of
+// their slots' rows and summing it first; the shared h (T x Is bf16) is
+// staged in LDS behind o with the routes' h.  Each row is summed as
+// se_down_rows sums it.
+template <int LD, int SLOTS, bool RS = false, bool SE = false>
 __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_kernel(FfnParams p) {
+  static_assert(RS || !SE, "shared rows ride along in route-slot mode only");
   extern __shared__ __align__(16) uint8_t s_dyn8[];   // [R, I] bf16 h, then [R, rpw] fp32 o
   __shared__ int s_src[kDcMaxRoutes];
   __shared__ float s_w[kDcMaxRoutes];
@@ -1278,6 +1340,29 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
     hv[i] = u32x4{0u, 0u, 0u, 0u};
     if ((uint32_t)(wave * kWave + i * kDcThreads) * 16 < h_bytes)
       hv[i] = __builtin_amdgcn_raw_buffer_load_b128(rh, (uint32_t)(tid + i * kDcThreads) * 16, 0, 0);
+  }
+  // the shared expert's h, one piece per thread, and the shared down row of
+  // each of the last rpw waves (one or two chunks per lane), ahead of the
+  // routes' weights
+  const uint32_t se_hbytes = SE ? (uint32_t)p.T * (uint32_t)p.sr.Is * 2u : 0u;
+  const int se_w0 = kDcWaves - rpw;
+  const bool se_wave = SE && wave >= se_w0;
+  const int se_row = row0 + wave - se_w0;
+  u32x4 se_hv = u32x4{0u, 0u, 0u, 0u};
+  u32x4 se_w[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+  if constexpr (SE) {
+    // issued by every thread, past the buffer where there is nothing to read
+    // (zeros, no memory traffic), so that the wait counts stay exact
+    constexpr uint32_t kOff = 0x80000000u;
+    se_hv = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(p.sr.h, se_hbytes),
+                                                  (uint32_t)tid * 16 < se_hbytes ? (uint32_t)tid * 16 : kOff, 0, 0);
+    const uint32_t se_rb = (uint32_t)p.sr.Is * 2u;
+    const auto rsd = make_rsrc(p.sr.wd, (uint32_t)p.H * se_rb);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      se_w[c] = __builtin_amdgcn_raw_buffer_load_b128(
+          rsd, se_wave && c < p.sr.dn_nc ? (uint32_t)se_row * se_rb + (uint32_t)(lane + 64 * c) * 16u : kOff, 0,
+          kStreamAux);
   }
   // route positions and gate weights (an index past R re-reads the last)
   const int rt = min(tid, R - 1);
@@ -1338,9 +1423,18 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
     s_src[tid] = min(max(src_r, 0), R - 1);
     s_w[tid] = w_r;
   }
+  uint8_t* const s_hs = s_dyn8 + dc_se_h_offset(R, p.I, rpw);   // the shared expert's h
+  if (SE && (uint32_t)tid * 16 < se_hbytes) *reinterpret_cast<u32x4*>(s_hs + tid * 16) = se_hv;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();                // h of every route is in LDS; weights still in flight
   compiler_fence();
+
+  if (se_wave) {
+    // y_shared[t, se_row] = bf16(W_down[se_row] . h_shared[t]), as se_down_rows
+    // sums it; its row was loaded ahead of the slots' rows
+    if (p.sr.dn_nc == 1) se_down_row_lds<1>(p.sr, se_w, s_hs, se_row, lane);
+    else se_down_row_lds<2>(p.sr, se_w, s_hs, se_row, lane);
+  }
 
   const bool row_ok = row0 + sub < p.H;
 #pragma unroll
@@ -1368,14 +1462,14 @@ __global__ __launch_bounds__(kDcThreads, SLOTS <= 4 ? 2 : 1) void down_combine_k
   }
 }
 
-template <int LD, bool RS = false>
+template <int LD, bool RS = false, bool SE = false>
 void launch_down_combine(const FfnParams& p, unsigned grid, size_t dyn, int slots, hipStream_t s) {
   const int per_wave = (slots + kDcWaves - 1) / kDcWaves;
-  if (per_wave <= 1) down_combine_kernel<LD, 1, RS><<<grid, kDcThreads, dyn, s>>>(p);
-  else if (per_wave == 2) down_combine_kernel<LD, 2, RS><<<grid, kDcThreads, dyn, s>>>(p);
-  else if (per_wave == 3) down_combine_kernel<LD, 3, RS><<<grid, kDcThreads, dyn, s>>>(p);
-  else if (per_wave == 4) down_combine_kernel<LD, 4, RS><<<grid, kDcThreads, dyn, s>>>(p);
-  else down_combine_kernel<LD, kDcMaxRoutes / kDcWaves, RS><<<grid, kDcThreads, dyn, s>>>(p);
+  if (per_wave <= 1) down_combine_kernel<LD, 1, RS, SE><<<grid, kDcThreads, dyn, s>>>(p);
+  else if (per_wave == 2) down_combine_kernel<LD, 2, RS, SE><<<grid, kDcThreads, dyn, s>>>(p);
+  else if (per_wave == 3) down_combine_kernel<LD, 3, RS, SE><<<grid, kDcThreads, dyn, s>>>(p);
+  else if (per_wave == 4) down_combine_kernel<LD, 4, RS, SE><<<grid, kDcThreads, dyn, s>>>(p);
+  else down_combine_kernel<LD, kDcMaxRoutes / kDcWaves, RS, SE><<<grid, kDcThreads, dyn, s>>>(p);
 }
 
 // ------------------------------------------------------------------ rows of several chunks per lane
@@ -2121,8 +2215,8 @@ bool small_step_ok(int T, int H, int I, int E, int k) {
 // select_gate_up_nc_kernel<.., nc> (compiled for nc = 1..6 and 8)
 template <int V, int KC>
 void launch_select_gate_up(int nc, const FfnParams& p, const float* logits, const float* bias, int32_t* topk_idx,
-                           float* topk_w, int tasks, hipStream_t s) {
-  const unsigned grid = (unsigned)tasks + 1;
+                           float* topk_w, int tasks, int extra, hipStream_t s) {
+  const unsigned grid = (unsigned)tasks + 1 + (unsigned)extra;
   switch (nc) {
     case 0: select_gate_up_kernel<V, KC><<<grid, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks); break;
     case 1: select_gate_up_nc_kernel<V, KC, 1><<<grid, kThreads, 0, s>>>(p, logits, bias, topk_idx, topk_w, tasks); break;
@@ -2137,9 +2231,23 @@ void launch_select_gate_up(int nc, const FfnParams& p, const float* logits, cons
 
 template <int V>
 void launch_select_gate_up_k(int k, int nc, const FfnParams& p, const float* logits, const float* bias,
-                             int32_t* topk_idx, float* topk_w, int tasks, hipStream_t s) {
-  if (k == 10) launch_select_gate_up<V, 10>(nc, p, logits, bias, topk_idx, topk_w, tasks, s);
-  else launch_select_gate_up<V, 0>(nc, p, logits, bias, topk_idx, topk_w, tasks, s);
+                             int32_t* topk_idx, float* topk_w, int tasks, int extra, hipStream_t s) {
+  if (k == 10) launch_select_gate_up<V, 10>(nc, p, logits, bias, topk_idx, topk_w, tasks, extra, s);
+  else launch_select_gate_up<V, 0>(nc, p, logits, bias, topk_idx, topk_w, tasks, extra, s);
+}
+
+// A shared expert's rows ride along in the small step (gate/up rows in the
+// selection launch, down rows in the route-slot down/unroute) when the
+// step's rows are of one chunk per lane (H = 2048), the shared rows of H =
+// 2048 and Is = 512 or 1024, each down/unroute workgroup's rows fit its
+// waves, and the shared h joins the LDS of the down/unroute.
+bool small_step_side_ok(int T, int H, int I, int E, int k, const SharedRows& sr) {
+  if (!small_step_ok(T, H, I, E, k) || H != 64 * 32 || nc_chunks(I / 32) != 0) return false;
+  if (sr.gu_nc != 4 || (sr.dn_nc != 1 && sr.dn_nc != 2) || sr.T != T || sr.H != H) return false;
+  const int R = T * k, rpw = kWave / lanes_per_row(I / 32);
+  const size_t hs_bytes = (size_t)T * sr.Is * 2;
+  return rpw <= kDcWaves && hs_bytes <= (size_t)kDcThreads * 16 &&
+         dc_se_h_offset(R, I, rpw) + hs_bytes <= (size_t)kDcMaxLds;
 }
 
 moe_status small_step(const uint16_t* x, const float* logits, const float* bias, const uint8_t* w_gate,
@@ -2147,7 +2255,7 @@ moe_status small_step(const uint16_t* x, const float* logits, const float* bias,
                       const uint8_t* s_down, const float* g_scale, int T, int H, int I, int E, int k,
                       int32_t* topk_idx, float* topk_w, int32_t* expert_count, int32_t* expert_offset,
                       int32_t* active_experts, int32_t* n_active, int32_t* route_src, int32_t* route_pos,
-                      void* workspace, uint16_t* y, hipStream_t s, int stage) {
+                      void* workspace, uint16_t* y, hipStream_t s, int stage, const SharedRows* side) {
   const WorkspaceLayout L = workspace_layout(T, H, I, E, k);
   FfnParams p{};
   p.x = x; p.wg = w_gate; p.sg = s_gate; p.wu = w_up; p.su = s_up; p.wd = w_down; p.sd = s_down;
@@ -2159,7 +2267,7 @@ moe_status small_step(const uint16_t* x, const float* logits, const float* bias,
   p.h = reinterpret_cast<uint16_t*>(ws + L.h_off);
   p.o = reinterpret_cast<uint16_t*>(ws + L.o_off);
   p.y = y;
-  p.sr = SharedRows{};
+  p.sr = side ? *side : SharedRows{};       // the caller has checked small_step_side_ok
   const int nc_gu = H == 64 * 32 ? 0 : nc_chunks(H / 32), nc_d = nc_chunks(I / 32);
   p.lr_gu = nc_gu ? kNcLanes : 64;
   p.lr_d = nc_d ? kNcLanes : lanes_per_row(I / 32);
@@ -2169,22 +2277,27 @@ moe_status small_step(const uint16_t* x, const float* logits, const float* bias,
   const int tiles = (I + kWavesPerBlock * kGuUnits - 1) / (kWavesPerBlock * kGuUnits);
   const int tasks = R * tiles;                       // and one routing workgroup after them
   const int V = (E + kWave - 1) / kWave;
+  // the shared expert's gate/up rows: one workgroup per four rows after the routing workgroup
+  const int se_blocks = side ? (side->Is + kWavesPerBlock - 1) / kWavesPerBlock : 0;
   if (stage & 1) {
-    if (V <= 1) launch_select_gate_up_k<1>(k, nc_gu, p, logits, bias, topk_idx, topk_w, tasks, s);
-    else if (V <= 2) launch_select_gate_up_k<2>(k, nc_gu, p, logits, bias, topk_idx, topk_w, tasks, s);
-    else if (V <= 4) launch_select_gate_up_k<4>(k, nc_gu, p, logits, bias, topk_idx, topk_w, tasks, s);
-    else launch_select_gate_up_k<8>(k, nc_gu, p, logits, bias, topk_idx, topk_w, tasks, s);
+    if (V <= 1) launch_select_gate_up_k<1>(k, nc_gu, p, logits, bias, topk_idx, topk_w, tasks, se_blocks, s);
+    else if (V <= 2) launch_select_gate_up_k<2>(k, nc_gu, p, logits, bias, topk_idx, topk_w, tasks, se_blocks, s);
+    else if (V <= 4) launch_select_gate_up_k<4>(k, nc_gu, p, logits, bias, topk_idx, topk_w, tasks, se_blocks, s);
+    else launch_select_gate_up_k<8>(k, nc_gu, p, logits, bias, topk_idx, topk_w, tasks, se_blocks, s);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
   if (!(stage & 2)) return MOE_OK;
   // route-slot down/unroute over rows of y
   const int rpw = kWave / p.lr_d;
   const size_t h_bytes = (size_t)R * I * 2;
-  const size_t dyn = (nc_d ? dc_nc_h_lds((uint32_t)h_bytes) : h_bytes) + (size_t)R * rpw * 4;
+  const size_t dyn = side ? dc_se_h_offset(R, I, rpw) + (size_t)T * side->Is * 2
+                          : (nc_d ? dc_nc_h_lds((uint32_t)h_bytes) : h_bytes) + (size_t)R * rpw * 4;
   const unsigned grid = (unsigned)((H + rpw - 1) / rpw);
   if (nc_d) {
     if (!launch_down_combine_nc<true>(nc_d, p, grid, dyn, R, s)) return MOE_ERR_UNSUPPORTED;
   }
+  else if (side && p.lr_d == 16) launch_down_combine<16, true, true>(p, grid, dyn, R, s);
+  else if (side) launch_down_combine<0, true, true>(p, grid, dyn, R, s);
   else if (p.lr_d == 16) launch_down_combine<16, true>(p, grid, dyn, R, s);
   else launch_down_combine<0, true>(p, grid, dyn, R, s);
   return launch_status();

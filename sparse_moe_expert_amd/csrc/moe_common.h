@@ -169,13 +169,17 @@ moe_status route_bucket(const float* logits, const float* bias, int T, int E, in
 // for the routing outputs), then the route-slot down/unroute.
 // Outputs identical to route_bucket + expert_ffn.  Arguments already checked.
 // stage 1: the selection and gate/up launch only; 2: the down/unroute launch
-// only (after stage 1 on the same workspace); 3: both.
+// only (after stage 1 on the same workspace); 3: both.  `side`: a shared
+// expert whose rows ride along (small_step_side_ok), or null.
 bool small_step_ok(int T, int H, int I, int E, int k);
+// Whether a shared expert's rows can ride along in the small step's launches.
+bool small_step_side_ok(int T, int H, int I, int E, int k, const SharedRows& sr);
 moe_status small_step(const uint16_t* x, const float* logits, const float* bias, const uint8_t* w_gate,
                       const uint8_t* s_gate, const uint8_t* w_up, const uint8_t* s_up, const uint8_t* w_down,
                       const uint8_t* s_down, const float* g_scale, int T, int H, int I, int E, int k,
                       int32_t* topk_idx, float* topk_w, int32_t* expert_count, int32_t* expert_offset,
                       int32_t* active_experts, int32_t* n_active, int32_t* route_src, int32_t* route_pos,
-                      void* workspace, uint16_t* y, hipStream_t s, int stage = 3);
+                      void* workspace, uint16_t* y, hipStream_t s, int stage = 3,
+                      const SharedRows* side = nullptr);
 
 }  // namespace moe

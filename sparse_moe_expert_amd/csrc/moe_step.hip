@@ -71,11 +71,12 @@ static moe_status step(const uint16_t* x, const float* logits, const float* bias
   if (chk != MOE_OK || T == 0) return chk;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   // small batches: the selection and the routing outputs inside the gate/up
-  // launch (no routing kernel), then the route-slot down/unroute
-  if (!side && moe::small_step_ok(T, H, I, E, k))
+  // launch (no routing kernel), then the route-slot down/unroute; a shared
+  // expert's rows ride along in the same two launches where they fit
+  if (side ? moe::small_step_side_ok(T, H, I, E, k, *side) : moe::small_step_ok(T, H, I, E, k))
     return moe::small_step(x, logits, bias, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, T, H, I, E, k,
                            topk_idx, topk_w, expert_count, expert_offset, active_experts, n_active, route_src,
-                           route_pos, workspace, y, s, stage);
+                           route_pos, workspace, y, s, stage, side);
   if (stage == 2)                                  // the expert FFN's second stage (it rebuilds its work lists)
     return moe::expert_ffn(2, x, w_gate, s_gate, w_up, s_up, w_down, s_down, g_scale, topk_w, expert_count,
                            expert_offset, active_experts, n_active, route_src, route_pos, packed, T, H, I, E, k,
@@ -135,8 +136,10 @@ extern "C" moe_status moe_step_packed(const uint16_t* x, const float* logits, co
 // The step and a dense bf16 shared expert of the same tokens: y as
 // moe_step(_packed) computes it, y_shared as moe_shared_expert does, bit for
 // bit.  At decode sizes the shared expert's rows ride along in the step's own
-// launches (gate/up in the routing kernel, down in the gate/up row-dot
-// kernel) instead of two kernels of their own.
+// launches instead of two kernels of their own: in the small step (up to 40
+// routes at H = 2048) gate/up in the selection launch and down in the
+// route-slot down/unroute; otherwise gate/up in the routing kernel and down
+// in the gate/up row-dot kernel.
 extern "C" moe_status moe_step_shared(const uint16_t* x, const float* logits, const float* bias,
                                       const uint8_t* w_gate, const uint8_t* s_gate, const uint8_t* w_up,
                                       const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,

@@ -73,14 +73,21 @@ def _custom(T, H, I, E, k):
 
 
 # (workload, Is, packed): which of the shared expert's halves ride along in
-# the step's launches - decode_t4: both (512-thread routing workgroup);
-# T=12: both (1024-thread routing workgroup, two chunks per down row);
+# the step's launches - the small step (up to 40 routes at H = 2048):
+# gate/up rows in the selection launch, down rows in the last waves of the
+# route-slot down/unroute (decode_t4: 4 rows per workgroup, one chunk per
+# lane; T=1, Is=1024: two chunks per lane; I=256: 8 rows per workgroup, E=64;
+# I=1024: 2 rows per workgroup, 40 routes); T=3, Is=2048 (four chunks per
+# down row): the three-kernel step, down on its own.  T=12: both in the
+# three-kernel step (1024-thread routing workgroup, two chunks per down row);
 # verify_t32: gate/up on its own (routing takes several kernels), down in
 # the row-dot kernel; decode_t256_zipf packed: down on its own (no row-dot
 # kernel), standard layout: down beside the sorted row-dot experts; H=512,
 # Is=2048: gate/up with one chunk per row, down on its own (four chunks).
 STEP_SHARED_CASES = [
-    ("decode_t4", 512, True), ((12, 2048, 512, 512, 10), 1024, True), ("verify_t32", 512, True),
+    ("decode_t4", 512, True), ((1, 2048, 512, 512, 10), 1024, True), ((4, 2048, 256, 64, 8), 512, False),
+    ((2, 2048, 1024, 128, 20), 512, True), ((3, 2048, 512, 512, 10), 2048, True),
+    ((12, 2048, 512, 512, 10), 1024, True), ("verify_t32", 512, True),
     ("decode_t256_zipf", 512, True), ("decode_t256_zipf", 512, False), ((5, 512, 256, 64, 4), 2048, False),
 ]
 
@@ -161,3 +168,29 @@ def test_step_shared_graph_replays():
         assert torch.equal(ys.view(torch.int16), eager[name][1].view(torch.int16)), name
         torch.add(ys, 1.0)   # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_step_shared_small_guard_regions():
+    """The small step with the shared rows riding along (decode_t4, Is=1024):
+    canaries around y_shared and the shared workspace stay untouched, and
+    both outputs match the separate calls bit for bit."""
+    wl = make_workload("decode_t4", x_seed=23)
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    Is = 1024
+    wg, wu, wd = _weights(H, Is, seed=29)
+    gw, uw, dw = _dev_bf16(wg), _dev_bf16(wu), _dev_bf16(wd)
+    x, logits, W = x_bits(wl.x), to_dev(wl.logits), device_weights(wl.bank)
+    ref_step = sme.MoeStep(T, H, I, E, k, DEV, path="step")
+    ref_step.run(x, logits, None, W)
+    ref_shared = sme.moe_shared_expert(x, gw, uw, dw)
+    ws_bytes = sme.load_library().moe_shared_expert_workspace_size(T, H, Is)
+    big_ws = torch.full((ws_bytes + 512,), 0xA5, dtype=torch.uint8, device=DEV)
+    big_ys = torch.full((T + 2, H), 3.0, dtype=torch.bfloat16, device=DEV)
+    st = sme.MoeStep(T, H, I, E, k, DEV, path="step")
+    sme.moe_step_shared(x, logits, None, W, k, st.topk_idx, st.topk_w, st.buckets, st.workspace, st.y,
+                        (gw, uw, dw), big_ys[1: T + 1], big_ws[256: 256 + ws_bytes])
+    torch.cuda.synchronize()
+    assert torch.all(big_ws[:256] == 0xA5) and torch.all(big_ws[256 + ws_bytes:] == 0xA5)
+    assert torch.all(big_ys[0] == 3.0) and torch.all(big_ys[T + 1] == 3.0)
+    assert torch.equal(st.y.view(torch.int16), ref_step.y.view(torch.int16))
+    assert torch.equal(big_ys[1: T + 1].view(torch.int16), ref_shared.view(torch.int16))
