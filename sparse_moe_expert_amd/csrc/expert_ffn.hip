@@ -458,9 +458,11 @@ __global__ __launch_bounds__(kThreads, 4) void select_gate_up_kernel(FfnParams p
   const u32x4 xv =
       __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(p.x + (size_t)t * p.H, kSgXBytes), (uint32_t)tid * 16, 0, 0);
   compiler_fence();
-  if (g.wave == 0) {
+  if (g.wave == (int)(blockIdx.x & (kWavesPerBlock - 1))) {
     // only slot j's expert: the rounds of the selection up to round j (the
-    // routing workgroup writes the full top-k and its weights)
+    // routing workgroup writes the full top-k and its weights); the selecting
+    // wave rotates with the workgroup so that neighbouring workgroups' rounds
+    // run on different SIMDs
     const int e_j = select_slot<V, KC>(logits + (size_t)t * p.E, bias, p.E, j, lane);
     if (lane == 0) s_e = e_j;
   }
@@ -1595,8 +1597,9 @@ __global__ __launch_bounds__(kThreads, 2) void select_gate_up_nc_kernel(FfnParam
   for (int q = 0; q < kXLoads; ++q)
     xv[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(tid + q * kThreads) * 16, 0, 0);
   compiler_fence();
-  if (wave == 0) {
-    // only slot j's expert: the rounds of the selection up to round j
+  if (wave == (int)(blockIdx.x & (kWavesPerBlock - 1))) {
+    // only slot j's expert: the rounds of the selection up to round j (the
+    // selecting wave rotates with the workgroup, as in select_gate_up_kernel)
     const int e_j = select_slot<V, KC>(logits + (size_t)t * p.E, bias, p.E, j, lane);
     if (lane == 0) s_e = e_j;
   }
