@@ -77,7 +77,8 @@ def _custom(T, H, I, E, k):
 # gate/up rows in the selection launch, down rows in the last waves of the
 # route-slot down/unroute (decode_t4: 4 rows per workgroup, one chunk per
 # lane; T=1, Is=1024: two chunks per lane; I=256: 8 rows per workgroup, E=64;
-# I=1024: 2 rows per workgroup, 40 routes); T=3, Is=2048 (four chunks per
+# I=1024: 2 rows per workgroup, 40 routes; T=8, Is=1024: the shared h at the
+# 16 KB limit and the down rows' token loop); T=3, Is=2048 (four chunks per
 # down row): the three-kernel step, down on its own.  T=12: both in the
 # three-kernel step (1024-thread routing workgroup, two chunks per down row);
 # verify_t32: gate/up on its own (routing takes several kernels), down in
@@ -86,7 +87,8 @@ def _custom(T, H, I, E, k):
 # Is=2048: gate/up with one chunk per row, down on its own (four chunks).
 STEP_SHARED_CASES = [
     ("decode_t4", 512, True), ((1, 2048, 512, 512, 10), 1024, True), ((4, 2048, 256, 64, 8), 512, False),
-    ((2, 2048, 1024, 128, 20), 512, True), ((3, 2048, 512, 512, 10), 2048, True),
+    ((2, 2048, 1024, 128, 20), 512, True), ((8, 2048, 512, 512, 5), 1024, True),
+    ((3, 2048, 512, 512, 10), 2048, True),
     ((12, 2048, 512, 512, 10), 1024, True), ("verify_t32", 512, True),
     ("decode_t256_zipf", 512, True), ("decode_t256_zipf", 512, False), ((5, 512, 256, 64, 4), 2048, False),
 ]
