@@ -83,12 +83,15 @@ struct FfnParams {
   int lr_d;      // lanes per down row
   int mfma_min;  // experts with at least this many routes take the MFMA kernels (0: none do)
   const uint8_t* packed;   // the weights also in MFMA tile order (moe_pack_weights), or null
-  int32_t* plan;           // workspace: MFMA work items (plan_kernel), see there
+  int32_t* plan;           // workspace: MFMA work items (plan_kernel), see there; gate/up's
+  int32_t* plan_down;      // workspace: the down MFMA kernels' items (chunks of up to 128 routes)
   int plan_max;            // capacity of the item list
   int32_t* rd_list;        // workspace: row-dot experts, most routes first (plan_kernel)
   int rd_plan;             // the row-dot kernels take their experts from rd_list
   int32_t* queues;         // workspace: unit counters of the streaming down kernel
   SharedRows sr;           // shared-expert down rows riding along in gate_up_kernel (dn_nc 0: none)
+  int layer_items;         // MFMA gate/up: items per XCD that fill its CUs once (0: list order)
+  int split_items;         // work lists: items of at most 64 routes up to this many (WorkLists)
 };
 
 constexpr int kGuUnits = 4;          // gate rows (and as many up rows) per wave per tile
@@ -730,6 +733,27 @@ struct MmTile {
   }
 };
 
+// Item order per XCD.  Workgroups reach an XCD's compute units in index
+// order, one per CU first (a layer of L = CUs / row tiles items), then a
+// second one beside the first ones.  When an XCD has between L and 2L items
+// (one round, some CUs shared), item slot s of the second layer shares the
+// CUs of slot s - L of the first, and the first-layer slots D .. L - 1 (D =
+// items - L) keep their CUs to themselves.  Those go to the D..L-1 longest
+// items (the list runs longest first), so that no long item shares its CUs
+// with another: a CU running two workgroups gives each about half its issue
+// slots, and a long item's partner set the launch's span at 256
+// Zipf-routed tokens.  Returns the list rank of item slot s on XCD xcd; a
+// bijection on 0 .. items-1, so the items computed do not change.
+__device__ __forceinline__ int mfma_item_rank(int s, int xcd, int n_items, int L) {
+  if (L <= 0) return s;
+  const int items = (n_items - xcd + kXcds - 1) / kXcds;   // items of this XCD
+  if (items <= L || items > 2 * L) return s;
+  const int D = items - L;
+  if (s < D) return s + (L - D);       // first layer, shared with a second-layer slot
+  if (s < L) return s - D;             // first layer, alone: the longest items
+  return s;                            // second layer
+}
+
 template <bool GU, bool PACKED, int NSUB>
 __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
   static_assert(GU ? NSUB == 1 : (NSUB == 1 || PACKED), "several row tiles per wave: down on packed weights");
@@ -754,14 +778,16 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_kernel(FfnParams p) {
   // j % tiles_n: the tiles of one item share an XCD, and the items (longest
   // first) start in plan order
   const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-  const int it = (j / tiles_n) * kXcds + xcd, n0 = (j % tiles_n) * kWgRows;
   // the item is read together with the count (the list has room for every
   // item index of the grid), so the head costs one round of scalar loads
-  const int n_items = min(sload(p.plan, 0), p.plan_max);
+  const int32_t* const plan = GU ? p.plan : p.plan_down;
+  const int n_items = min(sload(plan, 0), p.plan_max);
+  const int it = mfma_item_rank(j / tiles_n, xcd, n_items, GU ? p.layer_items : 0) * kXcds + xcd;
+  const int n0 = (j % tiles_n) * kWgRows;
   const int R = p.T * p.k;
-  const int e = min(max(sload(p.plan, 4 + 4 * it), 0), p.E - 1);
-  const int off = min(max(sload(p.plan, 5 + 4 * it), 0), R);
-  const int cnt = min(max(sload(p.plan, 6 + 4 * it), 0), min(kMmRoutes, R - off));
+  const int e = min(max(sload(plan, 4 + 4 * it), 0), p.E - 1);
+  const int off = min(max(sload(plan, 5 + 4 * it), 0), R);
+  const int cnt = min(max(sload(plan, 6 + 4 * it), 0), min(kMmRoutes, R - off));
   if (it >= n_items || cnt <= 0) return;
 
   Tile t;
@@ -994,7 +1020,7 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_down_stream_kernel(Ffn
   const int steps = K / kMmK;
   const int cls = blockIdx.x % kXcds;
   int32_t* const ctr = queue + cls * kQueueStride;
-  const int n_items = min(sload(p.plan, 0), p.plan_max);
+  const int n_items = min(sload(p.plan_down, 0), p.plan_max);
   const int R = p.T * p.k;
   const size_t mat = packed_matrix_bytes(N, K), codes = packed_code_bytes(N, K);
   const uint8_t* const mbase = p.packed + 2 * (size_t)p.E * packed_matrix_bytes(p.I, p.H);
@@ -1008,9 +1034,9 @@ __global__ __launch_bounds__(kMmThreads, 2) void ffn_mfma_down_stream_kernel(Ffn
     Unit w = {0, 0, 0, 0};
     const int it = (u / tiles_n) * kXcds + cls;
     if (u >= 0 && it < n_items) {
-      w.e = min(max(sload(p.plan, 4 + 4 * it), 0), p.E - 1);
-      w.off = min(max(sload(p.plan, 5 + 4 * it), 0), R);
-      w.cnt = min(max(sload(p.plan, 6 + 4 * it), 0), min(kMmRoutes, R - w.off));
+      w.e = min(max(sload(p.plan_down, 4 + 4 * it), 0), p.E - 1);
+      w.off = min(max(sload(p.plan_down, 5 + 4 * it), 0), R);
+      w.cnt = min(max(sload(p.plan_down, 6 + 4 * it), 0), min(kMmRoutes, R - w.off));
       w.n0 = (u % tiles_n) * kWgRows;
     }
     return w;
@@ -1177,6 +1203,8 @@ __global__ __launch_bounds__(kWlThreads) void plan_kernel(FfnParams p) {
   wl.mfma_min = p.mfma_min;
   wl.rd_plan = p.rd_plan;
   wl.queues = p.queues;
+  wl.split_items = p.split_items;
+  wl.plan_down = p.plan_down;
   build_work_lists(wl, sh, e, cnt, off);
 }
 
@@ -1891,7 +1919,7 @@ bool launch_down_combine_nc(int nc, const FfnParams& p, unsigned grid, size_t dy
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WorkspaceLayout {
-  size_t h_off, o_off, plan_off, rd_off, q_off, total;   // h [R, I] bf16, o [R, H] fp16, MFMA work plan, row-dot list, unit counters
+  size_t h_off, o_off, plan_off, plan_down_off, rd_off, q_off, total;   // h [R, I] bf16, o [R, H] fp16, MFMA work plans (gate/up, down), row-dot list, unit counters
   int plan_max;
 };
 
@@ -1905,7 +1933,8 @@ WorkspaceLayout workspace_layout(int T, int H, int I, int E, int k) {
   // the list has room for a multiple of 8 items (the MFMA grids' bound)
   L.plan_max = (int)(std::min<size_t>((size_t)E, R) + R / kMmRoutes);
   const size_t cap = ((size_t)L.plan_max + kXcds - 1) / kXcds * kXcds;
-  L.rd_off = L.plan_off + align256((4 + 4 * cap) * 4);
+  L.plan_down_off = L.plan_off + align256((4 + 4 * cap) * 4);
+  L.rd_off = L.plan_down_off + align256((4 + 4 * cap) * 4);
   // the row-dot list: its length and one expert per slot
   L.q_off = L.rd_off + align256((1 + std::min<size_t>((size_t)E, R)) * 4);
   L.total = L.q_off + align256((size_t)kWlQueueInts * 4);
@@ -1987,6 +2016,15 @@ struct FfnPolicy {
   bool rd_plan;        // row-dot kernels read the sorted expert list
 };
 
+// Largest item count for which the MFMA work lists halve their route chunks:
+// the items whose gate/up row tiles fill every compute unit twice (two
+// workgroups per CU), within the list's capacity; 0 when no MFMA kernel runs.
+int mfma_split_items(const FfnPolicy& f, int I, int plan_max) {
+  if (!f.mfma) return 0;
+  const int tiles_gu = (I + kMmRows - 1) / kMmRows;
+  return std::min(plan_max, 2 * device_cu_count() / tiles_gu);
+}
+
 FfnPolicy ffn_policy(int T, int H, int I, int E, int k, bool packed) {
   FfnPolicy f;
   const long long R = (long long)T * k;
@@ -2030,6 +2068,8 @@ bool ffn_work_lists(int T, int H, int I, int E, int k, bool packed, void* worksp
   wl->mfma_min = f.mfma_min;
   wl->rd_plan = f.rd_plan ? 1 : 0;
   wl->queues = reinterpret_cast<int32_t*>(ws + L.q_off);
+  wl->split_items = mfma_split_items(f, I, L.plan_max);
+  wl->plan_down = reinterpret_cast<int32_t*>(ws + L.plan_down_off);
   *scratch_bytes = L.plan_off;
   return f.mfma || f.rd_plan;
 }
@@ -2072,6 +2112,7 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   p.h = reinterpret_cast<uint16_t*>(ws + L.h_off);
   p.o = reinterpret_cast<uint16_t*>(ws + L.o_off);
   p.plan = reinterpret_cast<int32_t*>(ws + L.plan_off);
+  p.plan_down = reinterpret_cast<int32_t*>(ws + L.plan_down_off);
   p.plan_max = L.plan_max;
   p.rd_list = reinterpret_cast<int32_t*>(ws + L.rd_off);
   p.queues = reinterpret_cast<int32_t*>(ws + L.q_off);
@@ -2080,12 +2121,19 @@ moe_status expert_ffn(int stage, const uint16_t* x, const uint8_t* w_gate, const
   p.lr_gu = lr_gu;
   p.lr_d = lr_d;
   p.packed = packed;
+  // MFMA gate/up items per XCD that fill its compute units once
+  {
+    const int cus_per_xcd = device_cu_count() / kXcds;
+    const int tiles_gu = (I + kMmRows - 1) / kMmRows;
+    p.layer_items = (cus_per_xcd > 0 && cus_per_xcd % tiles_gu == 0) ? cus_per_xcd / tiles_gu : 0;
+  }
   const long long R = (long long)T * k;
   const size_t h_bytes = (size_t)R * I * 2;
   const FfnPolicy pol = ffn_policy(T, H, I, E, k, packed != nullptr);
   const bool down_combine = pol.down_combine, mfma = pol.mfma, row_dots = pol.row_dots;
   p.mfma_min = pol.mfma_min;
   p.rd_plan = pol.rd_plan ? 1 : 0;
+  p.split_items = mfma_split_items(pol, I, L.plan_max);
 
   const long long slots = std::min<long long>(E, (long long)T * k);
   const int rpt_gu = nc_gu ? kWavesPerBlock * kNcRowsPerWave : kWavesPerBlock * (kWave / lr_gu) * kGuUnits;

@@ -104,6 +104,8 @@ struct WorkLists {
   int mfma_min;       // experts with at least this many routes take the MFMA kernels (0: none do)
   int rd_plan;        // the row-dot kernels read rd_list
   int32_t* queues;    // unit counters of the streaming down kernel (zeroed with the lists), or null
+  int split_items;    // gate/up MFMA items take at most 64 routes when that makes at most this many items (0: never)
+  int32_t* plan_down; // the down MFMA kernels' items, always chunks of up to 128 routes (layout of plan)
 };
 
 // A dense bf16 shared expert computed within a routed step (moe_step_shared):

@@ -9,6 +9,13 @@
 // route tiles of 32, the full chunks first, so that workgroups, which start
 // in list order, begin with the longest items, and an expert with several
 // chunks has them side by side.  plan[0] = item count; items from plan[4].
+// When chunks of half that size (64 routes) still make at most
+// wl.split_items items, the gate/up list's chunks are halved: a batch that
+// fills the device's workgroup slots once (256 Zipf-routed tokens) then has
+// no item of three or four route tiles, whose step time set the span of the
+// whole launch.  The down kernels' list (plan_down, same layout) keeps
+// chunks of up to kWlRoutes routes: their row tiles outnumber the slots
+// already, and halved items would add a partial round.
 //
 // Row-dot list (rd_plan): the experts with fewer routes than mfma_min (all
 // experts when no MFMA kernel runs), most routes first - a counting sort
@@ -33,14 +40,36 @@ constexpr int kRdBins = 64;
 
 struct WorkListShared {
   int cnt[4], base[4];
+  int cnt_d[4], base_d[4];          // the down list's classes
   int rh[kRdBins];
+  int n_half;                       // items with chunks of kWlRoutes / 2 routes
 };
+
+// Items of one expert's mcnt routes in chunks of cs: `full` whole chunks and
+// a rest; their classes (0: four route tiles .. 3: one) and list slots.
+__device__ __forceinline__ void wl_chunks(int mcnt, int cs, int& full, int& rest, int& full_cls, int& rest_cls) {
+  full = mcnt / cs;
+  rest = mcnt - full * cs;
+  full_cls = 4 - cs / 32;
+  rest_cls = rest > 0 ? 4 - ((rest + 31) >> 5) : -1;
+}
+
+__device__ __forceinline__ void wl_write(int4* items, int plan_max, int b_full, int b_rest, int e, int off, int cs,
+                                         int full, int rest, int rest_cls) {
+  for (int c = 0; c < full; ++c)
+    if (b_full + c < plan_max) items[b_full + c] = make_int4(e, off + c * cs, cs, 0);
+  if (rest_cls >= 0 && b_rest < plan_max) items[b_rest] = make_int4(e, off + full * cs, rest, 0);
+}
 
 // Called by all kWlThreads threads of the workgroup, in uniform control flow;
 // thread t brings expert e (or -1) with cnt routes from bucket position off.
 __device__ __forceinline__ void build_work_lists(const WorkLists& wl, WorkListShared& sh, int e, int cnt, int off) {
   const int tid = threadIdx.x;
-  if (tid < 4) sh.cnt[tid] = 0;
+  if (tid < 4) {
+    sh.cnt[tid] = 0;
+    sh.cnt_d[tid] = 0;
+  }
+  if (tid == 0) sh.n_half = 0;
   if (wl.queues && tid < kWlQueueInts / kWlQueueStride) wl.queues[tid * kWlQueueStride] = 0;
   if (tid < kRdBins) sh.rh[tid] = 0;
   __syncthreads();
@@ -49,20 +78,33 @@ __device__ __forceinline__ void build_work_lists(const WorkLists& wl, WorkListSh
     if (wl.mfma_min > 0 && cnt >= wl.mfma_min) mcnt = cnt;
     else rcnt = cnt;
   }
-  const int full = mcnt / kWlRoutes, rest = mcnt - full * kWlRoutes;
-  const int rest_cls = rest > 0 ? 4 - ((rest + 31) >> 5) : -1;   // 0: four route tiles .. 3: one
-  if (full > 0) atomicAdd(&sh.cnt[0], full);
+  constexpr int kHalf = kWlRoutes / 2;
+  if (wl.split_items > 0 && mcnt > 0) atomicAdd(&sh.n_half, (mcnt + kHalf - 1) / kHalf);
+  __syncthreads();
+  const int cs = (wl.split_items > 0 && sh.n_half <= wl.split_items) ? kHalf : kWlRoutes;   // uniform
+  int full, rest, full_cls, rest_cls;
+  wl_chunks(mcnt, cs, full, rest, full_cls, rest_cls);
+  if (full > 0) atomicAdd(&sh.cnt[full_cls], full);
   if (rest_cls >= 0) atomicAdd(&sh.cnt[rest_cls], 1);
+  int full_d, rest_d, full_cls_d, rest_cls_d;
+  wl_chunks(mcnt, kWlRoutes, full_d, rest_d, full_cls_d, rest_cls_d);
+  if (wl.plan_down) {
+    if (full_d > 0) atomicAdd(&sh.cnt_d[full_cls_d], full_d);
+    if (rest_cls_d >= 0) atomicAdd(&sh.cnt_d[rest_cls_d], 1);
+  }
   const int rbin = kRdBins - 1 - min(rcnt, kRdBins - 1);          // 0: most routes
   if (wl.rd_plan && rcnt > 0) atomicAdd(&sh.rh[rbin], 1);
   __syncthreads();
   if (tid == 0) {
-    int t = 0;
+    int t = 0, td = 0;
     for (int c = 0; c < 4; ++c) {
       sh.base[c] = t;
       t += sh.cnt[c];
+      sh.base_d[c] = td;
+      td += sh.cnt_d[c];
     }
     wl.plan[0] = min(t, wl.plan_max);
+    if (wl.plan_down) wl.plan_down[0] = min(td, wl.plan_max);
   }
   if (wl.rd_plan && tid < kWave) {
     // exclusive scan of the bins, one per lane
@@ -78,15 +120,16 @@ __device__ __forceinline__ void build_work_lists(const WorkLists& wl, WorkListSh
   }
   __syncthreads();
   if (wl.rd_plan && rcnt > 0) wl.rd_list[1 + atomicAdd(&sh.rh[rbin], 1)] = e;
-  int4* items = reinterpret_cast<int4*>(wl.plan + 4);
-  if (full > 0) {
-    const int b = atomicAdd(&sh.base[0], full);
-    for (int c = 0; c < full; ++c)
-      if (b + c < wl.plan_max) items[b + c] = make_int4(e, off + c * kWlRoutes, kWlRoutes, 0);
+  if (full > 0 || rest_cls >= 0) {
+    const int bf = full > 0 ? atomicAdd(&sh.base[full_cls], full) : 0;
+    const int br = rest_cls >= 0 ? atomicAdd(&sh.base[rest_cls], 1) : 0;
+    wl_write(reinterpret_cast<int4*>(wl.plan + 4), wl.plan_max, bf, br, e, off, cs, full, rest, rest_cls);
   }
-  if (rest_cls >= 0) {
-    const int b = atomicAdd(&sh.base[rest_cls], 1);
-    if (b < wl.plan_max) items[b] = make_int4(e, off + full * kWlRoutes, rest, 0);
+  if (wl.plan_down && (full_d > 0 || rest_cls_d >= 0)) {
+    const int bf = full_d > 0 ? atomicAdd(&sh.base_d[full_cls_d], full_d) : 0;
+    const int br = rest_cls_d >= 0 ? atomicAdd(&sh.base_d[rest_cls_d], 1) : 0;
+    wl_write(reinterpret_cast<int4*>(wl.plan_down + 4), wl.plan_max, bf, br, e, off, kWlRoutes, full_d, rest_d,
+             rest_cls_d);
   }
 }
 
