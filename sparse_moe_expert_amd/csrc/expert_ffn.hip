@@ -83,7 +83,7 @@ struct FfnParams {
   int lr_d;      // lanes per down row
   int mfma_min;  // experts with at least this many routes take the MFMA kernels (0: none do)
   const uint8_t* packed;   // the weights also in MFMA tile order (moe_pack_weights), or null
-  int32_t* plan;           // workspace: MFMA work items (plan_kernel), see there; gate/up's
+  int32_t* plan;           // workspace: the gate/up MFMA kernels' items (plan_kernel, see there)
   int32_t* plan_down;      // workspace: the down MFMA kernels' items (chunks of up to 128 routes)
   int plan_max;            // capacity of the item list
   int32_t* rd_list;        // workspace: row-dot experts, most routes first (plan_kernel)
@@ -738,8 +738,8 @@ struct MmTile {
 // second one beside the first ones.  When an XCD has between L and 2L items
 // (one round, some CUs shared), item slot s of the second layer shares the
 // CUs of slot s - L of the first, and the first-layer slots D .. L - 1 (D =
-// items - L) keep their CUs to themselves.  Those go to the D..L-1 longest
-// items (the list runs longest first), so that no long item shares its CUs
+// items - L) keep their CUs to themselves.  Those slots take the L - D
+// longest items (the list runs longest first), so that no long item shares its CUs
 // with another: a CU running two workgroups gives each about half its issue
 // slots, and a long item's partner set the launch's span at 256
 // Zipf-routed tokens.  Returns the list rank of item slot s on XCD xcd; a
