@@ -191,8 +191,9 @@ moe_status moe_router_route_bucket(const uint16_t* x, const float* w_router, con
 /*
  * Bytes of device workspace moe_expert_ffn needs for these sizes (0 when
  * T == 0 or a size is not positive): the per-route intermediates, 2*I + 2*H
- * bytes per route; the dense kernels' work list, 16 bytes for each of at
- * most min(E, T*k) + T*k/128 items (rounded up to a multiple of 8) plus 16;
+ * bytes per route; the dense kernels' two work lists (gate/up and down),
+ * each 16 bytes for each of at most min(E, T*k) + T*k/128 items (rounded up
+ * to a multiple of 8) plus 16;
  * the row-dot kernels' expert list, 4 bytes for each of min(E, T*k)
  * experts plus 4; and the streaming down kernel's unit counters, 9 of them
  * 128 bytes apart (1152 bytes); each region rounded up to 256 bytes.

@@ -167,15 +167,16 @@ def test_step_host_checks(lib):
 
 def _workspace_formula(T, H, I, E, k):
     """moe_expert_ffn_workspace_size as the header states it: h (2*I bytes
-    per route), o (2*H bytes per route), a work list of 16 bytes per item
-    for min(E, T*k) + T*k // 128 items rounded up to 8, plus 16, an expert
+    per route), o (2*H bytes per route), two work lists (gate/up, down) of
+    16 bytes per item for min(E, T*k) + T*k // 128 items rounded up to 8,
+    plus 16, an expert
     list of 4 bytes per slot, min(E, T*k) of them, plus 4, and 9 unit
     counters 128 bytes apart; each region rounded up to 256 bytes."""
     up = lambda v: (v + 255) // 256 * 256
     R = T * k
     items = min(E, R) + R // 128
     items = (items + 7) // 8 * 8
-    return up(R * I * 2) + up(R * H * 2) + up(16 + 16 * items) + up(4 + 4 * min(E, R)) + up(9 * 128)
+    return up(R * I * 2) + up(R * H * 2) + 2 * up(16 + 16 * items) + up(4 + 4 * min(E, R)) + up(9 * 128)
 
 
 def test_workspace_size_formula(lib):
