@@ -2,8 +2,10 @@
 
 A step is one pass of the whole path over one batch: routing (top-k and
 bucketing) and the expert FFN with the weighted unroute.  By default it is
-one moe_step_packed call (moe_route_bucket + moe_expert_ffn: three kernels
-at decode size), the weights also packed once in MFMA tile order at load
+one moe_step_packed call (at decode size two launches: the selection with
+the gate/up projection, then the down projection with the weighted unroute;
+larger batches route, bucket and run the expert kernels), the weights also
+packed once in MFMA tile order at load
 time, outside every timed region (only the MFMA tiles of large batches read
 that copy); --path step runs moe_step on the standard layout alone, --path
 calls_unfused the three separate calls.  Steps are captured in HIP graphs.
@@ -18,7 +20,8 @@ of traffic (the 256 MB MALL would otherwise hold a step's ~69 MB).
 Output: one JSON line.  `value` is the effective HBM bandwidth on unique
 expert bytes (unique experts of the step x 1,769,484 B) divided by the
 measured step time; `us_per_step` is the step time.  `roofline` covers the
-dominant kernel, the gate/up projection: HIP events on its stream around a
+dominant kernel, the selection + gate/up launch at decode size (the gate/up
+projection at larger batches): HIP events on its stream around a
 graph of back-to-back launches of that kernel alone.
 `cpu_baseline` is the fp64 CPU oracle timed on this host on a bounded sample.
 `router` times the router projection that produces the logits
